@@ -1,0 +1,245 @@
+// Host side of the C ABI declared in include/ssd.h: argument validation and
+// kernel dispatch.  Every check runs before anything is enqueued, so an
+// invalid call returns a negative ssd_status and leaves the stream untouched.
+// Megatron-LM #6808 (description section "Not supported yet") likewise refuses
+// unsupported configurations outright instead of computing something wrong.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <utility>
+#include <vector>
+
+#include "ssd_internal.h"
+
+using namespace ssd;
+
+namespace {
+
+bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+// Validates the problem and fills Dims.  Returns SSD_OK or an error.
+int check_problem(const ssd_problem* p, Dims* d) {
+    if (!p) return SSD_ERR_NULL;
+    if (p->batch < 1 || p->seqlen < 1 || p->nheads < 1 || p->headdim < 1 || p->dstate < 1 ||
+        p->ngroups < 1 || p->conv_width < 1)
+        return SSD_ERR_SHAPE;
+    if (p->nheads % p->ngroups != 0) return SSD_ERR_SHAPE;
+    if (p->act_dtype != SSD_F32 && p->act_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (!(p->dt_min >= 0.f) || !(p->dt_max >= p->dt_min)) return SSD_ERR_SHAPE;
+    if (p->chunk != 64 && p->chunk != 128 && p->chunk != 256) return SSD_ERR_UNSUPPORTED;
+    if (p->conv_width > 8) return SSD_ERR_UNSUPPORTED;
+    if (p->seqlen % p->chunk != 0) return SSD_ERR_SHAPE;
+    if (!kernels_supported(p->headdim, p->dstate, p->act_dtype)) return SSD_ERR_UNSUPPORTED;
+    if (!chunk_supported(p->headdim, p->dstate, p->chunk, p->act_dtype)) return SSD_ERR_UNSUPPORTED;
+    const int64_t C = (int64_t)p->nheads * p->headdim + 2LL * p->ngroups * p->dstate;
+    if (C > (1LL << 30) || p->seqlen / p->chunk > (1LL << 30) ||
+        p->batch > 65535 || p->nheads > 65535)
+        return SSD_ERR_SHAPE;
+    d->batch = p->batch;
+    d->L = p->seqlen;
+    d->H = p->nheads;
+    d->P = p->headdim;
+    d->N = p->dstate;
+    d->G = p->ngroups;
+    d->Q = p->chunk;
+    d->W = p->conv_width;
+    d->C = (int)C;
+    d->hpg = p->nheads / p->ngroups;
+    d->nchunk = (int)(p->seqlen / p->chunk);
+    d->nseg = 0;
+    d->dt_min = p->dt_min;
+    d->dt_max = p->dt_max;
+    return SSD_OK;
+}
+
+// Segments must tile [0, L) with chunk-aligned starts and lengths.
+int check_segments(const ssd_segment* segs, int32_t nseg, Dims* d, SegTab* t) {
+    if (!segs) return SSD_ERR_NULL;
+    if (nseg < 1 || nseg > SSD_MAX_SEGMENTS) return SSD_ERR_SEGMENTS;
+    std::vector<std::pair<int64_t, int64_t>> v;
+    int64_t total = 0;
+    std::memset(t, 0, sizeof(*t));
+    for (int i = 0; i < nseg; ++i) {
+        const int64_t s = segs[i].start, l = segs[i].len;
+        if (l < 1 || s < 0 || s + l > d->L || s % d->Q != 0 || l % d->Q != 0)
+            return SSD_ERR_SEGMENTS;
+        v.emplace_back(s, l);
+        total += l;
+        t->start[i] = s;
+        t->len[i] = l;
+    }
+    if (total != d->L) return SSD_ERR_SEGMENTS;
+    std::sort(v.begin(), v.end());
+    int64_t pos = 0;
+    for (auto& e : v) {
+        if (e.first != pos) return SSD_ERR_SEGMENTS;
+        pos += e.second;
+    }
+    t->n = nseg;
+    d->nseg = nseg;
+    return SSD_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_status_string(int status) {
+    switch (status) {
+        case SSD_OK: return "ok";
+        case SSD_ERR_NULL: return "a required pointer is NULL";
+        case SSD_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+        case SSD_ERR_UNSUPPORTED: return "no kernel for this (headdim, dstate, chunk, dtype, conv width)";
+        case SSD_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+        case SSD_ERR_HIP: return "HIP launch error";
+        case SSD_ERR_SEGMENTS: return "segment table does not tile the sequence in chunk units";
+        default: return "unknown status";
+    }
+}
+
+int32_t ssd_abi_version(void) { return 1; }
+
+int32_t ssd_supported(int32_t headdim, int32_t dstate, int32_t act_dtype) {
+    return kernels_supported(headdim, dstate, act_dtype) ? 1 : 0;
+}
+
+size_t ssd_workspace_bytes(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                           int32_t kind) {
+    Dims d;
+    SegTab t;
+    if (check_problem(problem, &d) != SSD_OK) return 0;
+    if (check_segments(segs, nseg, &d, &t) != SSD_OK) return 0;
+    if (kind == SSD_WS_FORWARD) return fwd_ws_layout(d, problem->act_dtype).total;
+    return 0;
+}
+
+int ssd_conv1d_fwd(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                   const void* xBC, const float* conv_w, const int32_t* seq_idx, void* xBC_conv,
+                   void* stream) {
+    Dims d;
+    SegTab t;
+    int rc = check_problem(problem, &d);
+    if (rc) return rc;
+    if ((rc = check_segments(segs, nseg, &d, &t))) return rc;
+    if (!xBC || !conv_w || !xBC_conv) return SSD_ERR_NULL;
+    if (!aligned16(xBC) || !aligned16(conv_w) || !aligned16(seq_idx) || !aligned16(xBC_conv))
+        return SSD_ERR_ALIGN;
+    return hip_status(launch_conv1d_fwd(d, t, problem->act_dtype, xBC, conv_w, seq_idx, xBC_conv,
+                                        (hipStream_t)stream));
+}
+
+namespace {
+int check_states_args(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                      const void* xBC_conv, const void* dt_raw, const float* dt_bias,
+                      const float* A_log, const int32_t* seq_idx, const float* summary,
+                      const void* ws, size_t ws_bytes, Dims* d, SegTab* t) {
+    int rc = check_problem(problem, d);
+    if (rc) return rc;
+    if ((rc = check_segments(segs, nseg, d, t))) return rc;
+    if (!xBC_conv || !dt_raw || !dt_bias || !A_log || !summary) return SSD_ERR_NULL;
+    if (!ws) return SSD_ERR_WORKSPACE;
+    if (ws_bytes < fwd_ws_layout(*d, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
+    if (!aligned16(xBC_conv) || !aligned16(dt_raw) || !aligned16(dt_bias) || !aligned16(A_log) ||
+        !aligned16(seq_idx) || !aligned16(summary) || !aligned16(ws))
+        return SSD_ERR_ALIGN;
+    return SSD_OK;
+}
+
+int check_output_args(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                      const void* xBC_conv, const int32_t* seq_idx, const void* ws,
+                      size_t ws_bytes, const float* y_zero, Dims* d, SegTab* t) {
+    int rc = check_problem(problem, d);
+    if (rc) return rc;
+    if ((rc = check_segments(segs, nseg, d, t))) return rc;
+    if (!xBC_conv || !y_zero) return SSD_ERR_NULL;
+    if (!ws) return SSD_ERR_WORKSPACE;
+    if (ws_bytes < fwd_ws_layout(*d, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
+    if (!aligned16(xBC_conv) || !aligned16(seq_idx) || !aligned16(ws) || !aligned16(y_zero))
+        return SSD_ERR_ALIGN;
+    return SSD_OK;
+}
+}  // namespace
+
+int ssd_segment_states(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                       const void* xBC_conv, const void* dt_raw, const float* dt_bias,
+                       const float* A_log, const int32_t* seq_idx, float* summary, void* ws,
+                       size_t ws_bytes, void* stream) {
+    Dims d;
+    SegTab t;
+    int rc = check_states_args(problem, segs, nseg, xBC_conv, dt_raw, dt_bias, A_log, seq_idx,
+                               summary, ws, ws_bytes, &d, &t);
+    if (rc) return rc;
+    return hip_status(launch_segment_states(d, t, problem->act_dtype, xBC_conv, dt_raw, dt_bias,
+                                            A_log, seq_idx, summary, ws, (hipStream_t)stream));
+}
+
+int ssd_segment_output(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                       const void* xBC_conv, const int32_t* seq_idx, const void* ws,
+                       size_t ws_bytes, float* y_zero, void* stream) {
+    Dims d;
+    SegTab t;
+    int rc = check_output_args(problem, segs, nseg, xBC_conv, seq_idx, ws, ws_bytes, y_zero, &d,
+                               &t);
+    if (rc) return rc;
+    return hip_status(launch_segment_output(d, t, problem->act_dtype, xBC_conv, seq_idx, ws, y_zero,
+                                            (hipStream_t)stream));
+}
+
+int ssd_segment_fwd(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                    const void* xBC_conv, const void* dt_raw, const float* dt_bias,
+                    const float* A_log, const int32_t* seq_idx, float* y_zero, float* summary,
+                    void* ws, size_t ws_bytes, void* stream) {
+    Dims d;
+    SegTab t;
+    int rc = check_states_args(problem, segs, nseg, xBC_conv, dt_raw, dt_bias, A_log, seq_idx,
+                               summary, ws, ws_bytes, &d, &t);
+    if (rc) return rc;
+    if ((rc = check_output_args(problem, segs, nseg, xBC_conv, seq_idx, ws, ws_bytes, y_zero, &d,
+                                &t)))
+        return rc;
+    rc = hip_status(launch_segment_states(d, t, problem->act_dtype, xBC_conv, dt_raw, dt_bias,
+                                          A_log, seq_idx, summary, ws, (hipStream_t)stream));
+    if (rc) return rc;
+    return hip_status(launch_segment_output(d, t, problem->act_dtype, xBC_conv, seq_idx, ws, y_zero,
+                                            (hipStream_t)stream));
+}
+
+int ssd_boundary_scan(const ssd_problem* problem, int32_t nseg, const float* summary,
+                      const float* init, int32_t reverse, float* out, float* final_state,
+                      void* stream) {
+    Dims d;
+    int rc = check_problem(problem, &d);
+    if (rc) return rc;
+    if (nseg < 1 || nseg > SSD_MAX_SEGMENTS) return SSD_ERR_SEGMENTS;
+    if (reverse != 0 && reverse != 1) return SSD_ERR_SHAPE;
+    if (!summary || !out) return SSD_ERR_NULL;
+    if (!aligned16(summary) || !aligned16(init) || !aligned16(out) || !aligned16(final_state))
+        return SSD_ERR_ALIGN;
+    return hip_status(
+        launch_boundary_scan(d, nseg, summary, init, reverse, out, final_state, (hipStream_t)stream));
+}
+
+int ssd_apply_init_state(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                         const float* y_zero, const void* xBC_conv, const float* D,
+                         const int32_t* seq_idx, const float* S_in, const void* ws,
+                         size_t ws_bytes, void* y, void* stream) {
+    Dims d;
+    SegTab t;
+    int rc = check_problem(problem, &d);
+    if (rc) return rc;
+    if ((rc = check_segments(segs, nseg, &d, &t))) return rc;
+    if (!y_zero || !xBC_conv || !D || !S_in || !y) return SSD_ERR_NULL;
+    if (!ws) return SSD_ERR_WORKSPACE;
+    if (ws_bytes < fwd_ws_layout(d, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
+    if (!aligned16(y_zero) || !aligned16(xBC_conv) || !aligned16(D) || !aligned16(seq_idx) ||
+        !aligned16(S_in) || !aligned16(ws) || !aligned16(y))
+        return SSD_ERR_ALIGN;
+    return hip_status(launch_apply_init_state(d, t, problem->act_dtype, y_zero, xBC_conv, D,
+                                              seq_idx, S_in, ws, y, (hipStream_t)stream));
+}
+
+}  // extern "C"

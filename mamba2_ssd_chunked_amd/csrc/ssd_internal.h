@@ -1,0 +1,145 @@
+// Internal types and device helpers shared by the gfx950 kernels of libssd.
+//
+// Everything here is wave64 CDNA4 code: MFMA fragments are built for
+// v_mfma_f32_16x16x32_bf16 (bf16 activations) and v_mfma_f32_16x16x4_f32
+// (float32 activations, four instructions per 16-deep k step).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ssd.h"
+
+namespace ssd {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// Problem sizes as the kernels see them (passed by value).
+struct Dims {
+    int64_t batch, L;  // rows, tokens per row
+    int H, P, N, G, Q, W, C, hpg;
+    int nchunk;        // L / Q
+    int nseg;
+    float dt_min, dt_max;
+};
+
+// Segment table in causal order; start and len in tokens (memory offsets).
+struct SegTab {
+    int64_t start[SSD_MAX_SEGMENTS];
+    int64_t len[SSD_MAX_SEGMENTS];
+    int n;
+};
+
+// Segment holding memory chunk `cm` (chunk index = token offset / Q).
+__device__ __forceinline__ int seg_of_chunk(const SegTab& t, int cm, int Q) {
+    const int64_t tok = (int64_t)cm * Q;
+    int k = 0;
+    for (int i = 0; i < t.n; ++i)
+        if (tok >= t.start[i] && tok < t.start[i] + t.len[i]) k = i;
+    return k;
+}
+
+// Memory position of the token that causally precedes segment k's first token
+// (-1 when k is the row's first segment).
+__device__ __forceinline__ int64_t seg_pred_token(const SegTab& t, int k) {
+    return k > 0 ? t.start[k - 1] + t.len[k - 1] - 1 : -1;
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f(T v) { return (float)v; }
+
+// ---------------------------------------------------------------------------
+// MFMA fragments.
+//
+// A 16x16 output tile lives in one wave: lane l holds column (l % 16) and rows
+// 4*(l/16) + r, r = 0..3 (one f32x4).  For the operands, lane l holds row (A) or
+// column (B) l % 16 and SL "slots" of the k dimension; the k index a slot stands
+// for is the caller's choice, as long as A and B use the same map (the product
+// sums over k, so any common bijection gives the same result).  The "natural"
+// map is k = SL*(l/16) + s, i.e. SL consecutive k per lane (one 16-byte load).
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16> {
+    static constexpr int SL = 8;   // k slots per lane
+    static constexpr int KS = 32;  // k consumed per mma()
+    typedef bf16x8 Frag;
+    __device__ static __forceinline__ f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ Frag load(const bf16* p) { return *(const bf16x8*)p; }
+    // Same as load, scaled by w[s] per slot (rounded to bf16 once).
+    __device__ static __forceinline__ Frag load_scaled(const bf16* p, const float* w) {
+        Frag v = *(const bf16x8*)p;
+        Frag r;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) r[s] = (bf16)((float)v[s] * w[s]);
+        return r;
+    }
+    __device__ static __forceinline__ Frag from_f(const float* f) {
+        Frag r;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) r[s] = (bf16)f[s];
+        return r;
+    }
+};
+
+template <> struct Mma<float> {
+    static constexpr int SL = 4;
+    static constexpr int KS = 16;
+    typedef f32x4 Frag;
+    __device__ static __forceinline__ f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+        return c;
+    }
+    __device__ static __forceinline__ Frag load(const float* p) { return *(const f32x4*)p; }
+    __device__ static __forceinline__ Frag load_scaled(const float* p, const float* w) {
+        f32x4 v = *(const f32x4*)p;
+        return f32x4{v[0] * w[0], v[1] * w[1], v[2] * w[2], v[3] * w[3]};
+    }
+    __device__ static __forceinline__ Frag from_f(const float* f) {
+        return f32x4{f[0], f[1], f[2], f[3]};
+    }
+};
+
+// Host-side launchers (defined in the .hip files).  Each returns hipSuccess or
+// the launch error.
+hipError_t launch_conv1d_fwd(const Dims& d, const SegTab& t, int act, const void* xBC,
+                             const float* w, const int32_t* seq, void* out, hipStream_t s);
+hipError_t launch_segment_states(const Dims& d, const SegTab& t, int act, const void* xBC_conv,
+                                 const void* dt_raw, const float* dt_bias, const float* A_log,
+                                 const int32_t* seq, float* summary, void* ws, hipStream_t s);
+hipError_t launch_segment_output(const Dims& d, const SegTab& t, int act, const void* xBC_conv,
+                                 const int32_t* seq, const void* ws, float* y_zero,
+                                 hipStream_t s);
+hipError_t launch_boundary_scan(const Dims& d, int nseg, const float* summary, const float* init,
+                                int reverse, float* out, float* final_state, hipStream_t s);
+hipError_t launch_apply_init_state(const Dims& d, const SegTab& t, int act, const float* y_zero,
+                                   const void* xBC_conv, const float* D, const int32_t* seq,
+                                   const float* S_in, const void* ws, void* y, hipStream_t s);
+bool kernels_supported(int P, int N, int act);
+bool chunk_supported(int P, int N, int Q, int act);
+
+// Forward workspace layout (byte offsets), shared by the host code and launchers.
+struct FwdWs {
+    size_t dt, cs, ctot, hst, total;
+};
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline FwdWs fwd_ws_layout(const Dims& d, int act) {
+    FwdWs w;
+    const size_t esz = act == SSD_BF16 ? 2 : 4;
+    const size_t bhl = (size_t)d.batch * d.H * d.L;
+    w.dt = 0;
+    w.cs = align256(w.dt + bhl * 4);
+    w.ctot = align256(w.cs + bhl * 4);
+    w.hst = align256(w.ctot + (size_t)d.batch * d.H * d.nchunk * 4);
+    w.total = align256(w.hst + (size_t)d.batch * d.nchunk * d.H * d.P * d.N * esz);
+    return w;
+}
+
+}  // namespace ssd

@@ -23,7 +23,7 @@
  *   A       = -exp(A_log[h])
  *   a_t     = exp(dt_t * A), or exactly 0 when token t starts a new packed
  *             sequence (seq_idx[t] != seq_idx[t-1]); the NeMo Automodel pull
- *             request #1441 ("feat: context-parallel with nemotron v3", Key
+ *             request #1441 (context parallelism for Nemotron v3, section Key
  *             changes) derives seq_idx from cu_seqlens for exactly these resets
  *   h_t     = a_t * h_{t-1} + dt_t * x_t (outer) B_t          h_{-1} = init (0)
  *   y_t     = h_t C_t + D[h] * x_t

@@ -34,11 +34,13 @@ DT_MAX = 0.1
 
 def round_to_bf16(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even), kept as float32."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    bias = ((u >> np.uint64(16)) & np.uint64(1)) + np.uint64(0x7FFF)
-    r = ((u + bias) >> np.uint64(16)) << np.uint64(16)
-    return r.astype(np.uint32).view(np.float32)
+    # Finite float32 bit patterns stay below 2**32 after adding at most 0x8000.
+    u = np.array(a, dtype=np.float32, copy=True).view(np.uint32)
+    bias = (u >> np.uint32(16)) & np.uint32(1)
+    bias += np.uint32(0x7FFF)
+    u += bias
+    u &= np.uint32(0xFFFF0000)
+    return u.view(np.float32)
 
 
 def _inv_softplus(y: np.ndarray) -> np.ndarray:
@@ -154,21 +156,27 @@ def make_workload(name: str, *, batch: int, seqlen: int, nheads: int, headdim: i
                   act: str = "bf16", nseg: int = 1, layout: str = "contiguous",
                   seed: int = 0, packed: Optional[Tuple[int, int]] = None,
                   lengths: Optional[List[int]] = None, slow_decay: bool = False,
-                  with_dy: bool = False) -> Workload:
+                  with_dy: bool = False, seg_lens: Optional[List[int]] = None) -> Workload:
     """Build a seeded workload.
 
     ``packed=(lo, hi)`` draws packed sequence lengths U[lo, hi] over each row
     (the same lengths for every row); ``lengths`` gives them explicitly.
     ``nseg`` is the number of causal segments.  With ``layout="virtual"`` it
     must be even and memory holds the balanced front/back order with
-    cp = nseg // 2 (see ``virtual_layout``).
+    cp = nseg // 2 (see ``virtual_layout``).  ``seg_lens`` gives contiguous
+    segments of unequal lengths instead.
     """
     rng = np.random.default_rng(seed)
     H, P, N, G, W = nheads, headdim, dstate, ngroups, conv_width
     C = H * P + 2 * G * N
     L = seqlen
 
-    if layout == "contiguous":
+    if seg_lens is not None:
+        assert layout == "contiguous" and sum(seg_lens) == L
+        starts = np.concatenate([[0], np.cumsum(seg_lens)[:-1]])
+        segs = [(int(a), int(n)) for a, n in zip(starts, seg_lens)]
+        perm = np.arange(L, dtype=np.int64)
+    elif layout == "contiguous":
         segs = contiguous_segments(L, nseg)
         perm = np.arange(L, dtype=np.int64)
     elif layout == "virtual":

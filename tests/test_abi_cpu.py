@@ -1,0 +1,142 @@
+"""C ABI checks that need no GPU: exports, host-side validation, workspace sizes.
+
+Every call here is made with arguments that fail validation, so the library
+returns an error before touching the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba2_ssd_chunked_amd as ssd
+from mamba2_ssd_chunked_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(ssd_\w+)\s*\(", text))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib.load()
+    names = _declared()
+    assert {"ssd_conv1d_fwd", "ssd_segment_fwd", "ssd_boundary_scan",
+            "ssd_apply_init_state"} <= names
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"{n} has no ctypes signature"
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(_lib.Problem) == 56
+    assert ctypes.sizeof(_lib.Segment) == 16
+
+
+def _p(**kw):
+    base = dict(batch=2, seqlen=8192, nheads=32, headdim=64, dstate=128, ngroups=1, chunk=256,
+                conv_width=4, act="bf16")
+    base.update(kw)
+    return ssd.make_problem(**base)
+
+
+SEGS8 = [(i * 1024, 1024) for i in range(8)]
+FAKE = ctypes.c_void_p(0x100000)       # never dereferenced: every call below fails validation
+MISALIGNED = ctypes.c_void_p(0x100004)
+
+
+def _conv(p, segs, xbc=FAKE, w=FAKE, seq=None, out=FAKE):
+    s = ssd.Segments(segs)
+    return _lib.load().ssd_conv1d_fwd(ctypes.byref(p) if p is not None else None, s.ptr(), s.n,
+                                      xbc, w, seq, out, None)
+
+
+def test_workspace_bytes():
+    p = _p()
+    b, H, L, nc, P, N = 2, 32, 8192, 32, 64, 128
+    al = lambda x: (x + 255) // 256 * 256
+    want = al(al(al(b * H * L * 4) + b * H * L * 4) + b * H * nc * 4)
+    want = al(want + b * nc * H * P * N * 2)
+    assert ssd.ssd_workspace_bytes(p, SEGS8) == want
+    assert ssd.ssd_workspace_bytes(p, SEGS8, kind=7) == 0
+    assert ssd.ssd_workspace_bytes(_p(chunk=100), SEGS8) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nheads=30, ngroups=4), -2),
+    (dict(chunk=96), -3),
+    (dict(conv_width=9), -3),
+    (dict(headdim=48), -3),
+    (dict(act=5), -3),
+    (dict(seqlen=8000), -2),
+    (dict(batch=0), -2),
+])
+def test_problem_validation(kw, code):
+    assert _conv(_p(**kw), SEGS8) == code
+
+
+def test_null_and_alignment():
+    assert _lib.load().ssd_conv1d_fwd(None, ssd.Segments(SEGS8).ptr(), 8, FAKE, FAKE, None, FAKE,
+                                      None) == -1
+    assert _conv(_p(), SEGS8, xbc=None) == -1
+    assert _conv(_p(), SEGS8, out=MISALIGNED) == -4
+    assert _conv(_p(), SEGS8, seq=MISALIGNED) == -4
+
+
+@pytest.mark.parametrize("segs", [
+    [(i * 1024, 1024) for i in range(7)],                        # does not cover
+    [(0, 1024)] * 8,                                             # overlapping
+    [(i * 1024 + 128, 1024) for i in range(8)],                  # out of range
+    [(0, 1000), (1000, 7192)],                                   # not chunk aligned
+    [(i * 128, 128) for i in range(64)] + [(8192, 0)],           # too many segments / empty
+])
+def test_segment_validation(segs):
+    assert _conv(_p(), segs) == -7
+
+
+def test_workspace_too_small_enqueues_nothing():
+    p = _p()
+    s = ssd.Segments(SEGS8)
+    lib = _lib.load()
+    need = ssd.ssd_workspace_bytes(p, SEGS8)
+    rc = lib.ssd_segment_fwd(ctypes.byref(p), s.ptr(), s.n, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                             FAKE, FAKE, need - 1, None)
+    assert rc == -5
+    rc = lib.ssd_apply_init_state(ctypes.byref(p), s.ptr(), s.n, FAKE, FAKE, FAKE, None, FAKE,
+                                  None, need, FAKE, None)
+    assert rc == -5
+
+
+def test_boundary_scan_validation():
+    lib = _lib.load()
+    p = _p()
+    assert lib.ssd_boundary_scan(ctypes.byref(p), 0, FAKE, None, 0, FAKE, None, None) == -7
+    assert lib.ssd_boundary_scan(ctypes.byref(p), 65, FAKE, None, 0, FAKE, None, None) == -7
+    assert lib.ssd_boundary_scan(ctypes.byref(p), 8, FAKE, None, 2, FAKE, None, None) == -2
+    assert lib.ssd_boundary_scan(ctypes.byref(p), 8, None, None, 0, FAKE, None, None) == -1
+    assert lib.ssd_boundary_scan(ctypes.byref(p), 8, FAKE, MISALIGNED, 0, FAKE, None, None) == -4
+
+
+def test_status_strings_and_support():
+    lib = _lib.load()
+    for code in range(-7, 1):
+        assert lib.ssd_status_string(code)
+    assert lib.ssd_supported(64, 128, 1) == 1
+    assert lib.ssd_supported(16, 16, 0) == 1
+    assert lib.ssd_supported(16, 16, 1) == 0
+    assert lib.ssd_abi_version() >= 1
+
+
+def test_binding_rejects_wrong_sizes_before_the_library():
+    import torch
+    p = _p(batch=1, seqlen=256, nheads=2, headdim=16, dstate=16, chunk=64, act="f32")
+    x = torch.zeros(10)
+    with pytest.raises(ValueError):
+        ssd.ssd_conv1d_fwd(p, [(0, 256)], x, x, None, x)
