@@ -49,13 +49,18 @@ template <> struct KPerm<float> {
 };
 
 // ---------------------------------------------------------------------------
+// The cumsum restarts at every packed-sequence start inside the chunk (a
+// segmented scan), so a sequence's decays are computed from its own tokens
+// only and perturbing one sequence cannot change another's bits.
 template <typename T>
 __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ dt_raw,
                                                 const float* __restrict__ dt_bias,
                                                 const float* __restrict__ A_log,
+                                                const int32_t* __restrict__ seq,
                                                 float* __restrict__ dt_ws, float* __restrict__ cs_ws,
                                                 float* __restrict__ ctot) {
     __shared__ float raw[256][17];
+    __shared__ int sseq[256];
     const int cm = blockIdx.x, h0 = blockIdx.y * 16;
     const int64_t b = blockIdx.z;
     const int Q = d.Q;
@@ -65,9 +70,20 @@ __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ d
         const int j = idx / 16, hh = idx % 16;
         raw[j][hh] = hh < nh ? to_f(dt_raw[(b * d.L + tok0 + j) * d.H + h0 + hh]) : 0.f;
     }
+    for (int j = threadIdx.x; j < Q; j += blockDim.x) sseq[j] = seq ? seq[b * d.L + tok0 + j] : 0;
     __syncthreads();
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int E = Q / 64;  // tokens per lane (1, 2 or 4)
+    bool rs[4];            // a sequence starts at or before this token, inside this lane
+    bool lflag = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (e < E) {
+            const int j = lane * E + e;
+            lflag = lflag || (j > 0 && sseq[j] != sseq[j - 1]);
+            rs[e] = lflag;
+        }
+    }
     for (int hh = wave; hh < nh; hh += 4) {
         const int h = h0 + hh;
         const float A = -expf(A_log[h]);
@@ -77,30 +93,40 @@ __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ d
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             if (e < E) {
-                const float z = raw[lane * E + e][hh] + bias;
+                const int j = lane * E + e;
+                if (j > 0 && sseq[j] != sseq[j - 1]) run = 0.f;
+                const float z = raw[j][hh] + bias;
                 const float dt = fminf(fmaxf(softplus_f(z), d.dt_min), d.dt_max);
                 dtv[e] = dt;
                 run += dt * A;
                 csl[e] = run;
             }
         }
-        float incl = run;
+        // Segmented inclusive scan of (flag, sum) across the wave:
+        // (f1, v1) then (f2, v2) -> (f1 | f2, f2 ? v2 : v1 + v2).
+        float iv = run;
+        bool ifl = lflag;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += y;
+            const float v = __shfl_up(iv, off, 64);
+            const int f = __shfl_up((int)ifl, off, 64);
+            if (lane >= off) {
+                if (!ifl) iv += v;
+                ifl = ifl || f;
+            }
         }
-        const float excl = incl - run;
+        float ev = __shfl_up(iv, 1, 64);
+        if (lane == 0) ev = 0.f;
         float* dtp = dt_ws + ((int64_t)b * d.H + h) * d.L + tok0;
         float* csp = cs_ws + ((int64_t)b * d.H + h) * d.L + tok0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             if (e < E) {
                 dtp[lane * E + e] = dtv[e];
-                csp[lane * E + e] = excl + csl[e];
+                csp[lane * E + e] = rs[e] ? csl[e] : ev + csl[e];
             }
         }
-        if (lane == 63) ctot[((int64_t)b * d.H + h) * d.nchunk + cm] = incl;
+        if (lane == 63) ctot[((int64_t)b * d.H + h) * d.nchunk + cm] = iv;
     }
 }
 
@@ -147,8 +173,11 @@ __global__ void __launch_bounds__(256) k_state_fwd(Dims d, SegTab tab, const T* 
         const int cm = (int)(t0 / Q);
         const float cs_e = csp[t0 + Q - 1];
         const int seq_e = seq ? seq[rb + t0 + Q - 1] : 0;
-        const int64_t ptok = c > 0 ? t0 - 1 : pred;
-        const bool cont = ptok < 0 || !seq || seq[rb + ptok] == seq_e;
+        // The state entering chunk c belongs to the sequence of the token just
+        // before it; for a row's first segment that is the sequence of the
+        // row's first token (an initial state feeds the first sequence).
+        const int64_t ptok = c > 0 ? t0 - 1 : (pred >= 0 ? pred : s0);
+        const bool cont = !seq || seq[rb + ptok] == seq_e;
         const float alpha = cont ? expf(cs_e) : 0.f;
         ablk *= alpha;
         if (c > 0) {
@@ -482,7 +511,7 @@ static void segment_states_t(const Dims& d, const SegTab& t, const void* xc_, co
     T* hst = (T*)(w + L.hst);
     hipLaunchKernelGGL(k_dt_prep<T>, dim3((unsigned)d.nchunk, (unsigned)((d.H + 15) / 16),
                                           (unsigned)d.batch),
-                       dim3(256), 0, s, d, (const T*)dt_raw, dt_bias, A_log, dtw, csw, ctot);
+                       dim3(256), 0, s, d, (const T*)dt_raw, dt_bias, A_log, seq, dtw, csw, ctot);
     hipLaunchKernelGGL((k_state_fwd<T, P, N>), dim3((unsigned)d.H, (unsigned)d.nseg,
                                                     (unsigned)d.batch),
                        dim3(256), 0, s, d, t, xc, dtw, csw, seq, hst, summary);

@@ -68,9 +68,10 @@ def test_conv(small_run):
     wl, p, x, bufs = small_run
     g = wl.to_causal(to_np(bufs.xBC_conv))
     o = oracle_v(wl)
+    # float32: fp32 accumulation error only; bf16: plus one rounding to bf16 (2^-9 relative)
     tol = 1e-5 if wl.act == "f32" else 2.0 ** -8
-    err = np.max(np.abs(g - o) / (np.abs(o) + 1e-3))
-    log(f"  conv max rel err {err:.3e}")
+    err = err_fp32(g, o)
+    log(f"  conv max rel err (floored at RMS) {err:.3e}")
     assert err <= tol
 
 
@@ -84,10 +85,12 @@ def test_summaries_and_zero_state_output(small_run):
     a_blk = summ[S * b * H * P * N:].reshape(S, b, H)
     yz = wl.to_causal(to_np(bufs.y_zero))
     seq = wl.causal_seq_idx()
+    v_no_x = v.copy()
+    v_no_x[..., :H * P] = 0.0  # with x = 0 the final state is exactly a_block * init
     for k, (a, e) in enumerate(causal_ranges(wl)):
         y0, f0 = oracle_segment(wl, v, k)
-        _, f1 = oracle_segment(wl, v, k, init=np.ones((b, H, P, N)))
-        a_ref = (f1 - f0)[:, :, 0, 0]
+        _, f1 = oracle_segment(wl, v_no_x, k, init=np.ones((b, H, P, N)))
+        a_ref = f1[:, :, 0, 0]
         assert_close(S_ext[k], f0, wl.act, f"S_ext[{k}]")
         assert_close(yz[:, a:e], y0, wl.act, f"y_zero[{k}]")
         np.testing.assert_allclose(a_blk[k], a_ref, rtol=1e-4, atol=1e-30)
