@@ -191,6 +191,42 @@ int ssd_apply_init_state(const ssd_problem* problem, const ssd_segment* segs, in
                          const int32_t* seq_idx, const float* S_in, const void* ws,
                          size_t ws_bytes, void* y, void* stream);
 
+/* Backward, summary phase.  Recomputes the conv output, dt and the
+ * cumulative decays into `ws` (sequence-length-sized intermediates are
+ * recomputed, never saved from the forward), then walks every segment's chunks
+ * in reverse causal order carrying the state gradient.  Writes, in the summary
+ * layout of ssd_segment_fwd:
+ *   M[k] = dL/dS_in[k] caused by segment k's own outputs   [nseg][batch][H][P][N]
+ *   a[k] = segment k's block decay                          [nseg][batch][H]
+ * ssd_boundary_scan(reverse = 1) over this summary then yields every segment's
+ * final-state gradient dS_out.
+ *   xBC, conv_w, dt_raw, dt_bias, A_log, seq_idx   forward inputs           (in)
+ *   dy        [batch][seqlen][H][P] act_dtype                                (in)
+ *   summary   float32, summary layout                                        (out)
+ *   ws        ssd_workspace_bytes(..., SSD_WS_BACKWARD) bytes                (out) */
+int ssd_segment_bwd_summary(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                            const void* xBC, const float* conv_w, const void* dt_raw,
+                            const float* dt_bias, const float* A_log, const int32_t* seq_idx,
+                            const void* dy, float* summary, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Backward, segment phase: every gradient of the path.
+ *   S_in      [nseg][batch][H][P][N] float32: initial states from the forward
+ *             boundary scan (segment-count sized, so it may be kept)         (in)
+ *   dS_out    [nseg][batch][H][P][N] float32: final-state gradients from the
+ *             reverse boundary scan                                          (in)
+ *   ws        the workspace ssd_segment_bwd_summary filled                   (in/out)
+ *   dxBC      [batch][seqlen][C] act_dtype                                   (out)
+ *   ddt_raw   [batch][seqlen][H] act_dtype                                   (out)
+ *   dconv_w   [C][W], ddt_bias [H], dA_log [H], dD [H] float32, summed over
+ *             every row and segment of this call                             (out) */
+int ssd_segment_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                    const void* xBC, const float* conv_w, const void* dt_raw, const float* dt_bias,
+                    const float* A_log, const float* D, const int32_t* seq_idx, const void* dy,
+                    const float* S_in, const float* dS_out, void* ws, size_t ws_bytes, void* dxBC,
+                    void* ddt_raw, float* dconv_w, float* ddt_bias, float* dA_log, float* dD,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,6 +52,11 @@ SIGNATURES = {
     "ssd_segment_output": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp,
                                           _vp]),
     "ssd_boundary_scan": (ctypes.c_int, [_PP, _i32, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "ssd_segment_bwd_summary": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                               _vp, _vp, ctypes.c_size_t, _vp]),
+    "ssd_segment_bwd": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _vp, _vp, ctypes.c_size_t, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _vp]),
     "ssd_apply_init_state": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                             ctypes.c_size_t, _vp, _vp]),
 }

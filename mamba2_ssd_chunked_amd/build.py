@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["ssd_api.cpp", "conv1d.hip", "ssd_fwd.hip", "scan.hip"]
+SOURCES = ["ssd_api.cpp", "conv1d.hip", "ssd_fwd.hip", "scan.hip", "ssd_bwd.hip"]
 
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -114,6 +114,10 @@ size_t ssd_workspace_bytes(const ssd_problem* problem, const ssd_segment* segs, 
     if (check_problem(problem, &d) != SSD_OK) return 0;
     if (check_segments(segs, nseg, &d, &t) != SSD_OK) return 0;
     if (kind == SSD_WS_FORWARD) return fwd_ws_layout(d, problem->act_dtype).total;
+    if (kind == SSD_WS_BACKWARD) {
+        if (!bwd_supported(d.P, d.N, d.Q, problem->act_dtype)) return 0;
+        return bwd_ws_layout(d, problem->act_dtype).total;
+    }
     return 0;
 }
 
@@ -240,6 +244,62 @@ int ssd_apply_init_state(const ssd_problem* problem, const ssd_segment* segs, in
         return SSD_ERR_ALIGN;
     return hip_status(launch_apply_init_state(d, t, problem->act_dtype, y_zero, xBC_conv, D,
                                               seq_idx, S_in, ws, y, (hipStream_t)stream));
+}
+
+int ssd_segment_bwd_summary(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                            const void* xBC, const float* conv_w, const void* dt_raw,
+                            const float* dt_bias, const float* A_log, const int32_t* seq_idx,
+                            const void* dy, float* summary, void* ws, size_t ws_bytes,
+                            void* stream) {
+    Dims d;
+    SegTab t;
+    int rc = check_problem(problem, &d);
+    if (rc) return rc;
+    if ((rc = check_segments(segs, nseg, &d, &t))) return rc;
+    if (!bwd_supported(d.P, d.N, d.Q, problem->act_dtype)) return SSD_ERR_UNSUPPORTED;
+    if (!xBC || !conv_w || !dt_raw || !dt_bias || !A_log || !dy || !summary) return SSD_ERR_NULL;
+    if (!ws) return SSD_ERR_WORKSPACE;
+    if (ws_bytes < bwd_ws_layout(d, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
+    if (!aligned16(xBC) || !aligned16(conv_w) || !aligned16(dt_raw) || !aligned16(dt_bias) ||
+        !aligned16(A_log) || !aligned16(seq_idx) || !aligned16(dy) || !aligned16(summary) ||
+        !aligned16(ws))
+        return SSD_ERR_ALIGN;
+    BwdArgs ar = {};
+    ar.xBC = xBC;
+    ar.conv_w = conv_w;
+    ar.dt_raw = dt_raw;
+    ar.dt_bias = dt_bias;
+    ar.A_log = A_log;
+    ar.seq = seq_idx;
+    ar.dy = dy;
+    return hip_status(launch_bwd_summary(d, t, problem->act_dtype, ar, summary, ws,
+                                         (hipStream_t)stream));
+}
+
+int ssd_segment_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                    const void* xBC, const float* conv_w, const void* dt_raw, const float* dt_bias,
+                    const float* A_log, const float* D, const int32_t* seq_idx, const void* dy,
+                    const float* S_in, const float* dS_out, void* ws, size_t ws_bytes, void* dxBC,
+                    void* ddt_raw, float* dconv_w, float* ddt_bias, float* dA_log, float* dD,
+                    void* stream) {
+    Dims d;
+    SegTab t;
+    int rc = check_problem(problem, &d);
+    if (rc) return rc;
+    if ((rc = check_segments(segs, nseg, &d, &t))) return rc;
+    if (!bwd_supported(d.P, d.N, d.Q, problem->act_dtype)) return SSD_ERR_UNSUPPORTED;
+    if (!xBC || !conv_w || !dt_raw || !dt_bias || !A_log || !D || !dy || !S_in || !dS_out ||
+        !dxBC || !ddt_raw || !dconv_w || !ddt_bias || !dA_log || !dD)
+        return SSD_ERR_NULL;
+    if (!ws) return SSD_ERR_WORKSPACE;
+    if (ws_bytes < bwd_ws_layout(d, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
+    const void* ptrs[] = {xBC, conv_w, dt_raw, dt_bias, A_log, D, seq_idx, dy, S_in, dS_out,
+                          ws, dxBC, ddt_raw, dconv_w, ddt_bias, dA_log, dD};
+    for (const void* q : ptrs)
+        if (!aligned16(q)) return SSD_ERR_ALIGN;
+    BwdArgs ar = {xBC, conv_w, dt_raw, dt_bias, A_log, D, seq_idx, dy, S_in, dS_out,
+                  dxBC, ddt_raw, dconv_w, ddt_bias, dA_log, dD};
+    return hip_status(launch_segment_bwd(d, t, problem->act_dtype, ar, ws, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -3,8 +3,8 @@
 // Kernels, in launch order:
 //   k_dt_prep      dt = clamp(softplus(dt_raw + dt_bias)), l = dt*A, and the
 //                  chunk-local inclusive cumsum cs of l, per (row, head, chunk).
-//   k_state_fwd    one workgroup per (row, segment, head) walks the segment's
-//                  chunks in causal order.  The running state H (P x N, FP32)
+//   k_state_walk   (state_walk.h) one workgroup per (row, segment, head) walks
+//                  the segment's chunks in causal order.  The running state H (P x N, FP32)
 //                  lives in MFMA accumulators: for chunk c it first writes H
 //                  (the state entering c), scales it by the chunk decay
 //                  alpha_c = exp(cs_end) (exactly 0 across a sequence start)
@@ -26,6 +26,7 @@
 #include <type_traits>
 
 #include "ssd_internal.h"
+#include "state_walk.h"
 
 namespace ssd {
 
@@ -128,138 +129,6 @@ __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ d
         }
         if (lane == 63) ctot[((int64_t)b * d.H + h) * d.nchunk + cm] = iv;
     }
-}
-
-// ---------------------------------------------------------------------------
-template <typename T, int P, int N>
-__global__ void __launch_bounds__(256) k_state_fwd(Dims d, SegTab tab, const T* __restrict__ xc,
-                                                  const float* __restrict__ dt_ws,
-                                                  const float* __restrict__ cs_ws,
-                                                  const int32_t* __restrict__ seq,
-                                                  T* __restrict__ hst, float* __restrict__ summary) {
-    typedef Mma<T> M;
-    typedef typename M::Frag Frag;
-    constexpr int SL = M::SL, KS = M::KS;
-    constexpr int KT = 64;                  // tokens per LDS slice
-    constexpr int VEC = 16 / sizeof(T);     // elements per 16-byte load
-    constexpr int PITCH = KT + VEC;         // padded LDS row (keeps 16-byte alignment)
-    constexpr int PT = P / 16, NTT = N / 16, NTW = (NTT + 3) / 4;
-    __shared__ __attribute__((aligned(16))) T Xt[P * PITCH];
-    __shared__ __attribute__((aligned(16))) T Bt[N * PITCH];
-    __shared__ float wv[KT];
-
-    const int h = blockIdx.x, k = blockIdx.y;
-    const int64_t b = blockIdx.z;
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
-    const int g = h / d.hpg;
-    const int Q = d.Q;
-    const int64_t rb = b * d.L;
-    const int64_t s0 = tab.start[k];
-    const int nc = (int)(tab.len[k] / Q);
-    const int64_t pred = seg_pred_token(tab, k);
-    const float* dtp = dt_ws + ((int64_t)b * d.H + h) * d.L;
-    const float* csp = cs_ws + ((int64_t)b * d.H + h) * d.L;
-    const int64_t xoff = (int64_t)h * P, boff = (int64_t)d.H * P + (int64_t)g * N;
-
-    f32x4 acc[PT][NTW];
-#pragma unroll
-    for (int i = 0; i < PT; ++i)
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float ablk = 1.f;
-
-    for (int c = 0; c < nc; ++c) {
-        const int64_t t0 = s0 + (int64_t)c * Q;
-        const int cm = (int)(t0 / Q);
-        const float cs_e = csp[t0 + Q - 1];
-        const int seq_e = seq ? seq[rb + t0 + Q - 1] : 0;
-        // The state entering chunk c belongs to the sequence of the token just
-        // before it; for a row's first segment that is the sequence of the
-        // row's first token (an initial state feeds the first sequence).
-        const int64_t ptok = c > 0 ? t0 - 1 : (pred >= 0 ? pred : s0);
-        const bool cont = !seq || seq[rb + ptok] == seq_e;
-        const float alpha = cont ? expf(cs_e) : 0.f;
-        ablk *= alpha;
-        if (c > 0) {
-            // H entering chunk c, then H <- alpha H.
-            T* hp = hst + (((int64_t)b * d.nchunk + cm) * d.H + h) * (P * N);
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                for (int j = 0; j < NTW; ++j) {
-                    const int nt = wave + 4 * j;
-                    if (nt < NTT) {
-                        const int n = nt * 16 + lr;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int p = pt * 16 + 4 * lg + r;
-                            hp[p * N + n] = (T)acc[pt][j][r];
-                            acc[pt][j][r] *= alpha;
-                        }
-                    }
-                }
-        }
-        for (int sl = 0; sl < Q / KT; ++sl) {
-            const int64_t tb = t0 + (int64_t)sl * KT;
-            __syncthreads();
-            for (int idx = threadIdx.x; idx < KT * (P / VEC); idx += blockDim.x) {
-                const int jj = idx / (P / VEC), pv = idx % (P / VEC);
-                typedef T vt __attribute__((ext_vector_type(VEC)));
-                const vt v = *(const vt*)(xc + (rb + tb + jj) * d.C + xoff + pv * VEC);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) Xt[(pv * VEC + e) * PITCH + jj] = v[e];
-            }
-            for (int idx = threadIdx.x; idx < KT * (N / VEC); idx += blockDim.x) {
-                const int jj = idx / (N / VEC), nv = idx % (N / VEC);
-                typedef T vt __attribute__((ext_vector_type(VEC)));
-                const vt v = *(const vt*)(xc + (rb + tb + jj) * d.C + boff + nv * VEC);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) Bt[(nv * VEC + e) * PITCH + jj] = v[e];
-            }
-            if (threadIdx.x < KT) {
-                const int64_t tok = tb + threadIdx.x;
-                const bool same = !seq || seq[rb + tok] == seq_e;
-                wv[threadIdx.x] = same ? expf(cs_e - csp[tok]) * dtp[tok] : 0.f;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int kk = 0; kk < KT / KS; ++kk) {
-                const int jl = kk * KS + SL * lg;
-                float wl[SL];
-#pragma unroll
-                for (int s = 0; s < SL; ++s) wl[s] = wv[jl + s];
-                Frag a[PT];
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-                    a[pt] = M::load_scaled(&Xt[(pt * 16 + lr) * PITCH + jl], wl);
-#pragma unroll
-                for (int j = 0; j < NTW; ++j) {
-                    const int nt = wave + 4 * j;
-                    if (nt < NTT) {
-                        const Frag bb = M::load(&Bt[(nt * 16 + lr) * PITCH + jl]);
-#pragma unroll
-                        for (int pt = 0; pt < PT; ++pt) acc[pt][j] = M::mma(a[pt], bb, acc[pt][j]);
-                    }
-                }
-            }
-        }
-    }
-
-    const int64_t per = (int64_t)d.batch * d.H * P * N;
-    float* sx = summary + (int64_t)k * per + ((int64_t)b * d.H + h) * (P * N);
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-            const int nt = wave + 4 * j;
-            if (nt < NTT) {
-                const int n = nt * 16 + lr;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sx[(pt * 16 + 4 * lg + r) * N + n] = acc[pt][j][r];
-            }
-        }
-    if (threadIdx.x == 0)
-        summary[(int64_t)d.nseg * per + ((int64_t)k * d.batch + b) * d.H + h] = ablk;
 }
 
 // ---------------------------------------------------------------------------
@@ -509,12 +378,11 @@ static void segment_states_t(const Dims& d, const SegTab& t, const void* xc_, co
     float* csw = (float*)(w + L.cs);
     float* ctot = (float*)(w + L.ctot);
     T* hst = (T*)(w + L.hst);
-    hipLaunchKernelGGL(k_dt_prep<T>, dim3((unsigned)d.nchunk, (unsigned)((d.H + 15) / 16),
-                                          (unsigned)d.batch),
-                       dim3(256), 0, s, d, (const T*)dt_raw, dt_bias, A_log, seq, dtw, csw, ctot);
-    hipLaunchKernelGGL((k_state_fwd<T, P, N>), dim3((unsigned)d.H, (unsigned)d.nseg,
-                                                    (unsigned)d.batch),
-                       dim3(256), 0, s, d, t, xc, dtw, csw, seq, hst, summary);
+    launch_dt_prep(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32, dt_raw, dt_bias, A_log,
+                   seq, dtw, csw, ctot, s);
+    hipLaunchKernelGGL((k_state_walk<T, P, N, WALK_FWD_PN>),
+                       dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0, s,
+                       d, t, xc, (int64_t)d.C, xc, (int64_t)d.H * P, dtw, csw, seq, hst, summary);
 }
 
 template <typename T, int P, int N>
@@ -543,6 +411,19 @@ static void apply_init_t(const Dims& d, const SegTab& t, const float* y_zero, co
                                                      (unsigned)d.batch),
                        dim3(256), 0, s, d, t, y_zero, (const T*)xc, D, seq, S_in,
                        (const float*)(w + L.cs), (const float*)(w + L.ctot), (T*)y);
+}
+
+hipError_t launch_dt_prep(const Dims& d, int act, const void* dt_raw, const float* dt_bias,
+                          const float* A_log, const int32_t* seq, float* dt_ws, float* cs_ws,
+                          float* ctot, hipStream_t s) {
+    const dim3 grid((unsigned)d.nchunk, (unsigned)((d.H + 15) / 16), (unsigned)d.batch);
+    if (act == SSD_BF16)
+        hipLaunchKernelGGL(k_dt_prep<bf16>, grid, dim3(256), 0, s, d, (const bf16*)dt_raw, dt_bias,
+                           A_log, seq, dt_ws, cs_ws, ctot);
+    else
+        hipLaunchKernelGGL(k_dt_prep<float>, grid, dim3(256), 0, s, d, (const float*)dt_raw,
+                           dt_bias, A_log, seq, dt_ws, cs_ws, ctot);
+    return hipGetLastError();
 }
 
 // (P, N) pairs with kernels.  bf16 needs N % 32 == 0 (one MFMA consumes 32 of k).

@@ -123,6 +123,30 @@ hipError_t launch_apply_init_state(const Dims& d, const SegTab& t, int act, cons
                                    const void* xBC_conv, const float* D, const int32_t* seq,
                                    const float* S_in, const void* ws, void* y, hipStream_t s);
 bool kernels_supported(int P, int N, int act);
+hipError_t launch_dt_prep(const Dims& d, int act, const void* dt_raw, const float* dt_bias,
+                          const float* A_log, const int32_t* seq, float* dt_ws, float* cs_ws,
+                          float* ctot, hipStream_t s);
+
+// Arguments of the backward entry points (device pointers).
+struct BwdArgs {
+    const void* xBC;
+    const float* conv_w;
+    const void* dt_raw;
+    const float* dt_bias;
+    const float* A_log;
+    const float* D;
+    const int32_t* seq;
+    const void* dy;
+    const float* S_in;
+    const float* dS_out;
+    void* dxBC;
+    void* ddt_raw;
+    float* dconv_w;
+    float* ddt_bias;
+    float* dA_log;
+    float* dD;
+};
+bool bwd_supported(int P, int N, int Q, int act);
 bool chunk_supported(int P, int N, int Q, int act);
 
 // Forward workspace layout (byte offsets), shared by the host code and launchers.
@@ -141,5 +165,36 @@ inline FwdWs fwd_ws_layout(const Dims& d, int act) {
     w.total = align256(w.hst + (size_t)d.batch * d.nchunk * d.H * d.P * d.N * esz);
     return w;
 }
+
+// Backward workspace layout (byte offsets).  Filled by the summary phase
+// (xc, bct, dt, cs, ctot, gst) and used by the segment phase.
+struct BwdWs {
+    size_t xc, bct, dt, cs, ctot, hstT, gst, dvx, dbc, red, dwp, total;
+};
+inline BwdWs bwd_ws_layout(const Dims& d, int act) {
+    BwdWs w;
+    const size_t e = act == SSD_BF16 ? 2 : 4;
+    const size_t BL = (size_t)d.batch * d.L;
+    const size_t st = (size_t)d.batch * d.nchunk * d.H * d.P * d.N;
+    size_t o = 0;
+    w.xc = o;   o = align256(o + BL * d.C * e);
+    w.bct = o;  o = align256(o + (size_t)d.batch * d.nchunk * d.G * 2 * d.N * d.Q * e);
+    w.dt = o;   o = align256(o + (size_t)d.batch * d.H * d.L * 4);
+    w.cs = o;   o = align256(o + (size_t)d.batch * d.H * d.L * 4);
+    w.ctot = o; o = align256(o + (size_t)d.batch * d.H * d.nchunk * 4);
+    w.hstT = o; o = align256(o + st * e);
+    w.gst = o;  o = align256(o + st * e);
+    w.dvx = o;  o = align256(o + BL * d.H * d.P * 4);
+    w.dbc = o;  o = align256(o + BL * d.H * 2 * d.N * 4);
+    w.red = o;  o = align256(o + (size_t)d.batch * d.nchunk * d.H * 3 * 4);
+    w.dwp = o;  o = align256(o + (size_t)d.batch * (d.L / 64) * d.C * d.W * 4);
+    w.total = o;
+    return w;
+}
+
+hipError_t launch_bwd_summary(const Dims& d, const SegTab& t, int act, const BwdArgs& a,
+                              float* summary, void* ws, hipStream_t s);
+hipError_t launch_segment_bwd(const Dims& d, const SegTab& t, int act, const BwdArgs& a, void* ws,
+                              hipStream_t s);
 
 }  // namespace ssd

@@ -183,6 +183,47 @@ def ssd_apply_init_state(problem: Problem, segs, y_zero, xBC_conv, D, seq_idx, S
         _stream(stream)))
 
 
+def ssd_segment_bwd_summary(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log, seq_idx,
+                            dy, summary, ws, stream=None):
+    s = _segs(segs)
+    act = _TORCH_ACT[problem.act_dtype]
+    BL, C, H, P = problem.batch * problem.seqlen, _conv_dim(problem), problem.nheads, problem.headdim
+    f32 = torch.float32
+    args = (_need(xBC, "xBC", BL * C, act),
+            _need(conv_w, "conv_w", C * problem.conv_width, f32),
+            _need(dt_raw, "dt_raw", BL * H, act), _need(dt_bias, "dt_bias", H, f32),
+            _need(A_log, "A_log", H, f32),
+            _need(seq_idx, "seq_idx", BL, torch.int32, optional=True),
+            _need(dy, "dy", BL * H * P, act),
+            _need(summary, "summary", summary_numel(problem, s.n), f32))
+    ws_p, nbytes = _ws(ws)
+    _check("ssd_segment_bwd_summary", _lib.load().ssd_segment_bwd_summary(
+        ctypes.byref(problem), s.ptr(), s.n, *args, ws_p, nbytes, _stream(stream)))
+
+
+def ssd_segment_bwd(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log, D, seq_idx, dy,
+                    S_in, dS_out, ws, dxBC, ddt_raw, dconv_w, ddt_bias, dA_log, dD, stream=None):
+    s = _segs(segs)
+    act = _TORCH_ACT[problem.act_dtype]
+    BL, C, H, P, N = (problem.batch * problem.seqlen, _conv_dim(problem), problem.nheads,
+                      problem.headdim, problem.dstate)
+    f32 = torch.float32
+    W = problem.conv_width
+    st = s.n * problem.batch * H * P * N
+    ins = (_need(xBC, "xBC", BL * C, act), _need(conv_w, "conv_w", C * W, f32),
+           _need(dt_raw, "dt_raw", BL * H, act), _need(dt_bias, "dt_bias", H, f32),
+           _need(A_log, "A_log", H, f32), _need(D, "D", H, f32),
+           _need(seq_idx, "seq_idx", BL, torch.int32, optional=True),
+           _need(dy, "dy", BL * H * P, act), _need(S_in, "S_in", st, f32),
+           _need(dS_out, "dS_out", st, f32))
+    ws_p, nbytes = _ws(ws)
+    outs = (_need(dxBC, "dxBC", BL * C, act), _need(ddt_raw, "ddt_raw", BL * H, act),
+            _need(dconv_w, "dconv_w", C * W, f32), _need(ddt_bias, "ddt_bias", H, f32),
+            _need(dA_log, "dA_log", H, f32), _need(dD, "dD", H, f32))
+    _check("ssd_segment_bwd", _lib.load().ssd_segment_bwd(
+        ctypes.byref(problem), s.ptr(), s.n, *ins, ws_p, nbytes, *outs, _stream(stream)))
+
+
 # ---------------------------------------------------------------------------
 # Convenience: buffers for one forward pass and the four calls in order.
 
@@ -227,4 +268,57 @@ def forward(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log, D, seq_
     ssd_boundary_scan(problem, s.n, bufs.summary, init, False, bufs.S_in, None, stream)
     ssd_apply_init_state(problem, s, bufs.y_zero, bufs.xBC_conv, D, seq_idx, bufs.S_in, bufs.ws,
                          bufs.y, stream)
+    return bufs
+
+
+@dataclass
+class BackwardBuffers:
+    summary: torch.Tensor
+    dS_out: torch.Tensor
+    ws: torch.Tensor
+    dxBC: torch.Tensor
+    ddt_raw: torch.Tensor
+    dconv_w: torch.Tensor
+    ddt_bias: torch.Tensor
+    dA_log: torch.Tensor
+    dD: torch.Tensor
+
+    @staticmethod
+    def allocate(problem: Problem, segs, device) -> "BackwardBuffers":
+        s = _segs(segs)
+        act = _TORCH_ACT[problem.act_dtype]
+        b, L, H, P, N = (problem.batch, problem.seqlen, problem.nheads, problem.headdim,
+                         problem.dstate)
+        C, W = _conv_dim(problem), problem.conv_width
+        wsb = ssd_workspace_bytes(problem, s, SSD_WS_BACKWARD)
+        if wsb == 0:
+            raise SSDError("ssd_workspace_bytes", -3)
+        f32 = torch.float32
+        return BackwardBuffers(
+            summary=torch.empty(summary_numel(problem, s.n), dtype=f32, device=device),
+            dS_out=torch.empty((s.n, b, H, P, N), dtype=f32, device=device),
+            ws=torch.empty(wsb, dtype=torch.uint8, device=device),
+            dxBC=torch.empty((b, L, C), dtype=act, device=device),
+            ddt_raw=torch.empty((b, L, H), dtype=act, device=device),
+            dconv_w=torch.empty((C, W), dtype=f32, device=device),
+            ddt_bias=torch.empty(H, dtype=f32, device=device),
+            dA_log=torch.empty(H, dtype=f32, device=device),
+            dD=torch.empty(H, dtype=f32, device=device))
+
+
+def backward(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log, D, dy, S_in,
+             seq_idx=None, bufs: Optional[BackwardBuffers] = None, stream=None) -> BackwardBuffers:
+    """Summary phase -> reverse boundary scan -> segment phase; returns the buffers.
+
+    ``S_in`` is the forward boundary scan's output (ForwardBuffers.S_in).
+    """
+    s = _segs(segs)
+    if bufs is None:
+        bufs = BackwardBuffers.allocate(problem, s, xBC.device)
+    ssd_segment_bwd_summary(problem, s, xBC, conv_w, dt_raw, dt_bias, A_log, seq_idx, dy,
+                            bufs.summary, bufs.ws, stream)
+    ssd_boundary_scan(problem, s.n, bufs.summary, None, True, bufs.dS_out, None, stream)
+    ssd_segment_bwd(problem, s, xBC, conv_w, dt_raw, dt_bias, A_log, D, seq_idx, dy, S_in,
+                    bufs.dS_out, bufs.ws, bufs.dxBC, bufs.ddt_raw, bufs.dconv_w, bufs.ddt_bias,
+                    bufs.dA_log, bufs.dD, stream)
     return bufs
