@@ -1,9 +1,12 @@
 """Benchmark of the conv1d + SSD state-passing path on one MI355X.
 
-One step = one pass of the whole hot path over one batch of synthetic input,
-every call going through the C ABI on torch's current stream:
-  ssd_conv1d_fwd -> ssd_segment_states -> ssd_segment_output
-  -> ssd_boundary_scan -> ssd_apply_init_state.
+One step = one pass of the whole hot path (forward and backward) over one
+batch of synthetic input, every call going through the C ABI on torch's
+current stream:
+  forward : ssd_conv1d_fwd -> ssd_segment_states -> ssd_segment_output
+            -> ssd_boundary_scan -> ssd_apply_init_state
+  backward: ssd_segment_bwd_summary -> ssd_boundary_scan (reverse)
+            -> ssd_segment_bwd_chunks -> ssd_conv1d_bwd
 Workload: 2 rows x 8192 tokens, 32 heads, headdim 64, d_state 128, 1 group,
 chunk 256, conv width 4, bf16 activations with FP32 state, cut into 8
 contiguous causal segments of 1024 tokens (one device's context-parallel
@@ -37,7 +40,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="1", help="workload: 1, 2c, 2v or 3")
+    ap.add_argument("--workload", default="mixer_shard_bwd_bf16",
+                    help="a name from ssd_workloads.WORKLOADS (default: the mixer shard with dy, "
+                         "forward+backward)")
+    ap.add_argument("--pass", dest="which", default=None, choices=["fwd", "fwd+bwd"],
+                    help="default: fwd+bwd when the workload has dy, else fwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-runs", type=int, default=3)
     return ap.parse_args()
@@ -58,7 +65,14 @@ def algorithmic_bytes(wl):
     summary = S * b * H * (P * N + 1) * 4
     states = S * b * H * P * N * 4
     dtcs = 2 * BL * H * 4
+    dy = BL * H * P * e
     return {
+        "ssd_segment_bwd_summary": BL * C * e + BL * H * e + dy + BL * C * e + dtcs + 2 * hst
+                                   + summary + seq,
+        "ssd_boundary_scan(reverse)": summary + states,
+        "ssd_segment_bwd_chunks": BL * C * e + dy + BL * H * e + dtcs + 2 * hst + 2 * states
+                                  + BL * H * P * 4 + BL * 2 * G * N * 4 + BL * H * e + seq,
+        "ssd_conv1d_bwd": BL * C * e + BL * C * 4 + BL * C * e + seq,
         "ssd_conv1d_fwd": 2 * BL * C * e + C * wl.conv_width * 4 + seq,
         "ssd_segment_states": BL * (H * P + G * N) * e + BL * H * e + 2 * dtcs + hst + summary + seq,
         "ssd_segment_output": BL * C * e + hst + dtcs + BL * H * P * 4 + seq,
@@ -75,18 +89,31 @@ def output_flops(wl):
     return b * (L // Q) * H * per_chunk_head
 
 
-def cpu_baseline(wl, runs):
+def chunk_bwd_flops(wl):
+    """MFMA flops of ssd_segment_bwd_chunks: C B^T, dy x^T (twice), their products with
+    dy, C and B, and the three entering/exit-state products (causal pairs only)."""
+    b, L, H, P, N, Q = wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.chunk
+    pairs = Q * (Q + 1) // 2
+    per_chunk_head = 2 * pairs * (3 * N + 3 * P) + 6 * Q * P * N
+    return b * (L // Q) * H * per_chunk_head
+
+
+def cpu_baseline(wl, runs, backward):
     import oracle
     threads = oracle.num_threads()
     times = []
     for _ in range(runs):
         t = time.perf_counter()
-        oracle.forward(wl)
+        if backward:
+            oracle.backward(wl)  # runs the forward too
+        else:
+            oracle.forward(wl)
         times.append(time.perf_counter() - t)
     med = statistics.median(times)
+    what = "forward + backward (adjoint)" if backward else "forward"
     return {"value": wl.tokens / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole workload ({wl.tokens} tokens, all heads), float64 token-by-token "
-                      f"recurrence, median of {runs} runs ({med:.2f} s each)"}
+                      f"recurrence, {what}, median of {runs} runs ({med:.2f} s each)"}
 
 
 def main():
@@ -102,7 +129,11 @@ def main():
     import mamba2_ssd_chunked_amd as ssd
     import ssd_workloads as W
 
-    wl = W.config(args.config)
+    wl = W.config(args.workload)
+    which = args.which or ("fwd+bwd" if wl.dy is not None else "fwd")
+    if which == "fwd+bwd" and wl.dy is None:
+        raise SystemExit("this workload has no dy; use --pass fwd")
+    do_bwd = which == "fwd+bwd"
     dev = torch.device("cuda:0")
     act = torch.bfloat16 if wl.act == "bf16" else torch.float32
     f32 = torch.float32
@@ -110,12 +141,14 @@ def main():
     xBC, conv_w, dt_raw = t(wl.xBC, act), t(wl.conv_w, f32), t(wl.dt_raw, act)
     dt_bias, A_log, D = t(wl.dt_bias, f32), t(wl.A_log, f32), t(wl.D, f32)
     seq = None if wl.seq_idx is None else t(wl.seq_idx, torch.int32)
+    dy = t(wl.dy, act) if do_bwd else None
     p = ssd.make_problem(batch=wl.batch, seqlen=wl.seqlen, nheads=wl.nheads, headdim=wl.headdim,
                          dstate=wl.dstate, ngroups=wl.ngroups, chunk=wl.chunk,
                          conv_width=wl.conv_width, act=wl.act, dt_min=wl.dt_min,
                          dt_max=wl.dt_max)
     segs = ssd.Segments(wl.segments)
     bufs = ssd.ForwardBuffers.allocate(p, segs, dev)
+    bb = ssd.BackwardBuffers.allocate(p, segs, dev) if do_bwd else None
     stream = torch.cuda.current_stream()
 
     calls = [
@@ -129,8 +162,22 @@ def main():
         ("ssd_apply_init_state", lambda: ssd.ssd_apply_init_state(
             p, segs, bufs.y_zero, bufs.xBC_conv, D, seq, bufs.S_in, bufs.ws, bufs.y)),
     ]
+    if do_bwd:
+        calls += [
+            ("ssd_segment_bwd_summary", lambda: ssd.ssd_segment_bwd_summary(
+                p, segs, xBC, conv_w, dt_raw, dt_bias, A_log, seq, dy, bb.summary, bb.ws)),
+            ("ssd_boundary_scan(reverse)", lambda: ssd.ssd_boundary_scan(
+                p, segs.n, bb.summary, None, True, bb.dS_out)),
+            ("ssd_segment_bwd_chunks", lambda: ssd.ssd_segment_bwd_chunks(
+                p, segs, dt_raw, dt_bias, A_log, D, seq, dy, bufs.S_in, bb.dS_out, bb.ws,
+                bb.ddt_raw)),
+            ("ssd_conv1d_bwd", lambda: ssd.ssd_conv1d_bwd(
+                p, segs, xBC, conv_w, A_log, seq, bb.ws, bb.dxBC, bb.dconv_w, bb.ddt_bias,
+                bb.dA_log, bb.dD)),
+        ]
     single_kernel = {"ssd_conv1d_fwd", "ssd_segment_output", "ssd_boundary_scan",
-                     "ssd_apply_init_state"}
+                     "ssd_apply_init_state", "ssd_boundary_scan(reverse)",
+                     "ssd_segment_bwd_chunks"}
 
     def step(events=None):
         for i, (_, fn) in enumerate(calls):
@@ -167,10 +214,13 @@ def main():
                           "GB_per_s": round(abytes[name] / (ms * 1e-3) / 1e9, 1)}
     dom = max(single_kernel, key=lambda n: per_call[n]["ms"])
     achieved = per_call[dom]["GB_per_s"]
-    fl = output_flops(wl)
-    out_ms = per_call["ssd_segment_output"]["ms"]
     mfma_peak = BF16_PEAK_TFLOPS if wl.act == "bf16" else F32_PEAK_TFLOPS
-    out_tflops = fl / (out_ms * 1e-3) / 1e12
+    mfma = {}
+    for name, fl in [("ssd_segment_output", output_flops(wl))] + \
+            ([("ssd_segment_bwd_chunks", chunk_bwd_flops(wl))] if do_bwd else []):
+        tf = fl / (per_call[name]["ms"] * 1e-3) / 1e12
+        mfma[name] = {"achieved": round(tf, 2), "peak": mfma_peak, "unit": "TFLOP/s",
+                      "frac": round(tf / mfma_peak, 4), "algorithmic_GFLOP": round(fl / 1e9, 2)}
 
     result = {
         "metric": METRIC,
@@ -185,7 +235,7 @@ def main():
         "vs_baseline": None,
         "dtype": wl.act,
         "data": "synthetic (seeded N(0,1) activations, Mamba2-style dt_bias and A_log)",
-        "config": {"workload": wl.name, "pass": "forward", "batch": wl.batch,
+        "config": {"workload": wl.name, "pass": which, "batch": wl.batch,
                    "seq_len": wl.seqlen, "nheads": wl.nheads, "headdim": wl.headdim,
                    "dstate": wl.dstate, "ngroups": wl.ngroups, "chunk": wl.chunk,
                    "conv_width": wl.conv_width, "segments": len(wl.segments),
@@ -193,13 +243,12 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None},
-        "mfma": {"kernel": "ssd_segment_output", "achieved": round(out_tflops, 2),
-                 "peak": mfma_peak, "unit": "TFLOP/s", "frac": round(out_tflops / mfma_peak, 4)},
+        "mfma": mfma,
         "calls": per_call,
         "wall_s_timed_region": round(wall, 4),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_runs)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_runs, do_bwd)
     print(json.dumps(result), flush=True)
 
 

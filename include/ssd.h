@@ -227,6 +227,24 @@ int ssd_segment_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t
                     void* ddt_raw, float* dconv_w, float* ddt_bias, float* dA_log, float* dD,
                     void* stream);
 
+/* The two phases of ssd_segment_bwd.  ssd_segment_bwd_chunks computes, per
+ * chunk and head, dx, dB, dC (written into `ws`, the buffers the conv backward
+ * consumes, as #6808's first commit does) and ddt_raw, plus per-chunk partial
+ * sums of the parameter gradients.  ssd_conv1d_bwd then applies SiLU' and the
+ * transposed causal conv (its right halo read from the causal successor
+ * segment) to produce dxBC and dconv_w, and reduces ddt_bias, dA_log and dD.
+ * Calling both in this order is the same as ssd_segment_bwd; both read the
+ * workspace ssd_segment_bwd_summary filled. */
+int ssd_segment_bwd_chunks(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                           const void* dt_raw, const float* dt_bias, const float* A_log,
+                           const float* D, const int32_t* seq_idx, const void* dy,
+                           const float* S_in, const float* dS_out, void* ws, size_t ws_bytes,
+                           void* ddt_raw, void* stream);
+int ssd_conv1d_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                   const void* xBC, const float* conv_w, const float* A_log,
+                   const int32_t* seq_idx, void* ws, size_t ws_bytes, void* dxBC, float* dconv_w,
+                   float* ddt_bias, float* dA_log, float* dD, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -276,6 +276,74 @@ int ssd_segment_bwd_summary(const ssd_problem* problem, const ssd_segment* segs,
                                          (hipStream_t)stream));
 }
 
+namespace {
+// Common checks of the chunk and conv phases of the backward.
+int check_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg, Dims* d,
+              SegTab* t, const void* ws, size_t ws_bytes) {
+    int rc = check_problem(problem, d);
+    if (rc) return rc;
+    if ((rc = check_segments(segs, nseg, d, t))) return rc;
+    if (!bwd_supported(d->P, d->N, d->Q, problem->act_dtype)) return SSD_ERR_UNSUPPORTED;
+    if (!ws) return SSD_ERR_WORKSPACE;
+    if (ws_bytes < bwd_ws_layout(*d, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
+    if (!aligned16(ws)) return SSD_ERR_ALIGN;
+    return SSD_OK;
+}
+}  // namespace
+
+int ssd_segment_bwd_chunks(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                           const void* dt_raw, const float* dt_bias, const float* A_log,
+                           const float* D, const int32_t* seq_idx, const void* dy,
+                           const float* S_in, const float* dS_out, void* ws, size_t ws_bytes,
+                           void* ddt_raw, void* stream) {
+    Dims d;
+    SegTab t;
+    int rc = check_bwd(problem, segs, nseg, &d, &t, ws, ws_bytes);
+    if (rc) return rc;
+    if (!dt_raw || !dt_bias || !A_log || !D || !dy || !S_in || !dS_out || !ddt_raw)
+        return SSD_ERR_NULL;
+    const void* ptrs[] = {dt_raw, dt_bias, A_log, D, seq_idx, dy, S_in, dS_out, ddt_raw};
+    for (const void* q : ptrs)
+        if (!aligned16(q)) return SSD_ERR_ALIGN;
+    BwdArgs ar = {};
+    ar.dt_raw = dt_raw;
+    ar.dt_bias = dt_bias;
+    ar.A_log = A_log;
+    ar.D = D;
+    ar.seq = seq_idx;
+    ar.dy = dy;
+    ar.S_in = S_in;
+    ar.dS_out = dS_out;
+    ar.ddt_raw = ddt_raw;
+    return hip_status(launch_bwd_chunks(d, t, problem->act_dtype, ar, ws, (hipStream_t)stream));
+}
+
+int ssd_conv1d_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                   const void* xBC, const float* conv_w, const float* A_log,
+                   const int32_t* seq_idx, void* ws, size_t ws_bytes, void* dxBC, float* dconv_w,
+                   float* ddt_bias, float* dA_log, float* dD, void* stream) {
+    Dims d;
+    SegTab t;
+    int rc = check_bwd(problem, segs, nseg, &d, &t, ws, ws_bytes);
+    if (rc) return rc;
+    if (!xBC || !conv_w || !A_log || !dxBC || !dconv_w || !ddt_bias || !dA_log || !dD)
+        return SSD_ERR_NULL;
+    const void* ptrs[] = {xBC, conv_w, A_log, seq_idx, dxBC, dconv_w, ddt_bias, dA_log, dD};
+    for (const void* q : ptrs)
+        if (!aligned16(q)) return SSD_ERR_ALIGN;
+    BwdArgs ar = {};
+    ar.xBC = xBC;
+    ar.conv_w = conv_w;
+    ar.A_log = A_log;
+    ar.seq = seq_idx;
+    ar.dxBC = dxBC;
+    ar.dconv_w = dconv_w;
+    ar.ddt_bias = ddt_bias;
+    ar.dA_log = dA_log;
+    ar.dD = dD;
+    return hip_status(launch_conv1d_bwd(d, t, problem->act_dtype, ar, ws, (hipStream_t)stream));
+}
+
 int ssd_segment_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
                     const void* xBC, const float* conv_w, const void* dt_raw, const float* dt_bias,
                     const float* A_log, const float* D, const int32_t* seq_idx, const void* dy,
@@ -284,22 +352,20 @@ int ssd_segment_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t
                     void* stream) {
     Dims d;
     SegTab t;
-    int rc = check_problem(problem, &d);
+    int rc = check_bwd(problem, segs, nseg, &d, &t, ws, ws_bytes);
     if (rc) return rc;
-    if ((rc = check_segments(segs, nseg, &d, &t))) return rc;
-    if (!bwd_supported(d.P, d.N, d.Q, problem->act_dtype)) return SSD_ERR_UNSUPPORTED;
     if (!xBC || !conv_w || !dt_raw || !dt_bias || !A_log || !D || !dy || !S_in || !dS_out ||
         !dxBC || !ddt_raw || !dconv_w || !ddt_bias || !dA_log || !dD)
         return SSD_ERR_NULL;
-    if (!ws) return SSD_ERR_WORKSPACE;
-    if (ws_bytes < bwd_ws_layout(d, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
     const void* ptrs[] = {xBC, conv_w, dt_raw, dt_bias, A_log, D, seq_idx, dy, S_in, dS_out,
-                          ws, dxBC, ddt_raw, dconv_w, ddt_bias, dA_log, dD};
+                          dxBC, ddt_raw, dconv_w, ddt_bias, dA_log, dD};
     for (const void* q : ptrs)
         if (!aligned16(q)) return SSD_ERR_ALIGN;
     BwdArgs ar = {xBC, conv_w, dt_raw, dt_bias, A_log, D, seq_idx, dy, S_in, dS_out,
                   dxBC, ddt_raw, dconv_w, ddt_bias, dA_log, dD};
-    return hip_status(launch_segment_bwd(d, t, problem->act_dtype, ar, ws, (hipStream_t)stream));
+    rc = hip_status(launch_bwd_chunks(d, t, problem->act_dtype, ar, ws, (hipStream_t)stream));
+    if (rc) return rc;
+    return hip_status(launch_conv1d_bwd(d, t, problem->act_dtype, ar, ws, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -12,12 +12,15 @@
 //     the same packed layout as the forward summary.
 //   reverse boundary scan (ssd_boundary_scan, reverse = 1) -> the gradient of
 //     every segment's final state.
-//   segment phase (ssd_segment_bwd)
-//     forward chunk walk (entering states, stored transposed), k_chunk_bwd
-//     (per chunk and head: dx, dB, dC and ddt with the true entering state
-//     H + decay S_in and the true exit gradient G + decay dS_out), k_conv_bwd
-//     (SiLU' and the transposed conv, with a right halo from the causal
-//     successor segment) and k_bwd_reduce (deterministic parameter gradients).
+//     It also recomputes the zero-initial-state entering state of every chunk
+//     (forward walk, stored transposed).
+//   chunk phase (ssd_segment_bwd_chunks): k_chunk_bwd, per chunk and head:
+//     dx, dB, dC and ddt with the true entering state H + decay S_in and the
+//     true exit gradient G + decay dS_out, written into the buffers the conv
+//     backward consumes.
+//   conv phase (ssd_conv1d_bwd): k_conv_bwd (SiLU' and the transposed conv,
+//     with a right halo from the causal successor segment) and k_bwd_reduce
+//     (deterministic parameter gradients).
 //
 // ddt without recomputing y.  dL/d(dt_t A) sums, over every (source j, output
 // i) pair with j < t <= i, the derivative of their decay.  Per chunk that is
@@ -759,6 +762,11 @@ static void bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a, floa
     launch_dt_prep(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32, a.dt_raw, a.dt_bias,
                    a.A_log, a.seq, (float*)(ws + L.dt), (float*)(ws + L.cs),
                    (float*)(ws + L.ctot), s);
+    hipLaunchKernelGGL((k_state_walk<T, P, N, WALK_FWD_NP>),
+                       dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0, s,
+                       d, t, (const T*)xc, (int64_t)d.C, (const T*)xc, (int64_t)d.H * P,
+                       (const float*)(ws + L.dt), (const float*)(ws + L.cs), a.seq,
+                       (T*)(ws + L.hstT), (float*)nullptr);
     hipLaunchKernelGGL((k_state_walk<T, P, N, WALK_BWD_PN>),
                        dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0, s,
                        d, t, (const T*)a.dy, (int64_t)d.H * P, (const T*)xc,
@@ -767,19 +775,22 @@ static void bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a, floa
 }
 
 template <typename T, int P, int N>
-static void bwd_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* ws_, hipStream_t s) {
+static void bwd_chunks_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* ws_,
+                         hipStream_t s) {
     const BwdWs L = bwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
     char* ws = (char*)ws_;
-    hipLaunchKernelGGL((k_state_walk<T, P, N, WALK_FWD_NP>),
-                       dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0, s,
-                       d, t, (const T*)(ws + L.xc), (int64_t)d.C, (const T*)(ws + L.xc),
-                       (int64_t)d.H * P, (const float*)(ws + L.dt), (const float*)(ws + L.cs),
-                       a.seq, (T*)(ws + L.hstT), (float*)nullptr);
     switch (d.Q) {
         case 64: launch_chunk_bwd<T, P, N, 64>(d, t, a, L, ws, s); break;
         case 128: launch_chunk_bwd<T, P, N, 128>(d, t, a, L, ws, s); break;
         default: launch_chunk_bwd<T, P, N, 256>(d, t, a, L, ws, s); break;
     }
+}
+
+template <typename T>
+static void conv_bwd_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* ws_,
+                       hipStream_t s) {
+    const BwdWs L = bwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
+    char* ws = (char*)ws_;
     launch_conv_bwd<T>(d, t, a, L, ws, s);
     const int nout = d.C * d.W + 3 * d.H;
     hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, s, d,
@@ -821,12 +832,12 @@ hipError_t launch_bwd_summary(const Dims& d, const SegTab& t, int act, const Bwd
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_segment_bwd(const Dims& d, const SegTab& t, int act, const BwdArgs& a, void* ws,
-                              hipStream_t s) {
-#define X(p, n)                                \
-    if (d.P == p && d.N == n) {                \
-        bwd_t<T, p, n>(d, t, a, ws, s);        \
-        return hipGetLastError();              \
+hipError_t launch_bwd_chunks(const Dims& d, const SegTab& t, int act, const BwdArgs& a, void* ws,
+                             hipStream_t s) {
+#define X(p, n)                                  \
+    if (d.P == p && d.N == n) {                  \
+        bwd_chunks_t<T, p, n>(d, t, a, ws, s);   \
+        return hipGetLastError();                \
     }
     if (act == SSD_F32) {
         typedef float T;
@@ -837,6 +848,13 @@ hipError_t launch_segment_bwd(const Dims& d, const SegTab& t, int act, const Bwd
     }
 #undef X
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_conv1d_bwd(const Dims& d, const SegTab& t, int act, const BwdArgs& a, void* ws,
+                             hipStream_t s) {
+    if (act == SSD_BF16) conv_bwd_t<bf16>(d, t, a, ws, s);
+    else conv_bwd_t<float>(d, t, a, ws, s);
+    return hipGetLastError();
 }
 
 }  // namespace ssd

@@ -236,38 +236,37 @@ def make_workload(name: str, *, batch: int, seqlen: int, nheads: int, headdim: i
                     layout=layout)
 
 
-# The five named workloads.  Seeds are 1000 + index.
-def config(i: str | int) -> Workload:
-    i = str(i)
-    if i == "0":
-        return make_workload("cfg0_tiny_f32", batch=1, seqlen=256, nheads=2, headdim=16,
-                             dstate=16, ngroups=1, chunk=64, act="f32", nseg=2, seed=1000)
-    if i == "1":
-        return make_workload("cfg1_mixer_shard_bf16", batch=2, seqlen=8192, nheads=32,
-                             headdim=64, dstate=128, ngroups=1, chunk=256, act="bf16",
-                             nseg=8, seed=1001)
-    if i == "2c":
-        return make_workload("cfg2_long_contiguous", batch=1, seqlen=131072, nheads=64,
-                             headdim=64, dstate=128, ngroups=8, chunk=256, act="bf16",
-                             nseg=8, seed=1002)
-    if i == "2v":
-        return make_workload("cfg2_long_virtual", batch=1, seqlen=131072, nheads=64,
-                             headdim=64, dstate=128, ngroups=8, chunk=256, act="bf16",
-                             nseg=16, layout="virtual", seed=1002)
-    if i == "3":
-        return make_workload("cfg3_packed_thd", batch=1, seqlen=32768, nheads=32,
-                             headdim=64, dstate=128, ngroups=1, chunk=256, act="bf16",
-                             nseg=4, packed=(512, 8192), seed=1003)
-    if i == "4":
-        return make_workload("cfg4_backward_of_cfg1", batch=2, seqlen=8192, nheads=32,
-                             headdim=64, dstate=128, ngroups=1, chunk=256, act="bf16",
-                             nseg=8, seed=1001, with_dy=True)
-    if i == "S0":
-        return make_workload("slow_decay_tiny_f32", batch=1, seqlen=256, nheads=2,
-                             headdim=16, dstate=16, ngroups=1, chunk=64, act="f32",
-                             nseg=2, seed=2000, slow_decay=True)
-    if i == "S1":
-        return make_workload("slow_decay_mixer_shard_bf16", batch=2, seqlen=8192,
-                             nheads=32, headdim=64, dstate=128, ngroups=1, chunk=256,
-                             act="bf16", nseg=8, seed=2001, slow_decay=True)
-    raise KeyError(i)
+# Named workloads (seeds fixed per workload).
+WORKLOADS = {
+    # 1 x 256 tokens, 2 heads, P = N = 16, chunk 64, float32, 2 segments
+    "tiny_f32": dict(batch=1, seqlen=256, nheads=2, headdim=16, dstate=16, ngroups=1, chunk=64,
+                     act="f32", nseg=2, seed=1000),
+    # Mamba2 mixer shard: 2 x 8192 tokens, 32 heads, P 64, N 128, 8 segments of 1024
+    "mixer_shard_bf16": dict(batch=2, seqlen=8192, nheads=32, headdim=64, dstate=128, ngroups=1,
+                             chunk=256, act="bf16", nseg=8, seed=1001),
+    # long context: 131072 tokens, 64 heads in 8 groups, 8 contiguous segments
+    "long_context_bf16": dict(batch=1, seqlen=131072, nheads=64, headdim=64, dstate=128,
+                              ngroups=8, chunk=256, act="bf16", nseg=8, seed=1002),
+    # the same, as 16 half-shards in the virtual front/back layout
+    "long_context_virtual_bf16": dict(batch=1, seqlen=131072, nheads=64, headdim=64, dstate=128,
+                                      ngroups=8, chunk=256, act="bf16", nseg=16,
+                                      layout="virtual", seed=1002),
+    # packed variable-length batch: 32768 tokens, lengths U[512, 8192], 4 segments
+    "packed_thd_bf16": dict(batch=1, seqlen=32768, nheads=32, headdim=64, dstate=128, ngroups=1,
+                            chunk=256, act="bf16", nseg=4, packed=(512, 8192), seed=1003),
+    # the mixer shard with an upstream gradient dy (forward + backward)
+    "mixer_shard_bwd_bf16": dict(batch=2, seqlen=8192, nheads=32, headdim=64, dstate=128,
+                                 ngroups=1, chunk=256, act="bf16", nseg=8, seed=1001,
+                                 with_dy=True),
+    # slow-decay variants: block decays far from 0 so the scan composes segments
+    "slow_tiny_f32": dict(batch=1, seqlen=256, nheads=2, headdim=16, dstate=16, ngroups=1,
+                          chunk=64, act="f32", nseg=2, seed=2000, slow_decay=True),
+    "slow_mixer_shard_bf16": dict(batch=2, seqlen=8192, nheads=32, headdim=64, dstate=128,
+                                  ngroups=1, chunk=256, act="bf16", nseg=8, seed=2001,
+                                  slow_decay=True),
+}
+
+
+def config(name: str) -> Workload:
+    """Build one of the named workloads."""
+    return make_workload(name, **WORKLOADS[name])

@@ -2,7 +2,7 @@
 
 Also: the backward summary (dL/dS_in of each segment's own outputs) against the
 oracle's initial-state gradient per segment, central finite differences of the
-oracle forward on config 0, full config 4, determinism, and bitwise isolation
+oracle forward on the tiny float32 workload, the full mixer shard, determinism, and bitwise isolation
 of packed sequences.
 """
 import numpy as np
@@ -22,11 +22,11 @@ GRADS = ["dxBC", "dconv_w", "ddt_raw", "ddt_bias", "dA_log", "dD"]
 def _bwd_small(name):
     mk = W.make_workload
     kw = dict(with_dy=True)
-    if name == "cfg0":
-        return mk("cfg0_tiny_f32", batch=1, seqlen=256, nheads=2, headdim=16, dstate=16,
+    if name == "tiny_f32":
+        return mk("tiny_f32", batch=1, seqlen=256, nheads=2, headdim=16, dstate=16,
                   ngroups=1, chunk=64, act="f32", nseg=2, seed=1000, **kw)
-    if name == "S0":
-        return mk("S0", batch=1, seqlen=256, nheads=2, headdim=16, dstate=16, ngroups=1,
+    if name == "slow_tiny_f32":
+        return mk("slow_tiny_f32", batch=1, seqlen=256, nheads=2, headdim=16, dstate=16, ngroups=1,
                   chunk=64, act="f32", nseg=2, seed=2000, slow_decay=True, **kw)
     if name == "f32_head_thd":
         return mk(name, batch=2, seqlen=512, nheads=4, headdim=64, dstate=128, ngroups=2,
@@ -53,7 +53,7 @@ def _bwd_small(name):
     raise KeyError(name)
 
 
-SMALL = ["cfg0", "S0", "f32_head_thd", "f32_virtual", "bf16_small", "bf16_virtual", "bf16_thd",
+SMALL = ["tiny_f32", "slow_tiny_f32", "f32_head_thd", "f32_virtual", "bf16_small", "bf16_virtual", "bf16_thd",
          "bf16_q64", "bf16_q128"]
 
 
@@ -119,21 +119,21 @@ def test_backward_gradients(bwd_run):
         assert_close(got[name], ref[name], wl.act, name)
 
 
-def test_backward_config4_full():
-    wl = W.config(4)
-    log(f"[backward] config 4 ({wl.name})")
+def test_backward_mixer_shard_full():
+    wl = W.config("mixer_shard_bwd_bf16")
+    log(f"[backward] {wl.name}")
     _, _, _, bb = run_fwd_bwd(wl)
     ref = oracle.backward(wl)
     got = gpu_grads(wl, bb)
     for name in GRADS:
-        assert_close(got[name], ref[name], wl.act, f"config 4 {name}")
+        assert_close(got[name], ref[name], wl.act, f"mixer shard {name}")
 
 
-def test_config0_gradients_against_finite_differences():
+def test_tiny_gradients_against_finite_differences():
     """Central differences of L = <dy, y> with the float64 oracle forward, sampled entries."""
     import copy
-    wl = _bwd_small("cfg0")
-    log("[backward] config 0 finite differences")
+    wl = _bwd_small("tiny_f32")
+    log("[backward] tiny_f32 finite differences")
     _, _, _, bb = run_fwd_bwd(wl)
     got = gpu_grads(wl, bb)
 

@@ -3,7 +3,7 @@
 Component checks (conv, boundary scan, segment summaries, zero-state output,
 correction) and end-to-end checks on small workloads that span several tiles,
 unequal segments, packed sequences that start inside chunks and the virtual
-front/back layout, plus the full-size configurations (config 2 on sampled
+front/back layout, plus the full-size workloads (the 131072-token ones on sampled
 heads).  Tolerances: float32 inputs, max relative error 1e-4 (floored at the
 output RMS); bf16 inputs, relative RMS error 2e-2.
 """
@@ -21,10 +21,8 @@ pytestmark = pytest.mark.gpu
 
 def _small(name):
     mk = W.make_workload
-    if name == "cfg0":
-        return W.config(0)
-    if name == "S0":
-        return W.config("S0")
+    if name in ("tiny_f32", "slow_tiny_f32"):
+        return W.config(name)
     if name == "f32_head_thd":
         return mk(name, batch=2, seqlen=512, nheads=4, headdim=64, dstate=128, ngroups=2,
                   chunk=64, act="f32", seed=101, seg_lens=[128, 256, 128],
@@ -50,7 +48,7 @@ def _small(name):
     raise KeyError(name)
 
 
-SMALL = ["cfg0", "S0", "f32_head_thd", "f32_virtual", "bf16_small", "bf16_virtual", "bf16_thd",
+SMALL = ["tiny_f32", "slow_tiny_f32", "f32_head_thd", "f32_virtual", "bf16_small", "bf16_virtual", "bf16_thd",
          "bf16_q64", "bf16_q128"]
 
 
@@ -222,23 +220,23 @@ def test_determinism():
 # --------------------------------------------------------------------------- full sizes
 
 
-@pytest.mark.parametrize("cfg", ["1", "3", "S1"])
+@pytest.mark.parametrize("cfg", ["mixer_shard_bf16", "packed_thd_bf16", "slow_mixer_shard_bf16"])
 def test_full_config(cfg):
     wl = W.config(cfg)
-    log(f"[full] config {cfg} ({wl.name})")
+    log(f"[full] {cfg}")
     _, _, bufs = run_forward(wl)
     g = wl.to_causal(to_np(bufs.y))
     o = oracle.forward(wl)
-    assert_close(g, o, wl.act, f"y config {cfg}")
+    assert_close(g, o, wl.act, f"y {cfg}")
 
 
-@pytest.mark.parametrize("cfg", ["2c", "2v"])
-def test_config2_sampled_heads(cfg):
-    """Long context: the full path on the GPU, checked on two heads of one group and two of another."""
+@pytest.mark.parametrize("cfg", ["long_context_bf16", "long_context_virtual_bf16"])
+def test_long_context_sampled_heads(cfg):
+    """131072 tokens: the full path on the GPU, checked on two heads of one group and two of another."""
     wl = W.config(cfg)
-    log(f"[full] config {cfg} ({wl.name}) sampled heads")
+    log(f"[full] {cfg} sampled heads")
     _, _, bufs = run_forward(wl)
     heads = [0, 7, 57, 63]
     g = wl.to_causal(to_np(bufs.y[:, :, heads]))
     o = oracle.forward(wl, heads=heads)
-    assert_close(g, o, wl.act, f"y config {cfg} heads {heads}")
+    assert_close(g, o, wl.act, f"y {cfg} heads {heads}")
