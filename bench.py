@@ -47,6 +47,9 @@ def parse():
                     help="default: fwd+bwd when the workload has dy, else fwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-runs", type=int, default=3)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="run one device-to-device copy of this many MB before timing, so that "
+                         "hardware byte counters can be calibrated against a known size")
     return ap.parse_args()
 
 
@@ -187,6 +190,13 @@ def main():
             if events is not None:
                 events[i][1].record(stream)
 
+    if args.copy_probe_mb:
+        nb = args.copy_probe_mb * (1 << 20)
+        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -191,6 +191,7 @@ __global__ void __launch_bounds__(NW * 64) k_chunk_out(Dims d, SegTab tab, const
     __syncthreads();
 
     const T* hp = hst + (((int64_t)b * d.nchunk + cm) * d.H + h) * (P * N);
+#pragma unroll 1
     for (int m = 0;; ++m) {
         const int it = wave_tile(wave, NW, m);
         if (it >= QT) break;
@@ -223,6 +224,7 @@ __global__ void __launch_bounds__(NW * 64) k_chunk_out(Dims d, SegTab tab, const
         }
 
         // intra-chunk term, j-blocks of KS tokens up to the diagonal
+#pragma unroll 1
         for (int j0 = 0; j0 <= i0 + 15; j0 += KS) {
             float tv[SL];
 #pragma unroll

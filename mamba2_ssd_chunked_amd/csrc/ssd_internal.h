@@ -169,7 +169,7 @@ inline FwdWs fwd_ws_layout(const Dims& d, int act) {
 // Backward workspace layout (byte offsets).  Filled by the summary phase
 // (xc, bct, dt, cs, ctot, gst) and used by the segment phase.
 struct BwdWs {
-    size_t xc, bct, dt, cs, ctot, hstT, gst, dvx, dbc, red, dwp, total;
+    size_t xc, bct, dt, cs, ctot, hstT, gst, dv, dbc, rpart, tokp, dotgh, red4, red, dwp, total;
 };
 inline BwdWs bwd_ws_layout(const Dims& d, int act) {
     BwdWs w;
@@ -184,8 +184,12 @@ inline BwdWs bwd_ws_layout(const Dims& d, int act) {
     w.ctot = o; o = align256(o + (size_t)d.batch * d.H * d.nchunk * 4);
     w.hstT = o; o = align256(o + st * e);
     w.gst = o;  o = align256(o + st * e);
-    w.dvx = o;  o = align256(o + BL * d.H * d.P * 4);
-    w.dbc = o;  o = align256(o + BL * d.H * 2 * d.N * 4);
+    w.dv = o;   o = align256(o + BL * d.C * 4);  // d(conv output), every channel
+    w.dbc = o;  o = align256(o + BL * d.H * 2 * d.N * e);  // per-head dB, dC
+    w.rpart = o; o = align256(o + (size_t)d.batch * d.H * d.L * 2 * 4);
+    w.tokp = o; o = align256(o + (size_t)d.batch * d.H * d.L * 4 * 4);
+    w.dotgh = o; o = align256(o + (size_t)d.batch * d.nchunk * d.H * 4);
+    w.red4 = o; o = align256(o + (size_t)d.batch * d.nchunk * d.H * 2 * 4);
     w.red = o;  o = align256(o + (size_t)d.batch * d.nchunk * d.H * 3 * 4);
     w.dwp = o;  o = align256(o + (size_t)d.batch * (d.L / 64) * d.C * d.W * 4);
     w.total = o;
