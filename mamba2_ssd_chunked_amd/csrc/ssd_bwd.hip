@@ -6,18 +6,18 @@
 //
 //   summary phase (ssd_segment_bwd_summary)
 //     conv recompute -> xBC_conv (+ a chunk-transposed copy of the B and C
-//     channels, k_bc_transpose), dt/cumsum recompute (k_dt_prep), and the
-//     reverse chunk walk (k_state_walk, backward mode) that leaves, per
+//     channels, k_bc_transpose), dt/cumsum recompute (k_dt_prep), every
+//     chunk's own contribution to the state and to the state gradient, in
+//     parallel over chunks (k_bwd_chunk_states), and the reverse passing of
+//     those contributions inside each segment (k_state_pass) that leaves, per
 //     segment, dL/dS_in of the segment's own outputs and its block decay, in
 //     the same packed layout as the forward summary.
 //   reverse boundary scan (ssd_boundary_scan, reverse = 1) -> the gradient of
 //     every segment's final state.
-//     It also recomputes the zero-initial-state entering state of every chunk
-//     (forward walk, stored transposed).
-//   chunk phase (ssd_segment_bwd_chunks): k_chunk_bwd, per chunk and head:
-//     dx, dB, dC and ddt with the true entering state H + decay S_in and the
-//     true exit gradient G + decay dS_out, written into the buffers the conv
-//     backward consumes.
+//   chunk phase (ssd_segment_bwd_chunks): the true exit gradient and entering
+//     state of every chunk (k_state_pass from dS_out and S_in), then
+//     k_chunk_bwd per chunk and head: dx, dB, dC and the ddt partial sums,
+//     written into the buffers the conv backward consumes, and k_ddt.
 //   conv phase (ssd_conv1d_bwd): k_conv_bwd (SiLU' and the transposed conv,
 //     with a right halo from the causal successor segment) and k_bwd_reduce
 //     (deterministic parameter gradients).
@@ -35,7 +35,6 @@
 #include <type_traits>
 
 #include "ssd_internal.h"
-#include "state_walk.h"
 
 namespace ssd {
 
@@ -43,17 +42,30 @@ __device__ __forceinline__ float softplus_b(float z) {
     return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
 }
 
-template <typename T> struct KPermB;
-template <> struct KPermB<bf16> {
-    __device__ static __forceinline__ bf16x8 load(const bf16* p) {
-        const bf16x4 lo = *(const bf16x4*)p;
-        const bf16x4 hi = *(const bf16x4*)(p + 16);
-        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+// Token order inside the transposed [row][token] tiles of the backward.  A bf16
+// MFMA takes 32 tokens as its k dimension, 8 per lane group g, and an output
+// tile gives lane group g its rows 4g..4g+3.  Each 32-token block is stored as
+// tokens 4g..4g+3 and 16+4g..16+4g+3 at positions 8g..8g+7, so that one
+// 16-byte load fetches exactly the tokens that two stacked output tiles hold
+// in one lane: MFMA results then feed the next MFMA as its k operand.
+// float32 MFMAs take 16 tokens, 4 per lane group, in natural order.
+template <typename T> struct TokPerm;
+template <> struct TokPerm<bf16> {
+    static constexpr int BLK = 32;
+    __host__ __device__ static constexpr int pos(int i) {
+        return ((i & 15) >> 2) * 8 + (i >> 4) * 4 + (i & 3);
     }
 };
-template <> struct KPermB<float> {
-    __device__ static __forceinline__ f32x4 load(const float* p) { return *(const f32x4*)p; }
+template <> struct TokPerm<float> {
+    static constexpr int BLK = 16;
+    __host__ __device__ static constexpr int pos(int i) { return i; }
 };
+// Position of chunk-local token t in a permuted row.
+template <typename T>
+__device__ __forceinline__ int tpos(int t) {
+    constexpr int B = TokPerm<T>::BLK;
+    return (t & ~(B - 1)) + TokPerm<T>::pos(t & (B - 1));
+}
 
 template <typename T>
 __device__ __forceinline__ void load4(const T* p, float* o) {
@@ -68,10 +80,36 @@ __device__ __forceinline__ float sum_groups(float v) {
     return v;
 }
 
+// DPP lane moves inside rows of 16 lanes (VALU only, no LDS traffic).
+#define SSD_DPP(v, ctrl) \
+    __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), (ctrl), 0xF, 0xF, false))
+#define DPP_ROW_MIRROR 0x140
+#define DPP_ROW_HALF_MIRROR 0x141
+#define DPP_QUAD_XOR1 0xB1
+#define DPP_QUAD_XOR2 0x4E
+
+// Row sums of a 16x16 tile held as 4 rows per lane (rows 4g+r, column l%16):
+// reduces v[0..3] over the 16 lanes of each row group and returns, in lane l,
+// the sum for row r = 2*(l%16 >= 8) + ((l%8) >= 4) (all four lanes of a quad
+// hold the same value).
+__device__ __forceinline__ float row_sums16(const float v[4], int lr) {
+    const bool hi = lr >= 8;
+    const float k0 = hi ? v[2] : v[0], k1 = hi ? v[3] : v[1];
+    const float s0 = hi ? v[0] : v[2], s1 = hi ? v[1] : v[3];
+    const float a0 = k0 + SSD_DPP(s0, DPP_ROW_MIRROR);
+    const float a1 = k1 + SSD_DPP(s1, DPP_ROW_MIRROR);
+    const bool h2 = (lr & 4) != 0;
+    const float k = h2 ? a1 : a0, s = h2 ? a0 : a1;
+    float t = k + SSD_DPP(s, DPP_ROW_HALF_MIRROR);
+    t += SSD_DPP(t, DPP_QUAD_XOR2);
+    t += SSD_DPP(t, DPP_QUAD_XOR1);
+    return t;
+}
+
 // ---------------------------------------------------------------------------
 // B and C channels of one chunk, transposed to [part][n][token] (part 0 = B,
-// 1 = C), so that operands needing the token dimension as the MFMA k index
-// read them with contiguous loads.
+// 1 = C) in the permuted token order, so that operands needing the token
+// dimension as the MFMA k index read them with 16-byte loads.
 template <typename T>
 __global__ void __launch_bounds__(256) k_bc_transpose(Dims d, const T* __restrict__ xc,
                                                      T* __restrict__ bct) {
@@ -95,7 +133,7 @@ __global__ void __launch_bounds__(256) k_bc_transpose(Dims d, const T* __restric
                 const int jj = idx / (ns / VEC), nv = idx % (ns / VEC);
                 const vt v = *(const vt*)(xc + (rb + t0 + jj) * d.C + chan0 + n0 + nv * VEC);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) tile[(nv * VEC + e) * QP + jj] = v[e];
+                for (int e = 0; e < VEC; ++e) tile[(nv * VEC + e) * QP + tpos<T>(jj)] = v[e];
             }
             __syncthreads();
             for (int idx = threadIdx.x; idx < ns * (Q / VEC); idx += blockDim.x) {
@@ -107,226 +145,666 @@ __global__ void __launch_bounds__(256) k_bc_transpose(Dims d, const T* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Per (chunk, head, tile group): every wave owns one 16-token tile and computes,
-// for its tokens j as sources, dx_j and dB_j (outputs i >= j) and, for its
-// tokens i as outputs, dC_i (sources j <= i).  Chunks with more tiles than
-// waves are split over TG = Q / (16 NW) workgroups.  Per-token partial sums for
-// ddt go to the workspace; k_ddt assembles ddt per chunk.
-template <typename T, int P, int N, int Q, int NW>
-__global__ void __launch_bounds__(NW * 64) k_chunk_bwd(
+// Chunk states of the backward, every chunk in parallel (one workgroup per
+// chunk and head):
+//   Zh_c = sum_j exp(cs_e - cs_j) dt_j [seq_j = seq_e] x_j B_j^T   (what the
+//          chunk adds to the state leaving it),
+//   Zg_c = sum_i exp(cs_i) [seq_i = seq of the entering state] dy_i C_i^T
+//          (the gradient its outputs send to the state entering it),
+// both P x N in FP32, and the chunk's dy transposed to [p][token] (permuted
+// token order) for the chunk kernel.
+template <typename T, int P, int N>
+__global__ void __launch_bounds__(256) k_bwd_chunk_states(
     Dims d, SegTab tab, const T* __restrict__ xc, const T* __restrict__ bct,
-    const T* __restrict__ dy, const float* __restrict__ Dp, const float* __restrict__ dt_ws,
-    const float* __restrict__ cs_ws, const float* __restrict__ ctot,
-    const int32_t* __restrict__ seq, const T* __restrict__ hstT, const T* __restrict__ gst,
-    const float* __restrict__ S_in, const float* __restrict__ dS_out, float* __restrict__ dv,
-    T* __restrict__ dbc, float* __restrict__ rpart, float* __restrict__ tokp,
-    float* __restrict__ dotgh, float* __restrict__ red4) {
+    const T* __restrict__ dy, const float* __restrict__ dt_ws, const float* __restrict__ cs_ws,
+    const int32_t* __restrict__ seq, float* __restrict__ zh, float* __restrict__ zg,
+    T* __restrict__ dyT) {
     typedef Mma<T> M;
     typedef typename M::Frag Frag;
     constexpr int SL = M::SL, KS = M::KS;
+    constexpr int KT = 64;               // tokens per LDS slice
     constexpr int VEC = 16 / sizeof(T);
-    constexpr int QP = Q + VEC;  // pitch of dYt rows
-    constexpr int PP = P + VEC;  // pitch of [n][p] tiles
-    constexpr int NP = N + VEC;  // pitch of [p][n] tiles
-    constexpr int PT = P / 16, NT = N / 16, QT = Q / 16, KP = P / KS, KN = N / KS;
-    constexpr int TG = QT / NW;
-    static_assert(TG * NW == QT, "tiles must split evenly over the waves");
-    __shared__ __attribute__((aligned(16))) T dYt[P * QP];
-    __shared__ __attribute__((aligned(16))) T HT[N * PP];
-    __shared__ __attribute__((aligned(16))) T Gs[P * NP];
-    __shared__ __attribute__((aligned(16))) T GT[N * PP];
-    __shared__ float scs[Q], sdt[Q];
-    __shared__ int ssq[Q];
-    __shared__ float s_rw[NW][Q];  // per-wave row sums of F (summed in a fixed order)
-    __shared__ float s_red[NW][2];
-    // One KS-token block of operands shared by all waves, staged once per block:
-    // phase 1: C rows, dy rows, transposed C; phase 2: x rows, transposed B.
-    constexpr int RPN = N + VEC, RPP = P + VEC, TPK = KS + VEC;
-    // Two buffers: block k+1 is loaded from global memory into registers while
-    // block k is computed, then written to the other buffer.
-    __shared__ __attribute__((aligned(16))) T sRowN[2][KS * RPN];
-    __shared__ __attribute__((aligned(16))) T sRowP[2][KS * RPP];
-    __shared__ __attribute__((aligned(16))) T sTr[2][N * TPK];
-    // staging work per thread (vectors of VEC elements)
-    constexpr int NTH = NW * 64;
-    constexpr int V_RN = (KS * (N / VEC) + NTH - 1) / NTH;
-    constexpr int V_RP = (KS * (P / VEC) + NTH - 1) / NTH;
-    constexpr int V_TR = (N * (KS / VEC) + NTH - 1) / NTH;
-    __shared__ float s_pre, s_post;
+    constexpr int PITCH = KT + VEC;
+    constexpr int PT = P / 16, NT = N / 16, NTW = (NT + 3) / 4;
+    __shared__ __attribute__((aligned(16))) T sX[P * PITCH];
+    __shared__ __attribute__((aligned(16))) T sY[P * PITCH];
+    __shared__ __attribute__((aligned(16))) float wz[KT];
     typedef T vt __attribute__((ext_vector_type(VEC)));
 
-    const int cm = blockIdx.x, h = blockIdx.y;
-    const int64_t b = blockIdx.z / TG;
-    const int tg = blockIdx.z % TG;
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
+    const ChunkHead ch = chunk_head_of_block(d);
+    const int cm = ch.cm, h = ch.h;
+    const int64_t b = ch.b;
+    const int wave = wave_id(), lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
+    const int g = h / d.hpg;
+    const int Q = d.Q;
+    const int64_t rb = b * d.L, t0 = (int64_t)cm * Q, HPd = (int64_t)d.H * P;
+    const int k = seg_of_chunk(tab, cm, Q);
+    const int64_t s0 = tab.start[k];
+    const int64_t pred = seg_pred_token(tab, k);
+    const int64_t ptok = t0 > s0 ? t0 - 1 : (pred >= 0 ? pred : s0);
+    const int seq_ref = seq ? seq[rb + ptok] : 0;
+    const int seq_e = seq ? seq[rb + t0 + Q - 1] : 0;
+    const int64_t hl = ((int64_t)b * d.H + h) * d.L + t0;
+    const float cs_e = cs_ws[hl + Q - 1];
+    const T* bctB = bct + ((((int64_t)b * d.nchunk + cm) * d.G + g) * 2) * (int64_t)N * Q;
+    const T* bctC = bctB + (int64_t)N * Q;
+    T* yT = dyT + (((int64_t)b * d.nchunk + cm) * d.H + h) * (int64_t)P * Q;
+
+    f32x4 ah[PT][NTW], ag[PT][NTW];
+#pragma unroll
+    for (int i = 0; i < PT; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) ah[i][j] = ag[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int sl = 0; sl < Q / KT; ++sl) {
+        const int tb = sl * KT;
+        __syncthreads();
+        // token-fastest mapping: the transposed LDS stores of a wave hit
+        // consecutive 16-bit positions of one row
+        for (int idx = threadIdx.x; idx < KT * (P / VEC); idx += blockDim.x) {
+            const int pv = idx / KT, jj = idx % KT;
+            const int64_t tok = rb + t0 + tb + jj;
+            const bool same = !seq || seq[tok] == seq_e;
+            const float w = same ? __expf(cs_e - cs_ws[hl + tb + jj]) * dt_ws[hl + tb + jj] : 0.f;
+            const vt xv = *(const vt*)(xc + tok * d.C + (int64_t)h * P + pv * VEC);
+            const vt yv = *(const vt*)(dy + tok * HPd + (int64_t)h * P + pv * VEC);
+            const int q = tpos<T>(jj);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                sX[(pv * VEC + e) * PITCH + q] = (T)((float)xv[e] * w);
+                sY[(pv * VEC + e) * PITCH + q] = yv[e];
+            }
+        }
+        if (threadIdx.x < KT) {
+            const int jj = threadIdx.x;
+            const bool same = !seq || seq[rb + t0 + tb + jj] == seq_ref;
+            wz[tpos<T>(jj)] = same ? __expf(cs_ws[hl + tb + jj]) : 0.f;
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < P * (KT / VEC); idx += blockDim.x) {
+            const int p = idx / (KT / VEC), v = idx % (KT / VEC);
+            *(vt*)(yT + (int64_t)p * Q + tb + v * VEC) = *(const vt*)(sY + p * PITCH + v * VEC);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KT / KS; ++kk) {
+            const int jl = kk * KS + SL * lg;
+            Frag ax[PT], ay[PT];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                ax[pt] = M::load(&sX[(pt * 16 + lr) * PITCH + jl]);
+                ay[pt] = M::load(&sY[(pt * 16 + lr) * PITCH + jl]);
+            }
+            float wl[SL];
+#pragma unroll
+            for (int s = 0; s < SL; ++s) wl[s] = wz[jl + s];
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const int nt = wave + 4 * j;
+                if (nt < NT) {
+                    const int64_t o = (int64_t)(nt * 16 + lr) * Q + tb + jl;
+                    const Frag bB = M::load(bctB + o);
+                    const Frag bC = M::load_scaled(bctC + o, wl);
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) {
+                        ah[pt][j] = M::mma(ax[pt], bB, ah[pt][j]);
+                        ag[pt][j] = M::mma(ay[pt], bC, ag[pt][j]);
+                    }
+                }
+            }
+        }
+    }
+    const int64_t so = (((int64_t)b * d.nchunk + cm) * d.H + h) * (P * N);
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+            const int nt = wave + 4 * j;
+            if (nt < NT) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t o = so + (int64_t)(pt * 16 + 4 * lg + r) * N + nt * 16 + lr;
+                    zh[o] = ah[pt][j][r];
+                    zg[o] = ag[pt][j][r];
+                }
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk-to-chunk passing inside a segment, elementwise over P x N in FP32
+// (one workgroup per head, segment and row).  alpha_c = exp(cs at the chunk's
+// last token) when the state entering chunk c and that token belong to one
+// sequence, else exactly 0.  With G_c the gradient of the state leaving chunk
+// c and H_c the state entering it:
+//   PASS_SUMMARY: G <- alpha_c G + Zg_c from the last chunk with zero final
+//                 gradient; leaves L_k (dL/dS_in of the segment's own outputs)
+//                 and a_k = prod alpha_c in the summary layout.
+//   PASS_TRUE:    G from dS_out backwards, storing every G_c as [p][n] and
+//                 [n][p]; then H from S_in forwards, storing every H_c as
+//                 [n][p] and <G_c, H_c> per chunk.
+enum PassMode { PASS_SUMMARY = 0, PASS_TRUE = 1 };
+
+template <typename T, int P, int N, int MODE>
+__global__ void __launch_bounds__(256) k_state_pass(
+    Dims d, SegTab tab, const float* __restrict__ ctot, const int32_t* __restrict__ seq,
+    const float* __restrict__ zg, const float* __restrict__ zh, const float* __restrict__ S_in,
+    const float* __restrict__ dS_out, float* __restrict__ summary, T* __restrict__ gpn,
+    T* __restrict__ gnp, T* __restrict__ hnp, float* __restrict__ dotgh) {
+    constexpr int PN4 = P * N / 4;
+    constexpr int E4 = (PN4 + 255) / 256;  // float4 groups per thread
+    constexpr int TP = N + 1;              // fp32 transpose tile pitch
+    constexpr int VEC = 16 / sizeof(T);
+    typedef T vt __attribute__((ext_vector_type(VEC)));
+    typedef T vt4 __attribute__((ext_vector_type(4)));
+    __shared__ float tile[MODE == PASS_TRUE ? P * TP : 1];
+    __shared__ float sred[4];
+    const int h = blockIdx.x, k = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int Q = d.Q;
+    const int64_t rb = b * d.L;
+    const int64_t s0 = tab.start[k];
+    const int nc = (int)(tab.len[k] / Q);
+    const int cm0 = (int)(s0 / Q);
+    const int64_t pred = seg_pred_token(tab, k);
+    const float* ct = ctot + ((int64_t)b * d.H + h) * d.nchunk;
+    const int64_t per = (int64_t)d.batch * d.H * P * N;
+    const int64_t sg = ((int64_t)k * d.batch + b) * d.H + h;
+    auto alpha_of = [&](int c) {
+        const int64_t t0 = (int64_t)(cm0 + c) * Q;
+        const int64_t ptok = c > 0 ? t0 - 1 : (pred >= 0 ? pred : s0);
+        const bool same = !seq || seq[rb + ptok] == seq[rb + t0 + Q - 1];
+        return same ? expf(ct[cm0 + c]) : 0.f;
+    };
+    auto st_off = [&](int c) { return (((int64_t)b * d.nchunk + cm0 + c) * d.H + h) * (P * N); };
+
+    f32x4 acc[E4];
+    // reverse pass over the gradient
+#pragma unroll
+    for (int q = 0; q < E4; ++q) {
+        const int i4 = threadIdx.x + q * 256;
+        acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (MODE == PASS_TRUE && i4 < PN4) acc[q] = *(const f32x4*)(dS_out + sg * P * N + 4 * i4);
+    }
+    float ablk = 1.f;
+    for (int c = nc - 1; c >= 0; --c) {
+        const int64_t so = st_off(c);
+        if (MODE == PASS_TRUE) {
+#pragma unroll
+            for (int q = 0; q < E4; ++q) {
+                const int i4 = threadIdx.x + q * 256;
+                if (i4 < PN4) {
+                    vt4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = (T)acc[q][e];
+                    *(vt4*)(gpn + so + 4 * i4) = v;
+                    const int p = (4 * i4) / N, n = (4 * i4) % N;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) tile[p * TP + n + e] = acc[q][e];
+                }
+            }
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < N * (P / VEC); idx += 256) {
+                const int n = idx / (P / VEC), p0 = (idx % (P / VEC)) * VEC;
+                vt v;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) v[e] = (T)tile[(p0 + e) * TP + n];
+                *(vt*)(gnp + so + (int64_t)n * P + p0) = v;
+            }
+            __syncthreads();
+        }
+        const float a = alpha_of(c);
+        ablk *= a;
+#pragma unroll
+        for (int q = 0; q < E4; ++q) {
+            const int i4 = threadIdx.x + q * 256;
+            if (i4 < PN4) {
+                const f32x4 z = *(const f32x4*)(zg + so + 4 * i4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[q][e] = a * acc[q][e] + z[e];
+            }
+        }
+    }
+    if (MODE == PASS_SUMMARY) {
+#pragma unroll
+        for (int q = 0; q < E4; ++q) {
+            const int i4 = threadIdx.x + q * 256;
+            if (i4 < PN4) *(f32x4*)(summary + (int64_t)k * per + sg % (d.batch * d.H) * (P * N) +
+                                    4 * i4) = acc[q];
+        }
+        if (threadIdx.x == 0) summary[(int64_t)d.nseg * per + sg] = ablk;
+        return;
+    }
+    // forward pass over the state
+#pragma unroll
+    for (int q = 0; q < E4; ++q) {
+        const int i4 = threadIdx.x + q * 256;
+        acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (i4 < PN4) acc[q] = *(const f32x4*)(S_in + sg * P * N + 4 * i4);
+    }
+    const int wave = wave_id(), lane = threadIdx.x % 64;
+    for (int c = 0; c < nc; ++c) {
+        const int64_t so = st_off(c);
+        float dot = 0.f;
+#pragma unroll
+        for (int q = 0; q < E4; ++q) {
+            const int i4 = threadIdx.x + q * 256;
+            if (i4 < PN4) {
+                const vt4 gv = *(const vt4*)(gpn + so + 4 * i4);  // written by this thread
+                const int p = (4 * i4) / N, n = (4 * i4) % N;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dot += (float)gv[e] * acc[q][e];
+                    tile[p * TP + n + e] = acc[q][e];
+                }
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+        if (lane == 0) sred[wave] = dot;
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < N * (P / VEC); idx += 256) {
+            const int n = idx / (P / VEC), p0 = (idx % (P / VEC)) * VEC;
+            vt v;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[e] = (T)tile[(p0 + e) * TP + n];
+            *(vt*)(hnp + so + (int64_t)n * P + p0) = v;
+        }
+        if (threadIdx.x == 0)
+            dotgh[((int64_t)b * d.nchunk + cm0 + c) * d.H + h] = sred[0] + sred[1] + sred[2] + sred[3];
+        const float a = alpha_of(c);
+#pragma unroll
+        for (int q = 0; q < E4; ++q) {
+            const int i4 = threadIdx.x + q * 256;
+            if (i4 < PN4) {
+                const f32x4 z = *(const f32x4*)(zh + so + 4 * i4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[q][e] = a * acc[q][e] + z[e];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The chunk backward, one workgroup per (chunk, head) with NW = Q/(16 TPW)
+// waves of TPW 16-token tiles each.  Tiles come in pairs (t, Q/16-1-t), one
+// from each end of the chunk, so that every wave meets the same number of
+// causal (i >= j) tile pairs; every operand fragment read from LDS feeds the
+// MFMAs of all TPW tiles of the wave.
+//
+//   phase A (its tiles as outputs i):  dC_i = f_i H^T dy_i
+//                                        + sum_{j<=i} M_ij dt_j (dy_i.x_j) B_j
+//   phase B1 (its tiles as sources j): dx_j = dt_j (g_j G B_j + sum_{i>=j} M_ij (C_i.B_j) dy_i)
+//                                      and the per-token ddt terms
+//   phase B2 (its tiles as sources j): dB_j = dt_j (g_j G^T x_j + sum_{i>=j} M_ij (dy_i.x_j) C_i)
+// with M_ij = exp(cs_i - cs_j) [same sequence], f_i = exp(cs_i) [i in the
+// entering state's sequence], g_j = exp(cs_e - cs_j) [j in the last token's
+// sequence], H the state entering the chunk and G the gradient of the state
+// leaving it.  B1 and B2 are separate passes (B2 recomputes dy_i.x_j) so that
+// the dx and dB accumulators are never live together.  The i-blocks (phase B)
+// and j-blocks (phase A) of KS tokens are
+// staged once per workgroup in LDS, double buffered; transposed operands come
+// pre-transposed in the permuted token order.  Per-token partial sums for ddt
+// go to the workspace; k_ddt assembles ddt per chunk.
+template <typename T, int P, int N, int Q, int TPW>
+struct ChunkBwd {
+    typedef Mma<T> M;
+    static constexpr int SL = M::SL, KS = M::KS;
+    static constexpr int VEC = 16 / sizeof(T);
+    static constexpr int QT = Q / 16, NW = QT / TPW, NTH = NW * 64;
+    static constexpr int PT = P / 16, NT = N / 16, KP = P / KS, KN = N / KS;
+    static constexpr int RPN = N + VEC, RPP = P + VEC, TPK = KS + VEC;
+    // staging buffers, elements per buffer
+    static constexpr int S_CROW = KS * RPN, S_DROW = KS * RPP, S_CT = N * TPK, S_DT = P * TPK;
+    static constexpr int STAGE_A = S_DROW + S_CT;            // phase A: x rows, B^T
+    static constexpr int STAGE_B1 = S_CROW + S_DROW + S_DT;  // phase B1: C rows, dy rows, dy^T
+    static constexpr int STAGE_B2 = S_DROW + S_CT;           // phase B2: dy rows, C^T
+    static constexpr int ST_G = P * RPN;                     // G [p][n]
+    static constexpr int ST_GT = N * RPP;                    // G^T or H^T [n][p]
+    static constexpr int cmax(int a, int b) { return a > b ? a : b; }
+    static constexpr int U_ELEMS =
+        cmax(cmax(2 * STAGE_A, 2 * STAGE_B1), cmax(2 * STAGE_B2, cmax(ST_G, ST_GT)));
+    static constexpr size_t U_BYTES = (size_t)U_ELEMS * sizeof(T);
+    static constexpr size_t TOK_BYTES = (size_t)Q * 20 + (size_t)NW * Q * 4 + QT * QT * 4;
+    static constexpr size_t LDS = U_BYTES + TOK_BYTES + 64;
+    static_assert(NW * TPW == QT && TPW % 2 == 0, "tiles in pairs");
+    // tile index of slot s of wave w: pairs (t, QT-1-t)
+    __device__ static __forceinline__ int tile(int w, int s) {
+        const int t = (s / 2) * (QT / 2) + ((s / 2) % 2 ? NW - 1 - w : w);
+        return s % 2 ? QT - 1 - t : t;
+    }
+};
+
+template <typename T, int P, int N, int Q, int TPW>
+__global__ void __launch_bounds__(Q / (16 * TPW) * 64) k_chunk_bwd(
+    Dims d, SegTab tab, const T* __restrict__ xc, const T* __restrict__ bct,
+    const T* __restrict__ dy, const T* __restrict__ dyT, const float* __restrict__ Dp,
+    const float* __restrict__ dt_ws, const float* __restrict__ cs_ws,
+    const int32_t* __restrict__ seq, const T* __restrict__ gpn, const T* __restrict__ gnp,
+    const T* __restrict__ hnp, float* __restrict__ dv, T* __restrict__ dbc,
+    float* __restrict__ rpart, float* __restrict__ tokp, float* __restrict__ red4) {
+    typedef ChunkBwd<T, P, N, Q, TPW> K;
+    typedef Mma<T> M;
+    typedef typename M::Frag Frag;
+    typedef typename M::Elem E;
+    constexpr int SL = K::SL, KS = K::KS, VEC = K::VEC, NW = K::NW, NTH = K::NTH;
+    constexpr int PT = K::PT, NT = K::NT, KP = K::KP, KN = K::KN;
+    constexpr int RPN = K::RPN, RPP = K::RPP, TPK = K::TPK;
+    typedef T vt __attribute__((ext_vector_type(VEC)));
+    __shared__ __attribute__((aligned(16))) T U[K::U_ELEMS];
+    __shared__ __attribute__((aligned(16))) float scs[Q];
+    __shared__ __attribute__((aligned(16))) float sdt[Q];
+    __shared__ __attribute__((aligned(16))) int ssq[Q];
+    __shared__ float s_rw[NW][Q];  // per-wave row sums of F
+    __shared__ float s_red[NW];
+    // Decay factors for chunks without a sequence start inside (one continuous
+    // cumulative sum): with F_a, L_a the cumulative sums at the first and last
+    // token of 16-token tile a,
+    //   exp(cs_i - cs_j) = exp(cs_i - F_a(i)) exp(F_a(i) - L_b(j)) exp(L_b(j) - cs_j),
+    // every factor bounded by exp(24) (a tile spans 16 tokens, |dt A| <= 1.6), so
+    // the intra-chunk decays need no transcendental in the inner loops.
+    __shared__ __attribute__((aligned(16))) float sea[Q];  // exp(cs_t - F(t))
+    __shared__ __attribute__((aligned(16))) float seb[Q];  // exp(L(t) - cs_t) dt_t
+    __shared__ float stab[K::QT * K::QT];                   // exp(F_a - L_b), a >= b; else 0
+
+    const ChunkHead ch = chunk_head_of_block(d);
+    const int cm = ch.cm, h = ch.h;
+    const int64_t b = ch.b;
+    const int wave = wave_id(), lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
     const int g = h / d.hpg;
     const int64_t rb = b * d.L, t0 = (int64_t)cm * Q;
     const int64_t HPd = (int64_t)d.H * P;
     const int k = seg_of_chunk(tab, cm, Q);
     const int64_t s0 = tab.start[k];
-    const int nc = (int)(tab.len[k] / Q);
-    const int c = (int)((t0 - s0) / Q);
-    const int cseg0 = (int)(s0 / Q);
-    const bool first = c == 0, last = c == nc - 1;
     const int64_t pred = seg_pred_token(tab, k);
-    const int64_t segref = pred >= 0 ? pred : s0;
-    const int64_t refc = first ? segref : t0 - 1;
-    const int64_t segend = s0 + tab.len[k] - 1;
-    const int seq_segref = seq ? seq[rb + segref] : 0;
+    const int64_t refc = t0 > s0 ? t0 - 1 : (pred >= 0 ? pred : s0);
     const int seq_refc = seq ? seq[rb + refc] : 0;
     const int seq_e = seq ? seq[rb + t0 + Q - 1] : 0;
-    const int seq_segend = seq ? seq[rb + segend] : 0;
+    // a packed sequence starts inside the chunk: pairs need the sequence mask
+    const bool split = seq && seq[rb + t0] != seq_e;
     const int64_t xoff = (int64_t)h * P, boff = HPd + (int64_t)g * N;
     const int64_t coff = HPd + (int64_t)d.G * N + (int64_t)g * N;
     const T* bctB = bct + ((((int64_t)b * d.nchunk + cm) * d.G + g) * 2 + 0) * (int64_t)N * Q;
     const T* bctC = bctB + (int64_t)N * Q;
+    const T* yT = dyT + (((int64_t)b * d.nchunk + cm) * d.H + h) * (int64_t)P * Q;
     const int64_t st_off = (((int64_t)b * d.nchunk + cm) * d.H + h) * (P * N);
-    const int64_t sg_off = (((int64_t)k * d.batch + b) * d.H + h) * (P * N);
     const int64_t hl = ((int64_t)b * d.H + h) * d.L + t0;  // (row, head) token base
 
-    if (threadIdx.x == 0) {
-        const float* ct = ctot + ((int64_t)b * d.H + h) * d.nchunk;
-        float pre = 0.f, post = 0.f;
-        for (int cc = 0; cc < c; ++cc) pre += ct[cseg0 + cc];
-        for (int cc = c + 1; cc < nc; ++cc) post += ct[cseg0 + cc];
-        s_pre = pre;
-        s_post = post;
-    }
-    for (int idx = threadIdx.x; idx < Q * (P / VEC); idx += blockDim.x) {
-        const int jj = idx / (P / VEC), pv = idx % (P / VEC);
-        const vt v = *(const vt*)(dy + (rb + t0 + jj) * HPd + xoff + pv * VEC);
+    int tt[TPW];  // first token of each of this wave's tiles
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) dYt[(pv * VEC + e) * QP + jj] = v[e];
-    }
-    for (int j = threadIdx.x; j < Q; j += blockDim.x) {
+    for (int s = 0; s < TPW; ++s) tt[s] = K::tile(wave, s) * 16;
+
+    for (int j = threadIdx.x; j < Q; j += NTH) {
         scs[j] = cs_ws[hl + j];
         sdt[j] = dt_ws[hl + j];
         ssq[j] = seq ? seq[rb + t0 + j] : 0;
     }
-    for (int j = threadIdx.x; j < NW * Q; j += blockDim.x) (&s_rw[0][0])[j] = 0.f;
-    for (int idx = threadIdx.x; idx < N * (P / VEC); idx += blockDim.x) {
+    for (int j = threadIdx.x; j < NW * Q; j += NTH) (&s_rw[0][0])[j] = 0.f;
+    // H^T [n][p]
+    for (int idx = threadIdx.x; idx < N * (P / VEC); idx += NTH) {
         const int n = idx / (P / VEC), pv = idx % (P / VEC);
-        vt v;
-        if (first) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) v[e] = (T)0.f;
-        } else {
-            v = *(const vt*)(hstT + st_off + (int64_t)n * P + pv * VEC);
-        }
-        *(vt*)&HT[n * PP + pv * VEC] = v;
+        *(vt*)&U[n * RPP + pv * VEC] = *(const vt*)(hnp + st_off + (int64_t)n * P + pv * VEC);
     }
     __syncthreads();
-    // True entering state H = H_zero + exp(pre) S_in (while no sequence starts
-    // between the segment start and the chunk), true exit gradient
-    // G = G_zero + exp(post) dS_out (while none starts after the chunk).
-    // Vector loads along n: 4 (fp32) or 8 (bf16) entries per step.
-    const float hs = (seq_refc == seq_segref) ? expf(s_pre) : 0.f;
-    const float gs = (seq_e == seq_segend) ? expf(s_post) : 0.f;
-    float dot = 0.f;
-    for (int idx = threadIdx.x; idx < P * (N / VEC); idx += blockDim.x) {
-        const int p = idx / (N / VEC), n0 = (idx % (N / VEC)) * VEC;
-        const int64_t o = (int64_t)p * N + n0;
-        vt gz;
-        if (last) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) gz[e] = (T)0.f;
-        } else {
-            gz = *(const vt*)(gst + st_off + o);
+    constexpr int QT = K::QT;
+    if (!split) {
+        for (int t = threadIdx.x; t < Q; t += NTH) {
+            const int t16 = t & ~15;
+            sea[t] = __expf(scs[t] - scs[t16]);
+            seb[t] = __expf(scs[t16 + 15] - scs[t]) * sdt[t];
         }
-        float so[VEC], si[VEC];
-#pragma unroll
-        for (int q = 0; q < VEC / 4; ++q) {
-            const f32x4 a4 = *(const f32x4*)(dS_out + sg_off + o + 4 * q);
-            const f32x4 b4 = *(const f32x4*)(S_in + sg_off + o + 4 * q);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                so[4 * q + e] = a4[e];
-                si[4 * q + e] = b4[e];
-            }
+        for (int q = threadIdx.x; q < QT * QT; q += NTH) {
+            const int a = q / QT, c = q % QT;
+            stab[q] = a >= c ? __expf(scs[16 * a] - scs[16 * c + 15]) : 0.f;
         }
-        vt gv;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const int n = n0 + e;
-            const float gt = (float)gz[e] + gs * so[e];
-            const float ht = (float)HT[n * PP + p] + hs * si[e];
-            HT[n * PP + p] = (T)ht;
-            GT[n * PP + p] = (T)gt;
-            gv[e] = (T)gt;
-            dot += gt * ht;
-        }
-        *(vt*)&Gs[p * NP + n0] = gv;
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
-    if (lane == 0) s_red[wave][0] = dot;
-    __syncthreads();
-    if (threadIdx.x == 0 && tg == 0) {
-        float t = 0.f;
-        for (int w = 0; w < NW; ++w) t += s_red[w][0];
-        dotgh[((int64_t)b * d.nchunk + cm) * d.H + h] = t;  // <G_exit, H_enter>
+        __syncthreads();
     }
 
     const float cs_e = scs[Q - 1];
     const float Dh = Dp[h];
-    float dD_part = 0.f;
-    {
-        const int it = tg * NW + wave;
-        const int j0T = it * 16;
-        const int tj = j0T + lr;  // this lane's token (column of every output tile)
-        const int64_t trow = rb + t0 + tj;
-        const float cs_j = scs[tj], dt_j = sdt[tj];
-        const int sq_j = ssq[tj];
-        const float g_j = (sq_j == seq_e) ? expf(cs_e - cs_j) : 0.f;
-        const float f_j = (sq_j == seq_refc) ? expf(cs_j) : 0.f;
-        const T* xrow = xc + trow * d.C + xoff + 4 * lg;   // x of token tj at rows p of a tile
-        const T* dyrow = dy + trow * HPd + xoff + 4 * lg;  // dy likewise
 
-        // ---- dx and dB of the tile's tokens (as sources j) ----
-        Frag Bn[KN], Xn[KP];
+    // =================== phase A: dC of the wave's tiles (outputs i) ===================
+    float u_t[TPW];
+    {
+        f32x4 adc[TPW][NT];
+        Frag Dn[TPW][KP];
+        float cs_i[TPW], e3[TPW];
+        int sq_i[TPW];
 #pragma unroll
-        for (int kn = 0; kn < KN; ++kn) Bn[kn] = M::load(xc + trow * d.C + boff + kn * KS + SL * lg);
-#pragma unroll
-        for (int kp = 0; kp < KP; ++kp) Xn[kp] = M::load(xc + trow * d.C + xoff + kp * KS + SL * lg);
-        f32x4 adx[PT], adb[NT];
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            adx[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kn = 0; kn < KN; ++kn)
-                adx[pt] = M::mma(M::load(&Gs[(pt * 16 + lr) * NP + kn * KS + SL * lg]), Bn[kn],
-                                 adx[pt]);
-            adx[pt] *= g_j;
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            adb[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int it = 0; it < TPW; ++it) {
+            const int ti = tt[it] + lr;
+            const int64_t trow = rb + t0 + ti;
+            cs_i[it] = scs[ti];
+            sq_i[it] = ssq[ti];
+            e3[it] = split ? 0.f : sea[ti];
+            const float f_i = (sq_i[it] == seq_refc) ? __expf(cs_i[it]) : 0.f;
 #pragma unroll
             for (int kp = 0; kp < KP; ++kp)
-                adb[nt] = M::mma(M::load(&GT[(nt * 16 + lr) * PP + kp * KS + SL * lg]), Xn[kp],
-                                 adb[nt]);
-            adb[nt] *= g_j;
-        }
-        // v_j: what source j adds, through the exit state, to every decay inside the chunk
-        float vpart = 0.f;
+                Dn[it][kp] = M::load(dy + trow * HPd + xoff + kp * KS + SL * lg);
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            float xv[4];
-            load4(xrow + pt * 16, xv);
+            for (int nt = 0; nt < NT; ++nt) {
+                f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) vpart += xv[r] * adx[pt][r];
+                for (int kp = 0; kp < KP; ++kp)
+                    a = M::mma(M::load(&U[(nt * 16 + lr) * RPP + kp * KS + SL * lg]), Dn[it][kp], a);
+                adc[it][nt] = a * f_i;
+            }
+            // u_i = C_i . (entering-state part of dC_i)
+            float up = 0.f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                float cv[4];
+                load4(xc + trow * d.C + coff + nt * 16 + 4 * lg, cv);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) up += cv[r] * adc[it][nt][r];
+            }
+            u_t[it] = sum_groups(up);
         }
-        const float v_j = dt_j * sum_groups(vpart);
-        // F[i][j] = (C_i.B_j)(dy_i.x_j) exp(cs_i - cs_j) dt_j [same sequence, i >= j]:
-        // row sums R_i (over this tile's j) go to s_rw, column sums K_j stay in kacc.
-        // Both come from the same fp32 products, so sum_{i>=t}(R_i - K_i) cancels
-        // in fp32 and equals sum_{i>=t} sum_{j<t} F[i][j].
-        float kacc = 0.f;
-        // Lockstep over the i-blocks this workgroup needs; a wave computes only
-        // for blocks that reach its tile (i >= j).
-        const int ib_lo = ((tg * NW * 16) / KS) * KS;
-        // phase-1 block loads: C rows, dy rows, transposed C
-        auto fetch1 = [&](int i0, vt (&rn)[V_RN], vt (&rp)[V_RP], vt (&tr)[V_TR]) {
+        __syncthreads();  // H^T consumed; the union now holds staging
+
+        constexpr int V_X = (KS * (P / VEC) + NTH - 1) / NTH;
+        constexpr int V_B = (N * (KS / VEC) + NTH - 1) / NTH;
+        auto fetchA = [&](int j0, vt (&rx)[V_X], vt (&rbt)[V_B]) {
+#pragma unroll
+            for (int q = 0; q < V_X; ++q) {
+                const int idx = threadIdx.x + q * NTH;
+                if (idx < KS * (P / VEC)) {
+                    const int jj = idx / (P / VEC), pv = idx % (P / VEC);
+                    rx[q] = *(const vt*)(xc + (rb + t0 + j0 + jj) * d.C + xoff + pv * VEC);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < V_B; ++q) {
+                const int idx = threadIdx.x + q * NTH;
+                if (idx < N * (KS / VEC)) {
+                    const int n = idx / (KS / VEC), kv = idx % (KS / VEC);
+                    rbt[q] = *(const vt*)(bctB + (int64_t)n * Q + j0 + kv * VEC);
+                }
+            }
+        };
+        auto storeA = [&](T* s, const vt (&rx)[V_X], const vt (&rbt)[V_B]) {
+#pragma unroll
+            for (int q = 0; q < V_X; ++q) {
+                const int idx = threadIdx.x + q * NTH;
+                if (idx < KS * (P / VEC))
+                    *(vt*)&s[(idx / (P / VEC)) * RPP + (idx % (P / VEC)) * VEC] = rx[q];
+            }
+#pragma unroll
+            for (int q = 0; q < V_B; ++q) {
+                const int idx = threadIdx.x + q * NTH;
+                if (idx < N * (KS / VEC))
+                    *(vt*)&s[K::S_DROW + (idx / (KS / VEC)) * TPK + (idx % (KS / VEC)) * VEC] = rbt[q];
+            }
+        };
+        {
+            vt rx[V_X], rbt[V_B];
+            fetchA(0, rx, rbt);
+            storeA(U, rx, rbt);
+        }
+        __syncthreads();
+        int buf = 0;
+#pragma unroll 1
+        for (int j0 = 0; j0 < Q; j0 += KS, buf ^= 1) {
+            const bool more = j0 + KS < Q;
+            vt rx[V_X], rbt[V_B];
+            if (more) fetchA(j0 + KS, rx, rbt);
+            const T* sX = U + buf * K::STAGE_A;
+            const T* sBT = sX + K::S_DROW;
+            // a tile is active for the block when some j of the block is <= some i of the tile
+            bool act[TPW], any_act = false;
+#pragma unroll
+            for (int it = 0; it < TPW; ++it) {
+                act[it] = j0 <= tt[it] + 15;
+                any_act = any_act || act[it];
+            }
+            if (any_act) {
+                Frag vf[TPW];
+#pragma unroll
+                for (int st = 0; st < KS / 16; ++st) {
+                    const int js = j0 + st * 16;
+                    Frag xf[KP];
+#pragma unroll
+                    for (int kp = 0; kp < KP; ++kp)
+                        xf[kp] = M::load(&sX[(st * 16 + lr) * RPP + kp * KS + SL * lg]);
+                    const f32x4 ej = *(const f32x4*)&seb[js + 4 * lg];
+#pragma unroll
+                    for (int it = 0; it < TPW; ++it) {
+                        const int i0 = tt[it];
+                        float vv[4] = {0.f, 0.f, 0.f, 0.f};
+                        if (js <= i0 + 15) {
+                            f32x4 w = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int kp = 0; kp < KP; ++kp) w = M::mma(xf[kp], Dn[it][kp], w);
+                            const int ti = i0 + lr;
+                            if (!split) {
+                                const float bi = e3[it] * stab[(i0 / 16) * QT + js / 16];
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) vv[r] = w[r] * (ej[r] * bi);
+                                if (js == i0) {
+#pragma unroll
+                                    for (int r = 0; r < 4; ++r)
+                                        if (js + 4 * lg + r > ti) vv[r] = 0.f;
+                                }
+                            } else {
+                                const f32x4 cj = *(const f32x4*)&scs[js + 4 * lg];
+                                const f32x4 dj = *(const f32x4*)&sdt[js + 4 * lg];
+                                const int4 sj = *(const int4*)&ssq[js + 4 * lg];
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const int j = js + 4 * lg + r;
+                                    const bool ok = j <= ti && sj[r] == sq_i[it];
+                                    vv[r] = ok ? w[r] * (__expf(cs_i[it] - cj[r]) * dj[r]) : 0.f;
+                                }
+                            }
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) vf[it][st * 4 + r] = (E)vv[r];
+                    }
+                }
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const Frag bt = M::load(&sBT[(nt * 16 + lr) * TPK + SL * lg]);
+#pragma unroll
+                    for (int it = 0; it < TPW; ++it) adc[it][nt] = M::mma(bt, vf[it], adc[it][nt]);
+                }
+            }
+            if (more) storeA(U + (buf ^ 1) * K::STAGE_A, rx, rbt);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int it = 0; it < TPW; ++it) {
+            const int64_t trow = rb + t0 + tt[it] + lr;
+            T* dcrow = dbc + (trow * d.H + h) * (2 * N) + N;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dcrow[nt * 16 + 4 * lg + r] = (T)adc[it][nt][r];
+        }
+    }
+
+    // ============ phase B1: dx and the ddt terms of the wave's tiles (sources j) ============
+    // G [p][n] into the union (every wave is past its last staging read)
+    for (int idx = threadIdx.x; idx < P * (N / VEC); idx += NTH) {
+        const int p = idx / (N / VEC), nv = idx % (N / VEC);
+        *(vt*)&U[p * RPN + nv * VEC] = *(const vt*)(gpn + st_off + (int64_t)p * N + nv * VEC);
+    }
+    __syncthreads();
+
+    float cs_j[TPW], dt_j[TPW], e2[TPW], gj[TPW];
+    int sq_j[TPW];
+#pragma unroll
+    for (int jt = 0; jt < TPW; ++jt) {
+        const int tj = tt[jt] + lr;
+        cs_j[jt] = scs[tj];
+        dt_j[jt] = sdt[tj];
+        sq_j[jt] = ssq[tj];
+        e2[jt] = split ? 0.f : __expf(scs[tt[jt] + 15] - cs_j[jt]);
+        gj[jt] = (sq_j[jt] == seq_e) ? __expf(cs_e - cs_j[jt]) : 0.f;
+    }
+    // decay of pair (i, j) for the i-sub-tile starting at `is`, rows 4 lg + r
+    auto pair_decay = [&](int is, int jt, const f32x4& ea, float (&m)[4]) {
+        const int j0 = tt[jt], tj = j0 + lr;
+        if (!split) {
+            const float bj = stab[(is / 16) * QT + j0 / 16] * e2[jt];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) m[r] = ea[r] * bj;
+            if (is == j0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (is + 4 * lg + r < tj) m[r] = 0.f;
+            }
+        } else {
+            const f32x4 ci = *(const f32x4*)&scs[is + 4 * lg];
+            const int4 si = *(const int4*)&ssq[is + 4 * lg];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool ok = is + 4 * lg + r >= tj && si[r] == sq_j[jt];
+                m[r] = ok ? __expf(ci[r] - cs_j[jt]) : 0.f;
+            }
+        }
+    };
+
+    float v_t[TPW], kq[TPW], q_t[TPW];
+    float dD_part = 0.f;
+    {
+        Frag Bn[TPW][KN], Xn[TPW][KP];
+        f32x4 adx[TPW][PT];
+#pragma unroll
+        for (int jt = 0; jt < TPW; ++jt) {
+            const int64_t trow = rb + t0 + tt[jt] + lr;
+            kq[jt] = 0.f;
+#pragma unroll
+            for (int kn = 0; kn < KN; ++kn)
+                Bn[jt][kn] = M::load(xc + trow * d.C + boff + kn * KS + SL * lg);
+#pragma unroll
+            for (int kp = 0; kp < KP; ++kp)
+                Xn[jt][kp] = M::load(xc + trow * d.C + xoff + kp * KS + SL * lg);
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kn = 0; kn < KN; ++kn)
+                    a = M::mma(M::load(&U[(pt * 16 + lr) * RPN + kn * KS + SL * lg]), Bn[jt][kn], a);
+                adx[jt][pt] = a * gj[jt];
+            }
+            // v_j: what source j adds, through the exit state, to every decay inside the chunk
+            float vp = 0.f;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                float xv[4];
+                load4(xc + trow * d.C + xoff + pt * 16 + 4 * lg, xv);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vp += xv[r] * adx[jt][pt][r];
+            }
+            v_t[jt] = dt_j[jt] * sum_groups(vp);
+        }
+        __syncthreads();  // G consumed
+
+        constexpr int V_RN = (KS * (N / VEC) + NTH - 1) / NTH;
+        constexpr int V_RP = (KS * (P / VEC) + NTH - 1) / NTH;
+        constexpr int V_DT = (P * (KS / VEC) + NTH - 1) / NTH;
+        constexpr int SB1 = K::S_CROW + K::S_DROW + K::S_DT;  // C rows, dy rows, dy^T
+        auto fetch = [&](int i0, vt (&rn)[V_RN], vt (&rp)[V_RP], vt (&rd)[V_DT]) {
 #pragma unroll
             for (int q = 0; q < V_RN; ++q) {
                 const int idx = threadIdx.x + q * NTH;
@@ -344,248 +822,281 @@ __global__ void __launch_bounds__(NW * 64) k_chunk_bwd(
                 }
             }
 #pragma unroll
-            for (int q = 0; q < V_TR; ++q) {
+            for (int q = 0; q < V_DT; ++q) {
                 const int idx = threadIdx.x + q * NTH;
-                if (idx < N * (KS / VEC)) {
-                    const int n = idx / (KS / VEC), kv = idx % (KS / VEC);
-                    tr[q] = *(const vt*)(bctC + (int64_t)n * Q + i0 + kv * VEC);
+                if (idx < P * (KS / VEC)) {
+                    const int p = idx / (KS / VEC), kv = idx % (KS / VEC);
+                    rd[q] = *(const vt*)(yT + (int64_t)p * Q + i0 + kv * VEC);
                 }
             }
         };
-        auto store1 = [&](int buf, const vt (&rn)[V_RN], const vt (&rp)[V_RP], const vt (&tr)[V_TR]) {
+        auto store = [&](T* s, const vt (&rn)[V_RN], const vt (&rp)[V_RP], const vt (&rd)[V_DT]) {
 #pragma unroll
             for (int q = 0; q < V_RN; ++q) {
                 const int idx = threadIdx.x + q * NTH;
                 if (idx < KS * (N / VEC))
-                    *(vt*)&sRowN[buf][(idx / (N / VEC)) * RPN + (idx % (N / VEC)) * VEC] = rn[q];
+                    *(vt*)&s[(idx / (N / VEC)) * RPN + (idx % (N / VEC)) * VEC] = rn[q];
             }
 #pragma unroll
             for (int q = 0; q < V_RP; ++q) {
                 const int idx = threadIdx.x + q * NTH;
                 if (idx < KS * (P / VEC))
-                    *(vt*)&sRowP[buf][(idx / (P / VEC)) * RPP + (idx % (P / VEC)) * VEC] = rp[q];
+                    *(vt*)&s[K::S_CROW + (idx / (P / VEC)) * RPP + (idx % (P / VEC)) * VEC] = rp[q];
             }
 #pragma unroll
-            for (int q = 0; q < V_TR; ++q) {
+            for (int q = 0; q < V_DT; ++q) {
                 const int idx = threadIdx.x + q * NTH;
-                if (idx < N * (KS / VEC))
-                    *(vt*)&sTr[buf][(idx / (KS / VEC)) * TPK + (idx % (KS / VEC)) * VEC] = tr[q];
+                if (idx < P * (KS / VEC))
+                    *(vt*)&s[K::S_CROW + K::S_DROW + (idx / (KS / VEC)) * TPK +
+                             (idx % (KS / VEC)) * VEC] = rd[q];
             }
         };
         {
-            vt rn[V_RN], rp[V_RP], tr[V_TR];
-            fetch1(ib_lo, rn, rp, tr);
-            store1(0, rn, rp, tr);
+            vt rn[V_RN], rp[V_RP], rd[V_DT];
+            fetch(0, rn, rp, rd);
+            store(U, rn, rp, rd);
         }
         __syncthreads();
         int buf = 0;
 #pragma unroll 1
-        for (int i0 = ib_lo; i0 < Q; i0 += KS, buf ^= 1) {
+        for (int i0 = 0; i0 < Q; i0 += KS, buf ^= 1) {
             const bool more = i0 + KS < Q;
-            vt rn[V_RN], rp[V_RP], tr[V_TR];
-            if (more) fetch1(i0 + KS, rn, rp, tr);
-            if (i0 + KS - 1 >= j0T) {  // the block reaches this wave's tile (i >= j)
-            float uv[SL], wv[SL];
+            vt rn[V_RN], rp[V_RP], rd[V_DT];
+            if (more) fetch(i0 + KS, rn, rp, rd);
+            const T* sC = U + buf * SB1;
+            const T* sD = sC + K::S_CROW;
+            const T* sDT = sD + K::S_DROW;
+            // a tile is active for the block when some i of the block is >= some j of the tile
+            bool any_act = false;
 #pragma unroll
-            for (int st = 0; st < KS / 16; ++st) {
-                const int is = i0 + st * 16;
-                f32x4 ut = f32x4{0.f, 0.f, 0.f, 0.f}, wt = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (is + 15 >= j0T) {
+            for (int jt = 0; jt < TPW; ++jt) any_act = any_act || (i0 + KS - 1 >= tt[jt]);
+            if (any_act) {
+                Frag uf[TPW];
+#pragma unroll
+                for (int st = 0; st < KS / 16; ++st) {
+                    const int is = i0 + st * 16;
+                    Frag cf[KN], df[KP];
 #pragma unroll
                     for (int kn = 0; kn < KN; ++kn)
-                        ut = M::mma(M::load(&sRowN[buf][(st * 16 + lr) * RPN + kn * KS + SL * lg]),
-                                    Bn[kn], ut);
+                        cf[kn] = M::load(&sC[(st * 16 + lr) * RPN + kn * KS + SL * lg]);
 #pragma unroll
                     for (int kp = 0; kp < KP; ++kp)
-                        wt = M::mma(M::load(&sRowP[buf][(st * 16 + lr) * RPP + kp * KS + SL * lg]),
-                                    Xn[kp], wt);
-                }
-                float fr[4];
+                        df[kp] = M::load(&sD[(st * 16 + lr) * RPP + kp * KS + SL * lg]);
+                    const f32x4 ea = *(const f32x4*)&sea[is + 4 * lg];
+                    float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = is + 4 * lg + r;
-                    float m = 0.f;
-                    if (i >= tj && ssq[i] == sq_j) m = expf(scs[i] - cs_j);
-                    uv[st * 4 + r] = ut[r] * m;
-                    wv[st * 4 + r] = wt[r] * m;
-                    fr[r] = ut[r] * wt[r] * m * dt_j;
-                    kacc += fr[r];
-                }
-                if (is + 15 >= j0T) {
+                    for (int jt = 0; jt < TPW; ++jt) {
+                        float uv[4] = {0.f, 0.f, 0.f, 0.f};
+                        if (is + 15 >= tt[jt]) {
+                            f32x4 ut = f32x4{0.f, 0.f, 0.f, 0.f}, wt = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float x = fr[r];
-                        x += __shfl_xor(x, 1, 64);
-                        x += __shfl_xor(x, 2, 64);
-                        x += __shfl_xor(x, 4, 64);
-                        x += __shfl_xor(x, 8, 64);
-                        if (lr == 0) s_rw[wave][is + 4 * lg + r] += x;
+                            for (int kn = 0; kn < KN; ++kn) ut = M::mma(cf[kn], Bn[jt][kn], ut);
+#pragma unroll
+                            for (int kp = 0; kp < KP; ++kp) wt = M::mma(df[kp], Xn[jt][kp], wt);
+                            float m[4];
+                            pair_decay(is, jt, ea, m);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                uv[r] = ut[r] * m[r];
+                                const float f = uv[r] * wt[r];  // F_ij / dt_j
+                                kq[jt] += f;
+                                rs[r] += f * dt_j[jt];
+                            }
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) uf[jt][st * 4 + r] = (E)uv[r];
+                    }
+                    const float t = row_sums16(rs, lr);
+                    if ((lr & 3) == 0) {
+                        const int r = 2 * (lr >> 3) + ((lr >> 2) & 1);
+                        s_rw[wave][is + 4 * lg + r] = t;
                     }
                 }
-            }
-            const Frag uf = M::from_f(uv), wf = M::from_f(wv);
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-                adx[pt] = M::mma(KPermB<T>::load(&dYt[(pt * 16 + lr) * QP + i0 + 4 * lg]), uf,
-                                 adx[pt]);
+                for (int pt = 0; pt < PT; ++pt) {
+                    const Frag a = M::load(&sDT[(pt * 16 + lr) * TPK + SL * lg]);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                adb[nt] = M::mma(KPermB<T>::load(&sTr[buf][(nt * 16 + lr) * TPK + 4 * lg]), wf,
-                                 adb[nt]);
+                    for (int jt = 0; jt < TPW; ++jt) adx[jt][pt] = M::mma(a, uf[jt], adx[jt][pt]);
+                }
             }
-            if (more) store1(buf ^ 1, rn, rp, tr);
+            if (more) store(U + (buf ^ 1) * SB1, rn, rp, rd);
             __syncthreads();
         }
-        float qpart = 0.f;
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            float xv[4], dyv[4];
-            load4(xrow + pt * 16, xv);
-            load4(dyrow + pt * 16, dyv);
-            f32x4 o;
+        for (int jt = 0; jt < TPW; ++jt) {
+            const int64_t trow = rb + t0 + tt[jt] + lr;
+            float qp = 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                qpart += xv[r] * adx[pt][r];
-                o[r] = dt_j * adx[pt][r] + Dh * dyv[r];
-                dD_part += dyv[r] * xv[r];
+            for (int pt = 0; pt < PT; ++pt) {
+                float xv[4], dyv[4];
+                load4(xc + trow * d.C + xoff + pt * 16 + 4 * lg, xv);
+                load4(dy + trow * HPd + xoff + pt * 16 + 4 * lg, dyv);
+                f32x4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    qp += xv[r] * adx[jt][pt][r];
+                    o[r] = dt_j[jt] * adx[jt][pt][r] + Dh * dyv[r];
+                    dD_part += dyv[r] * xv[r];
+                }
+                *(f32x4*)(dv + trow * d.C + xoff + pt * 16 + 4 * lg) = o;
             }
-            *(f32x4*)(dv + trow * d.C + xoff + pt * 16 + 4 * lg) = o;
+            q_t[jt] = sum_groups(qp);
         }
-        const float q_j = sum_groups(qpart);
-        T* dbrow = dbc + (trow * d.H + h) * (2 * N);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dbrow[nt * 16 + 4 * lg + r] = (T)(adb[nt][r] * dt_j);
+    }
 
-        // ---- dC of the tile's tokens (as outputs i) ----
-        Frag Dn[KP];
+    // =================== phase B2: dB of the wave's tiles (sources j) ===================
+    // G^T [n][p] into the union
+    for (int idx = threadIdx.x; idx < N * (P / VEC); idx += NTH) {
+        const int n = idx / (P / VEC), pv = idx % (P / VEC);
+        *(vt*)&U[n * RPP + pv * VEC] = *(const vt*)(gnp + st_off + (int64_t)n * P + pv * VEC);
+    }
+    __syncthreads();
+    {
+        Frag Xn[TPW][KP];
+        f32x4 adb[TPW][NT];
 #pragma unroll
-        for (int kp = 0; kp < KP; ++kp) Dn[kp] = M::load(dy + trow * HPd + xoff + kp * KS + SL * lg);
-        f32x4 adc[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            adc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int jt = 0; jt < TPW; ++jt) {
+            const int64_t trow = rb + t0 + tt[jt] + lr;
 #pragma unroll
             for (int kp = 0; kp < KP; ++kp)
-                adc[nt] = M::mma(M::load(&HT[(nt * 16 + lr) * PP + kp * KS + SL * lg]), Dn[kp],
-                                 adc[nt]);
-            adc[nt] *= f_j;
-        }
-        // u_i = C_i . (entering-state part of dC_i): what the entering state adds to
-        // output i, dotted with dy_i
-        float upart = 0.f;
+                Xn[jt][kp] = M::load(xc + trow * d.C + xoff + kp * KS + SL * lg);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            float cv[4];
-            load4(xc + trow * d.C + coff + nt * 16 + 4 * lg, cv);
+            for (int nt = 0; nt < NT; ++nt) {
+                f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) upart += cv[r] * adc[nt][r];
+                for (int kp = 0; kp < KP; ++kp)
+                    a = M::mma(M::load(&U[(nt * 16 + lr) * RPP + kp * KS + SL * lg]), Xn[jt][kp], a);
+                adb[jt][nt] = a * gj[jt];
+            }
         }
-        const float u_j = sum_groups(upart);
-        // Lockstep over the j-blocks up to this workgroup's last tile.
-        const int jb_hi = (tg + 1) * NW * 16 - 1;
-        // phase-2 block loads: x rows, transposed B (reusing the row/transpose buffers)
-        auto fetch2 = [&](int j0, vt (&rp)[V_RP], vt (&tr)[V_TR]) {
+        __syncthreads();  // G^T consumed
+
+        constexpr int V_RP = (KS * (P / VEC) + NTH - 1) / NTH;
+        constexpr int V_CT = (N * (KS / VEC) + NTH - 1) / NTH;
+        constexpr int SB2 = K::S_DROW + K::S_CT;  // dy rows, C^T
+        auto fetch = [&](int i0, vt (&rp)[V_RP], vt (&rc)[V_CT]) {
 #pragma unroll
             for (int q = 0; q < V_RP; ++q) {
                 const int idx = threadIdx.x + q * NTH;
                 if (idx < KS * (P / VEC)) {
-                    const int jj = idx / (P / VEC), pv = idx % (P / VEC);
-                    rp[q] = *(const vt*)(xc + (rb + t0 + j0 + jj) * d.C + xoff + pv * VEC);
+                    const int ii = idx / (P / VEC), pv = idx % (P / VEC);
+                    rp[q] = *(const vt*)(dy + (rb + t0 + i0 + ii) * HPd + xoff + pv * VEC);
                 }
             }
 #pragma unroll
-            for (int q = 0; q < V_TR; ++q) {
+            for (int q = 0; q < V_CT; ++q) {
                 const int idx = threadIdx.x + q * NTH;
                 if (idx < N * (KS / VEC)) {
                     const int n = idx / (KS / VEC), kv = idx % (KS / VEC);
-                    tr[q] = *(const vt*)(bctB + (int64_t)n * Q + j0 + kv * VEC);
+                    rc[q] = *(const vt*)(bctC + (int64_t)n * Q + i0 + kv * VEC);
                 }
             }
         };
-        auto store2 = [&](int bf, const vt (&rp)[V_RP], const vt (&tr)[V_TR]) {
+        auto store = [&](T* s, const vt (&rp)[V_RP], const vt (&rc)[V_CT]) {
 #pragma unroll
             for (int q = 0; q < V_RP; ++q) {
                 const int idx = threadIdx.x + q * NTH;
                 if (idx < KS * (P / VEC))
-                    *(vt*)&sRowP[bf][(idx / (P / VEC)) * RPP + (idx % (P / VEC)) * VEC] = rp[q];
+                    *(vt*)&s[(idx / (P / VEC)) * RPP + (idx % (P / VEC)) * VEC] = rp[q];
             }
 #pragma unroll
-            for (int q = 0; q < V_TR; ++q) {
+            for (int q = 0; q < V_CT; ++q) {
                 const int idx = threadIdx.x + q * NTH;
                 if (idx < N * (KS / VEC))
-                    *(vt*)&sTr[bf][(idx / (KS / VEC)) * TPK + (idx % (KS / VEC)) * VEC] = tr[q];
+                    *(vt*)&s[K::S_DROW + (idx / (KS / VEC)) * TPK + (idx % (KS / VEC)) * VEC] = rc[q];
             }
         };
         {
-            vt rp[V_RP], tr[V_TR];
-            fetch2(0, rp, tr);
-            store2(0, rp, tr);
+            vt rp[V_RP], rc[V_CT];
+            fetch(0, rp, rc);
+            store(U, rp, rc);
         }
         __syncthreads();
-        buf = 0;
+        int buf = 0;
 #pragma unroll 1
-        for (int j0 = 0; j0 <= jb_hi; j0 += KS, buf ^= 1) {
-            const bool more = j0 + KS <= jb_hi;
-            vt rp[V_RP], tr[V_TR];
-            if (more) fetch2(j0 + KS, rp, tr);
-            if (j0 <= j0T) {  // the block reaches back to this wave's tile (j <= i)
-            float vv[SL];
+        for (int i0 = 0; i0 < Q; i0 += KS, buf ^= 1) {
+            const bool more = i0 + KS < Q;
+            vt rp[V_RP], rc[V_CT];
+            if (more) fetch(i0 + KS, rp, rc);
+            const T* sD = U + buf * SB2;
+            const T* sCT = sD + K::S_DROW;
+            bool any_act = false;
 #pragma unroll
-            for (int st = 0; st < KS / 16; ++st) {
-                const int js = j0 + st * 16;
-                f32x4 vt4 = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (js <= j0T) {
+            for (int jt = 0; jt < TPW; ++jt) any_act = any_act || (i0 + KS - 1 >= tt[jt]);
+            if (any_act) {
+                Frag wf[TPW];
+#pragma unroll
+                for (int st = 0; st < KS / 16; ++st) {
+                    const int is = i0 + st * 16;
+                    Frag df[KP];
 #pragma unroll
                     for (int kp = 0; kp < KP; ++kp)
-                        vt4 = M::mma(M::load(&sRowP[buf][(st * 16 + lr) * RPP + kp * KS + SL * lg]),
-                                     Dn[kp], vt4);
+                        df[kp] = M::load(&sD[(st * 16 + lr) * RPP + kp * KS + SL * lg]);
+                    const f32x4 ea = *(const f32x4*)&sea[is + 4 * lg];
+#pragma unroll
+                    for (int jt = 0; jt < TPW; ++jt) {
+                        float wv[4] = {0.f, 0.f, 0.f, 0.f};
+                        if (is + 15 >= tt[jt]) {
+                            f32x4 wt = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int kp = 0; kp < KP; ++kp) wt = M::mma(df[kp], Xn[jt][kp], wt);
+                            float m[4];
+                            pair_decay(is, jt, ea, m);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) wv[r] = wt[r] * m[r];
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) wf[jt][st * 4 + r] = (E)wv[r];
+                    }
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = js + 4 * lg + r;
-                    float m = 0.f;
-                    if (j <= tj && ssq[j] == sq_j) m = expf(cs_j - scs[j]) * sdt[j];
-                    vv[st * 4 + r] = vt4[r] * m;
+                for (int nt = 0; nt < NT; ++nt) {
+                    const Frag a = M::load(&sCT[(nt * 16 + lr) * TPK + SL * lg]);
+#pragma unroll
+                    for (int jt = 0; jt < TPW; ++jt) adb[jt][nt] = M::mma(a, wf[jt], adb[jt][nt]);
                 }
             }
-            const Frag vf = M::from_f(vv);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                adc[nt] = M::mma(KPermB<T>::load(&sTr[buf][(nt * 16 + lr) * TPK + 4 * lg]), vf,
-                                 adc[nt]);
-            }
-            if (more) store2(buf ^ 1, rp, tr);
+            if (more) store(U + (buf ^ 1) * SB2, rp, rc);
             __syncthreads();
         }
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int jt = 0; jt < TPW; ++jt) {
+            const int64_t trow = rb + t0 + tt[jt] + lr;
+            T* dbrow = dbc + (trow * d.H + h) * (2 * N);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dbrow[N + nt * 16 + 4 * lg + r] = (T)adc[nt][r];
-        const float K_j = sum_groups(kacc);
-        if (lg == 0) {
-            float* tp = tokp + (hl + tj) * 4;
-            tp[0] = u_j - K_j;  // R_i is added by k_ddt from the row sums
-            tp[1] = q_j;
-            tp[2] = v_j;
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dbrow[nt * 16 + 4 * lg + r] = (T)(adb[jt][nt][r] * dt_j[jt]);
         }
     }
 
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) dD_part += __shfl_xor(dD_part, off, 64);
-    __syncthreads();
-    if (lane == 0) s_red[wave][1] = dD_part;
-    for (int t = threadIdx.x; t < Q; t += blockDim.x) {
-        float rsum = 0.f;
-        for (int w = 0; w < NW; ++w) rsum += s_rw[w][t];
-        rpart[(hl + t) * TG + tg] = rsum;
+    for (int jt = 0; jt < TPW; ++jt) {
+        const int tj = tt[jt] + lr;
+        const float K_j = dt_j[jt] * sum_groups(kq[jt]);
+        if (lg == 0) {
+            float* tp = tokp + (hl + tj) * 4;
+            tp[0] = u_t[jt] - K_j;  // R_i is added by k_ddt from the row sums
+            tp[1] = q_t[jt];
+            tp[2] = v_t[jt];
+        }
     }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dD_part += __shfl_xor(dD_part, off, 64);
+    if (lane == 0) s_red[wave] = dD_part;
     __syncthreads();
+    for (int t = threadIdx.x; t < Q; t += NTH) {
+        float rsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) rsum += s_rw[w][t];
+        rpart[hl + t] = rsum;
+    }
     if (threadIdx.x == 0) {
         float dd = 0.f;
-        for (int w = 0; w < NW; ++w) dd += s_red[w][1];
-        red4[(((int64_t)b * d.nchunk + cm) * d.H + h) * TG + tg] = dd;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) dd += s_red[w];
+        red4[((int64_t)b * d.nchunk + cm) * d.H + h] = dd;
     }
 }
 
@@ -596,7 +1107,7 @@ __global__ void __launch_bounds__(NW * 64) k_chunk_bwd(
 // exactly 0 at a token that starts a packed sequence; then
 // ddt_t = q_t + A dL/d(dt_t A) and the chain through clamp and softplus.
 template <typename T>
-__global__ void __launch_bounds__(64) k_ddt(Dims d, SegTab tab, int TG,
+__global__ void __launch_bounds__(64) k_ddt(Dims d, SegTab tab,
                                            const T* __restrict__ dt_raw,
                                            const float* __restrict__ dt_bias,
                                            const float* __restrict__ A_log,
@@ -637,8 +1148,7 @@ __global__ void __launch_bounds__(64) k_ddt(Dims d, SegTab tab, int TG,
             const bool cut = t < Q - 1 && sq(t + 1) != sq(t);
             if (cut) run = 0.f;
             cut_any = cut_any || cut;
-            float s = tokp[(hl + t) * 4 + 0];
-            for (int g = 0; g < TG; ++g) s += rpart[(hl + t) * TG + g];
+            const float s = tokp[(hl + t) * 4 + 0] + rpart[hl + t];
             run += s;
             sl[e] = run;
             rs[e] = cut_any;
@@ -699,8 +1209,7 @@ __global__ void __launch_bounds__(64) k_ddt(Dims d, SegTab tab, int TG,
         s_da += __shfl_xor(s_da, off, 64);
     }
     if (lane == 0) {
-        float dd = 0.f;
-        for (int g = 0; g < TG; ++g) dd += red4[(((int64_t)b * d.nchunk + cm) * d.H + h) * TG + g];
+        const float dd = red4[((int64_t)b * d.nchunk + cm) * d.H + h];
         float* rp = red + (((int64_t)b * d.nchunk + cm) * d.H + h) * 3;
         rp[0] = s_db;
         rp[1] = s_da;
@@ -890,7 +1399,7 @@ __global__ void __launch_bounds__(256) k_conv_bwd(Dims d, SegTab tab, const T* _
             x += __shfl_xor(x, 32, 64);
             dw[e][kk] = x;
         }
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int wave = wave_id(), lane = threadIdx.x % 64;
     if (lane < CV) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
@@ -951,42 +1460,43 @@ __global__ void __launch_bounds__(256) k_bwd_reduce(Dims d, const float* __restr
 // ---------------------------------------------------------------------------
 // Dispatch.
 
-template <typename T, int P, int N, int Q>
-constexpr size_t chunk_bwd_lds() {
-    constexpr size_t V = 16 / sizeof(T);
-    constexpr size_t NW = Q >= 128 ? 8 : 4;
-    constexpr size_t KS = sizeof(T) == 2 ? 32 : 16;
-    return sizeof(T) * ((size_t)P * (Q + V) + 2 * (size_t)N * (P + V) + (size_t)P * (N + V) +
-                        2 * (KS * (N + V) + KS * (P + V) + (size_t)N * (KS + V))) +
-           (size_t)Q * 12 + NW * Q * 4 + 256;
-}
 constexpr size_t BWD_LDS_LIMIT = 160 * 1024;
+
+// Tiles per wave (two: with four the accumulators no longer fit in registers).
+template <typename T, int Q>
+constexpr int chunk_bwd_tpw() {
+    return 2;
+}
+
+template <typename T, int P, int N, int Q>
+constexpr bool chunk_bwd_fits() {
+    return ChunkBwd<T, P, N, Q, chunk_bwd_tpw<T, Q>()>::LDS <= BWD_LDS_LIMIT;
+}
 
 template <typename T, int P, int N>
 static bool bwd_shape_ok(int Q) {
-    if (Q == 64) return chunk_bwd_lds<T, P, N, 64>() <= BWD_LDS_LIMIT;
-    if (Q == 128) return chunk_bwd_lds<T, P, N, 128>() <= BWD_LDS_LIMIT;
-    if (Q == 256) return chunk_bwd_lds<T, P, N, 256>() <= BWD_LDS_LIMIT;
+    if (Q == 64) return chunk_bwd_fits<T, P, N, 64>();
+    if (Q == 128) return chunk_bwd_fits<T, P, N, 128>();
+    if (Q == 256) return chunk_bwd_fits<T, P, N, 256>();
     return false;
 }
 
 template <typename T, int P, int N, int Q>
 static void launch_chunk_bwd(const Dims& d, const SegTab& t, const BwdArgs& a, const BwdWs& L,
                              char* ws, hipStream_t s) {
-    if constexpr (chunk_bwd_lds<T, P, N, Q>() <= BWD_LDS_LIMIT) {
-        constexpr int NW = Q >= 128 ? 8 : 4;
-        constexpr int TG = Q / 16 / NW;
-        hipLaunchKernelGGL((k_chunk_bwd<T, P, N, Q, NW>),
-                           dim3((unsigned)d.nchunk, (unsigned)d.H, (unsigned)(d.batch * TG)),
+    if constexpr (chunk_bwd_fits<T, P, N, Q>()) {
+        constexpr int TPW = chunk_bwd_tpw<T, Q>();
+        constexpr int NW = ChunkBwd<T, P, N, Q, TPW>::NW;
+        hipLaunchKernelGGL((k_chunk_bwd<T, P, N, Q, TPW>), chunk_head_grid(d),
                            dim3(NW * 64), 0, s, d, t, (const T*)(ws + L.xc),
-                           (const T*)(ws + L.bct), (const T*)a.dy, a.D, (const float*)(ws + L.dt),
-                           (const float*)(ws + L.cs), (const float*)(ws + L.ctot), a.seq,
-                           (const T*)(ws + L.hstT), (const T*)(ws + L.gst), a.S_in, a.dS_out,
+                           (const T*)(ws + L.bct), (const T*)a.dy, (const T*)(ws + L.dyT), a.D,
+                           (const float*)(ws + L.dt), (const float*)(ws + L.cs), a.seq,
+                           (const T*)(ws + L.gpn), (const T*)(ws + L.gnp), (const T*)(ws + L.hnp),
                            (float*)(ws + L.dv), (T*)(ws + L.dbc), (float*)(ws + L.rpart),
-                           (float*)(ws + L.tokp), (float*)(ws + L.dotgh), (float*)(ws + L.red4));
+                           (float*)(ws + L.tokp), (float*)(ws + L.red4));
         hipLaunchKernelGGL((k_ddt<T>),
                            dim3((unsigned)d.nchunk, (unsigned)d.H, (unsigned)d.batch), dim3(64), 0,
-                           s, d, t, TG, (const T*)a.dt_raw, a.dt_bias, a.A_log,
+                           s, d, t, (const T*)a.dt_raw, a.dt_bias, a.A_log,
                            (const float*)(ws + L.dt), (const float*)(ws + L.cs), a.seq,
                            (const float*)(ws + L.rpart), (const float*)(ws + L.tokp),
                            (const float*)(ws + L.dotgh), (const float*)(ws + L.red4),
@@ -1031,16 +1541,15 @@ static void bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a, floa
     launch_dt_prep(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32, a.dt_raw, a.dt_bias,
                    a.A_log, a.seq, (float*)(ws + L.dt), (float*)(ws + L.cs),
                    (float*)(ws + L.ctot), s);
-    hipLaunchKernelGGL((k_state_walk<T, P, N, WALK_FWD_NP>),
-                       dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0, s,
-                       d, t, (const T*)xc, (int64_t)d.C, (const T*)xc, (int64_t)d.H * P,
+    hipLaunchKernelGGL((k_bwd_chunk_states<T, P, N>), chunk_head_grid(d), dim3(256), 0, s,
+                       d, t, (const T*)xc, (const T*)(ws + L.bct), (const T*)a.dy,
                        (const float*)(ws + L.dt), (const float*)(ws + L.cs), a.seq,
-                       (T*)(ws + L.hstT), (float*)nullptr);
-    hipLaunchKernelGGL((k_state_walk<T, P, N, WALK_BWD_PN>),
+                       (float*)(ws + L.zh), (float*)(ws + L.zg), (T*)(ws + L.dyT));
+    hipLaunchKernelGGL((k_state_pass<T, P, N, PASS_SUMMARY>),
                        dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0, s,
-                       d, t, (const T*)a.dy, (int64_t)d.H * P, (const T*)xc,
-                       (int64_t)d.H * P + (int64_t)d.G * N, (const float*)(ws + L.dt),
-                       (const float*)(ws + L.cs), a.seq, (T*)(ws + L.gst), summary);
+                       d, t, (const float*)(ws + L.ctot), a.seq, (const float*)(ws + L.zg),
+                       (const float*)(ws + L.zh), (const float*)nullptr, (const float*)nullptr,
+                       summary, (T*)nullptr, (T*)nullptr, (T*)nullptr, (float*)nullptr);
 }
 
 template <typename T, int P, int N>
@@ -1048,6 +1557,12 @@ static void bwd_chunks_t(const Dims& d, const SegTab& t, const BwdArgs& a, void*
                          hipStream_t s) {
     const BwdWs L = bwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
     char* ws = (char*)ws_;
+    hipLaunchKernelGGL((k_state_pass<T, P, N, PASS_TRUE>),
+                       dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0, s,
+                       d, t, (const float*)(ws + L.ctot), a.seq, (const float*)(ws + L.zg),
+                       (const float*)(ws + L.zh), a.S_in, a.dS_out, (float*)nullptr,
+                       (T*)(ws + L.gpn), (T*)(ws + L.gnp), (T*)(ws + L.hnp),
+                       (float*)(ws + L.dotgh));
     switch (d.Q) {
         case 64: launch_chunk_bwd<T, P, N, 64>(d, t, a, L, ws, s); break;
         case 128: launch_chunk_bwd<T, P, N, 128>(d, t, a, L, ws, s); break;

@@ -73,7 +73,7 @@ __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ d
     }
     for (int j = threadIdx.x; j < Q; j += blockDim.x) sseq[j] = seq ? seq[b * d.L + tok0 + j] : 0;
     __syncthreads();
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int wave = wave_id(), lane = threadIdx.x % 64;
     const int E = Q / 64;  // tokens per lane (1, 2 or 4)
     bool rs[4];            // a sequence starts at or before this token, inside this lane
     bool lflag = false;
@@ -127,7 +127,10 @@ __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ d
                 csp[lane * E + e] = rs[e] ? csl[e] : ev + csl[e];
             }
         }
-        if (lane == 63) ctot[((int64_t)b * d.H + h) * d.nchunk + cm] = iv;
+        // the chunk total is the last token's cumulative sum, bit for bit
+        if (lane == 63)
+            ctot[((int64_t)b * d.H + h) * d.nchunk + cm] =
+                rs[E - 1] ? csl[E - 1] : ev + csl[E - 1];
     }
 }
 
@@ -158,9 +161,10 @@ __global__ void __launch_bounds__(NW * 64) k_chunk_out(Dims d, SegTab tab, const
     __shared__ float scs[Q], sdt[Q];
     __shared__ int ssq[Q];
 
-    const int cm = blockIdx.x, h = blockIdx.y;
-    const int64_t b = blockIdx.z;
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
+    const ChunkHead ch = chunk_head_of_block(d);
+    const int cm = ch.cm, h = ch.h;
+    const int64_t b = ch.b;
+    const int wave = wave_id(), lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
     const int g = h / d.hpg;
     const int64_t rb = b * d.L;
     const int64_t t0 = (int64_t)cm * Q;
@@ -274,9 +278,10 @@ __global__ void __launch_bounds__(256) k_apply_init(Dims d, SegTab tab, const fl
     constexpr int PT = P / 16, NKF = N / KS;
     __shared__ float s_pre;
 
-    const int cm = blockIdx.x, h = blockIdx.y;
-    const int64_t b = blockIdx.z;
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
+    const ChunkHead ch = chunk_head_of_block(d);
+    const int cm = ch.cm, h = ch.h;
+    const int64_t b = ch.b;
+    const int wave = wave_id(), lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
     const int g = h / d.hpg;
     const int Q = d.Q;
     const int64_t rb = b * d.L;
@@ -363,8 +368,7 @@ static void launch_chunk_out(const Dims& d, const SegTab& t, const T* xc, const 
                              hipStream_t s) {
     if constexpr (chunk_out_lds<T, P, N, Q>() <= LDS_LIMIT) {
         constexpr int NW = Q >= 128 ? 8 : 4;
-        dim3 grid((unsigned)d.nchunk, (unsigned)d.H, (unsigned)d.batch);
-        hipLaunchKernelGGL((k_chunk_out<T, P, N, Q, NW>), grid, dim3(NW * 64), 0, s, d, t, xc, dtw,
+        hipLaunchKernelGGL((k_chunk_out<T, P, N, Q, NW>), chunk_head_grid(d), dim3(NW * 64), 0, s, d, t, xc, dtw,
                            csw, seq, hst, y_zero);
     }
 }
@@ -409,8 +413,7 @@ static void apply_init_t(const Dims& d, const SegTab& t, const float* y_zero, co
                          void* y, hipStream_t s) {
     const FwdWs L = fwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
     const char* w = (const char*)ws;
-    hipLaunchKernelGGL((k_apply_init<T, P, N>), dim3((unsigned)d.nchunk, (unsigned)d.H,
-                                                     (unsigned)d.batch),
+    hipLaunchKernelGGL((k_apply_init<T, P, N>), chunk_head_grid(d),
                        dim3(256), 0, s, d, t, y_zero, (const T*)xc, D, seq, S_in,
                        (const float*)(w + L.cs), (const float*)(w + L.ctot), (T*)y);
 }

@@ -51,6 +51,36 @@ __device__ __forceinline__ int64_t seg_pred_token(const SegTab& t, int k) {
 template <typename T>
 __device__ __forceinline__ float to_f(T v) { return (float)v; }
 
+// (chunk, head, row) of a workgroup in a 1-D grid of nchunk * H * batch
+// workgroups.  The hardware hands workgroup i to XCD i % 8; giving each XCD one
+// contiguous range of logical items, heads fastest, makes the workgroups that
+// share a chunk's B and C channels (all heads of a group) run on one XCD at
+// about the same time, so those channels are read into its L2 once.
+struct ChunkHead {
+    int cm, h;
+    int64_t b;
+};
+__device__ __forceinline__ ChunkHead chunk_head_of_block(const Dims& d) {
+    constexpr int NXCD = 8;
+    const int64_t n = gridDim.x, i = blockIdx.x;
+    const int64_t item = (n % NXCD == 0) ? (i % NXCD) * (n / NXCD) + i / NXCD : i;
+    ChunkHead c;
+    c.h = (int)(item % d.H);
+    const int64_t rest = item / d.H;
+    c.cm = (int)(rest % d.nchunk);
+    c.b = rest / d.nchunk;
+    return c;
+}
+inline dim3 chunk_head_grid(const Dims& d) {
+    return dim3((unsigned)((int64_t)d.nchunk * d.H * d.batch));
+}
+
+// Index of the calling wave in its workgroup as a scalar (wave-uniform) value,
+// so that branches on it compile to scalar branches rather than exec masks.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / 64));
+}
+
 // ---------------------------------------------------------------------------
 // MFMA fragments.
 //
@@ -66,6 +96,7 @@ template <> struct Mma<bf16> {
     static constexpr int SL = 8;   // k slots per lane
     static constexpr int KS = 32;  // k consumed per mma()
     typedef bf16x8 Frag;
+    typedef bf16 Elem;
     __device__ static __forceinline__ f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
@@ -90,6 +121,7 @@ template <> struct Mma<float> {
     static constexpr int SL = 4;
     static constexpr int KS = 16;
     typedef f32x4 Frag;
+    typedef float Elem;
     __device__ static __forceinline__ f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
@@ -167,29 +199,35 @@ inline FwdWs fwd_ws_layout(const Dims& d, int act) {
 }
 
 // Backward workspace layout (byte offsets).  Filled by the summary phase
-// (xc, bct, dt, cs, ctot, gst) and used by the segment phase.
+// (xc, bct, dt, cs, ctot, zh, zg, dyT) and used by the segment phase.
 struct BwdWs {
-    size_t xc, bct, dt, cs, ctot, hstT, gst, dv, dbc, rpart, tokp, dotgh, red4, red, dwp, total;
+    size_t xc, bct, dt, cs, ctot, zh, zg, gpn, gnp, hnp, dyT, dv, dbc, rpart, tokp, dotgh, red4,
+        red, dwp, total;
 };
 inline BwdWs bwd_ws_layout(const Dims& d, int act) {
     BwdWs w;
     const size_t e = act == SSD_BF16 ? 2 : 4;
     const size_t BL = (size_t)d.batch * d.L;
     const size_t st = (size_t)d.batch * d.nchunk * d.H * d.P * d.N;
+    const size_t bhl = (size_t)d.batch * d.H * d.L;
     size_t o = 0;
     w.xc = o;   o = align256(o + BL * d.C * e);
     w.bct = o;  o = align256(o + (size_t)d.batch * d.nchunk * d.G * 2 * d.N * d.Q * e);
-    w.dt = o;   o = align256(o + (size_t)d.batch * d.H * d.L * 4);
-    w.cs = o;   o = align256(o + (size_t)d.batch * d.H * d.L * 4);
+    w.dt = o;   o = align256(o + bhl * 4);
+    w.cs = o;   o = align256(o + bhl * 4);
     w.ctot = o; o = align256(o + (size_t)d.batch * d.H * d.nchunk * 4);
-    w.hstT = o; o = align256(o + st * e);
-    w.gst = o;  o = align256(o + st * e);
+    w.zh = o;   o = align256(o + st * 4);  // chunk contributions to the state, FP32
+    w.zg = o;   o = align256(o + st * 4);  // chunk contributions to the state gradient, FP32
+    w.gpn = o;  o = align256(o + st * e);  // exit gradient per chunk, [p][n]
+    w.gnp = o;  o = align256(o + st * e);  // the same, [n][p]
+    w.hnp = o;  o = align256(o + st * e);  // entering state per chunk, [n][p]
+    w.dyT = o;  o = align256(o + bhl * d.P * e);  // dy per chunk and head, [p][token]
     w.dv = o;   o = align256(o + BL * d.C * 4);  // d(conv output), every channel
     w.dbc = o;  o = align256(o + BL * d.H * 2 * d.N * e);  // per-head dB, dC
-    w.rpart = o; o = align256(o + (size_t)d.batch * d.H * d.L * 2 * 4);
-    w.tokp = o; o = align256(o + (size_t)d.batch * d.H * d.L * 4 * 4);
+    w.rpart = o; o = align256(o + bhl * 4);
+    w.tokp = o; o = align256(o + bhl * 4 * 4);
     w.dotgh = o; o = align256(o + (size_t)d.batch * d.nchunk * d.H * 4);
-    w.red4 = o; o = align256(o + (size_t)d.batch * d.nchunk * d.H * 2 * 4);
+    w.red4 = o; o = align256(o + (size_t)d.batch * d.nchunk * d.H * 4);
     w.red = o;  o = align256(o + (size_t)d.batch * d.nchunk * d.H * 3 * 4);
     w.dwp = o;  o = align256(o + (size_t)d.batch * (d.L / 64) * d.C * d.W * 4);
     w.total = o;

@@ -53,7 +53,7 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
 
     const int h = blockIdx.x, k = blockIdx.y;
     const int64_t b = blockIdx.z;
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
+    const int wave = wave_id(), lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
     const int g = h / d.hpg;
     const int Q = d.Q;
     const int64_t rb = b * d.L;
