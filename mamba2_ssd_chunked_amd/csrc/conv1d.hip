@@ -1,108 +1,79 @@
 // Causal depthwise conv1d + SiLU with a causal-predecessor halo (gfx950).
 //
-// Each workgroup owns 64 consecutive tokens (memory order, inside one segment)
-// and 128 channels.  It stages the 64 + W - 1 input rows in LDS with coalesced
-// 16-byte loads; the first W - 1 rows are the halo, read from the last tokens
-// of the causal predecessor segment when the tile starts a segment (the conv
-// halo that Megatron-LM #6808's first commit exchanges between causal shards).  Taps that reach before the row start or across a packed
+// No LDS: every thread owns 4 consecutive channels and TPT consecutive tokens
+// (memory order, inside one segment), loads the TPT + W - 1 input rows it needs
+// straight into registers (the first W - 1 are the halo, read from the last
+// tokens of the causal predecessor segment when the group starts a segment:
+// the conv halo that Megatron-LM #6808's first commit exchanges between causal
+// shards) and slides the taps over them.  The 64 lanes of a wave own 256
+// consecutive channels of the same tokens, so every load and store of a wave is
+// one contiguous run.  Taps that reach before the row start or across a packed
 // sequence start are zero.  HBM-bound: 2*C*sizeof(act) bytes per token.
 #include "ssd_internal.h"
 
 namespace ssd {
-
-constexpr int CONV_TT = 64;   // tokens per workgroup
-constexpr int CONV_CT = 128;  // channels per workgroup
-constexpr int CONV_MAXW = 8;  // widest supported conv
-constexpr int CONV_ROWS = CONV_TT + CONV_MAXW - 1;
 
 template <typename T, int W>
 __global__ void __launch_bounds__(256) k_conv1d_silu(Dims d, SegTab tab, const T* __restrict__ xBC,
                                                     const float* __restrict__ w,
                                                     const int32_t* __restrict__ seq,
                                                     T* __restrict__ out) {
-    constexpr int VEC = 8;                // channels per thread vector
-    constexpr int CV = CONV_CT / VEC;     // vectors per row
-    typedef T vec_t __attribute__((ext_vector_type(8)));
-    __shared__ __attribute__((aligned(16))) T tile[CONV_ROWS * CONV_CT];
-    __shared__ int64_t rowmem[CONV_ROWS];
-    __shared__ int rowseq[CONV_ROWS];
-
+    constexpr int R = CONV_TPT + W - 1;
+    typedef typename Vec4<T>::type vt;
+    const int lane = threadIdx.x % 64;
+    const int c = (blockIdx.x * 64 + lane) * CONV_VEC;
     const int64_t b = blockIdx.z;
-    const int64_t t0 = (int64_t)blockIdx.y * CONV_TT;
-    const int c0 = blockIdx.x * CONV_CT;
-    const int rows = CONV_TT + W - 1;
+    const int64_t t0 = (int64_t)blockIdx.y * CONV_TT + wave_id() * CONV_TPT;
     const int64_t rb = b * d.L;
+    if (c >= d.C) return;  // no barriers below
+    const int k = conv_seg(tab, t0);
 
-    int k = 0;
-    for (int i = 0; i < tab.n; ++i)
-        if (t0 >= tab.start[i] && t0 < tab.start[i] + tab.len[i]) k = i;
-    const int64_t s0 = tab.start[k];
-
-    // LDS row r holds causal token (t0 - (W-1) + r); find its memory position.
-    for (int r = threadIdx.x; r < rows; r += blockDim.x) {
-        const int64_t m = t0 - (W - 1) + r;
-        int64_t mem;
-        if (m >= s0) mem = m;
-        else if (k > 0) mem = tab.start[k - 1] + tab.len[k - 1] - (s0 - m);
-        else mem = -1;
-        rowmem[r] = mem;
-        rowseq[r] = (mem >= 0 && seq) ? seq[rb + mem] : 0;
-    }
-    __syncthreads();
-
-    for (int idx = threadIdx.x; idx < rows * CV; idx += blockDim.x) {
-        const int r = idx / CV, v = idx % CV;
-        const int c = c0 + v * VEC;
-        vec_t val;
-        if (c < d.C && rowmem[r] >= 0) {
-            val = *(const vec_t*)(xBC + (rb + rowmem[r]) * d.C + c);
-        } else {
+    float wr[CONV_VEC][W];
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) val[e] = (T)0.f;
-        }
-        *(vec_t*)(tile + r * CONV_CT + v * VEC) = val;
-    }
-    __syncthreads();
-
-    // Every thread keeps one channel vector (idx % CV is fixed since blockDim % CV == 0).
-    const int v = threadIdx.x % CV;
-    const int c = c0 + v * VEC;
-    if (c >= d.C) return;
-    float wr[VEC][W];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e)
+    for (int e = 0; e < CONV_VEC; ++e)
 #pragma unroll
         for (int kk = 0; kk < W; ++kk) wr[e][kk] = w[(c + e) * W + kk];
 
-    for (int idx = threadIdx.x; idx < CONV_TT * CV; idx += blockDim.x) {
-        const int t = idx / CV;
-        const int ro = t + W - 1;  // LDS row of the output token
-        const int sq = rowseq[ro];
-        float acc[VEC];
+    // row r is the token r - (W-1) places after t0
+    vt xs[R];
+    int sq[R];
+    bool ok[R];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+    for (int r = 0; r < R; ++r) {
+        const int mem = (int)(r >= W - 1 ? t0 + (r - (W - 1)) : conv_row(tab, k, t0, r - (W - 1)));
+        ok[r] = mem >= 0;
+        sq[r] = (ok[r] && seq) ? seq[rb + mem] : 0;
+        if (ok[r]) {
+            xs[r] = *(const vt*)(xBC + (rb + mem) * d.C + c);
+        } else {
+#pragma unroll
+            for (int e = 0; e < CONV_VEC; ++e) xs[r][e] = (T)0.f;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < CONV_TPT; ++t) {
+        const int ro = t + W - 1;
+        float acc[CONV_VEC] = {};
 #pragma unroll
         for (int kk = 0; kk < W; ++kk) {
             const int r = t + kk;
-            if (rowmem[r] < 0 || rowseq[r] != sq) continue;
-            const vec_t xv = *(const vec_t*)(tile + r * CONV_CT + v * VEC);
+            if (ok[r] && sq[r] == sq[ro]) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[e] += wr[e][kk] * (float)xv[e];
+                for (int e = 0; e < CONV_VEC; ++e) acc[e] += wr[e][kk] * (float)xs[r][e];
+            }
         }
-        vec_t o;
+        vt o;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const float u = acc[e];
-            o[e] = (T)(u / (1.f + expf(-u)));
-        }
-        *(vec_t*)(out + (rb + t0 + t) * d.C + c) = o;
+        for (int e = 0; e < CONV_VEC; ++e) o[e] = (T)(acc[e] / (1.f + __expf(-acc[e])));
+        *(vt*)(out + (rb + t0 + t) * d.C + c) = o;
     }
 }
 
 template <typename T, int W>
 static void launch_w(const Dims& d, const SegTab& t, const void* xBC, const float* w,
                      const int32_t* seq, void* out, hipStream_t s) {
-    dim3 grid((d.C + CONV_CT - 1) / CONV_CT, (unsigned)(d.L / CONV_TT), (unsigned)d.batch);
+    dim3 grid((d.C + 64 * CONV_VEC - 1) / (64 * CONV_VEC), (unsigned)(d.L / CONV_TT),
+              (unsigned)d.batch);
     hipLaunchKernelGGL((k_conv1d_silu<T, W>), grid, dim3(256), 0, s, d, t, (const T*)xBC, w, seq,
                        (T*)out);
 }

@@ -3,6 +3,7 @@
 // invalid call returns a negative ssd_status and leaves the stream untouched.
 // Megatron-LM #6808 (description section "Not supported yet") likewise refuses
 // unsupported configurations outright instead of computing something wrong.
+#include <climits>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -33,8 +34,10 @@ int check_problem(const ssd_problem* p, Dims* d) {
     if (!kernels_supported(p->headdim, p->dstate, p->act_dtype)) return SSD_ERR_UNSUPPORTED;
     if (!chunk_supported(p->headdim, p->dstate, p->chunk, p->act_dtype)) return SSD_ERR_UNSUPPORTED;
     const int64_t C = (int64_t)p->nheads * p->headdim + 2LL * p->ngroups * p->dstate;
-    if (C > (1LL << 30) || p->seqlen / p->chunk > (1LL << 30) ||
-        p->batch > 65535 || p->nheads > 65535)
+    // token positions inside a row are 32-bit in the kernels; the per-(chunk,
+    // head) kernels use one 1-D grid of at most 2^32 work-items
+    if (C > (1LL << 30) || p->seqlen > INT32_MAX || p->batch > 65535 || p->nheads > 65535 ||
+        (p->seqlen / p->chunk) * p->nheads * p->batch * 512 >= (1LL << 32))
         return SSD_ERR_SHAPE;
     d->batch = p->batch;
     d->L = p->seqlen;

@@ -1223,195 +1223,159 @@ __global__ void __launch_bounds__(64) k_ddt(Dims d, SegTab tab,
 template <typename T>
 __global__ void __launch_bounds__(256) k_bc_headsum(Dims d, const T* __restrict__ dbc,
                                                    float* __restrict__ dv) {
-    const int GN2 = 2 * d.G * d.N;
+    constexpr int VEC = 16 / sizeof(T);  // outputs per thread (one 16-byte load per head)
+    typedef T vt __attribute__((ext_vector_type(VEC)));
+    const int GN = d.G * d.N, nv = 2 * GN / VEC;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= d.batch * d.L * GN2) return;
-    const int64_t tok = idx / GN2;
-    const int o = (int)(idx % GN2);
-    const int part = o / (d.G * d.N), gn = o % (d.G * d.N), g = gn / d.N, n = gn % d.N;
+    if (idx >= d.batch * d.L * nv) return;
+    const int64_t tok = idx / nv;
+    const int o = (int)(idx % nv) * VEC;
+    const int part = o / GN, gn = o % GN, g = gn / d.N, n = gn % d.N;
     const T* src = dbc + (tok * d.H + (int64_t)g * d.hpg) * (2 * d.N) + part * d.N + n;
-    float s = 0.f;
-    for (int hh = 0; hh < d.hpg; ++hh) s += (float)src[(int64_t)hh * 2 * d.N];
-    dv[tok * d.C + (int64_t)d.H * d.P + o] = s;
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+#pragma unroll 8
+    for (int hh = 0; hh < d.hpg; ++hh) {
+        const vt v = *(const vt*)(src + (int64_t)hh * 2 * d.N);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += (float)v[e];
+    }
+    float* dst = dv + tok * d.C + (int64_t)d.H * d.P + o;
+#pragma unroll
+    for (int q = 0; q < VEC / 4; ++q)
+        *(f32x4*)(dst + 4 * q) = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
 }
 
 // ---------------------------------------------------------------------------
-// SiLU' and the transposed causal conv.  A tile of 64 tokens needs du for its
-// own tokens and the W-1 that follow in causal order (the right halo, from the
-// causal successor segment), and xBC for W-1 tokens before those (to rebuild
-// the pre-activation).  dv holds the gradient of every conv output channel.  dconv_w is written per tile and reduced later.
+// SiLU' and the transposed causal conv, without LDS staging: every thread owns 4
+// consecutive channels and 16 consecutive tokens (one token group per wave,
+// 64 lanes = 256 consecutive channels).  It needs xBC for W-1 tokens before and
+// after its own (to rebuild the pre-activation u of its tokens and of the W-1
+// that follow) and d(conv output) for its tokens and the W-1 that follow in
+// causal order (the right halo, from the causal successor segment), all loaded
+// into registers; du is produced in causal order and the transposed conv
+// slides a W-row window over it.  dv holds the gradient of every conv output
+// channel.  dconv_w is written per 64-token block and reduced later.
 template <typename T, int W>
 __global__ void __launch_bounds__(256) k_conv_bwd(Dims d, SegTab tab, const T* __restrict__ xBC,
                                                  const float* __restrict__ w,
                                                  const int32_t* __restrict__ seq,
                                                  const float* __restrict__ dvall,
                                                  T* __restrict__ dxBC, float* __restrict__ dwp) {
-    constexpr int TT = 64, CT = 128, VEC = 8, CV = CT / VEC;
-    constexpr int R = TT + 2 * (W - 1);   // xBC rows: causal offsets -(W-1) .. TT+W-2
-    constexpr int RD = TT + W - 1;        // du rows: causal offsets 0 .. TT+W-2
-    typedef T vec_t __attribute__((ext_vector_type(8)));
-    __shared__ __attribute__((aligned(16))) T xt[R * CT];
-    __shared__ __attribute__((aligned(16))) float dus[RD * CT];
-    __shared__ int64_t rowmem[R];
-    __shared__ int rowseq[R];
-    __shared__ float wred[4][CV][VEC * W];
-
+    constexpr int TPT = CONV_TPT;
+    constexpr int RX = TPT + 2 * (W - 1);  // x rows: offsets -(W-1) .. TPT+W-2
+    constexpr int RD = TPT + W - 1;        // du rows: offsets 0 .. TPT+W-2
+    typedef T vt __attribute__((ext_vector_type(4)));
+    __shared__ float wred[4][64][4 * W];
+    const int lane = threadIdx.x % 64, wave = wave_id();
+    const int c = (blockIdx.x * 64 + lane) * 4;
     const int64_t b = blockIdx.z;
-    const int tt = blockIdx.y;
-    const int64_t t0 = (int64_t)tt * TT;
-    const int c0 = blockIdx.x * CT;
+    const int64_t t0 = (int64_t)blockIdx.y * CONV_TT + wave * TPT;
     const int64_t rb = b * d.L;
-    int k = 0;
-    for (int i = 0; i < tab.n; ++i)
-        if (t0 >= tab.start[i] && t0 < tab.start[i] + tab.len[i]) k = i;
-    const int64_t s0 = tab.start[k], s1 = s0 + tab.len[k];
-
-    for (int r = threadIdx.x; r < R; r += blockDim.x) {
-        const int64_t m = t0 - (W - 1) + r;
-        int64_t mem;
-        if (m >= s0 && m < s1) mem = m;
-        else if (m < s0) mem = k > 0 ? tab.start[k - 1] + tab.len[k - 1] - (s0 - m) : -1;
-        else mem = k + 1 < tab.n ? tab.start[k + 1] + (m - s1) : -1;
-        rowmem[r] = mem;
-        rowseq[r] = (mem >= 0 && seq) ? seq[rb + mem] : 0;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < R * CV; idx += blockDim.x) {
-        const int r = idx / CV, v = idx % CV;
-        const int c = c0 + v * VEC;
-        vec_t val;
-        if (c < d.C && rowmem[r] >= 0) {
-            val = *(const vec_t*)(xBC + (rb + rowmem[r]) * d.C + c);
-        } else {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) val[e] = (T)0.f;
-        }
-        *(vec_t*)(xt + r * CT + v * VEC) = val;
-    }
-    __syncthreads();
-
-    const int v = threadIdx.x % CV;
-    const int c = c0 + v * VEC;
     const bool active = c < d.C;
-    float wr[VEC][W];
+    const int k = conv_seg(tab, t0);
+
+    float wr[4][W];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e)
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int kk = 0; kk < W; ++kk) wr[e][kk] = active ? w[(c + e) * W + kk] : 0.f;
 
-    // du for causal offsets 0 .. TT+W-2 (LDS rows W-1 .. R-1)
-    for (int idx = threadIdx.x; idx < RD * CV; idx += blockDim.x) {
-        const int o = idx / CV;
-        const int r = o + W - 1;
-        float dv8[VEC];
+    // x row r is the token r - (W-1) places after t0 in causal order
+    vt xs[RX];
+    int mem[RX];  // position in the row (< 2^31), -1 outside
+    int sq[RX];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) dv8[e] = 0.f;
-        const int64_t mem = rowmem[r];
-        if (active && mem >= 0) {
-            const f32x4* src = (const f32x4*)(dvall + (rb + mem) * d.C + c);
-            const f32x4 lo = src[0], hi = src[1];
+    for (int r = 0; r < RX; ++r) {
+        const int o = r - (W - 1);
+        mem[r] = (int)((o >= 0 && o < TPT) ? t0 + o : conv_row(tab, k, t0, o));
+        sq[r] = (mem[r] >= 0 && seq) ? seq[rb + mem[r]] : 0;
+        if (mem[r] >= 0 && active) {
+            xs[r] = *(const vt*)(xBC + (rb + mem[r]) * d.C + c);
+        } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                dv8[e] = lo[e];
-                dv8[e + 4] = hi[e];
-            }
+            for (int e = 0; e < 4; ++e) xs[r][e] = (T)0.f;
         }
-        const int sq = rowseq[r];
-        float u[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) u[e] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < W; ++kk) {
-            const int rr = r - (W - 1) + kk;
-            if (rowmem[rr] >= 0 && rowseq[rr] == sq) {
-                const vec_t xv = *(const vec_t*)(xt + rr * CT + v * VEC);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) u[e] += wr[e][kk] * (float)xv[e];
-            }
-        }
-        f32x4 lo, hi;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const float sg = 1.f / (1.f + expf(-u[e]));
-            const float g = (mem >= 0) ? dv8[e] * sg * (1.f + u[e] * (1.f - sg)) : 0.f;
-            if (e < 4) lo[e] = g;
-            else hi[e - 4] = g;
-        }
-        *(f32x4*)&dus[o * CT + v * VEC] = lo;
-        *(f32x4*)&dus[o * CT + v * VEC + 4] = hi;
     }
-    __syncthreads();
+    auto tap = [&](int src, int dst) { return mem[src] >= 0 && mem[dst] >= 0 && sq[src] == sq[dst]; };
 
-    float dw[VEC][W];
+    float dw[4][W];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e)
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int kk = 0; kk < W; ++kk) dw[e][kk] = 0.f;
-    for (int idx = threadIdx.x; idx < TT * CV; idx += blockDim.x) {
-        const int o = idx / CV;   // output token offset (source s of the forward taps)
-        const int rs = o + W - 1;  // its LDS row
-        const int sq = rowseq[rs];
-        float acc[VEC];
+    float win[W][4];  // du of offsets o-(W-1) .. o
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+    for (int q = 0; q < W; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) win[q][e] = 0.f;
+
+#pragma unroll
+    for (int o = 0; o < RD; ++o) {
+        const int r = o + W - 1;  // x row of du offset o
+        float u[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < W; ++kk) {
-            const int ot = o + (W - 1) - kk;  // forward output token that read s with tap kk
-            const int rt = ot + W - 1;
-            if (rowmem[rt] >= 0 && rowseq[rt] == sq) {
-                const f32x4 lo = *(const f32x4*)&dus[ot * CT + v * VEC];
-                const f32x4 hi = *(const f32x4*)&dus[ot * CT + v * VEC + 4];
+            if (tap(o + kk, r)) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc[e] += wr[e][kk] * lo[e];
-                    acc[e + 4] += wr[e + 4][kk] * hi[e];
+                for (int e = 0; e < 4; ++e) u[e] += wr[e][kk] * (float)xs[o + kk][e];
+            }
+        }
+        float g[4] = {0.f, 0.f, 0.f, 0.f};
+        if (mem[r] >= 0 && active) {
+            const f32x4 dv4 = *(const f32x4*)(dvall + (rb + mem[r]) * d.C + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float sg = 1.f / (1.f + __expf(-u[e]));
+                g[e] = dv4[e] * sg * (1.f + u[e] * (1.f - sg));
+            }
+        }
+        if (o < TPT) {  // dconv_w from this thread's own outputs
+#pragma unroll
+            for (int kk = 0; kk < W; ++kk) {
+                if (tap(o + kk, r)) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dw[e][kk] += g[e] * (float)xs[o + kk][e];
                 }
             }
         }
-        vec_t outv;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) outv[e] = (T)acc[e];
-        // dconv_w: forward output o read source o-(W-1)+kk with tap kk
-        const f32x4 dlo = *(const f32x4*)&dus[o * CT + v * VEC];
-        const f32x4 dhi = *(const f32x4*)&dus[o * CT + v * VEC + 4];
+        for (int q = 0; q + 1 < W; ++q)
 #pragma unroll
-        for (int kk = 0; kk < W; ++kk) {
-            const int rr = o + kk;
-            if (rowmem[rr] >= 0 && rowseq[rr] == sq) {
-                const vec_t xv = *(const vec_t*)(xt + rr * CT + v * VEC);
+            for (int e = 0; e < 4; ++e) win[q][e] = win[q + 1][e];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    dw[e][kk] += dlo[e] * (float)xv[e];
-                    dw[e + 4][kk] += dhi[e] * (float)xv[e + 4];
+        for (int e = 0; e < 4; ++e) win[W - 1][e] = g[e];
+        if (o >= W - 1) {
+            // source s = o-(W-1) feeds outputs s .. s+W-1 (du offsets), tap kk = W-1-(t-s)
+            const int s = o - (W - 1), rs = s + W - 1;
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < W; ++kk) {
+                const int ot = s + W - 1 - kk;  // du offset of the output
+                if (tap(rs, ot + W - 1)) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] += wr[e][kk] * win[ot - s][e];
                 }
             }
+            if (active) {
+                vt ov;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ov[e] = (T)acc[e];
+                *(vt*)(dxBC + (rb + t0 + s) * d.C + c) = ov;
+            }
         }
-        if (active) *(vec_t*)(dxBC + (rb + t0 + o) * d.C + c) = outv;
     }
-    // reduce dw over the 16 threads sharing this channel vector: lanes l, l^16,
-    // l^32, l^48 of a wave by shuffles, then the four waves through LDS.
 #pragma unroll
-    for (int e = 0; e < VEC; ++e)
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int kk = 0; kk < W; ++kk) {
-            float x = dw[e][kk];
-            x += __shfl_xor(x, 16, 64);
-            x += __shfl_xor(x, 32, 64);
-            dw[e][kk] = x;
-        }
-    const int wave = wave_id(), lane = threadIdx.x % 64;
-    if (lane < CV) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-#pragma unroll
-            for (int kk = 0; kk < W; ++kk) wred[wave][lane][e * W + kk] = dw[e][kk];
-    }
+        for (int kk = 0; kk < W; ++kk) wred[wave][lane][e * W + kk] = dw[e][kk];
     __syncthreads();
-    for (int q = threadIdx.x; q < CV * VEC * W; q += blockDim.x) {
-        const int vv = q / (VEC * W), j = q % (VEC * W);
-        const float sum = wred[0][vv][j] + wred[1][vv][j] + wred[2][vv][j] + wred[3][vv][j];
-        const int cc = c0 + vv * VEC + j / W;
-        if (cc < d.C) dwp[(((int64_t)b * (d.L / TT) + tt) * d.C + cc) * W + (j % W)] = sum;
+    for (int q = threadIdx.x; q < 64 * 4 * W; q += blockDim.x) {
+        const int ln = q / (4 * W), j = q % (4 * W);
+        const int cc = (blockIdx.x * 64 + ln) * 4 + j / W;
+        const float sum = wred[0][ln][j] + wred[1][ln][j] + wred[2][ln][j] + wred[3][ln][j];
+        if (cc < d.C) dwp[(((int64_t)b * (d.L / CONV_TT) + blockIdx.y) * d.C + cc) * W + (j % W)] = sum;
     }
 }
 
@@ -1507,10 +1471,9 @@ static void launch_chunk_bwd(const Dims& d, const SegTab& t, const BwdArgs& a, c
 template <typename T, int W>
 static void launch_conv_bwd_w(const Dims& d, const SegTab& t, const BwdArgs& a, const BwdWs& L,
                               char* ws, hipStream_t s) {
-    dim3 grid((d.C + 127) / 128, (unsigned)(d.L / 64), (unsigned)d.batch);
+    dim3 grid((d.C + 255) / 256, (unsigned)(d.L / CONV_TT), (unsigned)d.batch);
     hipLaunchKernelGGL((k_conv_bwd<T, W>), grid, dim3(256), 0, s, d, t, (const T*)a.xBC, a.conv_w,
-                       a.seq, (const float*)(ws + L.dv), (T*)a.dxBC,
-                       (float*)(ws + L.dwp));
+                       a.seq, (const float*)(ws + L.dv), (T*)a.dxBC, (float*)(ws + L.dwp));
 }
 
 template <typename T>
@@ -1575,7 +1538,7 @@ static void conv_bwd_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* w
                        hipStream_t s) {
     const BwdWs L = bwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
     char* ws = (char*)ws_;
-    const int64_t nbc = d.batch * d.L * 2 * d.G * d.N;
+    const int64_t nbc = d.batch * d.L * 2 * d.G * d.N / (16 / sizeof(T));
     hipLaunchKernelGGL(k_bc_headsum<T>, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, d,
                        (const T*)(ws + L.dbc), (float*)(ws + L.dv));
     launch_conv_bwd<T>(d, t, a, L, ws, s);

@@ -51,6 +51,35 @@ __device__ __forceinline__ int64_t seg_pred_token(const SegTab& t, int k) {
 template <typename T>
 __device__ __forceinline__ float to_f(T v) { return (float)v; }
 
+// Conv tiling shared by the forward and backward conv kernels: a thread owns
+// CONV_VEC channels and CONV_TPT tokens, a workgroup four token groups.
+constexpr int CONV_VEC = 4;   // channels per thread
+constexpr int CONV_TPT = 16;  // tokens per thread
+constexpr int CONV_TT = 4 * CONV_TPT;  // tokens per workgroup (one group per wave)
+
+template <typename T>
+struct Vec4 {
+    typedef T type __attribute__((ext_vector_type(4)));
+};
+
+// Memory position of the token `o` places after memory token t0 (o may be
+// negative: causal predecessors), for t0 inside segment k; -1 when outside the
+// row.  Callers keep |o| below a segment length.
+__device__ __forceinline__ int64_t conv_row(const SegTab& tab, int k, int64_t t0, int o) {
+    const int64_t s0 = tab.start[k], s1 = s0 + tab.len[k];
+    const int64_t m = t0 + o;
+    if (m >= s0 && m < s1) return m;
+    if (m < s0) return k > 0 ? tab.start[k - 1] + tab.len[k - 1] - (s0 - m) : -1;
+    return k + 1 < tab.n ? tab.start[k + 1] + (m - s1) : -1;
+}
+
+__device__ __forceinline__ int conv_seg(const SegTab& tab, int64_t t0) {
+    int k = 0;
+    for (int i = 0; i < tab.n; ++i)
+        if (t0 >= tab.start[i] && t0 < tab.start[i] + tab.len[i]) k = i;
+    return k;
+}
+
 // (chunk, head, row) of a workgroup in a 1-D grid of nchunk * H * batch
 // workgroups.  The hardware hands workgroup i to XCD i % 8; giving each XCD one
 // contiguous range of logical items, heads fastest, makes the workgroups that
