@@ -3,8 +3,8 @@
 One step = one pass of the whole hot path (forward and backward) over one
 batch of synthetic input, every call going through the C ABI on torch's
 current stream:
-  forward : ssd_conv1d_fwd -> ssd_segment_states -> ssd_segment_output
-            -> ssd_boundary_scan -> ssd_apply_init_state
+  forward : ssd_conv1d_fwd -> ssd_segment_states -> ssd_boundary_scan
+            -> ssd_segment_output_fused (output pass with the correction folded in)
   backward: ssd_segment_bwd_summary -> ssd_boundary_scan (reverse)
             -> ssd_segment_bwd_chunks -> ssd_conv1d_bwd
 Workload: 2 rows x 8192 tokens, 32 heads, headdim 64, d_state 128, 1 group,
@@ -79,6 +79,7 @@ def algorithmic_bytes(wl):
         "ssd_conv1d_fwd": 2 * BL * C * e + C * wl.conv_width * 4 + seq,
         "ssd_segment_states": BL * (H * P + G * N) * e + BL * H * e + 2 * dtcs + hst + summary + seq,
         "ssd_segment_output": BL * C * e + hst + dtcs + BL * H * P * 4 + seq,
+        "ssd_segment_output_fused": BL * C * e + hst + dtcs + states + BL * H * P * e + seq,
         "ssd_boundary_scan": summary + states,
         "ssd_apply_init_state": BL * H * P * 4 + BL * (H * P + G * N) * e + BL * H * 4 + states
                                 + BL * H * P * e + seq,
@@ -86,7 +87,7 @@ def algorithmic_bytes(wl):
 
 
 def output_flops(wl):
-    """MFMA flops of ssd_segment_output: causal C B^T, its product with X, and C H^T."""
+    """MFMA flops of the output pass: causal C B^T, its product with X, and C H^T."""
     b, L, H, P, N, Q = wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.chunk
     per_chunk_head = Q * (Q + 1) // 2 * 2 * (N + P) + 2 * Q * P * N
     return b * (L // Q) * H * per_chunk_head
@@ -158,12 +159,10 @@ def main():
         ("ssd_conv1d_fwd", lambda: ssd.ssd_conv1d_fwd(p, segs, xBC, conv_w, seq, bufs.xBC_conv)),
         ("ssd_segment_states", lambda: ssd.ssd_segment_states(
             p, segs, bufs.xBC_conv, dt_raw, dt_bias, A_log, seq, bufs.summary, bufs.ws)),
-        ("ssd_segment_output", lambda: ssd.ssd_segment_output(
-            p, segs, bufs.xBC_conv, seq, bufs.ws, bufs.y_zero)),
         ("ssd_boundary_scan", lambda: ssd.ssd_boundary_scan(
             p, segs.n, bufs.summary, None, False, bufs.S_in)),
-        ("ssd_apply_init_state", lambda: ssd.ssd_apply_init_state(
-            p, segs, bufs.y_zero, bufs.xBC_conv, D, seq, bufs.S_in, bufs.ws, bufs.y)),
+        ("ssd_segment_output_fused", lambda: ssd.ssd_segment_output_fused(
+            p, segs, bufs.xBC_conv, D, seq, bufs.S_in, bufs.ws, bufs.y)),
     ]
     if do_bwd:
         calls += [
@@ -178,9 +177,8 @@ def main():
                 p, segs, xBC, conv_w, A_log, seq, bb.ws, bb.dxBC, bb.dconv_w, bb.ddt_bias,
                 bb.dA_log, bb.dD)),
         ]
-    single_kernel = {"ssd_conv1d_fwd", "ssd_segment_output", "ssd_boundary_scan",
-                     "ssd_apply_init_state", "ssd_boundary_scan(reverse)",
-                     "ssd_segment_bwd_chunks"}
+    single_kernel = {"ssd_conv1d_fwd", "ssd_segment_output_fused", "ssd_boundary_scan",
+                     "ssd_boundary_scan(reverse)", "ssd_segment_bwd_chunks"}
 
     def step(events=None):
         for i, (_, fn) in enumerate(calls):
@@ -226,7 +224,7 @@ def main():
     achieved = per_call[dom]["GB_per_s"]
     mfma_peak = BF16_PEAK_TFLOPS if wl.act == "bf16" else F32_PEAK_TFLOPS
     mfma = {}
-    for name, fl in [("ssd_segment_output", output_flops(wl))] + \
+    for name, fl in [("ssd_segment_output_fused", output_flops(wl))] + \
             ([("ssd_segment_bwd_chunks", chunk_bwd_flops(wl))] if do_bwd else []):
         tf = fl / (per_call[name]["ms"] * 1e-3) / 1e12
         mfma[name] = {"achieved": round(tf, 2), "peak": mfma_peak, "unit": "TFLOP/s",

@@ -191,6 +191,23 @@ int ssd_apply_init_state(const ssd_problem* problem, const ssd_segment* segs, in
                          const int32_t* seq_idx, const float* S_in, const void* ws,
                          size_t ws_bytes, void* y, void* stream);
 
+/* ssd_segment_output and ssd_apply_init_state in one pass, for callers that run
+ * the boundary scan between ssd_segment_states and the output pass (the
+ * summaries of #6808 depend only on the chunk states, so the scan can precede
+ * the output work).  Every chunk's output uses its true entering state (the
+ * zero-state walk plus decay * S_in) and D x is added in the same pass, so
+ * y_zero is never written and x and C are read once.  Same result as
+ * ssd_segment_output followed by ssd_apply_init_state, up to rounding.
+ *   xBC_conv, D, seq_idx   as for ssd_apply_init_state                         (in)
+ *   S_in      [nseg][batch][H][P][N] float32 (ssd_boundary_scan output)         (in)
+ *   ws        the workspace ssd_segment_states filled for the same problem,
+ *             segments and inputs (read only)                                   (in)
+ *   y         [batch][seqlen][H][P] act_dtype                                   (out) */
+int ssd_segment_output_fused(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                             const void* xBC_conv, const float* D, const int32_t* seq_idx,
+                             const float* S_in, const void* ws, size_t ws_bytes, void* y,
+                             void* stream);
+
 /* Backward, summary phase.  Recomputes the conv output, dt and the
  * cumulative decays into `ws` (sequence-length-sized intermediates are
  * recomputed, never saved from the forward), then walks every segment's chunks

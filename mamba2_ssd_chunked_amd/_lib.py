@@ -63,6 +63,8 @@ SIGNATURES = {
                                       _vp, _vp, _vp, _vp, _vp, _vp]),
     "ssd_apply_init_state": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                             ctypes.c_size_t, _vp, _vp]),
+    "ssd_segment_output_fused": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, _vp, _vp,
+                                                ctypes.c_size_t, _vp, _vp]),
 }
 
 _lib = None

@@ -1,0 +1,64 @@
+// Causal Gram tiles of a chunk: G_ab[j][i] = B_j . C_i for 16-token tiles
+// a >= b (output tile a holds i, source tile b holds j), one per (row, chunk,
+// group).  Every head of the group weights the same C B^T by its own decays, so
+// the product is formed once here instead of once per head.  This is the
+// "local CB computation" of Megatron-LM #6808 (first commit), which it overlaps
+// with the summary exchange.
+//
+// Tile layout: the MFMA output layout, stored lane by lane, so that one wave
+// reads a tile back with one 8-byte (bf16) or 16-byte (float32) load per lane:
+// lane l holds column i = l % 16 and rows j = 4 (l / 16) + r, r = 0..3.
+// Tiles of a (row, chunk, group) are numbered t = a (a + 1) / 2 + b.
+#pragma once
+
+#include "ssd_internal.h"
+
+namespace ssd {
+
+__host__ __device__ constexpr int gram_tiles(int qt) { return qt * (qt + 1) / 2; }
+__host__ __device__ constexpr int gram_index(int a, int b) { return a * (a + 1) / 2 + b; }
+
+// One wave per (output tiles w and QT-1-w, chunk, group, row).
+template <typename T, int N>
+__global__ void __launch_bounds__(64) k_gram(Dims d, const T* __restrict__ xc, T* __restrict__ gram) {
+    typedef Mma<T> M;
+    typedef typename M::Frag Frag;
+    constexpr int SL = M::SL, KS = M::KS, NKF = N / KS;
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    const int QT = d.Q / 16;
+    const int w = blockIdx.x;
+    const int g = blockIdx.y % d.G, cm = blockIdx.y / d.G;
+    const int64_t b = blockIdx.z;
+    const int lane = threadIdx.x, lr = lane % 16, lg = lane / 16;
+    const int64_t t0 = b * d.L + (int64_t)cm * d.Q;
+    const int64_t boff = (int64_t)d.H * d.P + (int64_t)g * N;
+    const int64_t coff = boff + (int64_t)d.G * N;
+    T* out = gram + (((int64_t)b * d.nchunk + cm) * d.G + g) * (int64_t)gram_tiles(QT) * 256;
+    for (int side = 0; side < 2; ++side) {
+        const int a = side == 0 ? w : QT - 1 - w;
+        if (side == 1 && a == w) break;
+        Frag cf[NKF];
+#pragma unroll
+        for (int kn = 0; kn < NKF; ++kn)
+            cf[kn] = M::load(xc + (t0 + a * 16 + lr) * d.C + coff + kn * KS + SL * lg);
+        for (int bt = 0; bt <= a; ++bt) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kn = 0; kn < NKF; ++kn)
+                acc = M::mma(M::load(xc + (t0 + bt * 16 + lr) * d.C + boff + kn * KS + SL * lg),
+                             cf[kn], acc);
+            *(t4*)(out + (int64_t)gram_index(a, bt) * 256 + lane * 4) =
+                t4{(T)acc[0], (T)acc[1], (T)acc[2], (T)acc[3]};
+        }
+    }
+}
+
+template <typename T, int N>
+inline void launch_gram(const Dims& d, const T* xc, T* gram, hipStream_t s) {
+    const int QT = d.Q / 16;
+    hipLaunchKernelGGL((k_gram<T, N>), dim3((unsigned)(QT / 2), (unsigned)(d.nchunk * d.G),
+                                            (unsigned)d.batch),
+                       dim3(64), 0, s, d, xc, gram);
+}
+
+}  // namespace ssd

@@ -249,6 +249,25 @@ int ssd_apply_init_state(const ssd_problem* problem, const ssd_segment* segs, in
                                               seq_idx, S_in, ws, y, (hipStream_t)stream));
 }
 
+int ssd_segment_output_fused(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                             const void* xBC_conv, const float* D, const int32_t* seq_idx,
+                             const float* S_in, const void* ws, size_t ws_bytes, void* y,
+                             void* stream) {
+    Dims d;
+    SegTab t;
+    int rc = check_problem(problem, &d);
+    if (rc) return rc;
+    if ((rc = check_segments(segs, nseg, &d, &t))) return rc;
+    if (!xBC_conv || !D || !S_in || !y) return SSD_ERR_NULL;
+    if (!ws) return SSD_ERR_WORKSPACE;
+    if (ws_bytes < fwd_ws_layout(d, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
+    if (!aligned16(xBC_conv) || !aligned16(D) || !aligned16(seq_idx) || !aligned16(S_in) ||
+        !aligned16(ws) || !aligned16(y))
+        return SSD_ERR_ALIGN;
+    return hip_status(launch_segment_output_fused(d, t, problem->act_dtype, xBC_conv, D, seq_idx,
+                                                  S_in, ws, y, (hipStream_t)stream));
+}
+
 int ssd_segment_bwd_summary(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
                             const void* xBC, const float* conv_w, const void* dt_raw,
                             const float* dt_bias, const float* A_log, const int32_t* seq_idx,

@@ -16,15 +16,18 @@
 //                  decay-weighted sum over earlier chunk states as the step that
 //                  must cross devices; Megatron-LM #6808 ships it as the FP32
 //                  segment summary.)
-//   k_chunk_out    one workgroup per (row, chunk, head): the intra-chunk term
+//   k_chunk_y      one workgroup per (row, chunk, head): the intra-chunk term
 //                  (C B^T masked by exp(cs_i - cs_j) dt_j, j <= i, same sequence)
-//                  times X, plus the inter-chunk term exp(cs_i) C_i H_c, into the
-//                  zero-initial-state output y_zero.  CB^T is produced tile by
-//                  tile in registers and fed straight back as an MFMA operand.
+//                  times X, plus the inter-chunk term exp(cs_i) C_i H_c.  Either
+//                  into the zero-initial-state output y_zero (FP32), or, given
+//                  the boundary scan's S_in, straight into y with the true
+//                  entering state and D x (the correction folded in).
 //   k_apply_init   y = y_zero + exp(cs_seg_i) C_i S_in^T + D x_i (the correction
-//                  of #6808 once the boundary scan has produced S_in).
+//                  of #6808 once the boundary scan has produced S_in), for
+//                  callers that keep y_zero.
 #include <type_traits>
 
+#include "gram.h"
 #include "ssd_internal.h"
 #include "state_walk.h"
 
@@ -50,9 +53,11 @@ template <> struct KPerm<float> {
 };
 
 // ---------------------------------------------------------------------------
-// The cumsum restarts at every packed-sequence start inside the chunk (a
-// segmented scan), so a sequence's decays are computed from its own tokens
-// only and perturbing one sequence cannot change another's bits.
+// dt prep, one wave per (row, chunk, head), four heads per workgroup; lane l
+// owns the Q/64 consecutive tokens l*Q/64 ...  The cumsum restarts at every
+// packed-sequence start inside the chunk (a segmented scan), so a sequence's
+// decays are computed from its own tokens only and perturbing one sequence
+// cannot change another's bits.
 template <typename T>
 __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ dt_raw,
                                                 const float* __restrict__ dt_bias,
@@ -60,205 +65,420 @@ __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ d
                                                 const int32_t* __restrict__ seq,
                                                 float* __restrict__ dt_ws, float* __restrict__ cs_ws,
                                                 float* __restrict__ ctot) {
-    __shared__ float raw[256][17];
-    __shared__ int sseq[256];
-    const int cm = blockIdx.x, h0 = blockIdx.y * 16;
+    const int cm = blockIdx.x, h = blockIdx.y * 4 + wave_id();
     const int64_t b = blockIdx.z;
+    if (h >= d.H) return;
+    const int lane = threadIdx.x % 64;
     const int Q = d.Q;
-    const int64_t tok0 = (int64_t)cm * Q;
-    const int nh = min(16, d.H - h0);
-    for (int idx = threadIdx.x; idx < Q * 16; idx += blockDim.x) {
-        const int j = idx / 16, hh = idx % 16;
-        raw[j][hh] = hh < nh ? to_f(dt_raw[(b * d.L + tok0 + j) * d.H + h0 + hh]) : 0.f;
-    }
-    for (int j = threadIdx.x; j < Q; j += blockDim.x) sseq[j] = seq ? seq[b * d.L + tok0 + j] : 0;
-    __syncthreads();
-    const int wave = wave_id(), lane = threadIdx.x % 64;
     const int E = Q / 64;  // tokens per lane (1, 2 or 4)
-    bool rs[4];            // a sequence starts at or before this token, inside this lane
+    const int64_t tok0 = b * d.L + (int64_t)cm * Q + lane * E;
+    const float A = -expf(A_log[h]);
+    const float bias = dt_bias[h];
+    float dtv[4], csl[4];
+    bool rs[4];  // a sequence starts at or before this token, inside this lane
     bool lflag = false;
+    float run = 0.f;
+    int sprev = (seq && lane * E > 0) ? seq[tok0 - 1] : 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         if (e < E) {
             const int j = lane * E + e;
-            lflag = lflag || (j > 0 && sseq[j] != sseq[j - 1]);
+            const int sj = seq ? seq[tok0 + e] : 0;
+            const bool start = j > 0 && sj != sprev;
+            sprev = sj;
+            lflag = lflag || start;
             rs[e] = lflag;
+            if (start) run = 0.f;
+            const float z = to_f(dt_raw[(tok0 + e) * d.H + h]) + bias;
+            const float dt = fminf(fmaxf(softplus_f(z), d.dt_min), d.dt_max);
+            dtv[e] = dt;
+            run += dt * A;
+            csl[e] = run;
         }
     }
-    for (int hh = wave; hh < nh; hh += 4) {
-        const int h = h0 + hh;
-        const float A = -expf(A_log[h]);
-        const float bias = dt_bias[h];
-        float dtv[4], csl[4];
-        float run = 0.f;
+    // Segmented inclusive scan of (flag, sum) across the wave:
+    // (f1, v1) then (f2, v2) -> (f1 | f2, f2 ? v2 : v1 + v2).
+    float iv = run;
+    bool ifl = lflag;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (e < E) {
-                const int j = lane * E + e;
-                if (j > 0 && sseq[j] != sseq[j - 1]) run = 0.f;
-                const float z = raw[j][hh] + bias;
-                const float dt = fminf(fmaxf(softplus_f(z), d.dt_min), d.dt_max);
-                dtv[e] = dt;
-                run += dt * A;
-                csl[e] = run;
-            }
+    for (int off = 1; off < 64; off <<= 1) {
+        const float v = __shfl_up(iv, off, 64);
+        const int f = __shfl_up((int)ifl, off, 64);
+        if (lane >= off) {
+            if (!ifl) iv += v;
+            ifl = ifl || f;
         }
-        // Segmented inclusive scan of (flag, sum) across the wave:
-        // (f1, v1) then (f2, v2) -> (f1 | f2, f2 ? v2 : v1 + v2).
-        float iv = run;
-        bool ifl = lflag;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float v = __shfl_up(iv, off, 64);
-            const int f = __shfl_up((int)ifl, off, 64);
-            if (lane >= off) {
-                if (!ifl) iv += v;
-                ifl = ifl || f;
-            }
-        }
-        float ev = __shfl_up(iv, 1, 64);
-        if (lane == 0) ev = 0.f;
-        float* dtp = dt_ws + ((int64_t)b * d.H + h) * d.L + tok0;
-        float* csp = cs_ws + ((int64_t)b * d.H + h) * d.L + tok0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (e < E) {
-                dtp[lane * E + e] = dtv[e];
-                csp[lane * E + e] = rs[e] ? csl[e] : ev + csl[e];
-            }
-        }
-        // the chunk total is the last token's cumulative sum, bit for bit
-        if (lane == 63)
-            ctot[((int64_t)b * d.H + h) * d.nchunk + cm] =
-                rs[E - 1] ? csl[E - 1] : ev + csl[E - 1];
     }
+    float ev = __shfl_up(iv, 1, 64);
+    if (lane == 0) ev = 0.f;
+    const int64_t o = ((int64_t)b * d.H + h) * d.L + (int64_t)cm * Q + lane * E;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (e < E) {
+            dt_ws[o + e] = dtv[e];
+            cs_ws[o + e] = rs[e] ? csl[e] : ev + csl[e];
+        }
+    }
+    // the chunk total is the last token's cumulative sum, bit for bit
+    if (lane == 63)
+        ctot[((int64_t)b * d.H + h) * d.nchunk + cm] = rs[E - 1] ? csl[E - 1] : ev + csl[E - 1];
 }
 
 // ---------------------------------------------------------------------------
-// Waves take 16-column output tiles in the order w, 2NW-1-w, 2NW+w, ... so that
-// the causal (triangular) work is balanced across waves.
-__device__ __forceinline__ int wave_tile(int wave, int nw, int m) {
-    const int pair = m / 2;
-    return (m % 2 == 0) ? 2 * nw * pair + wave : 2 * nw * pair + 2 * nw - 1 - wave;
-}
+// Transposed-operand reads of a [token][p] tile kept in LDS in its natural row
+// layout.  The result is the k operand of the MFMA that multiplies a weight
+// tile (k = source token j) with X: lane l holds column p0 + l % 16 and the k
+// slots of KPerm's order (slot s of lane group g is token 16 (s / 4) + 4 g +
+// s % 4 of the 32-token block).
+//
+// bf16: two ds_read_b64_tr_b16.  Within each 16-lane group that instruction
+// hands output lane i, element e, the element i % 4 of the 8 bytes addressed by
+// lane i / 4 + 4 e of the group; letting lane q of group g address token
+// jb + 4 g + q / 4, columns p0 + 4 (q % 4) .. +3, output lane i receives tokens
+// jb + 4 g + e of column p0 + i.
+// float32: four 4-byte reads (16 tokens per MFMA k step, natural order).
+template <typename T> struct XT;
+template <> struct XT<bf16> {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    __device__ static __forceinline__ bf16x8 load(const bf16* xs, int xr, int jb, int p0, int lane) {
+        const int q = lane % 16, g = lane / 16;
+        const bf16* a = xs + (jb + 4 * g + q / 4) * xr + p0 + 4 * (q % 4);
+        typedef __attribute__((address_space(3))) s4 lds_s4;
+        const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)a));
+        const bf16x4 hi =
+            __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(a + 16 * xr)));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+template <> struct XT<float> {
+    __device__ static __forceinline__ f32x4 load(const float* xs, int xr, int jb, int p0, int lane) {
+        const int i = lane % 16, g = lane / 16;
+        const float* a = xs + (jb + 4 * g) * xr + p0 + i;
+        return f32x4{a[0], a[xr], a[2 * xr], a[3 * xr]};
+    }
+};
 
-template <typename T, int P, int N, int Q, int NW>
-__global__ void __launch_bounds__(NW * 64) k_chunk_out(Dims d, SegTab tab, const T* __restrict__ xc,
-                                                      const float* __restrict__ dt_ws,
-                                                      const float* __restrict__ cs_ws,
-                                                      const int32_t* __restrict__ seq,
-                                                      const T* __restrict__ hst,
-                                                      float* __restrict__ y_zero) {
+// ---------------------------------------------------------------------------
+// Output pass, one workgroup per (row, chunk, head) with NW = Q/32 waves.  Wave
+// w owns the 16-token output tiles a0 = w and a1 = QT-1-w, so every wave meets
+// the same number of causal (source tile <= output tile) pairs.
+//
+// For output token i and source token j <= i of the same packed sequence the
+// intra-chunk weight is (C_i . B_j) exp(cs_i - cs_j) dt_j.  C_i . B_j comes
+// from the group's Gram tiles (k_gram); every load the workgroup needs (X of the
+// head in its natural layout, the entering state, the Gram tiles of the wave's
+// two output tiles, the decays) is issued up front, so one memory latency is
+// paid per workgroup and about 58 KB of LDS lets two workgroups share a CU.
+// In a chunk without a sequence start the decay is factored through the
+// 16-token tiles a of i and b of j, with F and L the cumulative sums at a
+// tile's first and last token:
+//   exp(cs_i - cs_j) = exp(cs_i - F_a) exp(F_a - L_b) exp(L_b - cs_j),
+// which needs no transcendental in the inner loop; chunks with a sequence start,
+// or a tile whose decay span would leave the normal float range, take the exact
+// per-element path.  The weighted Gram tile feeds the next MFMA as its k operand.
+//
+// FINAL = false: y_zero = intra-chunk term + exp(cs_i) C_i H_c^T with H_c the
+//                zero-initial-state entering state (none for a segment's first
+//                chunk), FP32, no D term.
+// FINAL = true:  y = the same with H_c replaced by the true entering state
+//                H_c + eps S_in (eps = exp(sum of dt A from the segment start to
+//                the chunk), 0 once a packed sequence started in between), plus
+//                D x, in the activation type.  This is the zero-state output and
+//                the correction pass of #6808 in one pass: y_zero never goes to
+//                memory and x and C are read once.  D is folded into the
+//                diagonal of the weight matrix (j = i), so D x comes out of the
+//                same MFMA.
+template <typename T, int P, int N, int Q, bool FINAL>
+__global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims d, SegTab tab, const T* __restrict__ xc,
+                                                        const T* __restrict__ gram,
+                                                        const float* __restrict__ dt_ws,
+                                                        const float* __restrict__ cs_ws,
+                                                        const float* __restrict__ ctot,
+                                                        const int32_t* __restrict__ seq,
+                                                        const T* __restrict__ hst,
+                                                        const float* __restrict__ S_in,
+                                                        const float* __restrict__ Dp,
+                                                        float* __restrict__ y_zero,
+                                                        T* __restrict__ y) {
     typedef Mma<T> M;
     typedef typename M::Frag Frag;
+    typedef typename M::Elem E;
     constexpr int SL = M::SL, KS = M::KS;
     constexpr int VEC = 16 / sizeof(T);
-    constexpr int XPITCH = Q + VEC;
-    constexpr int BPITCH = N + VEC;
-    constexpr int PT = P / 16, QT = Q / 16, NKF = N / KS;
-    __shared__ __attribute__((aligned(16))) T Xt[P * XPITCH];
-    __shared__ __attribute__((aligned(16))) T Bs[Q * BPITCH];
-    __shared__ float scs[Q], sdt[Q];
-    __shared__ int ssq[Q];
+    constexpr int NW = Q / 32, NTH = NW * 64, QT = Q / 16;
+    constexpr int PT = P / 16, NKF = N / KS;
+    constexpr int XR = P + VEC;  // X row pitch (16-byte aligned rows for the vector stores)
+    constexpr int HP = N + VEC;  // entering-state row pitch
+    constexpr int YP = P + VEC;  // output staging pitch
+    typedef T vt __attribute__((ext_vector_type(VEC)));
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    // X [Q][XR] and the entering state [P][HP]; the output staging of the FINAL
+    // variant reuses the same memory once the MFMAs are done
+    constexpr int E_X = Q * XR, E_H = P * HP, E_Y = 2 * NW * 16 * YP;
+    __shared__ __attribute__((aligned(16))) T U[E_X + E_H > E_Y ? E_X + E_H : E_Y];
+    T* const sX = U;
+    T* const sH = U + E_X;
+    T* const sY = U;
+    __shared__ __attribute__((aligned(16))) float scs[Q];
+    __shared__ __attribute__((aligned(16))) float sdt[Q];
+    __shared__ __attribute__((aligned(16))) float sea[Q];  // exp(cs_t - F(t))
+    __shared__ __attribute__((aligned(16))) float seb[Q];  // exp(L(t) - cs_t) dt_t
+    __shared__ __attribute__((aligned(16))) int ssq[Q];
+    __shared__ float stab[QT * QT];                         // exp(F_a - L_b), a >= b
+    __shared__ float s_eps;
 
     const ChunkHead ch = chunk_head_of_block(d);
     const int cm = ch.cm, h = ch.h;
     const int64_t b = ch.b;
     const int wave = wave_id(), lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
     const int g = h / d.hpg;
-    const int64_t rb = b * d.L;
-    const int64_t t0 = (int64_t)cm * Q;
+    const int64_t rb = b * d.L, t0 = (int64_t)cm * Q;
     const int k = seg_of_chunk(tab, cm, Q);
-    const bool first = (t0 == tab.start[k]);
-    const int64_t xoff = (int64_t)h * P, boff = (int64_t)d.H * P + (int64_t)g * N;
+    const int64_t s0 = tab.start[k];
+    const bool first = (t0 == s0);
+    const int64_t pred = seg_pred_token(tab, k);
+    // sequence of the state entering the segment, and of the one entering the chunk
+    const int seq_ref = seq ? seq[rb + (pred >= 0 ? pred : s0)] : 0;
+    const int seq_prev = (seq && !first) ? seq[rb + t0 - 1] : seq_ref;
+    const bool split = seq && seq[rb + t0] != seq[rb + t0 + Q - 1];
+    const int64_t xoff = (int64_t)h * P;
     const int64_t coff = (int64_t)d.H * P + (int64_t)d.G * N + (int64_t)g * N;
+    const int64_t hl = ((int64_t)b * d.H + h) * d.L + t0;
+    const bool inter = FINAL || !first;
+    const int a0 = wave, a1 = QT - 1 - wave;
 
-    typedef T vt __attribute__((ext_vector_type(VEC)));
-    for (int idx = threadIdx.x; idx < Q * (P / VEC); idx += blockDim.x) {
-        const int jj = idx / (P / VEC), pv = idx % (P / VEC);
-        const vt v = *(const vt*)(xc + (rb + t0 + jj) * d.C + xoff + pv * VEC);
+    // ---- issue every global load of the workgroup
+    constexpr int V_X = (Q * (P / VEC) + NTH - 1) / NTH;
+    vt rx[V_X];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) Xt[(pv * VEC + e) * XPITCH + jj] = v[e];
-    }
-    for (int idx = threadIdx.x; idx < Q * (N / VEC); idx += blockDim.x) {
-        const int jj = idx / (N / VEC), nv = idx % (N / VEC);
-        *(vt*)&Bs[jj * BPITCH + nv * VEC] = *(const vt*)(xc + (rb + t0 + jj) * d.C + boff + nv * VEC);
-    }
-    const float* csp = cs_ws + ((int64_t)b * d.H + h) * d.L + t0;
-    const float* dtp = dt_ws + ((int64_t)b * d.H + h) * d.L + t0;
-    for (int j = threadIdx.x; j < Q; j += blockDim.x) {
-        scs[j] = csp[j];
-        sdt[j] = dtp[j];
-        ssq[j] = seq ? seq[rb + t0 + j] : 0;
-    }
-    const int seq_prev = (!first && seq) ? seq[rb + t0 - 1] : 0;
-    __syncthreads();
-
-    const T* hp = hst + (((int64_t)b * d.nchunk + cm) * d.H + h) * (P * N);
-#pragma unroll 1
-    for (int m = 0;; ++m) {
-        const int it = wave_tile(wave, NW, m);
-        if (it >= QT) break;
-        const int i0 = it * 16;
-        const int i = i0 + lr;
-        const float cs_i = scs[i];
-        const int sq_i = ssq[i];
-
-        Frag cf[NKF];
-#pragma unroll
-        for (int kn = 0; kn < NKF; ++kn)
-            cf[kn] = M::load(xc + (rb + t0 + i) * d.C + coff + kn * KS + SL * lg);
-
-        f32x4 acc[PT];
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        if (!first) {
-            // inter-chunk term: exp(cs_i) C_i H_c^T, for tokens still in the
-            // sequence that was running when the chunk started.
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                for (int kn = 0; kn < NKF; ++kn)
-                    acc[pt] = M::mma(M::load(hp + (pt * 16 + lr) * N + kn * KS + SL * lg), cf[kn],
-                                     acc[pt]);
-            const float f = (sq_i == seq_prev) ? expf(cs_i) : 0.f;
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) acc[pt] *= f;
+    for (int q = 0; q < V_X; ++q) {
+        const int idx = threadIdx.x + q * NTH;
+        if (idx < Q * (P / VEC)) {
+            const int j = idx / (P / VEC), pv = idx % (P / VEC);
+            rx[q] = *(const vt*)(xc + (rb + t0 + j) * d.C + xoff + pv * VEC);
         }
-
-        // intra-chunk term, j-blocks of KS tokens up to the diagonal
-#pragma unroll 1
-        for (int j0 = 0; j0 <= i0 + 15; j0 += KS) {
-            float tv[SL];
+    }
+    constexpr int V_H = (P * (N / VEC) + NTH - 1) / NTH;
+    vt rh[V_H];
+    f32x4 rs[V_H][VEC / 4];
+    const T* hp = hst + (((int64_t)b * d.nchunk + cm) * d.H + h) * (P * N);
+    const float* sp = S_in + (((int64_t)k * d.batch + b) * d.H + h) * (P * N);
+    if (inter) {
 #pragma unroll
-            for (int st = 0; st < KS / 16; ++st) {
-                const int js = j0 + st * 16;
-                f32x4 tacc = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (js <= i0 + 15) {
+        for (int q = 0; q < V_H; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (idx < P * (N / VEC)) {
+                const int p = idx / (N / VEC), nv = idx % (N / VEC);
+                if (!first) {
+                    rh[q] = *(const vt*)(hp + (int64_t)p * N + nv * VEC);
+                } else {
 #pragma unroll
-                    for (int kn = 0; kn < NKF; ++kn)
-                        tacc = M::mma(M::load(&Bs[(js + lr) * BPITCH + kn * KS + SL * lg]), cf[kn],
-                                      tacc);
+                    for (int e = 0; e < VEC; ++e) rh[q][e] = (T)0.f;
                 }
+                if (FINAL) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = js + 4 * lg + r;
-                    float val = 0.f;
-                    if (j <= i && ssq[j] == sq_i) val = tacc[r] * expf(cs_i - scs[j]) * sdt[j];
-                    tv[st * 4 + r] = val;
+                    for (int e = 0; e < VEC / 4; ++e)
+                        rs[q][e] = *(const f32x4*)(sp + (int64_t)p * N + nv * VEC + 4 * e);
                 }
             }
-            const Frag tb = M::from_f(tv);
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-                acc[pt] = M::mma(KPerm<T>::load(&Xt[(pt * 16 + lr) * XPITCH + j0 + 4 * lg]), tb,
-                                 acc[pt]);
         }
-
-        float* yo = y_zero + ((rb + t0 + i) * d.H + h) * P;
+    }
+    for (int j = threadIdx.x; j < Q; j += NTH) {
+        scs[j] = cs_ws[hl + j];
+        sdt[j] = dt_ws[hl + j];
+        ssq[j] = seq ? seq[rb + t0 + j] : 0;
+    }
+    if (FINAL && wave == 0) {
+        // eps = exp(sum of the segment's earlier chunk totals), if no sequence
+        // started between the segment start and this chunk
+        const int cseg0 = (int)(s0 / Q);
+        const float* ct = ctot + ((int64_t)b * d.H + h) * d.nchunk;
+        float part = 0.f;
+        for (int c = cseg0 + lane; c < cm; c += 64) part += ct[c];
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) *(f32x4*)(yo + pt * 16 + 4 * lg) = acc[pt];
+        for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+        if (lane == 0) s_eps = (seq_prev == seq_ref) ? expf(part) : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < V_X; ++q) {
+        const int idx = threadIdx.x + q * NTH;
+        if (idx < Q * (P / VEC)) *(vt*)&sX[(idx / (P / VEC)) * XR + (idx % (P / VEC)) * VEC] = rx[q];
+    }
+    __syncthreads();
+    // The factored decay needs every tile's span cs(first) - cs(last) small
+    // enough that its exponential stays a normal float; chunks with a sequence
+    // start or a wider span take the exact per-element path.
+    int wide = 0;
+    for (int a = threadIdx.x; a < QT; a += NTH) wide |= (scs[16 * a] - scs[16 * a + 15] > 80.f);
+    const bool exact = __syncthreads_or(wide) || split;
+    if (inter) {
+        // entering state [p][n]: zero-state part (non-first chunks) + eps S_in
+        const float eps = FINAL ? s_eps : 0.f;
+#pragma unroll
+        for (int q = 0; q < V_H; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (idx < P * (N / VEC)) {
+                vt v = rh[q];
+                if (FINAL) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        v[e] = (T)((float)v[e] + eps * rs[q][e / 4][e % 4]);
+                }
+                *(vt*)&sH[(idx / (N / VEC)) * HP + (idx % (N / VEC)) * VEC] = v;
+            }
+        }
+    }
+    if (!exact) {
+        for (int t = threadIdx.x; t < Q; t += NTH) {
+            const int t16 = t & ~15;
+            sea[t] = __expf(scs[t] - scs[t16]);
+            seb[t] = __expf(scs[t16 + 15] - scs[t]) * sdt[t];
+        }
+        for (int q = threadIdx.x; q < QT * QT; q += NTH) {
+            const int a = q / QT, c = q % QT;
+            stab[q] = a >= c ? __expf(scs[16 * a] - scs[16 * c + 15]) : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // Gram tiles of the wave's output tiles, DEPTH k steps ahead of their use
+    // (the first ones overlap the inter-chunk term)
+    constexpr int TPK = KS / 16;  // source tiles per k step
+    constexpr int NKS = Q / KS;
+    constexpr int DEPTH = 3;
+    const T* gb = gram + (((int64_t)b * d.nchunk + cm) * d.G + g) * (int64_t)gram_tiles(QT) * 256 + lane * 4;
+    t4 cgr[DEPTH][2][TPK];
+    auto fetch_gram = [&](int ks, t4 (&dst)[2][TPK]) {
+#pragma unroll
+        for (int st = 0; st < TPK; ++st) {
+            const int bt = ks * TPK + st;
+            if (bt <= a0) dst[0][st] = *(const t4*)(gb + (int64_t)gram_index(a0, bt) * 256);
+            if (bt <= a1) dst[1][st] = *(const t4*)(gb + (int64_t)gram_index(a1, bt) * 256);
+        }
+    };
+#pragma unroll
+    for (int q = 0; q < DEPTH; ++q)
+        if (q < NKS) fetch_gram(q, cgr[q]);
+
+    // ---- inter-chunk term of the wave's two output tiles (C_i H^T, rows p, columns i)
+    int i0[2];
+    i0[0] = a0 * 16;
+    i0[1] = a1 * 16;
+    f32x4 acc[2][PT];
+    float rsc_i[2], cs_i[2];
+    int sq_i[2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int i = i0[it] + lr;
+        cs_i[it] = scs[i];
+        sq_i[it] = ssq[i];
+        rsc_i[it] = exact ? 0.f : sea[i];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[it][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (inter) {
+#pragma unroll
+            for (int kn = 0; kn < NKF; ++kn) {
+                const Frag cf = M::load(xc + (rb + t0 + i) * d.C + coff + kn * KS + SL * lg);
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+                    acc[it][pt] = M::mma(M::load(&sH[(pt * 16 + lr) * HP + kn * KS + SL * lg]), cf,
+                                         acc[it][pt]);
+            }
+            const float f = (sq_i[it] == seq_prev) ? expf(cs_i[it]) : 0.f;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) acc[it][pt] *= f;
+        }
+    }
+    const float Dh = FINAL ? Dp[h] : 0.f;
+
+    // ---- intra-chunk term, one 32-token (KS = 32) or 16-token (KS = 16) k step at a time
+    auto weight = [&](int it, int at, int bt, const t4& cgv, float (&vv)[4]) {
+        const int js = bt * 16;
+        const int i = i0[it] + lr;
+        if (!exact) {
+            const float rsc = rsc_i[it] * stab[at * QT + bt];
+            const f32x4 ej = *(const f32x4*)&seb[js + 4 * lg];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) vv[r] = (float)cgv[r] * (rsc * ej[r]);
+        } else {
+            const f32x4 cj = *(const f32x4*)&scs[js + 4 * lg];
+            const f32x4 dj = *(const f32x4*)&sdt[js + 4 * lg];
+            const int4 sj = *(const int4*)&ssq[js + 4 * lg];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                vv[r] = (sj[r] == sq_i[it] && js + 4 * lg + r <= i)
+                            ? (float)cgv[r] * (__expf(cs_i[it] - cj[r]) * dj[r])
+                            : 0.f;
+        }
+        if (bt == at) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = js + 4 * lg + r;
+                if (j > i) vv[r] = 0.f;
+                if (FINAL && j == i) vv[r] += Dh;
+            }
+        }
+    };
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        const bool act0 = ks * TPK <= a0, act1 = ks * TPK <= a1;
+        if (!act1) break;  // a1 >= a0: nothing left for either tile
+        t4 cur[2][TPK];
+#pragma unroll
+        for (int st = 0; st < TPK; ++st) {
+            cur[0][st] = cgr[ks % DEPTH][0][st];
+            cur[1][st] = cgr[ks % DEPTH][1][st];
+        }
+        if (ks + DEPTH < NKS) fetch_gram(ks + DEPTH, cgr[ks % DEPTH]);
+        Frag tb[2];
+#pragma unroll
+        for (int st = 0; st < TPK; ++st) {
+            const int bt = ks * TPK + st;
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int at = it == 0 ? a0 : a1;
+                float vv[4] = {0.f, 0.f, 0.f, 0.f};
+                if (bt <= at) weight(it, at, bt, cur[it][st], vv);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tb[it][st * 4 + r] = (E)vv[r];
+            }
+        }
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const Frag xf = XT<T>::load(sX, XR, ks * KS, pt * 16, lane);
+            if (act0) acc[0][pt] = M::mma(xf, tb[0], acc[0][pt]);
+            acc[1][pt] = M::mma(xf, tb[1], acc[1][pt]);
+        }
+    }
+
+    if (!FINAL) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            float* yo = y_zero + ((rb + t0 + i0[it] + lr) * d.H + h) * P;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) *(f32x4*)(yo + pt * 16 + 4 * lg) = acc[it][pt];
+        }
+        return;
+    }
+    // stage the wave's two [16 token][P] tiles in LDS, then store whole rows
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        T* st = sY + (wave * 2 + it) * 16 * YP;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+            *(t4*)&st[lr * YP + pt * 16 + 4 * lg] =
+                t4{(T)acc[it][pt][0], (T)acc[it][pt][1], (T)acc[it][pt][2], (T)acc[it][pt][3]};
+    }
+    __syncthreads();
+    constexpr int RV = P / VEC;  // 16-byte vectors per token row
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const T* st = sY + (wave * 2 + it) * 16 * YP;
+        for (int q = lane; q < 16 * RV; q += 64) {
+            const int r = q / RV, v = q % RV;
+            *(vt*)(y + ((rb + t0 + i0[it] + r) * d.H + h) * P + v * VEC) = *(const vt*)&st[r * YP + v * VEC];
+        }
     }
 }
 
@@ -347,29 +567,32 @@ __global__ void __launch_bounds__(256) k_apply_init(Dims d, SegTab tab, const fl
 // ---------------------------------------------------------------------------
 // Dispatch over the compiled (activation type, P, N, Q) combinations.
 
+// LDS of k_chunk_y.
 template <typename T, int P, int N, int Q>
-constexpr size_t chunk_out_lds() {
-    return sizeof(T) * ((size_t)P * (Q + 16 / sizeof(T)) + (size_t)Q * (N + 16 / sizeof(T))) +
-           (size_t)Q * 12;
+constexpr size_t chunk_y_lds() {
+    constexpr size_t V = 16 / sizeof(T), NW = Q / 32, QT = Q / 16;
+    constexpr size_t main_ = (size_t)Q * (P + V) + (size_t)P * (N + V);
+    constexpr size_t stage = 2 * NW * 16 * (P + V);
+    return sizeof(T) * (main_ > stage ? main_ : stage) + Q * 20 + QT * QT * 4 + 16;
 }
 constexpr size_t LDS_LIMIT = 160 * 1024;
 
 template <typename T, int P, int N>
 static bool shape_ok(int Q) {
-    if (Q == 64) return chunk_out_lds<T, P, N, 64>() <= LDS_LIMIT;
-    if (Q == 128) return chunk_out_lds<T, P, N, 128>() <= LDS_LIMIT;
-    if (Q == 256) return chunk_out_lds<T, P, N, 256>() <= LDS_LIMIT;
+    if (Q == 64) return chunk_y_lds<T, P, N, 64>() <= LDS_LIMIT;
+    if (Q == 128) return chunk_y_lds<T, P, N, 128>() <= LDS_LIMIT;
+    if (Q == 256) return chunk_y_lds<T, P, N, 256>() <= LDS_LIMIT;
     return false;
 }
 
-template <typename T, int P, int N, int Q>
-static void launch_chunk_out(const Dims& d, const SegTab& t, const T* xc, const float* dtw,
-                             const float* csw, const int32_t* seq, const T* hst, float* y_zero,
-                             hipStream_t s) {
-    if constexpr (chunk_out_lds<T, P, N, Q>() <= LDS_LIMIT) {
-        constexpr int NW = Q >= 128 ? 8 : 4;
-        hipLaunchKernelGGL((k_chunk_out<T, P, N, Q, NW>), chunk_head_grid(d), dim3(NW * 64), 0, s, d, t, xc, dtw,
-                           csw, seq, hst, y_zero);
+template <typename T, int P, int N, int Q, bool FINAL>
+static void launch_chunk_y(const Dims& d, const SegTab& t, const T* xc, const T* gram,
+                           const float* dtw, const float* csw, const float* ctot,
+                           const int32_t* seq, const T* hst, const float* S_in, const float* D,
+                           float* y_zero, T* y, hipStream_t s) {
+    if constexpr (chunk_y_lds<T, P, N, Q>() <= LDS_LIMIT) {
+        hipLaunchKernelGGL((k_chunk_y<T, P, N, Q, FINAL>), chunk_head_grid(d), dim3(Q / 32 * 64), 0,
+                           s, d, t, xc, gram, dtw, csw, ctot, seq, hst, S_in, D, y_zero, y);
     }
 }
 
@@ -391,19 +614,35 @@ static void segment_states_t(const Dims& d, const SegTab& t, const void* xc_, co
                        d, t, xc, (int64_t)d.C, xc, (int64_t)d.H * P, dtw, csw, seq, hst, summary);
 }
 
-template <typename T, int P, int N>
+// The group Gram tiles, then y_zero (FINAL = false) or the corrected y
+// (FINAL = true), from the workspace that segment_states_t filled.
+template <typename T, int P, int N, bool FINAL>
 static void segment_output_t(const Dims& d, const SegTab& t, const void* xc_, const int32_t* seq,
-                             const void* ws, float* y_zero, hipStream_t s) {
+                             const void* ws, const float* S_in, const float* D, float* y_zero,
+                             void* y, hipStream_t s) {
     const T* xc = (const T*)xc_;
     const FwdWs L = fwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
-    const char* w = (const char*)ws;
+    char* w = (char*)const_cast<void*>(ws);
     const float* dtw = (const float*)(w + L.dt);
     const float* csw = (const float*)(w + L.cs);
+    const float* ctot = (const float*)(w + L.ctot);
     const T* hst = (const T*)(w + L.hst);
+    T* gram = (T*)(w + L.gram);
+    T* yo = (T*)y;
+    launch_gram<T, N>(d, xc, gram, s);
     switch (d.Q) {
-        case 64: launch_chunk_out<T, P, N, 64>(d, t, xc, dtw, csw, seq, hst, y_zero, s); break;
-        case 128: launch_chunk_out<T, P, N, 128>(d, t, xc, dtw, csw, seq, hst, y_zero, s); break;
-        default: launch_chunk_out<T, P, N, 256>(d, t, xc, dtw, csw, seq, hst, y_zero, s); break;
+        case 64:
+            launch_chunk_y<T, P, N, 64, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst, S_in, D,
+                                               y_zero, yo, s);
+            break;
+        case 128:
+            launch_chunk_y<T, P, N, 128, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst, S_in, D,
+                                                y_zero, yo, s);
+            break;
+        default:
+            launch_chunk_y<T, P, N, 256, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst, S_in, D,
+                                                y_zero, yo, s);
+            break;
     }
 }
 
@@ -421,7 +660,7 @@ static void apply_init_t(const Dims& d, const SegTab& t, const float* y_zero, co
 hipError_t launch_dt_prep(const Dims& d, int act, const void* dt_raw, const float* dt_bias,
                           const float* A_log, const int32_t* seq, float* dt_ws, float* cs_ws,
                           float* ctot, hipStream_t s) {
-    const dim3 grid((unsigned)d.nchunk, (unsigned)((d.H + 15) / 16), (unsigned)d.batch);
+    const dim3 grid((unsigned)d.nchunk, (unsigned)((d.H + 3) / 4), (unsigned)d.batch);
     if (act == SSD_BF16)
         hipLaunchKernelGGL(k_dt_prep<bf16>, grid, dim3(256), 0, s, d, (const bf16*)dt_raw, dt_bias,
                            A_log, seq, dt_ws, cs_ws, ctot);
@@ -478,10 +717,30 @@ hipError_t launch_segment_states(const Dims& d, const SegTab& t, int act, const 
 hipError_t launch_segment_output(const Dims& d, const SegTab& t, int act, const void* xBC_conv,
                                  const int32_t* seq, const void* ws, float* y_zero,
                                  hipStream_t s) {
-#define X(p, n)                                                            \
-    if (d.P == p && d.N == n) {                                            \
-        segment_output_t<T, p, n>(d, t, xBC_conv, seq, ws, y_zero, s);     \
-        return hipGetLastError();                                          \
+#define X(p, n)                                                                                 \
+    if (d.P == p && d.N == n) {                                                                 \
+        segment_output_t<T, p, n, false>(d, t, xBC_conv, seq, ws, nullptr, nullptr, y_zero,     \
+                                         nullptr, s);                                           \
+        return hipGetLastError();                                                               \
+    }
+    if (act == SSD_F32) {
+        typedef float T;
+        SSD_F32_SHAPES(X)
+    } else {
+        typedef bf16 T;
+        SSD_BF16_SHAPES(X)
+    }
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_segment_output_fused(const Dims& d, const SegTab& t, int act,
+                                       const void* xBC_conv, const float* D, const int32_t* seq,
+                                       const float* S_in, const void* ws, void* y, hipStream_t s) {
+#define X(p, n)                                                                                 \
+    if (d.P == p && d.N == n) {                                                                 \
+        segment_output_t<T, p, n, true>(d, t, xBC_conv, seq, ws, S_in, D, nullptr, y, s);       \
+        return hipGetLastError();                                                               \
     }
     if (act == SSD_F32) {
         typedef float T;

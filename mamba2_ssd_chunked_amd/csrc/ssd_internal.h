@@ -178,6 +178,9 @@ hipError_t launch_segment_states(const Dims& d, const SegTab& t, int act, const 
 hipError_t launch_segment_output(const Dims& d, const SegTab& t, int act, const void* xBC_conv,
                                  const int32_t* seq, const void* ws, float* y_zero,
                                  hipStream_t s);
+hipError_t launch_segment_output_fused(const Dims& d, const SegTab& t, int act,
+                                       const void* xBC_conv, const float* D, const int32_t* seq,
+                                       const float* S_in, const void* ws, void* y, hipStream_t s);
 hipError_t launch_boundary_scan(const Dims& d, int nseg, const float* summary, const float* init,
                                 int reverse, float* out, float* final_state, hipStream_t s);
 hipError_t launch_apply_init_state(const Dims& d, const SegTab& t, int act, const float* y_zero,
@@ -212,7 +215,7 @@ bool chunk_supported(int P, int N, int Q, int act);
 
 // Forward workspace layout (byte offsets), shared by the host code and launchers.
 struct FwdWs {
-    size_t dt, cs, ctot, hst, total;
+    size_t dt, cs, ctot, hst, gram, total;
 };
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline FwdWs fwd_ws_layout(const Dims& d, int act) {
@@ -223,7 +226,9 @@ inline FwdWs fwd_ws_layout(const Dims& d, int act) {
     w.cs = align256(w.dt + bhl * 4);
     w.ctot = align256(w.cs + bhl * 4);
     w.hst = align256(w.ctot + (size_t)d.batch * d.H * d.nchunk * 4);
-    w.total = align256(w.hst + (size_t)d.batch * d.nchunk * d.H * d.P * d.N * esz);
+    w.gram = align256(w.hst + (size_t)d.batch * d.nchunk * d.H * d.P * d.N * esz);
+    const size_t qt = (size_t)d.Q / 16;
+    w.total = align256(w.gram + (size_t)d.batch * d.nchunk * d.G * (qt * (qt + 1) / 2) * 256 * esz);
     return w;
 }
 

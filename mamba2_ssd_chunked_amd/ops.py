@@ -183,6 +183,21 @@ def ssd_apply_init_state(problem: Problem, segs, y_zero, xBC_conv, D, seq_idx, S
         _stream(stream)))
 
 
+def ssd_segment_output_fused(problem: Problem, segs, xBC_conv, D, seq_idx, S_in, ws, y,
+                             stream=None):
+    s = _segs(segs)
+    act = _TORCH_ACT[problem.act_dtype]
+    BL, C, H, P = problem.batch * problem.seqlen, _conv_dim(problem), problem.nheads, problem.headdim
+    f32 = torch.float32
+    args = (_need(xBC_conv, "xBC_conv", BL * C, act), _need(D, "D", H, f32),
+            _need(seq_idx, "seq_idx", BL, torch.int32, optional=True),
+            _need(S_in, "S_in", s.n * problem.batch * H * P * problem.dstate, f32))
+    ws_p, nbytes = _ws(ws)
+    y_p = _need(y, "y", BL * H * P, act)
+    _check("ssd_segment_output_fused", _lib.load().ssd_segment_output_fused(
+        ctypes.byref(problem), s.ptr(), s.n, *args, ws_p, nbytes, y_p, _stream(stream)))
+
+
 def ssd_segment_bwd_summary(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log, seq_idx,
                             dy, summary, ws, stream=None):
     s = _segs(segs)
@@ -293,12 +308,26 @@ class ForwardBuffers:
 
 
 def forward(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log, D, seq_idx=None,
-            init=None, bufs: Optional[ForwardBuffers] = None, stream=None) -> ForwardBuffers:
-    """conv1d -> segment-local SSD -> boundary scan -> correction; returns the buffers."""
+            init=None, bufs: Optional[ForwardBuffers] = None, stream=None,
+            fused: bool = True) -> ForwardBuffers:
+    """The forward path; returns the buffers.
+
+    fused=True : conv1d -> segment states -> boundary scan -> fused output pass
+                 (y only; bufs.y_zero is left untouched).
+    fused=False: conv1d -> segment-local SSD (states and y_zero) -> boundary scan
+                 -> correction pass.
+    """
     s = _segs(segs)
     if bufs is None:
         bufs = ForwardBuffers.allocate(problem, s, xBC.device)
     ssd_conv1d_fwd(problem, s, xBC, conv_w, seq_idx, bufs.xBC_conv, stream)
+    if fused:
+        ssd_segment_states(problem, s, bufs.xBC_conv, dt_raw, dt_bias, A_log, seq_idx,
+                           bufs.summary, bufs.ws, stream)
+        ssd_boundary_scan(problem, s.n, bufs.summary, init, False, bufs.S_in, None, stream)
+        ssd_segment_output_fused(problem, s, bufs.xBC_conv, D, seq_idx, bufs.S_in, bufs.ws,
+                                 bufs.y, stream)
+        return bufs
     ssd_segment_fwd(problem, s, bufs.xBC_conv, dt_raw, dt_bias, A_log, seq_idx, bufs.y_zero,
                     bufs.summary, bufs.ws, stream)
     ssd_boundary_scan(problem, s.n, bufs.summary, init, False, bufs.S_in, None, stream)

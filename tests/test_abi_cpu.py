@@ -64,6 +64,8 @@ def test_workspace_bytes():
     al = lambda x: (x + 255) // 256 * 256
     want = al(al(al(b * H * L * 4) + b * H * L * 4) + b * H * nc * 4)
     want = al(want + b * nc * H * P * N * 2)
+    qt = 256 // 16
+    want = al(want + b * nc * 1 * (qt * (qt + 1) // 2) * 256 * 2)  # causal Gram tiles per group
     assert ssd.ssd_workspace_bytes(p, SEGS8) == want
     assert ssd.ssd_workspace_bytes(p, SEGS8, kind=7) == 0
     assert ssd.ssd_workspace_bytes(_p(chunk=100), SEGS8) == 0

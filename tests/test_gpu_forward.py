@@ -58,7 +58,7 @@ def small_run(request):
     log(f"[forward] case {wl.name}: b={wl.batch} L={wl.seqlen} H={wl.nheads} P={wl.headdim} "
         f"N={wl.dstate} G={wl.ngroups} Q={wl.chunk} act={wl.act} segs={len(wl.segments)} "
         f"layout={wl.layout} packed={wl.seq_idx is not None}")
-    p, x, bufs = run_forward(wl)
+    p, x, bufs = run_forward(wl, fused=False)
     return wl, p, x, bufs
 
 
@@ -123,6 +123,40 @@ def test_end_to_end(small_run):
     g = wl.to_causal(to_np(bufs.y))
     o = oracle.forward(wl)
     assert_close(g, o, wl.act, "y")
+
+
+def test_fused_output_end_to_end(small_run):
+    """States first, boundary scan, then the fused output pass (true entering
+    states and D x in one pass) against the oracle, from the workspace the
+    unfused run filled."""
+    import mamba2_ssd_chunked_amd as ssd
+    wl, p, x, bufs = small_run
+    y = torch.empty_like(bufs.y)
+    ssd.ssd_segment_output_fused(p, wl.segments, bufs.xBC_conv, x["D"], x["seq_idx"], bufs.S_in,
+                                 bufs.ws, y)
+    torch.cuda.synchronize()
+    g = wl.to_causal(to_np(y))
+    o = oracle.forward(wl)
+    assert_close(g, o, wl.act, "y (fused output)")
+
+
+def test_fused_output_random_states(small_run):
+    """The fused output pass from random S_in equals the oracle run of each
+    segment from that S_in (every chunk's entering state carries it)."""
+    import mamba2_ssd_chunked_amd as ssd
+    wl, p, x, bufs = small_run
+    S, b, H, P, N = len(wl.segments), wl.batch, wl.nheads, wl.headdim, wl.dstate
+    rng = np.random.default_rng(78)
+    S_in = rng.standard_normal((S, b, H, P, N)).astype(np.float32)
+    y = torch.empty_like(bufs.y)
+    ssd.ssd_segment_output_fused(p, wl.segments, bufs.xBC_conv, x["D"], x["seq_idx"],
+                                 torch.from_numpy(S_in).cuda(), bufs.ws, y)
+    torch.cuda.synchronize()
+    g = wl.to_causal(to_np(y))
+    v = oracle_v(wl)
+    for k, (a, e) in enumerate(causal_ranges(wl)):
+        yk, _ = oracle_segment(wl, v, k, init=S_in[k].astype(np.float64), D_zero=False)
+        assert_close(g[:, a:e], yk, wl.act, f"y fused (S_in random)[{k}]")
 
 
 # --------------------------------------------------------------------------- boundary scan
@@ -220,11 +254,12 @@ def test_determinism():
 # --------------------------------------------------------------------------- full sizes
 
 
-@pytest.mark.parametrize("cfg", ["mixer_shard_bf16", "packed_thd_bf16", "slow_mixer_shard_bf16"])
-def test_full_config(cfg):
+@pytest.mark.parametrize("cfg,fused", [("mixer_shard_bf16", True), ("mixer_shard_bf16", False),
+                                       ("packed_thd_bf16", True), ("slow_mixer_shard_bf16", True)])
+def test_full_config(cfg, fused):
     wl = W.config(cfg)
-    log(f"[full] {cfg}")
-    _, _, bufs = run_forward(wl)
+    log(f"[full] {cfg} fused={fused}")
+    _, _, bufs = run_forward(wl, fused=fused)
     g = wl.to_causal(to_np(bufs.y))
     o = oracle.forward(wl)
     assert_close(g, o, wl.act, f"y {cfg}")
