@@ -6,7 +6,7 @@ current stream:
   forward : ssd_conv1d_fwd -> ssd_segment_states -> ssd_boundary_scan
             -> ssd_segment_output_fused (output pass with the correction folded in)
   backward: ssd_segment_bwd_summary -> ssd_boundary_scan (reverse)
-            -> ssd_segment_bwd_chunks -> ssd_conv1d_bwd
+            -> ssd_segment_bwd_pass -> ssd_segment_bwd_chunks -> ssd_conv1d_bwd
 Workload: 2 rows x 8192 tokens, 32 heads, headdim 64, d_state 128, 1 group,
 chunk 256, conv width 4, bf16 activations with FP32 state, cut into 8
 contiguous causal segments of 1024 tokens (one device's context-parallel
@@ -54,7 +54,9 @@ def parse():
 
 
 def algorithmic_bytes(wl):
-    """Bytes each call must move at minimum (its own inputs and outputs)."""
+    """Bytes each call must move at minimum: its own inputs and outputs, with every
+    workspace intermediate counted once where one pass writes it and another reads
+    it, and no per-head copies of per-group quantities."""
     e = 2 if wl.act == "bf16" else 4
     b, L, H, P, N, G, Q = (wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.ngroups,
                            wl.chunk)
@@ -63,26 +65,41 @@ def algorithmic_bytes(wl):
     C = H * P + 2 * G * N
     seq = 4 * BL if wl.seq_idx is not None else 0
     nchunk = L // Q
+    qt = Q // 16
     hst_chunks = b * (nchunk - S)  # entering states of every non-first chunk of a segment
     hst = hst_chunks * H * P * N * e
+    st_all = b * nchunk * H * P * N  # one P x N matrix per chunk and head
+    gram = b * nchunk * G * (qt * (qt + 1) // 2) * 256 * e
     summary = S * b * H * (P * N + 1) * 4
     states = S * b * H * P * N * 4
     dtcs = 2 * BL * H * 4
     dy = BL * H * P * e
+    x, bc = BL * H * P * e, BL * 2 * G * N * e
     return {
-        "ssd_segment_bwd_summary": BL * C * e + BL * H * e + dy + BL * C * e + dtcs + 2 * hst
-                                   + summary + seq,
-        "ssd_boundary_scan(reverse)": summary + states,
-        "ssd_segment_bwd_chunks": BL * C * e + dy + BL * H * e + dtcs + 2 * hst + 2 * states
-                                  + BL * H * P * 4 + BL * 2 * G * N * 4 + BL * H * e + seq,
-        "ssd_conv1d_bwd": BL * C * e + BL * C * 4 + BL * C * e + seq,
         "ssd_conv1d_fwd": 2 * BL * C * e + C * wl.conv_width * 4 + seq,
-        "ssd_segment_states": BL * (H * P + G * N) * e + BL * H * e + 2 * dtcs + hst + summary + seq,
-        "ssd_segment_output": BL * C * e + hst + dtcs + BL * H * P * 4 + seq,
-        "ssd_segment_output_fused": BL * C * e + hst + dtcs + states + BL * H * P * e + seq,
+        # dt prep (dt_raw in, dt and cumsum out), the walk (x, B in; entering states and
+        # summary out) and the Gram tiles (B, C in; tiles out)
+        "ssd_segment_states": BL * H * e + dtcs + x + bc // 2 + dtcs + hst + summary + bc + gram + seq,
         "ssd_boundary_scan": summary + states,
-        "ssd_apply_init_state": BL * H * P * 4 + BL * (H * P + G * N) * e + BL * H * 4 + states
-                                + BL * H * P * e + seq,
+        # x, C, Gram tiles, entering states, S_in, decays in; y out
+        "ssd_segment_output_fused": x + bc // 2 + gram + hst + states + dtcs + x + seq,
+        "ssd_segment_output": x + bc // 2 + gram + hst + dtcs + BL * H * P * 4 + seq,
+        "ssd_apply_init_state": BL * H * P * 4 + x + bc // 2 + BL * H * 4 + states + x + seq,
+        # conv recompute, dt prep, chunk contributions to state and state gradient
+        # (FP32 out), the summary walk
+        "ssd_segment_bwd_summary": BL * C * e + BL * C * e + BL * H * e + dtcs + x + dy + bc
+                                   + 2 * st_all * 4 + summary + seq,
+        "ssd_boundary_scan(reverse)": summary + states,
+        # chunk contributions and the two boundary states in; entering state and exit
+        # gradient per chunk out
+        "ssd_segment_bwd_pass": 2 * st_all * 4 + 2 * states + 2 * st_all * e,
+        # x, B, C, dy, decays, entering state and exit gradient per chunk in; dx (FP32),
+        # dB and dC (FP32, summed over heads), per-token d(dt) partials out
+        "ssd_segment_bwd_chunks": BL * C * e + dy + dtcs + 2 * st_all * e + BL * H * P * 4
+                                  + BL * 2 * G * N * 4 + BL * H * 4 * 4 + seq,
+        # xBC and d(conv output) in, dxBC out; d(dt) partials and dt_raw in, ddt_raw out
+        "ssd_conv1d_bwd": BL * C * e + BL * C * 4 + BL * C * e + BL * H * 4 * 4 + 2 * BL * H * e
+                          + seq,
     }
 
 
@@ -170,15 +187,17 @@ def main():
                 p, segs, xBC, conv_w, dt_raw, dt_bias, A_log, seq, dy, bb.summary, bb.ws)),
             ("ssd_boundary_scan(reverse)", lambda: ssd.ssd_boundary_scan(
                 p, segs.n, bb.summary, None, True, bb.dS_out)),
+            ("ssd_segment_bwd_pass", lambda: ssd.ssd_segment_bwd_pass(
+                p, segs, seq, bufs.S_in, bb.dS_out, bb.ws)),
             ("ssd_segment_bwd_chunks", lambda: ssd.ssd_segment_bwd_chunks(
-                p, segs, dt_raw, dt_bias, A_log, D, seq, dy, bufs.S_in, bb.dS_out, bb.ws,
-                bb.ddt_raw)),
+                p, segs, D, seq, dy, bb.ws)),
             ("ssd_conv1d_bwd", lambda: ssd.ssd_conv1d_bwd(
-                p, segs, xBC, conv_w, A_log, seq, bb.ws, bb.dxBC, bb.dconv_w, bb.ddt_bias,
-                bb.dA_log, bb.dD)),
+                p, segs, xBC, conv_w, dt_raw, dt_bias, A_log, seq, bb.ws, bb.dxBC, bb.ddt_raw,
+                bb.dconv_w, bb.ddt_bias, bb.dA_log, bb.dD)),
         ]
     single_kernel = {"ssd_conv1d_fwd", "ssd_segment_output_fused", "ssd_boundary_scan",
-                     "ssd_boundary_scan(reverse)", "ssd_segment_bwd_chunks"}
+                     "ssd_boundary_scan(reverse)", "ssd_segment_bwd_pass",
+                     "ssd_segment_bwd_chunks"}
 
     def step(events=None):
         for i, (_, fn) in enumerate(calls):

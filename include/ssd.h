@@ -149,8 +149,9 @@ int ssd_segment_fwd(const ssd_problem* problem, const ssd_segment* segs, int32_t
  * exchange with the local intra-chunk work (#6808's first commit issues the
  * summary gather asynchronously and hides it behind the local C*B^T work).
  * ssd_segment_states computes dt, the cumulative decays, every chunk's entering
- * state and the segment summaries (into `summary` and `ws`); ssd_segment_output
- * then computes y_zero from the same inputs and `ws`.  Calling both in this
+ * state, the segment summaries (into `summary` and `ws`) and the causal C B^T
+ * Gram tiles of every chunk and group (into `ws`); ssd_segment_output then
+ * computes y_zero from the same inputs and `ws`.  Calling both in this
  * order is the same as ssd_segment_fwd.  */
 int ssd_segment_states(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
                        const void* xBC_conv, const void* dt_raw, const float* dt_bias,
@@ -244,23 +245,33 @@ int ssd_segment_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t
                     void* ddt_raw, float* dconv_w, float* ddt_bias, float* dA_log, float* dD,
                     void* stream);
 
-/* The two phases of ssd_segment_bwd.  ssd_segment_bwd_chunks computes, per
- * chunk and head, dx, dB, dC (written into `ws`, the buffers the conv backward
- * consumes, as #6808's first commit does) and ddt_raw, plus per-chunk partial
- * sums of the parameter gradients.  ssd_conv1d_bwd then applies SiLU' and the
- * transposed causal conv (its right halo read from the causal successor
- * segment) to produce dxBC and dconv_w, and reduces ddt_bias, dA_log and dD.
- * Calling both in this order is the same as ssd_segment_bwd; both read the
- * workspace ssd_segment_bwd_summary filled. */
+/* The three phases of ssd_segment_bwd, in this order (calling them is the same
+ * as ssd_segment_bwd; each reads the workspace ssd_segment_bwd_summary filled):
+ *  ssd_segment_bwd_pass    walks every segment's chunks from S_in forward and
+ *                          from dS_out backward, leaving in `ws` the true
+ *                          entering state and exit-state gradient of every chunk.
+ *  ssd_segment_bwd_chunks  per chunk and head: dx, dB, dC (into `ws`, the
+ *                          buffers the conv backward consumes, as #6808's first
+ *                          commit does) and the per-token and per-chunk partial
+ *                          sums of d(dt), dA and dD.
+ *  ssd_conv1d_bwd          assembles ddt_raw per token (the chain through the dt
+ *                          clamp and softplus), sums dB and dC over each group's
+ *                          heads, applies SiLU' and the transposed causal conv
+ *                          (its right halo read from the causal successor
+ *                          segment) to give dxBC, and reduces dconv_w, ddt_bias,
+ *                          dA_log and dD (fixed order, deterministic).
+ * Arguments mean what they mean for ssd_segment_bwd. */
+int ssd_segment_bwd_pass(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                         const int32_t* seq_idx, const float* S_in, const float* dS_out, void* ws,
+                         size_t ws_bytes, void* stream);
 int ssd_segment_bwd_chunks(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
-                           const void* dt_raw, const float* dt_bias, const float* A_log,
-                           const float* D, const int32_t* seq_idx, const void* dy,
-                           const float* S_in, const float* dS_out, void* ws, size_t ws_bytes,
-                           void* ddt_raw, void* stream);
+                           const float* D, const int32_t* seq_idx, const void* dy, void* ws,
+                           size_t ws_bytes, void* stream);
 int ssd_conv1d_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
-                   const void* xBC, const float* conv_w, const float* A_log,
-                   const int32_t* seq_idx, void* ws, size_t ws_bytes, void* dxBC, float* dconv_w,
-                   float* ddt_bias, float* dA_log, float* dD, void* stream);
+                   const void* xBC, const float* conv_w, const void* dt_raw, const float* dt_bias,
+                   const float* A_log, const int32_t* seq_idx, void* ws, size_t ws_bytes,
+                   void* dxBC, void* ddt_raw, float* dconv_w, float* ddt_bias, float* dA_log,
+                   float* dD, void* stream);
 
 #ifdef __cplusplus
 }

@@ -104,7 +104,7 @@ const char* ssd_status_string(int status) {
     }
 }
 
-int32_t ssd_abi_version(void) { return 1; }
+int32_t ssd_abi_version(void) { return 2; }
 
 int32_t ssd_supported(int32_t headdim, int32_t dstate, int32_t act_dtype) {
     return kernels_supported(headdim, dstate, act_dtype) ? 1 : 0;
@@ -313,52 +313,63 @@ int check_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
 }
 }  // namespace
 
-int ssd_segment_bwd_chunks(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
-                           const void* dt_raw, const float* dt_bias, const float* A_log,
-                           const float* D, const int32_t* seq_idx, const void* dy,
-                           const float* S_in, const float* dS_out, void* ws, size_t ws_bytes,
-                           void* ddt_raw, void* stream) {
+int ssd_segment_bwd_pass(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                         const int32_t* seq_idx, const float* S_in, const float* dS_out, void* ws,
+                         size_t ws_bytes, void* stream) {
     Dims d;
     SegTab t;
     int rc = check_bwd(problem, segs, nseg, &d, &t, ws, ws_bytes);
     if (rc) return rc;
-    if (!dt_raw || !dt_bias || !A_log || !D || !dy || !S_in || !dS_out || !ddt_raw)
-        return SSD_ERR_NULL;
-    const void* ptrs[] = {dt_raw, dt_bias, A_log, D, seq_idx, dy, S_in, dS_out, ddt_raw};
-    for (const void* q : ptrs)
-        if (!aligned16(q)) return SSD_ERR_ALIGN;
+    if (!S_in || !dS_out) return SSD_ERR_NULL;
+    if (!aligned16(seq_idx) || !aligned16(S_in) || !aligned16(dS_out)) return SSD_ERR_ALIGN;
     BwdArgs ar = {};
-    ar.dt_raw = dt_raw;
-    ar.dt_bias = dt_bias;
-    ar.A_log = A_log;
+    ar.seq = seq_idx;
+    ar.S_in = S_in;
+    ar.dS_out = dS_out;
+    return hip_status(launch_bwd_pass(d, t, problem->act_dtype, ar, ws, (hipStream_t)stream));
+}
+
+int ssd_segment_bwd_chunks(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                           const float* D, const int32_t* seq_idx, const void* dy, void* ws,
+                           size_t ws_bytes, void* stream) {
+    Dims d;
+    SegTab t;
+    int rc = check_bwd(problem, segs, nseg, &d, &t, ws, ws_bytes);
+    if (rc) return rc;
+    if (!D || !dy) return SSD_ERR_NULL;
+    if (!aligned16(D) || !aligned16(seq_idx) || !aligned16(dy)) return SSD_ERR_ALIGN;
+    BwdArgs ar = {};
     ar.D = D;
     ar.seq = seq_idx;
     ar.dy = dy;
-    ar.S_in = S_in;
-    ar.dS_out = dS_out;
-    ar.ddt_raw = ddt_raw;
     return hip_status(launch_bwd_chunks(d, t, problem->act_dtype, ar, ws, (hipStream_t)stream));
 }
 
 int ssd_conv1d_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
-                   const void* xBC, const float* conv_w, const float* A_log,
-                   const int32_t* seq_idx, void* ws, size_t ws_bytes, void* dxBC, float* dconv_w,
-                   float* ddt_bias, float* dA_log, float* dD, void* stream) {
+                   const void* xBC, const float* conv_w, const void* dt_raw, const float* dt_bias,
+                   const float* A_log, const int32_t* seq_idx, void* ws, size_t ws_bytes,
+                   void* dxBC, void* ddt_raw, float* dconv_w, float* ddt_bias, float* dA_log,
+                   float* dD, void* stream) {
     Dims d;
     SegTab t;
     int rc = check_bwd(problem, segs, nseg, &d, &t, ws, ws_bytes);
     if (rc) return rc;
-    if (!xBC || !conv_w || !A_log || !dxBC || !dconv_w || !ddt_bias || !dA_log || !dD)
+    if (!xBC || !conv_w || !dt_raw || !dt_bias || !A_log || !dxBC || !ddt_raw || !dconv_w ||
+        !ddt_bias || !dA_log || !dD)
         return SSD_ERR_NULL;
-    const void* ptrs[] = {xBC, conv_w, A_log, seq_idx, dxBC, dconv_w, ddt_bias, dA_log, dD};
+    const void* ptrs[] = {xBC,  conv_w,  dt_raw,  dt_bias,  A_log,  seq_idx,
+                          dxBC, ddt_raw, dconv_w, ddt_bias, dA_log, dD};
     for (const void* q : ptrs)
         if (!aligned16(q)) return SSD_ERR_ALIGN;
     BwdArgs ar = {};
     ar.xBC = xBC;
     ar.conv_w = conv_w;
+    ar.dt_raw = dt_raw;
+    ar.dt_bias = dt_bias;
     ar.A_log = A_log;
     ar.seq = seq_idx;
     ar.dxBC = dxBC;
+    ar.ddt_raw = ddt_raw;
     ar.dconv_w = dconv_w;
     ar.ddt_bias = ddt_bias;
     ar.dA_log = dA_log;
@@ -385,6 +396,8 @@ int ssd_segment_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t
         if (!aligned16(q)) return SSD_ERR_ALIGN;
     BwdArgs ar = {xBC, conv_w, dt_raw, dt_bias, A_log, D, seq_idx, dy, S_in, dS_out,
                   dxBC, ddt_raw, dconv_w, ddt_bias, dA_log, dD};
+    rc = hip_status(launch_bwd_pass(d, t, problem->act_dtype, ar, ws, (hipStream_t)stream));
+    if (rc) return rc;
     rc = hip_status(launch_bwd_chunks(d, t, problem->act_dtype, ar, ws, (hipStream_t)stream));
     if (rc) return rc;
     return hip_status(launch_conv1d_bwd(d, t, problem->act_dtype, ar, ws, (hipStream_t)stream));

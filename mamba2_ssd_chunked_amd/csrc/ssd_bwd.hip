@@ -14,13 +14,14 @@
 //     the same packed layout as the forward summary.
 //   reverse boundary scan (ssd_boundary_scan, reverse = 1) -> the gradient of
 //     every segment's final state.
-//   chunk phase (ssd_segment_bwd_chunks): the true exit gradient and entering
-//     state of every chunk (k_state_pass from dS_out and S_in), then
-//     k_chunk_bwd per chunk and head: dx, dB, dC and the ddt partial sums,
-//     written into the buffers the conv backward consumes, and k_ddt.
-//   conv phase (ssd_conv1d_bwd): k_conv_bwd (SiLU' and the transposed conv,
-//     with a right halo from the causal successor segment) and k_bwd_reduce
-//     (deterministic parameter gradients).
+//   pass phase (ssd_segment_bwd_pass): the true exit gradient and entering
+//     state of every chunk (k_state_pass from dS_out and S_in).
+//   chunk phase (ssd_segment_bwd_chunks): k_chunk_bwd per chunk and head: dx,
+//     dB, dC and the ddt partial sums, written into the buffers the conv
+//     backward consumes.
+//   conv phase (ssd_conv1d_bwd): k_ddt (ddt per token), k_bc_headsum, k_conv_bwd
+//     (SiLU' and the transposed conv, with a right halo from the causal
+//     successor segment) and k_bwd_reduce (deterministic parameter gradients).
 //
 // ddt without recomputing y.  dL/d(dt_t A) sums, over every (source j, output
 // i) pair with j < t <= i, the derivative of their decay.  Per chunk that is
@@ -1458,13 +1459,6 @@ static void launch_chunk_bwd(const Dims& d, const SegTab& t, const BwdArgs& a, c
                            (const T*)(ws + L.gpn), (const T*)(ws + L.gnp), (const T*)(ws + L.hnp),
                            (float*)(ws + L.dv), (T*)(ws + L.dbc), (float*)(ws + L.rpart),
                            (float*)(ws + L.tokp), (float*)(ws + L.red4));
-        hipLaunchKernelGGL((k_ddt<T>),
-                           dim3((unsigned)d.nchunk, (unsigned)d.H, (unsigned)d.batch), dim3(64), 0,
-                           s, d, t, (const T*)a.dt_raw, a.dt_bias, a.A_log,
-                           (const float*)(ws + L.dt), (const float*)(ws + L.cs), a.seq,
-                           (const float*)(ws + L.rpart), (const float*)(ws + L.tokp),
-                           (const float*)(ws + L.dotgh), (const float*)(ws + L.red4),
-                           (T*)a.ddt_raw, (float*)(ws + L.red));
     }
 }
 
@@ -1516,8 +1510,8 @@ static void bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a, floa
 }
 
 template <typename T, int P, int N>
-static void bwd_chunks_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* ws_,
-                         hipStream_t s) {
+static void bwd_pass_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* ws_,
+                       hipStream_t s) {
     const BwdWs L = bwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
     char* ws = (char*)ws_;
     hipLaunchKernelGGL((k_state_pass<T, P, N, PASS_TRUE>),
@@ -1526,6 +1520,13 @@ static void bwd_chunks_t(const Dims& d, const SegTab& t, const BwdArgs& a, void*
                        (const float*)(ws + L.zh), a.S_in, a.dS_out, (float*)nullptr,
                        (T*)(ws + L.gpn), (T*)(ws + L.gnp), (T*)(ws + L.hnp),
                        (float*)(ws + L.dotgh));
+}
+
+template <typename T, int P, int N>
+static void bwd_chunks_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* ws_,
+                         hipStream_t s) {
+    const BwdWs L = bwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
+    char* ws = (char*)ws_;
     switch (d.Q) {
         case 64: launch_chunk_bwd<T, P, N, 64>(d, t, a, L, ws, s); break;
         case 128: launch_chunk_bwd<T, P, N, 128>(d, t, a, L, ws, s); break;
@@ -1538,6 +1539,12 @@ static void conv_bwd_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* w
                        hipStream_t s) {
     const BwdWs L = bwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
     char* ws = (char*)ws_;
+    hipLaunchKernelGGL((k_ddt<T>), dim3((unsigned)d.nchunk, (unsigned)d.H, (unsigned)d.batch),
+                       dim3(64), 0, s, d, t, (const T*)a.dt_raw, a.dt_bias, a.A_log,
+                       (const float*)(ws + L.dt), (const float*)(ws + L.cs), a.seq,
+                       (const float*)(ws + L.rpart), (const float*)(ws + L.tokp),
+                       (const float*)(ws + L.dotgh), (const float*)(ws + L.red4), (T*)a.ddt_raw,
+                       (float*)(ws + L.red));
     const int64_t nbc = d.batch * d.L * 2 * d.G * d.N / (16 / sizeof(T));
     hipLaunchKernelGGL(k_bc_headsum<T>, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, d,
                        (const T*)(ws + L.dbc), (float*)(ws + L.dv));
@@ -1570,6 +1577,24 @@ hipError_t launch_bwd_summary(const Dims& d, const SegTab& t, int act, const Bwd
     if (d.P == p && d.N == n) {                                   \
         bwd_summary_t<T, p, n>(d, t, a, summary, ws, s);          \
         return hipGetLastError();                                 \
+    }
+    if (act == SSD_F32) {
+        typedef float T;
+        SSD_BWD_F32_SHAPES(X)
+    } else {
+        typedef bf16 T;
+        SSD_BWD_BF16_SHAPES(X)
+    }
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_pass(const Dims& d, const SegTab& t, int act, const BwdArgs& a, void* ws,
+                           hipStream_t s) {
+#define X(p, n)                                \
+    if (d.P == p && d.N == n) {                \
+        bwd_pass_t<T, p, n>(d, t, a, ws, s);   \
+        return hipGetLastError();              \
     }
     if (act == SSD_F32) {
         typedef float T;

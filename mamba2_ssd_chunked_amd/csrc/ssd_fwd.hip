@@ -612,24 +612,26 @@ static void segment_states_t(const Dims& d, const SegTab& t, const void* xc_, co
     hipLaunchKernelGGL((k_state_walk<T, P, N, WALK_FWD_PN>),
                        dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0, s,
                        d, t, xc, (int64_t)d.C, xc, (int64_t)d.H * P, dtw, csw, seq, hst, summary);
+    // the group Gram tiles the output pass reads (local work a multi-GPU caller
+    // overlaps with the summary exchange, like the walk above)
+    launch_gram<T, N>(d, xc, (T*)(w + L.gram), s);
 }
 
-// The group Gram tiles, then y_zero (FINAL = false) or the corrected y
-// (FINAL = true), from the workspace that segment_states_t filled.
+// y_zero (FINAL = false) or the corrected y (FINAL = true), from the workspace
+// that segment_states_t filled (decays, entering states, Gram tiles).
 template <typename T, int P, int N, bool FINAL>
 static void segment_output_t(const Dims& d, const SegTab& t, const void* xc_, const int32_t* seq,
                              const void* ws, const float* S_in, const float* D, float* y_zero,
                              void* y, hipStream_t s) {
     const T* xc = (const T*)xc_;
     const FwdWs L = fwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
-    char* w = (char*)const_cast<void*>(ws);
+    const char* w = (const char*)ws;
     const float* dtw = (const float*)(w + L.dt);
     const float* csw = (const float*)(w + L.cs);
     const float* ctot = (const float*)(w + L.ctot);
     const T* hst = (const T*)(w + L.hst);
-    T* gram = (T*)(w + L.gram);
+    const T* gram = (const T*)(w + L.gram);
     T* yo = (T*)y;
-    launch_gram<T, N>(d, xc, gram, s);
     switch (d.Q) {
         case 64:
             launch_chunk_y<T, P, N, 64, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst, S_in, D,

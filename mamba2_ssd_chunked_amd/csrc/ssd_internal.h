@@ -270,6 +270,8 @@ inline BwdWs bwd_ws_layout(const Dims& d, int act) {
 
 hipError_t launch_bwd_summary(const Dims& d, const SegTab& t, int act, const BwdArgs& a,
                               float* summary, void* ws, hipStream_t s);
+hipError_t launch_bwd_pass(const Dims& d, const SegTab& t, int act, const BwdArgs& a, void* ws,
+                           hipStream_t s);
 hipError_t launch_bwd_chunks(const Dims& d, const SegTab& t, int act, const BwdArgs& a, void* ws,
                              hipStream_t s);
 hipError_t launch_conv1d_bwd(const Dims& d, const SegTab& t, int act, const BwdArgs& a, void* ws,

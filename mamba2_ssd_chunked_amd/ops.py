@@ -239,38 +239,44 @@ def ssd_segment_bwd(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log,
         ctypes.byref(problem), s.ptr(), s.n, *ins, ws_p, nbytes, *outs, _stream(stream)))
 
 
-def ssd_segment_bwd_chunks(problem: Problem, segs, dt_raw, dt_bias, A_log, D, seq_idx, dy, S_in,
-                           dS_out, ws, ddt_raw, stream=None):
+def ssd_segment_bwd_pass(problem: Problem, segs, seq_idx, S_in, dS_out, ws, stream=None):
+    s = _segs(segs)
+    st = s.n * problem.batch * problem.nheads * problem.headdim * problem.dstate
+    f32 = torch.float32
+    ins = (_need(seq_idx, "seq_idx", problem.batch * problem.seqlen, torch.int32, optional=True),
+           _need(S_in, "S_in", st, f32), _need(dS_out, "dS_out", st, f32))
+    ws_p, nbytes = _ws(ws)
+    _check("ssd_segment_bwd_pass", _lib.load().ssd_segment_bwd_pass(
+        ctypes.byref(problem), s.ptr(), s.n, *ins, ws_p, nbytes, _stream(stream)))
+
+
+def ssd_segment_bwd_chunks(problem: Problem, segs, D, seq_idx, dy, ws, stream=None):
     s = _segs(segs)
     act = _TORCH_ACT[problem.act_dtype]
-    BL, H, P, N = problem.batch * problem.seqlen, problem.nheads, problem.headdim, problem.dstate
-    f32 = torch.float32
-    st = s.n * problem.batch * H * P * N
-    ins = (_need(dt_raw, "dt_raw", BL * H, act), _need(dt_bias, "dt_bias", H, f32),
-           _need(A_log, "A_log", H, f32), _need(D, "D", H, f32),
+    BL, H, P = problem.batch * problem.seqlen, problem.nheads, problem.headdim
+    ins = (_need(D, "D", H, torch.float32),
            _need(seq_idx, "seq_idx", BL, torch.int32, optional=True),
-           _need(dy, "dy", BL * H * P, act), _need(S_in, "S_in", st, f32),
-           _need(dS_out, "dS_out", st, f32))
+           _need(dy, "dy", BL * H * P, act))
     ws_p, nbytes = _ws(ws)
-    out = _need(ddt_raw, "ddt_raw", BL * H, act)
     _check("ssd_segment_bwd_chunks", _lib.load().ssd_segment_bwd_chunks(
-        ctypes.byref(problem), s.ptr(), s.n, *ins, ws_p, nbytes, out, _stream(stream)))
+        ctypes.byref(problem), s.ptr(), s.n, *ins, ws_p, nbytes, _stream(stream)))
 
 
-def ssd_conv1d_bwd(problem: Problem, segs, xBC, conv_w, A_log, seq_idx, ws, dxBC, dconv_w,
-                   ddt_bias, dA_log, dD, stream=None):
+def ssd_conv1d_bwd(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log, seq_idx, ws, dxBC,
+                   ddt_raw, dconv_w, ddt_bias, dA_log, dD, stream=None):
     s = _segs(segs)
     act = _TORCH_ACT[problem.act_dtype]
     BL, C, H, W = (problem.batch * problem.seqlen, _conv_dim(problem), problem.nheads,
                    problem.conv_width)
     f32 = torch.float32
     ins = (_need(xBC, "xBC", BL * C, act), _need(conv_w, "conv_w", C * W, f32),
+           _need(dt_raw, "dt_raw", BL * H, act), _need(dt_bias, "dt_bias", H, f32),
            _need(A_log, "A_log", H, f32),
            _need(seq_idx, "seq_idx", BL, torch.int32, optional=True))
     ws_p, nbytes = _ws(ws)
-    outs = (_need(dxBC, "dxBC", BL * C, act), _need(dconv_w, "dconv_w", C * W, f32),
-            _need(ddt_bias, "ddt_bias", H, f32), _need(dA_log, "dA_log", H, f32),
-            _need(dD, "dD", H, f32))
+    outs = (_need(dxBC, "dxBC", BL * C, act), _need(ddt_raw, "ddt_raw", BL * H, act),
+            _need(dconv_w, "dconv_w", C * W, f32), _need(ddt_bias, "ddt_bias", H, f32),
+            _need(dA_log, "dA_log", H, f32), _need(dD, "dD", H, f32))
     _check("ssd_conv1d_bwd", _lib.load().ssd_conv1d_bwd(
         ctypes.byref(problem), s.ptr(), s.n, *ins, ws_p, nbytes, *outs, _stream(stream)))
 

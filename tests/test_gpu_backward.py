@@ -120,6 +120,26 @@ def test_backward_gradients(bwd_run):
         assert_close(got[name], ref[name], wl.act, name)
 
 
+def test_backward_phases_equal_composite(bwd_run):
+    """summary -> reverse scan -> pass -> chunks -> conv backward, called one by one
+    through the C ABI, gives the composite ssd_segment_bwd's gradients bit for bit."""
+    import mamba2_ssd_chunked_amd as ssd
+    wl, p, x, fb, bb = bwd_run
+    s = ssd.Segments(wl.segments)
+    b2 = ssd.BackwardBuffers.allocate(p, s, x["xBC"].device)
+    ssd.ssd_segment_bwd_summary(p, s, x["xBC"], x["conv_w"], x["dt_raw"], x["dt_bias"],
+                                x["A_log"], x["seq_idx"], x["dy"], b2.summary, b2.ws)
+    ssd.ssd_boundary_scan(p, s.n, b2.summary, None, True, b2.dS_out)
+    ssd.ssd_segment_bwd_pass(p, s, x["seq_idx"], fb.S_in, b2.dS_out, b2.ws)
+    ssd.ssd_segment_bwd_chunks(p, s, x["D"], x["seq_idx"], x["dy"], b2.ws)
+    ssd.ssd_conv1d_bwd(p, s, x["xBC"], x["conv_w"], x["dt_raw"], x["dt_bias"], x["A_log"],
+                       x["seq_idx"], b2.ws, b2.dxBC, b2.ddt_raw, b2.dconv_w, b2.ddt_bias,
+                       b2.dA_log, b2.dD)
+    torch.cuda.synchronize()
+    for name in ("dxBC", "ddt_raw", "dconv_w", "ddt_bias", "dA_log", "dD"):
+        assert torch.equal(getattr(b2, name), getattr(bb, name)), name
+
+
 def test_backward_mixer_shard_full():
     wl = W.config("mixer_shard_bwd_bf16")
     log(f"[backward] {wl.name}")
