@@ -46,11 +46,112 @@ def parse():
     ap.add_argument("--pass", dest="which", default=None, choices=["fwd", "fwd+bwd"],
                     help="default: fwd+bwd when the workload has dy, else fwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-runs", type=int, default=3)
+    ap.add_argument("--cpu-runs", type=int, default=8)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one device-to-device copy of this many MB before timing, so that "
                          "hardware byte counters can be calibrated against a known size")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="no GPU work: read two rocprofv3 --pmc databases (FETCH_SIZE, then "
+                         "WRITE_SIZE) of a run made with --copy-probe-mb, and print the per-launch "
+                         "HBM traffic of every kernel as JSON, calibrated against the copy")
     return ap.parse_args()
+
+
+# The kernel each single-kernel call launches: a regex over kernel_short() names.
+CALL_KERNEL = {
+    "ssd_conv1d_fwd": r"k_conv1d_silu<",
+    "ssd_segment_output_fused": r"k_chunk_y<",
+    "ssd_boundary_scan": r"k_boundary_scan<",
+    "ssd_boundary_scan(reverse)": r"k_boundary_scan<",
+    "ssd_segment_bwd_pass": r"k_state_pass<.*Li1E?>",
+    "ssd_segment_bwd_chunks": r"k_chunk_bwd<",
+}
+CSRC = os.path.join(ROOT, "mamba2_ssd_chunked_amd", "csrc")
+
+
+def source_digest():
+    """sha256 over the HIP/C++ sources: counter figures are only valid for these exact kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def kernel_short(sym):
+    """Kernel name with its mangled template arguments, e.g. k_state_pass<DF16bLi64ELi128ELi1>."""
+    import re
+    m = re.match(r"_ZN3ssd\d+(k_\w+?)I(.*?)EEv", sym)
+    if m:
+        return f"{m.group(1)}<{m.group(2)}>"
+    m = re.match(r"_ZN3ssd\d+(k_\w+?)E", sym)
+    if m:
+        return m.group(1) + "<>"
+    m = re.match(r"ssd::(k_\w+)", sym)
+    return m.group(1) + "<>" if m else sym
+
+
+def summarize_traffic(fetch_db, write_db, probe_mb):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB, summed over the counter's instances),
+    averaged per kernel, each scaled by known bytes / counted bytes of the largest
+    __amd_rocclr_copyBuffer dispatch (the copy probe: reads and writes probe_mb MiB)."""
+    import collections
+    import sqlite3
+
+    def per_dispatch(db, counter):
+        vals = collections.defaultdict(float)
+        names = {}
+        cur = sqlite3.connect(db).cursor()
+        for disp, kname, cname, val in cur.execute(
+                "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+            if cname == counter:
+                vals[disp] += val
+                names[disp] = kname
+        return vals, names
+
+    probe_kib = probe_mb * 1024.0
+    out = {"probe_bytes": probe_mb * (1 << 20), "kernels": {}}
+    for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+        vals, names = per_dispatch(db, counter)
+        copies = [vals[k] for k in vals if "copyBuffer" in names[k]]
+        if not copies:
+            raise SystemExit(f"no copy-probe dispatch in {db}")
+        counted = max(copies)
+        factor = probe_kib / counted
+        if not 0.25 <= factor <= 4.0:
+            raise SystemExit(f"{counter}: copy probe counted {counted} KiB for {probe_kib} KiB")
+        out[counter] = {"probe_counted_KiB": counted, "factor": round(factor, 4)}
+        per_k = collections.defaultdict(list)
+        for k, v in vals.items():
+            if "copyBuffer" not in names[k]:
+                per_k[kernel_short(names[k])].append(v)
+        for kn, vs in per_k.items():
+            e = out["kernels"].setdefault(kn, {})
+            e[counter + "_KiB"] = round(statistics.mean(vs), 1)
+            e[counter + "_bytes"] = round(statistics.mean(vs) * 1024 * factor)
+            e["dispatches"] = len(vs)
+    for e in out["kernels"].values():
+        e["hbm_bytes"] = e.get("FETCH_SIZE_bytes", 0) + e.get("WRITE_SIZE_bytes", 0)
+    out["source_sha256"] = source_digest()
+    return out
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary of this
+    workload, or None when it is missing or the sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != source_digest():
+        return None
+    import re
+    hits = [e for k, e in t["kernels"].items() if re.match(kernel, k)]
+    return hits[0]["hbm_bytes"] if len(hits) == 1 else None
 
 
 def algorithmic_bytes(wl):
@@ -139,6 +240,11 @@ def cpu_baseline(wl, runs, backward):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        if not args.copy_probe_mb:
+            raise SystemExit("--summarize-traffic needs the --copy-probe-mb of the profiled run")
+        print(json.dumps(summarize_traffic(*args.summarize_traffic, args.copy_probe_mb), indent=1))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -269,7 +375,7 @@ def main():
                    "layout": wl.layout, "packed": wl.seq_idx is not None},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(wl.name, CALL_KERNEL[dom])},
         "mfma": mfma,
         "calls": per_call,
         "wall_s_timed_region": round(wall, 4),
