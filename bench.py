@@ -64,7 +64,7 @@ CALL_KERNEL = {
     "ssd_boundary_scan": r"k_boundary_scan<",
     "ssd_boundary_scan(reverse)": r"k_boundary_scan<",
     "ssd_segment_bwd_pass": r"k_state_pass<.*Li1E?>",
-    "ssd_segment_bwd_chunks": r"k_chunk_bwd<",
+    "ssd_segment_bwd_chunks": r"k_chunk_bwd(_hb)?<",
 }
 CSRC = os.path.join(ROOT, "mamba2_ssd_chunked_amd", "csrc")
 

@@ -1,0 +1,628 @@
+// Chunk backward with the heads of a group blocked: one workgroup per (chunk,
+// block of HB heads of one group).
+//
+// Per chunk, with S_ij = C_i . B_j (the group's causal Gram tiles, transposed
+// orientation from k_gram<TRANS>), W^h_ij = dy^h_i . x^h_j, the decay
+// L^h_ij = exp(cs_i - cs_j) [j <= i, same sequence] and
+//   Z_ij = sum over the block's heads of W^h_ij L^h_ij dt^h_j,
+// the gradients of the intra-chunk term are
+//   dx^h_j = dt_j sum_i S_ij L_ij dy_i          (per head)
+//   dB_j   = sum_i Z_ij C_i                      (per group: B and C are shared
+//   dC_i   = sum_j Z_ij B_j                       by the heads of a group)
+// so dB and dC cost two products per chunk and head block instead of two per
+// head, and the per-head dB / dC never go to memory.  The entering state H and
+// the exit gradient G of every chunk (from the pass phase) add
+//   dx_j += dt_j g_j G B_j,  dB_j += sum_h dt_j g_j G^T x_j,
+//   dC_i += sum_h f_i H^T dy_i,
+// with f_i = exp(cs_i) [i in the entering state's sequence] and
+// g_j = exp(cs_e - cs_j) [j in the last token's sequence].  The ddt terms are
+// the ones the per-head kernel produced (see k_ddt): row and column sums of
+// F = S W L dt, u_i = f_i dy_i . (H C_i), v_j = dt_j x_j . (g_j G B_j),
+// q_j = x_j . (dx_j / dt_j without the D term), and the dD partial.
+//
+// Work split: NW = Q/32 waves; wave w owns the 16-token tiles w and QT-1-w,
+// as columns j (dx, column sums, v, q, dB) and as rows i (u, dC).  For a
+// column tile the rows i >= j are visited one MFMA k step (KS tokens, TPK
+// row tiles) at a time; the (k step, column) blocks of the wave are mapped to
+// NKS + 1 fixed register slots of Z (column QT-1-w: slots 0.., column w:
+// slot = k step + 1), so Z stays in registers across the heads.  x, dy, G and
+// H of a head sit in LDS in their natural rows: row reads for the W and state
+// products, transposed reads (XT) of dy for dx; the Gram tiles come from L2 one
+// k step ahead of their use.  After the heads, Z goes to LDS as rows for dC,
+// the chunk's C^T and B^T are staged in turn for the Z products, and each
+// head's G^T and H^T for its state terms; dB is finished before dC starts.
+#pragma once
+
+#include "bwd_util.h"
+#include "gram.h"
+#include "ssd_internal.h"
+#include "xt.h"
+
+namespace ssd {
+
+template <typename T, int P, int N, int Q>
+struct ChunkBwdHB {
+    typedef Mma<T> M;
+    static constexpr int SL = M::SL, KS = M::KS, VEC = 16 / (int)sizeof(T);
+    static constexpr int QT = Q / 16, NW = QT / 2, NTH = NW * 64;
+    static constexpr int TPK = KS / 16;  // row tiles per MFMA k step
+    static constexpr int NKS = Q / KS;   // k steps per chunk
+    static constexpr int NB = NKS + 1;   // Z slots per wave
+    // slots of the later column QT-1-w (at most)
+    static constexpr int MAXA = TPK == 2 ? (NW - 1) / 2 + 1 : NW;
+    static constexpr int PT = P / 16, NT = N / 16, KP = P / KS, KN = N / KS;
+    static constexpr int XR = P + VEC;  // x / dy rows [token][p]
+    static constexpr int GR = N + VEC;  // G / H rows [p][n]
+    static constexpr int PR = P + VEC;  // G^T / H^T rows [n][p]
+    static constexpr int TR = Q + VEC;  // B^T / C^T rows [n][token]
+    // Z rows in LDS for dC: row tile a keeps columns [0, cw(a)) (whole k steps)
+    __host__ __device__ static constexpr int cw(int a) { return KS * (a / TPK + 1); }
+    __host__ __device__ static constexpr int zpitch(int a) { return cw(a) + VEC; }
+    __host__ __device__ static constexpr int zoff(int a) {
+        int o = 0;
+        for (int t = 0; t < a; ++t) o += 16 * zpitch(t);
+        return o;
+    }
+    static constexpr int cmax(int a, int b) { return a > b ? a : b; }
+    // head loop: x, dy, G, H of the head and the per-wave row sums
+    static constexpr int O_D = Q * XR, O_G = 2 * Q * XR, O_H = O_G + P * GR, O_RW = O_H + P * GR;
+    static constexpr int E_HEAD = O_RW + NW * Q * 4 / (int)sizeof(T);
+    // final phase: Z rows and C^T (then G^T of one head), later B^T and H^T
+    static constexpr int O_BT = zoff(QT), E_FIN = O_BT + N * TR, E_FS = N * PR;
+    static constexpr int E_U = cmax(E_HEAD, cmax(E_FIN, E_FS));
+    static constexpr size_t LDS =
+        (size_t)E_U * sizeof(T) + (size_t)Q * 20 + (size_t)QT * QT * 4 + (size_t)NW * 4 + 64;
+    static_assert(QT % 2 == 0 && P % KS == 0 && N % KS == 0, "shape");
+};
+
+template <typename T, int P, int N, int Q>
+__global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
+    Dims d, SegTab tab, int hbs, const T* __restrict__ xc, const T* __restrict__ dy,
+    const T* __restrict__ gramT, const T* __restrict__ bct, const float* __restrict__ Dp,
+    const float* __restrict__ dt_ws, const float* __restrict__ cs_ws,
+    const int32_t* __restrict__ seq, const T* __restrict__ gpn, const T* __restrict__ gnp,
+    const T* __restrict__ hpn, const T* __restrict__ hnp, float* __restrict__ dv,
+    T* __restrict__ dbcp, float* __restrict__ rpart, float* __restrict__ tokp,
+    float* __restrict__ red4) {
+    typedef ChunkBwdHB<T, P, N, Q> K;
+    typedef Mma<T> M;
+    typedef typename M::Frag Frag;
+    typedef typename M::Elem E;
+    constexpr int SL = K::SL, KS = K::KS, VEC = K::VEC, NW = K::NW, NTH = K::NTH, QT = K::QT;
+    constexpr int TPK = K::TPK, NKS = K::NKS, NB = K::NB, MAXA = K::MAXA;
+    constexpr int PT = K::PT, NT = K::NT, KP = K::KP, KN = K::KN, XR = K::XR;
+    typedef T vt __attribute__((ext_vector_type(VEC)));
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) T U[K::E_U];
+    T* const sX = U;                            // x of the current head [Q][XR]
+    T* const sD = U + K::O_D;                   // dy of the current head [Q][XR]
+    T* const sG = U + K::O_G;                   // exit gradient G [P][GR]
+    T* const sH = U + K::O_H;                   // entering state H [P][GR]
+    float* const s_rw = (float*)(U + K::O_RW);  // per-wave row sums of F [NW][Q]
+    T* const sZ = U;                            // final phase: Z rows, strip per row tile
+    T* const sBT = U + K::O_BT;                 // final phase: C^T, then B^T [N][TR]
+    constexpr int GR = K::GR, PR = K::PR, TR = K::TR;
+    __shared__ __attribute__((aligned(16))) float scs[Q];
+    __shared__ __attribute__((aligned(16))) float sdt[Q];
+    __shared__ __attribute__((aligned(16))) float sea[Q];  // exp(cs_t - F(t))
+    __shared__ __attribute__((aligned(16))) float seb[Q];  // exp(L(t) - cs_t)
+    __shared__ __attribute__((aligned(16))) int ssq[Q];
+    __shared__ float stab[QT * QT];  // exp(F_a - L_b), a >= b
+    __shared__ float s_dd[NW];
+
+    // block -> (head block, chunk, row); the head blocks of a chunk are adjacent
+    // items, and consecutive items go to one XCD
+    const int nhb = d.H / hbs;
+    int hbi, cm;
+    int64_t b;
+    {
+        constexpr int NXCD = 8;
+        const int64_t n = gridDim.x, i = blockIdx.x;
+        const int64_t item = (n % NXCD == 0) ? (i % NXCD) * (n / NXCD) + i / NXCD : i;
+        hbi = (int)(item % nhb);
+        const int64_t rest = item / nhb;
+        cm = (int)(rest % d.nchunk);
+        b = rest / d.nchunk;
+    }
+    const int wave = wave_id(), lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
+    const int h0 = hbi * hbs;
+    const int g = h0 / d.hpg;
+    const int64_t rb = b * d.L, t0 = (int64_t)cm * Q;
+    const int64_t HPd = (int64_t)d.H * P;
+    const int kseg = seg_of_chunk(tab, cm, Q);
+    const int64_t s0 = tab.start[kseg];
+    const int64_t pred = seg_pred_token(tab, kseg);
+    const int64_t refc = t0 > s0 ? t0 - 1 : (pred >= 0 ? pred : s0);
+    const int seq_refc = seq ? seq[rb + refc] : 0;
+    const int seq_e = seq ? seq[rb + t0 + Q - 1] : 0;
+    const bool split = seq && seq[rb + t0] != seq_e;
+    const int64_t boff = HPd + (int64_t)g * N;
+    const int64_t coff = HPd + (int64_t)d.G * N + (int64_t)g * N;
+    const int64_t cg = ((int64_t)b * d.nchunk + cm) * d.G + g;
+    const T* bctB = bct + (cg * 2 + 0) * (int64_t)N * Q;
+    const T* bctC = bctB + (int64_t)N * Q;
+    const T* gT0 = gramT + cg * (int64_t)gram_tiles(QT) * 256 + lane * 4;
+    const int j0 = wave, j1 = QT - 1 - wave;  // the wave's tiles
+    const int ks0 = j0 / TPK, ks1 = j1 / TPK;  // first k step of each as a column
+    const int n1 = NKS - ks1;                  // k steps of column j1
+    auto st_of = [&](int h) { return (((int64_t)b * d.nchunk + cm) * d.H + h) * (int64_t)(P * N); };
+    auto hl_of = [&](int h) { return ((int64_t)b * d.H + h) * d.L + t0; };
+
+    // ---- staging of x, dy, G and H of one head (registers, then LDS)
+    constexpr int V_X = (Q * (P / VEC) + NTH - 1) / NTH;
+    constexpr int V_S = (P * (N / VEC) + NTH - 1) / NTH;
+    vt rx[V_X], rd[V_X], rg[V_S], rh[V_S];
+    auto fetch = [&](int h) {
+        const int64_t so = st_of(h);
+#pragma unroll
+        for (int q = 0; q < V_X; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (idx < Q * (P / VEC)) {
+                const int j = idx / (P / VEC), pv = idx % (P / VEC);
+                rx[q] = *(const vt*)(xc + (rb + t0 + j) * d.C + (int64_t)h * P + pv * VEC);
+                rd[q] = *(const vt*)(dy + (rb + t0 + j) * HPd + (int64_t)h * P + pv * VEC);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < V_S; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (idx < P * (N / VEC)) {
+                rg[q] = *(const vt*)(gpn + so + (int64_t)idx * VEC);
+                rh[q] = *(const vt*)(hpn + so + (int64_t)idx * VEC);
+            }
+        }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int q = 0; q < V_X; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (idx < Q * (P / VEC)) {
+                const int j = idx / (P / VEC), pv = idx % (P / VEC);
+                *(vt*)&sX[j * XR + pv * VEC] = rx[q];
+                *(vt*)&sD[j * XR + pv * VEC] = rd[q];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < V_S; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (idx < P * (N / VEC)) {
+                const int p = idx / (N / VEC), nv = idx % (N / VEC);
+                *(vt*)&sG[p * GR + nv * VEC] = rg[q];
+                *(vt*)&sH[p * GR + nv * VEC] = rh[q];
+            }
+        }
+    };
+
+    f32x4 Z[NB][TPK];
+#pragma unroll
+    for (int s = 0; s < NB; ++s)
+#pragma unroll
+        for (int it = 0; it < TPK; ++it) Z[s][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int j = threadIdx.x; j < Q; j += NTH) ssq[j] = seq ? seq[rb + t0 + j] : 0;
+
+    for (int hh = 0; hh < hbs; ++hh) {
+        const int h = h0 + hh;
+        const int64_t hl = hl_of(h);
+        fetch(h);
+        // An opaque zero, new every head: lane-derived indices, masks and the
+        // Gram tile addresses depend on it, so they are recomputed where they
+        // are used instead of being hoisted out of the head loop (where they
+        // would hold registers for its whole length).
+        int opq;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(opq));
+        const int lane = threadIdx.x % 64 + opq, lr = lane % 16, lg = lane / 16;
+        const T* const gT = gT0 + opq;
+        // C rows of the wave's two tiles and B rows of tile j1 (state products)
+        Frag cfr[2][KN], bfr[KN];
+#pragma unroll
+        for (int kn = 0; kn < KN; ++kn) {
+            cfr[0][kn] = M::load(xc + (rb + t0 + j0 * 16 + lr) * d.C + coff + kn * KS + SL * lg);
+            cfr[1][kn] = M::load(xc + (rb + t0 + j1 * 16 + lr) * d.C + coff + kn * KS + SL * lg);
+            bfr[kn] = M::load(xc + (rb + t0 + j1 * 16 + lr) * d.C + boff + kn * KS + SL * lg);
+        }
+        __syncthreads();  // the previous head is done with the LDS
+        stash();
+        for (int j = threadIdx.x; j < Q; j += NTH) {
+            scs[j] = cs_ws[hl + j];
+            sdt[j] = dt_ws[hl + j];
+        }
+        for (int j = threadIdx.x; j < NW * Q; j += NTH) s_rw[j] = 0.f;
+        __syncthreads();
+        // factored decay unless a sequence starts in the chunk or a tile's span
+        // would leave the normal float range
+        int wide = 0;
+        for (int a = threadIdx.x; a < QT; a += NTH) wide |= (scs[16 * a] - scs[16 * a + 15] > 80.f);
+        const bool exact = __syncthreads_or(wide) || split;
+        if (!exact) {
+            for (int t = threadIdx.x; t < Q; t += NTH) {
+                const int t16 = t & ~15;
+                sea[t] = __expf(scs[t] - scs[t16]);
+                seb[t] = __expf(scs[t16 + 15] - scs[t]);
+            }
+            for (int q = threadIdx.x; q < QT * QT; q += NTH) {
+                const int a = q / QT, c = q % QT;
+                stab[q] = a >= c ? __expf(scs[16 * a] - scs[16 * c + 15]) : 0.f;
+            }
+        }
+        __syncthreads();
+        const float cs_e = scs[Q - 1];
+        const float Dh = Dp[h];
+        float ddp = 0.f;  // dy . x over the wave's tokens
+
+        // u_i = f_i dy_i . (H C_i) for the wave's two tiles as rows
+        float u[2];
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int i = (it == 0 ? j0 : j1) * 16 + lr;
+            f32x4 ys[PT];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) ys[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kn = 0; kn < KN; ++kn)
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+                    ys[pt] = M::mma(M::load(&sH[(pt * 16 + lr) * GR + kn * KS + SL * lg]), cfr[it][kn], ys[pt]);
+            float up = 0.f;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                float dyv[4];
+                load4(&sD[i * XR + pt * 16 + 4 * lg], dyv);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) up += dyv[r] * ys[pt][r];
+            }
+            const float f_i = (ssq[i] == seq_refc) ? __expf(scs[i]) : 0.f;
+            u[it] = f_i * sum_groups(up);
+        }
+
+        // ---- one column tile: its state part, its k steps, its outputs
+        int jc = 0;
+        float csj = 0.f, dtj = 0.f, e2j = 0.f, vj = 0.f, kacc = 0.f;
+        int sqj = 0;
+        f32x4 acc[PT];
+        Frag xB[KP];
+        auto col_begin = [&](int jc_, const Frag (&bf)[KN]) {
+            jc = jc_;
+            const int j = 16 * jc + lr;
+            csj = scs[j];
+            dtj = sdt[j];
+            sqj = ssq[j];
+            e2j = exact ? 0.f : seb[j];
+            const float gj = (sqj == seq_e) ? __expf(cs_e - csj) : 0.f;
+#pragma unroll
+            for (int kp = 0; kp < KP; ++kp) xB[kp] = M::load(&sX[j * XR + kp * KS + SL * lg]);
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kn = 0; kn < KN; ++kn)
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+                    acc[pt] = M::mma(M::load(&sG[(pt * 16 + lr) * GR + kn * KS + SL * lg]), bf[kn], acc[pt]);
+            float vp = 0.f;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                acc[pt] *= gj;
+                float xv[4];
+                load4(&sX[j * XR + pt * 16 + 4 * lg], xv);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vp += xv[r] * acc[pt][r];
+            }
+            vj = dtj * sum_groups(vp);
+            kacc = 0.f;
+        };
+        // Gram tiles of a k step (loaded one k step ahead of their use)
+        auto gload = [&](t4 (&dst)[TPK], int jc_, int ks_) {
+#pragma unroll
+            for (int it = 0; it < TPK; ++it) {
+                const int a = ks_ * TPK + it;
+                if (a >= jc_) dst[it] = *(const t4*)(gT + (int64_t)gram_index(a, jc_) * 256);
+            }
+        };
+        // k step ks of the current column, accumulating into Z slot z
+        auto kstep = [&](f32x4 (&z)[TPK], int ks, const t4 (&gv)[TPK]) {
+            Frag sl;
+#pragma unroll
+            for (int it = 0; it < TPK; ++it) {
+                const int a = ks * TPK + it;
+                float dd[4] = {0.f, 0.f, 0.f, 0.f}, ss[4] = {0.f, 0.f, 0.f, 0.f};
+                f32x4 w = f32x4{0.f, 0.f, 0.f, 0.f};
+                const bool live = a >= jc;  // wave-uniform
+                if (live) {
+#pragma unroll
+                    for (int kp = 0; kp < KP; ++kp)
+                        w = M::mma(M::load(&sD[(16 * a + lr) * XR + kp * KS + SL * lg]), xB[kp], w);
+                    const int ib = 16 * a + 4 * lg;
+                    if (!exact) {
+                        const float bj = stab[a * QT + jc] * e2j;
+                        const f32x4 ea = *(const f32x4*)&sea[ib];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) dd[r] = ea[r] * bj;
+                        if (a == jc) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (4 * lg + r < lr) dd[r] = 0.f;
+                        }
+                    } else {
+                        const f32x4 ci = *(const f32x4*)&scs[ib];
+                        const int4 si = *(const int4*)&ssq[ib];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            dd[r] = (ib + r >= 16 * jc + lr && si[r] == sqj) ? __expf(ci[r] - csj) : 0.f;
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) ss[r] = (float)gv[it][r];
+                }
+                float fr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float wd = w[r] * (dd[r] * dtj);
+                    z[it][r] += wd;
+                    fr[r] = ss[r] * wd;
+                    kacc += fr[r];
+                    sl[it * 4 + r] = (E)(ss[r] * dd[r]);
+                }
+                if (live) {
+                    const float t = row_sums16(fr, lr);
+                    if ((lr & 3) == 0) {
+                        const int r = 2 * (lr >> 3) + ((lr >> 2) & 1);
+                        s_rw[wave * Q + 16 * a + 4 * lg + r] += t;
+                    }
+                }
+            }
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
+                acc[pt] = M::mma(XT<T>::load(sD, XR, ks * KS, pt * 16, lane), sl, acc[pt]);
+        };
+        auto col_end = [&](float ui) {
+            const int j = 16 * jc + lr;
+            float qp = 0.f;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                float xv[4], dyv[4];
+                load4(&sX[j * XR + pt * 16 + 4 * lg], xv);
+                load4(&sD[j * XR + pt * 16 + 4 * lg], dyv);
+                f32x4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    qp += xv[r] * acc[pt][r];
+                    o[r] = dtj * acc[pt][r] + Dh * dyv[r];
+                    ddp += dyv[r] * xv[r];
+                }
+                *(f32x4*)(dv + (rb + t0 + j) * d.C + (int64_t)h * P + pt * 16 + 4 * lg) = o;
+            }
+            const float qj = sum_groups(qp);
+            const float Kj = sum_groups(kacc);
+            if (lg == 0) {
+                float* tp = tokp + (hl + j) * 4;
+                tp[0] = ui - Kj;  // R_j is added by k_ddt from the row sums
+                tp[1] = qj;
+                tp[2] = vj;
+            }
+        };
+
+        // (scheduling barriers keep the unrolled k steps from being interleaved,
+        // which would need more registers than Z leaves)
+        col_begin(j1, bfr);
+        Frag bf0[KN];  // B rows of tile j0, for its column start
+#pragma unroll
+        for (int kn = 0; kn < KN; ++kn)
+            bf0[kn] = M::load(xc + (rb + t0 + j0 * 16 + lr) * d.C + boff + kn * KS + SL * lg);
+        t4 gn[TPK];
+        gload(gn, j1, ks1);
+#pragma unroll
+        for (int m = 0; m < MAXA; ++m) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (m < n1) {
+                t4 gc[TPK];
+#pragma unroll
+                for (int it = 0; it < TPK; ++it) gc[it] = gn[it];
+                if (m + 1 < n1) gload(gn, j1, ks1 + m + 1);
+                else gload(gn, j0, ks0);
+                kstep(Z[m], ks1 + m, gc);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        col_end(u[1]);
+        col_begin(j0, bf0);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks >= ks0) {
+                t4 gc[TPK];
+#pragma unroll
+                for (int it = 0; it < TPK; ++it) gc[it] = gn[it];
+                if (ks + 1 < NKS) gload(gn, j0, ks + 1);
+                kstep(Z[ks + 1], ks, gc);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        col_end(u[0]);
+
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) ddp += __shfl_xor(ddp, off, 64);
+        if (lane % 64 == 0) s_dd[wave] = ddp;
+        __syncthreads();
+        for (int t = threadIdx.x; t < Q; t += NTH) {
+            float rsum = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) rsum += s_rw[w * Q + t];
+            rpart[hl + t] = rsum;
+        }
+        if (threadIdx.x == 0) {
+            float dd = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) dd += s_dd[w];
+            red4[((int64_t)b * d.nchunk + cm) * d.H + h] = dd;
+        }
+    }
+
+    // ================= dB and dC of the head block =================
+    // dB first (Z from registers, then the exit-gradient terms), then dC (Z
+    // rows from LDS, then the entering-state terms): one set of 2 x NT
+    // accumulators is live at a time.
+    int opq;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(opq));
+    const int lane2 = threadIdx.x % 64 + opq, lr2 = lane2 % 16, lg2 = lane2 / 16;
+    constexpr int V_T = (N * (Q / VEC) + NTH - 1) / NTH;
+    auto stage_bt = [&](const T* src) {  // [N][Q] -> sBT
+#pragma unroll
+        for (int q = 0; q < V_T; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (idx < N * (Q / VEC)) {
+                const int n = idx / (Q / VEC), tv = idx % (Q / VEC);
+                *(vt*)&sBT[n * TR + tv * VEC] = *(const vt*)(src + (int64_t)n * Q + tv * VEC);
+            }
+        }
+    };
+    // G^T or H^T [n][p] of head h -> LDS at dst
+    constexpr int V_GT = (N * (P / VEC) + NTH - 1) / NTH;
+    auto stage_state = [&](T* dst, const T* src) {
+#pragma unroll
+        for (int q = 0; q < V_GT; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (idx < N * (P / VEC)) {
+                const int n = idx / (P / VEC), pv = idx % (P / VEC);
+                *(vt*)&dst[n * PR + pv * VEC] = *(const vt*)(src + (int64_t)idx * VEC);
+            }
+        }
+    };
+    T* const dbp = dbcp + (int64_t)hbi * 2 * N;
+    const int64_t dbs = (int64_t)nhb * 2 * N;  // token stride of the partials
+    f32x4 ab[2][NT];  // [tile j0 / j1][n tile], transposed ([n][token])
+    auto ab_zero = [&]() {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) ab[c][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto ab_store = [&](int part) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            T* o = dbp + (rb + t0 + (c == 0 ? j0 : j1) * 16 + lr2) * dbs + part * N;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                *(t4*)(o + nt * 16 + 4 * lg2) =
+                    t4{(T)ab[c][nt][0], (T)ab[c][nt][1], (T)ab[c][nt][2], (T)ab[c][nt][3]};
+        }
+    };
+    // the state terms of one part over the heads: ab[c] += S^T (scaled rows of
+    // tile c), S^T = G^T (dB, rows of x scaled by dt g) or H^T (dC, rows of dy
+    // scaled by f), staged at sS
+    auto state_terms = [&](bool dB, T* sS) {
+        for (int hh = 0; hh < hbs; ++hh) {
+            const int h = h0 + hh;
+            const int64_t hl = hl_of(h), so = st_of(h);
+            Frag rr[2][KP];
+            float sc[2];
+            const float cse = cs_ws[hl + Q - 1];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int t = (c == 0 ? j0 : j1) * 16 + lr2;
+#pragma unroll
+                for (int kp = 0; kp < KP; ++kp)
+                    rr[c][kp] = dB ? M::load(xc + (rb + t0 + t) * d.C + (int64_t)h * P + kp * KS + SL * lg2)
+                                   : M::load(dy + (rb + t0 + t) * HPd + (int64_t)h * P + kp * KS + SL * lg2);
+                const float cst = cs_ws[hl + t];
+                sc[c] = dB ? ((ssq[t] == seq_e) ? dt_ws[hl + t] * __expf(cse - cst) : 0.f)
+                           : ((ssq[t] == seq_refc) ? __expf(cst) : 0.f);
+            }
+            __syncthreads();  // the previous head's products are done with sS
+            stage_state(sS, (dB ? gnp : hnp) + so);
+            __syncthreads();
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+#pragma unroll
+                for (int kp = 0; kp < KP; ++kp) {
+                    Frag sf;
+#pragma unroll
+                    for (int e = 0; e < SL; ++e) sf[e] = (E)((float)rr[c][kp][e] * sc[c]);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        ab[c][nt] = M::mma(M::load(&sS[(nt * 16 + lr2) * PR + kp * KS + SL * lg2]), sf,
+                                           ab[c][nt]);
+                }
+            }
+        }
+    };
+
+    __syncthreads();  // every wave is done with the head loop's LDS
+    // Z into LDS as natural rows (strip per row tile) for dC; C^T for dB
+    auto zstore = [&](const f32x4 (&z)[TPK], int jc, int ks) {
+#pragma unroll
+        for (int it = 0; it < TPK; ++it) {
+            const int a = ks * TPK + it;
+            T* st = sZ + K::zoff(a) + 16 * jc + lr2;
+            const int zp = K::zpitch(a);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st[(4 * lg2 + r) * zp] = (T)z[it][r];
+        }
+    };
+#pragma unroll
+    for (int m = 0; m < MAXA; ++m)
+        if (m < n1) zstore(Z[m], j1, ks1 + m);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+        if (ks >= ks0) zstore(Z[ks + 1], j0, ks);
+    stage_bt(bctC);
+    __syncthreads();
+
+    auto zfrag = [&](const f32x4 (&z)[TPK]) {
+        Frag f;
+#pragma unroll
+        for (int it = 0; it < TPK; ++it)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) f[it * 4 + r] = (E)z[it][r];
+        return f;
+    };
+    // ---- dB^T [n][j] = sum_i C^T[n][i] Z[i][j] + state terms
+    ab_zero();
+#pragma unroll
+    for (int m = 0; m < MAXA; ++m) {
+        if (m < n1) {
+            const Frag zf = zfrag(Z[m]);
+            const int ks = ks1 + m;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                ab[1][nt] = M::mma(M::load(&sBT[(nt * 16 + lr2) * TR + ks * KS + SL * lg2]), zf, ab[1][nt]);
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        if (ks >= ks0) {
+            const Frag zf = zfrag(Z[ks + 1]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                ab[0][nt] = M::mma(M::load(&sBT[(nt * 16 + lr2) * TR + ks * KS + SL * lg2]), zf, ab[0][nt]);
+        }
+    }
+    state_terms(true, sBT);  // G^T goes where C^T was (the Z rows stay)
+    ab_store(0);
+
+    // ---- dC^T [n][i] = sum_j B^T[n][j] Z[i][j] + state terms
+    __syncthreads();  // every wave is done with sBT
+    stage_bt(bctB);
+    __syncthreads();
+    ab_zero();
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int a = it == 0 ? j0 : j1;
+        const T* zr = sZ + K::zoff(a) + lr2 * K::zpitch(a);
+        for (int ks = 0; ks <= a / TPK; ++ks) {
+            Frag zf;
+            if constexpr (TPK == 2) {
+                const t4 lo = *(const t4*)&zr[ks * KS + 4 * lg2];
+                const t4 hi = *(const t4*)&zr[ks * KS + 16 + 4 * lg2];
+                zf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            } else {
+                zf = *(const Frag*)&zr[ks * KS + 4 * lg2];
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                ab[it][nt] = M::mma(M::load(&sBT[(nt * 16 + lr2) * TR + ks * KS + SL * lg2]), zf, ab[it][nt]);
+        }
+    }
+    state_terms(false, sZ);  // H^T goes where the Z rows were (after the first sync)
+    ab_store(1);
+}
+
+}  // namespace ssd

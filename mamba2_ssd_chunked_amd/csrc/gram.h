@@ -9,6 +9,9 @@
 // reads a tile back with one 8-byte (bf16) or 16-byte (float32) load per lane:
 // lane l holds column i = l % 16 and rows j = 4 (l / 16) + r, r = 0..3.
 // Tiles of a (row, chunk, group) are numbered t = a (a + 1) / 2 + b.
+// TRANS = true stores the transposed tiles S_ab[i][j] = C_i . B_j instead (lane
+// l holds column j = l % 16 and rows i = 4 (l / 16) + r), the orientation the
+// chunk backward consumes.
 #pragma once
 
 #include "ssd_internal.h"
@@ -19,7 +22,7 @@ __host__ __device__ constexpr int gram_tiles(int qt) { return qt * (qt + 1) / 2;
 __host__ __device__ constexpr int gram_index(int a, int b) { return a * (a + 1) / 2 + b; }
 
 // One wave per (output tiles w and QT-1-w, chunk, group, row).
-template <typename T, int N>
+template <typename T, int N, bool TRANS = false>
 __global__ void __launch_bounds__(64) k_gram(Dims d, const T* __restrict__ xc, T* __restrict__ gram) {
     typedef Mma<T> M;
     typedef typename M::Frag Frag;
@@ -44,19 +47,20 @@ __global__ void __launch_bounds__(64) k_gram(Dims d, const T* __restrict__ xc, T
         for (int bt = 0; bt <= a; ++bt) {
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kn = 0; kn < NKF; ++kn)
-                acc = M::mma(M::load(xc + (t0 + bt * 16 + lr) * d.C + boff + kn * KS + SL * lg),
-                             cf[kn], acc);
+            for (int kn = 0; kn < NKF; ++kn) {
+                const Frag bf = M::load(xc + (t0 + bt * 16 + lr) * d.C + boff + kn * KS + SL * lg);
+                acc = TRANS ? M::mma(cf[kn], bf, acc) : M::mma(bf, cf[kn], acc);
+            }
             *(t4*)(out + (int64_t)gram_index(a, bt) * 256 + lane * 4) =
                 t4{(T)acc[0], (T)acc[1], (T)acc[2], (T)acc[3]};
         }
     }
 }
 
-template <typename T, int N>
+template <typename T, int N, bool TRANS = false>
 inline void launch_gram(const Dims& d, const T* xc, T* gram, hipStream_t s) {
     const int QT = d.Q / 16;
-    hipLaunchKernelGGL((k_gram<T, N>), dim3((unsigned)(QT / 2), (unsigned)(d.nchunk * d.G),
+    hipLaunchKernelGGL((k_gram<T, N, TRANS>), dim3((unsigned)(QT / 2), (unsigned)(d.nchunk * d.G),
                                             (unsigned)d.batch),
                        dim3(64), 0, s, d, xc, gram);
 }

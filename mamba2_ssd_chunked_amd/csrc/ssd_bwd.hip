@@ -35,6 +35,9 @@
 // the same fp32 F tiles, so their telescoping cancels without bf16 noise.
 #include <type_traits>
 
+#include "bwd_util.h"
+#include "chunk_bwd.h"
+#include "gram.h"
 #include "ssd_internal.h"
 
 namespace ssd {
@@ -66,45 +69,6 @@ template <typename T>
 __device__ __forceinline__ int tpos(int t) {
     constexpr int B = TokPerm<T>::BLK;
     return (t & ~(B - 1)) + TokPerm<T>::pos(t & (B - 1));
-}
-
-template <typename T>
-__device__ __forceinline__ void load4(const T* p, float* o) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] = (float)p[r];
-}
-
-// Sum over the four lane groups (lanes l, l^16, l^32, l^48 share a column).
-__device__ __forceinline__ float sum_groups(float v) {
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
-}
-
-// DPP lane moves inside rows of 16 lanes (VALU only, no LDS traffic).
-#define SSD_DPP(v, ctrl) \
-    __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), (ctrl), 0xF, 0xF, false))
-#define DPP_ROW_MIRROR 0x140
-#define DPP_ROW_HALF_MIRROR 0x141
-#define DPP_QUAD_XOR1 0xB1
-#define DPP_QUAD_XOR2 0x4E
-
-// Row sums of a 16x16 tile held as 4 rows per lane (rows 4g+r, column l%16):
-// reduces v[0..3] over the 16 lanes of each row group and returns, in lane l,
-// the sum for row r = 2*(l%16 >= 8) + ((l%8) >= 4) (all four lanes of a quad
-// hold the same value).
-__device__ __forceinline__ float row_sums16(const float v[4], int lr) {
-    const bool hi = lr >= 8;
-    const float k0 = hi ? v[2] : v[0], k1 = hi ? v[3] : v[1];
-    const float s0 = hi ? v[0] : v[2], s1 = hi ? v[1] : v[3];
-    const float a0 = k0 + SSD_DPP(s0, DPP_ROW_MIRROR);
-    const float a1 = k1 + SSD_DPP(s1, DPP_ROW_MIRROR);
-    const bool h2 = (lr & 4) != 0;
-    const float k = h2 ? a1 : a0, s = h2 ? a0 : a1;
-    float t = k + SSD_DPP(s, DPP_ROW_HALF_MIRROR);
-    t += SSD_DPP(t, DPP_QUAD_XOR2);
-    t += SSD_DPP(t, DPP_QUAD_XOR1);
-    return t;
 }
 
 // ---------------------------------------------------------------------------
@@ -290,7 +254,7 @@ __global__ void __launch_bounds__(256) k_state_pass(
     Dims d, SegTab tab, const float* __restrict__ ctot, const int32_t* __restrict__ seq,
     const float* __restrict__ zg, const float* __restrict__ zh, const float* __restrict__ S_in,
     const float* __restrict__ dS_out, float* __restrict__ summary, T* __restrict__ gpn,
-    T* __restrict__ gnp, T* __restrict__ hnp, float* __restrict__ dotgh) {
+    T* __restrict__ gnp, T* __restrict__ hnp, T* __restrict__ hpn, float* __restrict__ dotgh) {
     constexpr int PN4 = P * N / 4;
     constexpr int E4 = (PN4 + 255) / 256;  // float4 groups per thread
     constexpr int TP = N + 1;              // fp32 transpose tile pitch
@@ -392,11 +356,14 @@ __global__ void __launch_bounds__(256) k_state_pass(
             if (i4 < PN4) {
                 const vt4 gv = *(const vt4*)(gpn + so + 4 * i4);  // written by this thread
                 const int p = (4 * i4) / N, n = (4 * i4) % N;
+                vt4 hv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     dot += (float)gv[e] * acc[q][e];
                     tile[p * TP + n + e] = acc[q][e];
+                    hv[e] = (T)acc[q][e];
                 }
+                if (hpn) *(vt4*)(hpn + so + 4 * i4) = hv;
             }
         }
 #pragma unroll
@@ -1219,10 +1186,13 @@ __global__ void __launch_bounds__(64) k_ddt(Dims d, SegTab tab,
 }
 
 // ---------------------------------------------------------------------------
-// dB and dC of a group are the sums of its heads' contributions; written into
-// the B and C channels of dv (the conv output gradient), coalesced along n.
+// dB and dC of a group are the sums of its heads' (or head blocks')
+// contributions, stored [token][nblk][2N] with the bpg blocks of group g at
+// g*bpg..; written into the B and C channels of dv (the conv output gradient),
+// coalesced along n.
 template <typename T>
-__global__ void __launch_bounds__(256) k_bc_headsum(Dims d, const T* __restrict__ dbc,
+__global__ void __launch_bounds__(256) k_bc_headsum(Dims d, int nblk, int bpg,
+                                                   const T* __restrict__ dbc,
                                                    float* __restrict__ dv) {
     constexpr int VEC = 16 / sizeof(T);  // outputs per thread (one 16-byte load per head)
     typedef T vt __attribute__((ext_vector_type(VEC)));
@@ -1232,12 +1202,12 @@ __global__ void __launch_bounds__(256) k_bc_headsum(Dims d, const T* __restrict_
     const int64_t tok = idx / nv;
     const int o = (int)(idx % nv) * VEC;
     const int part = o / GN, gn = o % GN, g = gn / d.N, n = gn % d.N;
-    const T* src = dbc + (tok * d.H + (int64_t)g * d.hpg) * (2 * d.N) + part * d.N + n;
+    const T* src = dbc + (tok * nblk + (int64_t)g * bpg) * (2 * d.N) + part * d.N + n;
     float acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
 #pragma unroll 8
-    for (int hh = 0; hh < d.hpg; ++hh) {
+    for (int hh = 0; hh < bpg; ++hh) {
         const vt v = *(const vt*)(src + (int64_t)hh * 2 * d.N);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[e] += (float)v[e];
@@ -1438,8 +1408,31 @@ constexpr bool chunk_bwd_fits() {
     return ChunkBwd<T, P, N, Q, chunk_bwd_tpw<T, Q>()>::LDS <= BWD_LDS_LIMIT;
 }
 
+// The head-blocked chunk kernel takes P <= 64 (its Z and dx accumulators share
+// the registers); larger heads use the per-head kernel.
+template <typename T, int P, int N, int Q>
+constexpr bool hb_fits() {
+    return P <= 64 && ChunkBwdHB<T, P, N, Q>::LDS <= BWD_LDS_LIMIT;
+}
+template <typename T, int P, int N>
+static bool hb_path(int Q) {
+    if (Q == 64) return hb_fits<T, P, N, 64>();
+    if (Q == 128) return hb_fits<T, P, N, 128>();
+    if (Q == 256) return hb_fits<T, P, N, 256>();
+    return false;
+}
+constexpr int HB_MAX = 4;  // heads per workgroup of the head-blocked kernel
+// heads per block: the largest divisor of the heads per group up to HB_MAX
+static int head_block(const Dims& d) {
+    int hb = 1;
+    for (int c = 1; c <= HB_MAX; ++c)
+        if (d.hpg % c == 0) hb = c;
+    return hb;
+}
+
 template <typename T, int P, int N>
 static bool bwd_shape_ok(int Q) {
+    if (hb_path<T, P, N>(Q)) return true;
     if (Q == 64) return chunk_bwd_fits<T, P, N, 64>();
     if (Q == 128) return chunk_bwd_fits<T, P, N, 128>();
     if (Q == 256) return chunk_bwd_fits<T, P, N, 256>();
@@ -1449,7 +1442,18 @@ static bool bwd_shape_ok(int Q) {
 template <typename T, int P, int N, int Q>
 static void launch_chunk_bwd(const Dims& d, const SegTab& t, const BwdArgs& a, const BwdWs& L,
                              char* ws, hipStream_t s) {
-    if constexpr (chunk_bwd_fits<T, P, N, Q>()) {
+    if constexpr (hb_fits<T, P, N, Q>()) {
+        const int hbs = head_block(d);
+        const unsigned nblk = (unsigned)((int64_t)d.nchunk * (d.H / hbs) * d.batch);
+        hipLaunchKernelGGL((k_chunk_bwd_hb<T, P, N, Q>), dim3(nblk),
+                           dim3(ChunkBwdHB<T, P, N, Q>::NTH), 0, s, d, t, hbs,
+                           (const T*)(ws + L.xc), (const T*)a.dy, (const T*)(ws + L.gramt),
+                           (const T*)(ws + L.bct), a.D, (const float*)(ws + L.dt),
+                           (const float*)(ws + L.cs), a.seq, (const T*)(ws + L.gpn),
+                           (const T*)(ws + L.gnp), (const T*)(ws + L.hpn), (const T*)(ws + L.hnp),
+                           (float*)(ws + L.dv), (T*)(ws + L.dbc), (float*)(ws + L.rpart),
+                           (float*)(ws + L.tokp), (float*)(ws + L.red4));
+    } else if constexpr (chunk_bwd_fits<T, P, N, Q>()) {
         constexpr int TPW = chunk_bwd_tpw<T, Q>();
         constexpr int NW = ChunkBwd<T, P, N, Q, TPW>::NW;
         hipLaunchKernelGGL((k_chunk_bwd<T, P, N, Q, TPW>), chunk_head_grid(d),
@@ -1495,6 +1499,7 @@ static void bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a, floa
                       a.seq, xc, s);
     hipLaunchKernelGGL(k_bc_transpose<T>, dim3((unsigned)d.nchunk, (unsigned)d.G, (unsigned)d.batch),
                        dim3(256), 0, s, d, (const T*)xc, (T*)(ws + L.bct));
+    if (hb_path<T, P, N>(d.Q)) launch_gram<T, N, true>(d, xc, (T*)(ws + L.gramt), s);
     launch_dt_prep(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32, a.dt_raw, a.dt_bias,
                    a.A_log, a.seq, (float*)(ws + L.dt), (float*)(ws + L.cs),
                    (float*)(ws + L.ctot), s);
@@ -1506,7 +1511,7 @@ static void bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a, floa
                        dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0, s,
                        d, t, (const float*)(ws + L.ctot), a.seq, (const float*)(ws + L.zg),
                        (const float*)(ws + L.zh), (const float*)nullptr, (const float*)nullptr,
-                       summary, (T*)nullptr, (T*)nullptr, (T*)nullptr, (float*)nullptr);
+                       summary, (T*)nullptr, (T*)nullptr, (T*)nullptr, (T*)nullptr, (float*)nullptr);
 }
 
 template <typename T, int P, int N>
@@ -1519,6 +1524,7 @@ static void bwd_pass_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* w
                        d, t, (const float*)(ws + L.ctot), a.seq, (const float*)(ws + L.zg),
                        (const float*)(ws + L.zh), a.S_in, a.dS_out, (float*)nullptr,
                        (T*)(ws + L.gpn), (T*)(ws + L.gnp), (T*)(ws + L.hnp),
+                       hb_path<T, P, N>(d.Q) ? (T*)(ws + L.hpn) : (T*)nullptr,
                        (float*)(ws + L.dotgh));
 }
 
@@ -1535,7 +1541,7 @@ static void bwd_chunks_t(const Dims& d, const SegTab& t, const BwdArgs& a, void*
 }
 
 template <typename T>
-static void conv_bwd_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* ws_,
+static void conv_bwd_t(const Dims& d, const SegTab& t, const BwdArgs& a, int hbs, void* ws_,
                        hipStream_t s) {
     const BwdWs L = bwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
     char* ws = (char*)ws_;
@@ -1547,7 +1553,7 @@ static void conv_bwd_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* w
                        (float*)(ws + L.red));
     const int64_t nbc = d.batch * d.L * 2 * d.G * d.N / (16 / sizeof(T));
     hipLaunchKernelGGL(k_bc_headsum<T>, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, d,
-                       (const T*)(ws + L.dbc), (float*)(ws + L.dv));
+                       d.H / hbs, d.hpg / hbs, (const T*)(ws + L.dbc), (float*)(ws + L.dv));
     launch_conv_bwd<T>(d, t, a, L, ws, s);
     const int nout = d.C * d.W + 3 * d.H;
     hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)((nout + 31) / 32)), dim3(256), 0, s, d,
@@ -1625,10 +1631,27 @@ hipError_t launch_bwd_chunks(const Dims& d, const SegTab& t, int act, const BwdA
     return hipErrorInvalidValue;
 }
 
+// Heads per dB / dC partial the chunk phase leaves: the head block of the
+// head-blocked kernel, else 1.
+static int dbc_heads(const Dims& d, int act) {
+#define X(p, n) \
+    if (d.P == p && d.N == n) return hb_path<T, p, n>(d.Q) ? head_block(d) : 1;
+    if (act == SSD_F32) {
+        typedef float T;
+        SSD_BWD_F32_SHAPES(X)
+    } else {
+        typedef bf16 T;
+        SSD_BWD_BF16_SHAPES(X)
+    }
+#undef X
+    return 1;
+}
+
 hipError_t launch_conv1d_bwd(const Dims& d, const SegTab& t, int act, const BwdArgs& a, void* ws,
                              hipStream_t s) {
-    if (act == SSD_BF16) conv_bwd_t<bf16>(d, t, a, ws, s);
-    else conv_bwd_t<float>(d, t, a, ws, s);
+    const int hbs = dbc_heads(d, act);
+    if (act == SSD_BF16) conv_bwd_t<bf16>(d, t, a, hbs, ws, s);
+    else conv_bwd_t<float>(d, t, a, hbs, ws, s);
     return hipGetLastError();
 }
 

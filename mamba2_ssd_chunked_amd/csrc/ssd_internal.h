@@ -235,8 +235,8 @@ inline FwdWs fwd_ws_layout(const Dims& d, int act) {
 // Backward workspace layout (byte offsets).  Filled by the summary phase
 // (xc, bct, dt, cs, ctot, zh, zg, dyT) and used by the segment phase.
 struct BwdWs {
-    size_t xc, bct, dt, cs, ctot, zh, zg, gpn, gnp, hnp, dyT, dv, dbc, rpart, tokp, dotgh, red4,
-        red, dwp, total;
+    size_t xc, bct, gramt, dt, cs, ctot, zh, zg, gpn, gnp, hnp, hpn, dyT, dv, dbc, rpart, tokp,
+        dotgh, red4, red, dwp, total;
 };
 inline BwdWs bwd_ws_layout(const Dims& d, int act) {
     BwdWs w;
@@ -247,6 +247,9 @@ inline BwdWs bwd_ws_layout(const Dims& d, int act) {
     size_t o = 0;
     w.xc = o;   o = align256(o + BL * d.C * e);
     w.bct = o;  o = align256(o + (size_t)d.batch * d.nchunk * d.G * 2 * d.N * d.Q * e);
+    // causal C_i . B_j tiles per (row, chunk, group), 256 elements each
+    const size_t qt = (size_t)d.Q / 16;
+    w.gramt = o; o = align256(o + (size_t)d.batch * d.nchunk * d.G * (qt * (qt + 1) / 2) * 256 * e);
     w.dt = o;   o = align256(o + bhl * 4);
     w.cs = o;   o = align256(o + bhl * 4);
     w.ctot = o; o = align256(o + (size_t)d.batch * d.H * d.nchunk * 4);
@@ -255,9 +258,10 @@ inline BwdWs bwd_ws_layout(const Dims& d, int act) {
     w.gpn = o;  o = align256(o + st * e);  // exit gradient per chunk, [p][n]
     w.gnp = o;  o = align256(o + st * e);  // the same, [n][p]
     w.hnp = o;  o = align256(o + st * e);  // entering state per chunk, [n][p]
+    w.hpn = o;  o = align256(o + st * e);  // the same, [p][n]
     w.dyT = o;  o = align256(o + bhl * d.P * e);  // dy per chunk and head, [p][token]
     w.dv = o;   o = align256(o + BL * d.C * 4);  // d(conv output), every channel
-    w.dbc = o;  o = align256(o + BL * d.H * 2 * d.N * e);  // per-head dB, dC
+    w.dbc = o;  o = align256(o + BL * d.H * 2 * d.N * e);  // dB, dC per head or head block
     w.rpart = o; o = align256(o + bhl * 4);
     w.tokp = o; o = align256(o + bhl * 4 * 4);
     w.dotgh = o; o = align256(o + (size_t)d.batch * d.nchunk * d.H * 4);
