@@ -67,8 +67,9 @@ struct ChunkBwdHB {
     // head loop: x, dy, G, H of the head and the per-wave row sums
     static constexpr int O_D = Q * XR, O_G = 2 * Q * XR, O_H = O_G + P * GR, O_RW = O_H + P * GR;
     static constexpr int E_HEAD = O_RW + NW * Q * 4 / (int)sizeof(T);
-    // final phase: Z rows and C^T (then G^T of one head), later B^T and H^T
-    static constexpr int O_BT = zoff(QT), E_FIN = O_BT + N * TR, E_FS = N * PR;
+    // final phase: Z rows and C^T (then G^T of HG heads), later B^T and H^T
+    static constexpr int HG = 4;  // heads per round of state terms
+    static constexpr int O_BT = zoff(QT), E_FIN = O_BT + N * TR, E_FS = O_BT + HG * N * PR;
     static constexpr int E_U = cmax(E_HEAD, cmax(E_FIN, E_FS));
     static constexpr size_t LDS =
         (size_t)E_U * sizeof(T) + (size_t)Q * 20 + (size_t)QT * QT * 4 + (size_t)NW * 4 + 64;
@@ -81,7 +82,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
     const T* __restrict__ gramT, const T* __restrict__ bct, const float* __restrict__ Dp,
     const float* __restrict__ dt_ws, const float* __restrict__ cs_ws,
     const int32_t* __restrict__ seq, const T* __restrict__ gpn, const T* __restrict__ gnp,
-    const T* __restrict__ hpn, const T* __restrict__ hnp, float* __restrict__ dv,
+    const T* __restrict__ hpn, const T* __restrict__ hnp, T* __restrict__ dv,
     T* __restrict__ dbcp, float* __restrict__ rpart, float* __restrict__ tokp,
     float* __restrict__ red4) {
     typedef ChunkBwdHB<T, P, N, Q> K;
@@ -381,14 +382,14 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
                 float xv[4], dyv[4];
                 load4(&sX[j * XR + pt * 16 + 4 * lg], xv);
                 load4(&sD[j * XR + pt * 16 + 4 * lg], dyv);
-                f32x4 o;
+                t4 o;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     qp += xv[r] * acc[pt][r];
-                    o[r] = dtj * acc[pt][r] + Dh * dyv[r];
+                    o[r] = (T)(dtj * acc[pt][r] + Dh * dyv[r]);
                     ddp += dyv[r] * xv[r];
                 }
-                *(f32x4*)(dv + (rb + t0 + j) * d.C + (int64_t)h * P + pt * 16 + 4 * lg) = o;
+                *(t4*)(dv + (rb + t0 + j) * HPd + (int64_t)h * P + pt * 16 + 4 * lg) = o;
             }
             const float qj = sum_groups(qp);
             const float Kj = sum_groups(kacc);
@@ -474,18 +475,6 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
             }
         }
     };
-    // G^T or H^T [n][p] of head h -> LDS at dst
-    constexpr int V_GT = (N * (P / VEC) + NTH - 1) / NTH;
-    auto stage_state = [&](T* dst, const T* src) {
-#pragma unroll
-        for (int q = 0; q < V_GT; ++q) {
-            const int idx = threadIdx.x + q * NTH;
-            if (idx < N * (P / VEC)) {
-                const int n = idx / (P / VEC), pv = idx % (P / VEC);
-                *(vt*)&dst[n * PR + pv * VEC] = *(const vt*)(src + (int64_t)idx * VEC);
-            }
-        }
-    };
     T* const dbp = dbcp + (int64_t)hbi * 2 * N;
     const int64_t dbs = (int64_t)nhb * 2 * N;  // token stride of the partials
     f32x4 ab[2][NT];  // [tile j0 / j1][n tile], transposed ([n][token])
@@ -507,39 +496,71 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
     };
     // the state terms of one part over the heads: ab[c] += S^T (scaled rows of
     // tile c), S^T = G^T (dB, rows of x scaled by dt g) or H^T (dC, rows of dy
-    // scaled by f), staged at sS
+    // scaled by f); HG heads per round, their S^T staged at sS
+    constexpr int HG = K::HG;
+    constexpr int V_GT = (N * (P / VEC) + NTH - 1) / NTH;
     auto state_terms = [&](bool dB, T* sS) {
-        for (int hh = 0; hh < hbs; ++hh) {
-            const int h = h0 + hh;
-            const int64_t hl = hl_of(h), so = st_of(h);
-            Frag rr[2][KP];
-            float sc[2];
-            const float cse = cs_ws[hl + Q - 1];
+        for (int hf = 0; hf < hbs; hf += HG) {
+            vt rs[HG][V_GT];
+            Frag rr[HG][2][KP];
+            float sc[HG][2];
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int t = (c == 0 ? j0 : j1) * 16 + lr2;
+            for (int q = 0; q < HG; ++q) {
+                if (hf + q < hbs) {
+                    const int h = h0 + hf + q;
+                    const int64_t hl = hl_of(h), so = st_of(h);
+                    const T* src = (dB ? gnp : hnp) + so;
 #pragma unroll
-                for (int kp = 0; kp < KP; ++kp)
-                    rr[c][kp] = dB ? M::load(xc + (rb + t0 + t) * d.C + (int64_t)h * P + kp * KS + SL * lg2)
-                                   : M::load(dy + (rb + t0 + t) * HPd + (int64_t)h * P + kp * KS + SL * lg2);
-                const float cst = cs_ws[hl + t];
-                sc[c] = dB ? ((ssq[t] == seq_e) ? dt_ws[hl + t] * __expf(cse - cst) : 0.f)
-                           : ((ssq[t] == seq_refc) ? __expf(cst) : 0.f);
+                    for (int v = 0; v < V_GT; ++v) {
+                        const int idx = threadIdx.x + v * NTH;
+                        if (idx < N * (P / VEC)) rs[q][v] = *(const vt*)(src + (int64_t)idx * VEC);
+                    }
+                    const float cse = cs_ws[hl + Q - 1];
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        const int t = (c == 0 ? j0 : j1) * 16 + lr2;
+#pragma unroll
+                        for (int kp = 0; kp < KP; ++kp)
+                            rr[q][c][kp] = dB ? M::load(xc + (rb + t0 + t) * d.C + (int64_t)h * P + kp * KS + SL * lg2)
+                                              : M::load(dy + (rb + t0 + t) * HPd + (int64_t)h * P + kp * KS + SL * lg2);
+                        const float cst = cs_ws[hl + t];
+                        sc[q][c] = dB ? ((ssq[t] == seq_e) ? dt_ws[hl + t] * __expf(cse - cst) : 0.f)
+                                      : ((ssq[t] == seq_refc) ? __expf(cst) : 0.f);
+                    }
+                }
             }
-            __syncthreads();  // the previous head's products are done with sS
-            stage_state(sS, (dB ? gnp : hnp) + so);
+            __syncthreads();  // the previous round's products are done with sS
+#pragma unroll
+            for (int q = 0; q < HG; ++q) {
+                if (hf + q < hbs) {
+#pragma unroll
+                    for (int v = 0; v < V_GT; ++v) {
+                        const int idx = threadIdx.x + v * NTH;
+                        if (idx < N * (P / VEC)) {
+                            const int n = idx / (P / VEC), pv = idx % (P / VEC);
+                            *(vt*)&sS[q * N * PR + n * PR + pv * VEC] = rs[q][v];
+                        }
+                    }
+                }
+            }
             __syncthreads();
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
+            for (int q = 0; q < HG; ++q) {
+                if (hf + q < hbs) {
+                    const T* sq_ = sS + q * N * PR;
 #pragma unroll
-                for (int kp = 0; kp < KP; ++kp) {
-                    Frag sf;
+                    for (int c = 0; c < 2; ++c) {
 #pragma unroll
-                    for (int e = 0; e < SL; ++e) sf[e] = (E)((float)rr[c][kp][e] * sc[c]);
+                        for (int kp = 0; kp < KP; ++kp) {
+                            Frag sf;
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        ab[c][nt] = M::mma(M::load(&sS[(nt * 16 + lr2) * PR + kp * KS + SL * lg2]), sf,
-                                           ab[c][nt]);
+                            for (int e = 0; e < SL; ++e) sf[e] = (E)((float)rr[q][c][kp][e] * sc[q][c]);
+#pragma unroll
+                            for (int nt = 0; nt < NT; ++nt)
+                                ab[c][nt] = M::mma(M::load(&sq_[(nt * 16 + lr2) * PR + kp * KS + SL * lg2]),
+                                                   sf, ab[c][nt]);
+                        }
+                    }
                 }
             }
         }

@@ -19,7 +19,8 @@
 //   chunk phase (ssd_segment_bwd_chunks): k_chunk_bwd per chunk and head: dx,
 //     dB, dC and the ddt partial sums, written into the buffers the conv
 //     backward consumes.
-//   conv phase (ssd_conv1d_bwd): k_ddt (ddt per token), k_bc_headsum, k_conv_bwd
+//   conv phase (ssd_conv1d_bwd): k_ddt (ddt per token), k_bc_blocksum (dB, dC
+//     summed over head blocks), k_conv_bwd
 //     (SiLU' and the transposed conv, with a right halo from the causal
 //     successor segment) and k_bwd_reduce (deterministic parameter gradients).
 //
@@ -449,7 +450,7 @@ __global__ void __launch_bounds__(Q / (16 * TPW) * 64) k_chunk_bwd(
     const T* __restrict__ dy, const T* __restrict__ dyT, const float* __restrict__ Dp,
     const float* __restrict__ dt_ws, const float* __restrict__ cs_ws,
     const int32_t* __restrict__ seq, const T* __restrict__ gpn, const T* __restrict__ gnp,
-    const T* __restrict__ hnp, float* __restrict__ dv, T* __restrict__ dbc,
+    const T* __restrict__ hnp, T* __restrict__ dv, T* __restrict__ dbc,
     float* __restrict__ rpart, float* __restrict__ tokp, float* __restrict__ red4) {
     typedef ChunkBwd<T, P, N, Q, TPW> K;
     typedef Mma<T> M;
@@ -899,14 +900,15 @@ __global__ void __launch_bounds__(Q / (16 * TPW) * 64) k_chunk_bwd(
                 float xv[4], dyv[4];
                 load4(xc + trow * d.C + xoff + pt * 16 + 4 * lg, xv);
                 load4(dy + trow * HPd + xoff + pt * 16 + 4 * lg, dyv);
-                f32x4 o;
+                typedef T ot4 __attribute__((ext_vector_type(4)));
+                ot4 o;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     qp += xv[r] * adx[jt][pt][r];
-                    o[r] = dt_j[jt] * adx[jt][pt][r] + Dh * dyv[r];
+                    o[r] = (T)(dt_j[jt] * adx[jt][pt][r] + Dh * dyv[r]);
                     dD_part += dyv[r] * xv[r];
                 }
-                *(f32x4*)(dv + trow * d.C + xoff + pt * 16 + 4 * lg) = o;
+                *(ot4*)(dv + trow * HPd + xoff + pt * 16 + 4 * lg) = o;
             }
             q_t[jt] = sum_groups(qp);
         }
@@ -1186,36 +1188,32 @@ __global__ void __launch_bounds__(64) k_ddt(Dims d, SegTab tab,
 }
 
 // ---------------------------------------------------------------------------
-// dB and dC of a group are the sums of its heads' (or head blocks')
-// contributions, stored [token][nblk][2N] with the bpg blocks of group g at
-// g*bpg..; written into the B and C channels of dv (the conv output gradient),
-// coalesced along n.
+// dB and dC of a group are the sums of its head blocks' contributions
+// (dbc[token][nblk][2N], blocks of group g at g*bpg..) -> dbcs[token][G][2N].
 template <typename T>
-__global__ void __launch_bounds__(256) k_bc_headsum(Dims d, int nblk, int bpg,
-                                                   const T* __restrict__ dbc,
-                                                   float* __restrict__ dv) {
-    constexpr int VEC = 16 / sizeof(T);  // outputs per thread (one 16-byte load per head)
+__global__ void __launch_bounds__(256) k_bc_blocksum(Dims d, int nblk, int bpg,
+                                                    const T* __restrict__ dbc,
+                                                    T* __restrict__ dbcs) {
+    constexpr int VEC = 16 / sizeof(T);
     typedef T vt __attribute__((ext_vector_type(VEC)));
-    const int GN = d.G * d.N, nv = 2 * GN / VEC;
+    const int n2 = 2 * d.N, nv = d.G * n2 / VEC;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= d.batch * d.L * nv) return;
     const int64_t tok = idx / nv;
-    const int o = (int)(idx % nv) * VEC;
-    const int part = o / GN, gn = o % GN, g = gn / d.N, n = gn % d.N;
-    const T* src = dbc + (tok * nblk + (int64_t)g * bpg) * (2 * d.N) + part * d.N + n;
+    const int o = (int)(idx % nv) * VEC, g = o / n2, r = o % n2;
+    const T* src = dbc + (tok * nblk + (int64_t)g * bpg) * n2 + r;
     float acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-#pragma unroll 8
-    for (int hh = 0; hh < bpg; ++hh) {
-        const vt v = *(const vt*)(src + (int64_t)hh * 2 * d.N);
+    for (int q = 0; q < bpg; ++q) {
+        const vt v = *(const vt*)(src + (int64_t)q * n2);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[e] += (float)v[e];
     }
-    float* dst = dv + tok * d.C + (int64_t)d.H * d.P + o;
+    vt out;
 #pragma unroll
-    for (int q = 0; q < VEC / 4; ++q)
-        *(f32x4*)(dst + 4 * q) = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    for (int e = 0; e < VEC; ++e) out[e] = (T)acc[e];
+    *(vt*)(dbcs + tok * (d.G * n2) + o) = out;
 }
 
 // ---------------------------------------------------------------------------
@@ -1226,13 +1224,15 @@ __global__ void __launch_bounds__(256) k_bc_headsum(Dims d, int nblk, int bpg,
 // that follow) and d(conv output) for its tokens and the W-1 that follow in
 // causal order (the right halo, from the causal successor segment), all loaded
 // into registers; du is produced in causal order and the transposed conv
-// slides a W-row window over it.  dv holds the gradient of every conv output
-// channel.  dconv_w is written per 64-token block and reduced later.
+// slides a W-row window over it.  The gradient of a conv output channel is
+// read from dvx (x channels, [token][H*P]) or dbc (B and C channels,
+// [token][G][2N]).  dconv_w is written per 64-token block and reduced later.
 template <typename T, int W>
 __global__ void __launch_bounds__(256) k_conv_bwd(Dims d, SegTab tab, const T* __restrict__ xBC,
                                                  const float* __restrict__ w,
                                                  const int32_t* __restrict__ seq,
-                                                 const float* __restrict__ dvall,
+                                                 const T* __restrict__ dvx,
+                                                 const T* __restrict__ dbc,
                                                  T* __restrict__ dxBC, float* __restrict__ dwp) {
     constexpr int TPT = CONV_TPT;
     constexpr int RX = TPT + 2 * (W - 1);  // x rows: offsets -(W-1) .. TPT+W-2
@@ -1246,6 +1246,18 @@ __global__ void __launch_bounds__(256) k_conv_bwd(Dims d, SegTab tab, const T* _
     const int64_t rb = b * d.L;
     const bool active = c < d.C;
     const int k = conv_seg(tab, t0);
+    // where this thread's four channels take their output gradient from
+    const int64_t HP = (int64_t)d.H * d.P;
+    const bool xch = c < HP;
+    const int64_t GN2 = 2 * (int64_t)d.G * d.N;
+    const int64_t bco = xch ? 0 : [&] {
+        const int o = (int)(c - HP), part = o / (d.G * d.N), gn = o % (d.G * d.N);
+        return (int64_t)(gn / d.N) * 2 * d.N + part * d.N + gn % d.N;
+    }();
+    auto grad4 = [&](int64_t tok) {
+        const vt v = xch ? *(const vt*)(dvx + tok * HP + c) : *(const vt*)(dbc + tok * GN2 + bco);
+        return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    };
 
     float wr[4][W];
 #pragma unroll
@@ -1295,7 +1307,7 @@ __global__ void __launch_bounds__(256) k_conv_bwd(Dims d, SegTab tab, const T* _
         }
         float g[4] = {0.f, 0.f, 0.f, 0.f};
         if (mem[r] >= 0 && active) {
-            const f32x4 dv4 = *(const f32x4*)(dvall + (rb + mem[r]) * d.C + c);
+            const f32x4 dv4 = grad4(rb + mem[r]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float sg = 1.f / (1.f + __expf(-u[e]));
@@ -1421,7 +1433,7 @@ static bool hb_path(int Q) {
     if (Q == 256) return hb_fits<T, P, N, 256>();
     return false;
 }
-constexpr int HB_MAX = 4;  // heads per workgroup of the head-blocked kernel
+constexpr int HB_MAX = 8;  // heads per workgroup of the head-blocked kernel
 // heads per block: the largest divisor of the heads per group up to HB_MAX
 static int head_block(const Dims& d) {
     int hb = 1;
@@ -1451,7 +1463,7 @@ static void launch_chunk_bwd(const Dims& d, const SegTab& t, const BwdArgs& a, c
                            (const T*)(ws + L.bct), a.D, (const float*)(ws + L.dt),
                            (const float*)(ws + L.cs), a.seq, (const T*)(ws + L.gpn),
                            (const T*)(ws + L.gnp), (const T*)(ws + L.hpn), (const T*)(ws + L.hnp),
-                           (float*)(ws + L.dv), (T*)(ws + L.dbc), (float*)(ws + L.rpart),
+                           (T*)(ws + L.dv), (T*)(ws + L.dbc), (float*)(ws + L.rpart),
                            (float*)(ws + L.tokp), (float*)(ws + L.red4));
     } else if constexpr (chunk_bwd_fits<T, P, N, Q>()) {
         constexpr int TPW = chunk_bwd_tpw<T, Q>();
@@ -1461,31 +1473,33 @@ static void launch_chunk_bwd(const Dims& d, const SegTab& t, const BwdArgs& a, c
                            (const T*)(ws + L.bct), (const T*)a.dy, (const T*)(ws + L.dyT), a.D,
                            (const float*)(ws + L.dt), (const float*)(ws + L.cs), a.seq,
                            (const T*)(ws + L.gpn), (const T*)(ws + L.gnp), (const T*)(ws + L.hnp),
-                           (float*)(ws + L.dv), (T*)(ws + L.dbc), (float*)(ws + L.rpart),
+                           (T*)(ws + L.dv), (T*)(ws + L.dbc), (float*)(ws + L.rpart),
                            (float*)(ws + L.tokp), (float*)(ws + L.red4));
     }
 }
 
 template <typename T, int W>
 static void launch_conv_bwd_w(const Dims& d, const SegTab& t, const BwdArgs& a, const BwdWs& L,
-                              char* ws, hipStream_t s) {
+                              int hbs, char* ws, hipStream_t s) {
     dim3 grid((d.C + 255) / 256, (unsigned)(d.L / CONV_TT), (unsigned)d.batch);
+    // one head block per group: its partials are already [token][G][2N]
+    const T* dbc = (const T*)(ws + (d.hpg / hbs == 1 ? L.dbc : L.dbcs));
     hipLaunchKernelGGL((k_conv_bwd<T, W>), grid, dim3(256), 0, s, d, t, (const T*)a.xBC, a.conv_w,
-                       a.seq, (const float*)(ws + L.dv), (T*)a.dxBC, (float*)(ws + L.dwp));
+                       a.seq, (const T*)(ws + L.dv), dbc, (T*)a.dxBC, (float*)(ws + L.dwp));
 }
 
 template <typename T>
 static void launch_conv_bwd(const Dims& d, const SegTab& t, const BwdArgs& a, const BwdWs& L,
-                            char* ws, hipStream_t s) {
+                            int hbs, char* ws, hipStream_t s) {
     switch (d.W) {
-        case 1: launch_conv_bwd_w<T, 1>(d, t, a, L, ws, s); break;
-        case 2: launch_conv_bwd_w<T, 2>(d, t, a, L, ws, s); break;
-        case 3: launch_conv_bwd_w<T, 3>(d, t, a, L, ws, s); break;
-        case 4: launch_conv_bwd_w<T, 4>(d, t, a, L, ws, s); break;
-        case 5: launch_conv_bwd_w<T, 5>(d, t, a, L, ws, s); break;
-        case 6: launch_conv_bwd_w<T, 6>(d, t, a, L, ws, s); break;
-        case 7: launch_conv_bwd_w<T, 7>(d, t, a, L, ws, s); break;
-        default: launch_conv_bwd_w<T, 8>(d, t, a, L, ws, s); break;
+        case 1: launch_conv_bwd_w<T, 1>(d, t, a, L, hbs, ws, s); break;
+        case 2: launch_conv_bwd_w<T, 2>(d, t, a, L, hbs, ws, s); break;
+        case 3: launch_conv_bwd_w<T, 3>(d, t, a, L, hbs, ws, s); break;
+        case 4: launch_conv_bwd_w<T, 4>(d, t, a, L, hbs, ws, s); break;
+        case 5: launch_conv_bwd_w<T, 5>(d, t, a, L, hbs, ws, s); break;
+        case 6: launch_conv_bwd_w<T, 6>(d, t, a, L, hbs, ws, s); break;
+        case 7: launch_conv_bwd_w<T, 7>(d, t, a, L, hbs, ws, s); break;
+        default: launch_conv_bwd_w<T, 8>(d, t, a, L, hbs, ws, s); break;
     }
 }
 
@@ -1551,10 +1565,12 @@ static void conv_bwd_t(const Dims& d, const SegTab& t, const BwdArgs& a, int hbs
                        (const float*)(ws + L.rpart), (const float*)(ws + L.tokp),
                        (const float*)(ws + L.dotgh), (const float*)(ws + L.red4), (T*)a.ddt_raw,
                        (float*)(ws + L.red));
-    const int64_t nbc = d.batch * d.L * 2 * d.G * d.N / (16 / sizeof(T));
-    hipLaunchKernelGGL(k_bc_headsum<T>, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, d,
-                       d.H / hbs, d.hpg / hbs, (const T*)(ws + L.dbc), (float*)(ws + L.dv));
-    launch_conv_bwd<T>(d, t, a, L, ws, s);
+    if (d.hpg / hbs > 1) {
+        const int64_t nv = d.batch * d.L * d.G * 2 * d.N / (16 / sizeof(T));
+        hipLaunchKernelGGL(k_bc_blocksum<T>, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, s, d,
+                           d.H / hbs, d.hpg / hbs, (const T*)(ws + L.dbc), (T*)(ws + L.dbcs));
+    }
+    launch_conv_bwd<T>(d, t, a, L, hbs, ws, s);
     const int nout = d.C * d.W + 3 * d.H;
     hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)((nout + 31) / 32)), dim3(256), 0, s, d,
                        (const float*)(ws + L.dwp), (const float*)(ws + L.red), a.A_log, a.dconv_w,

@@ -235,8 +235,8 @@ inline FwdWs fwd_ws_layout(const Dims& d, int act) {
 // Backward workspace layout (byte offsets).  Filled by the summary phase
 // (xc, bct, dt, cs, ctot, zh, zg, dyT) and used by the segment phase.
 struct BwdWs {
-    size_t xc, bct, gramt, dt, cs, ctot, zh, zg, gpn, gnp, hnp, hpn, dyT, dv, dbc, rpart, tokp,
-        dotgh, red4, red, dwp, total;
+    size_t xc, bct, gramt, dt, cs, ctot, zh, zg, gpn, gnp, hnp, hpn, dyT, dv, dbc, dbcs, rpart,
+        tokp, dotgh, red4, red, dwp, total;
 };
 inline BwdWs bwd_ws_layout(const Dims& d, int act) {
     BwdWs w;
@@ -260,8 +260,9 @@ inline BwdWs bwd_ws_layout(const Dims& d, int act) {
     w.hnp = o;  o = align256(o + st * e);  // entering state per chunk, [n][p]
     w.hpn = o;  o = align256(o + st * e);  // the same, [p][n]
     w.dyT = o;  o = align256(o + bhl * d.P * e);  // dy per chunk and head, [p][token]
-    w.dv = o;   o = align256(o + BL * d.C * 4);  // d(conv output), every channel
+    w.dv = o;   o = align256(o + BL * d.H * d.P * e);  // d(conv output), x channels
     w.dbc = o;  o = align256(o + BL * d.H * 2 * d.N * e);  // dB, dC per head or head block
+    w.dbcs = o; o = align256(o + BL * d.G * 2 * d.N * e);  // the same, summed per group
     w.rpart = o; o = align256(o + bhl * 4);
     w.tokp = o; o = align256(o + bhl * 4 * 4);
     w.dotgh = o; o = align256(o + (size_t)d.batch * d.nchunk * d.H * 4);
