@@ -30,7 +30,8 @@
 // products, transposed reads (XT) of dy for dx; the Gram tiles come from L2 one
 // k step ahead of their use.  After the heads, Z goes to LDS as rows for dC,
 // the chunk's C^T and B^T are staged in turn for the Z products, and each
-// head's G^T and H^T for its state terms; dB is finished before dC starts.
+// head's G and H for its state terms (read transposed); dB is finished before
+// dC starts.
 #pragma once
 
 #include "bwd_util.h"
@@ -39,6 +40,24 @@
 #include "xt.h"
 
 namespace ssd {
+
+// A k operand of consecutive row elements (bf16: 32, float32: 16, from the
+// k-th block) in the k slot order of XT, so that it meets an XT read of the
+// other operand: bf16 slot s of lane group g holds element 16 (s / 4) + 4 g +
+// s % 4, float32 slot s holds 4 g + s.
+template <typename T> struct KPermRow;
+template <> struct KPermRow<bf16> {
+    __device__ static __forceinline__ bf16x8 load(const bf16* row, int lg) {
+        const bf16x4 lo = *(const bf16x4*)(row + 4 * lg);
+        const bf16x4 hi = *(const bf16x4*)(row + 16 + 4 * lg);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+template <> struct KPermRow<float> {
+    __device__ static __forceinline__ f32x4 load(const float* row, int lg) {
+        return *(const f32x4*)(row + 4 * lg);
+    }
+};
 
 template <typename T, int P, int N, int Q>
 struct ChunkBwdHB {
@@ -53,7 +72,6 @@ struct ChunkBwdHB {
     static constexpr int PT = P / 16, NT = N / 16, KP = P / KS, KN = N / KS;
     static constexpr int XR = P + VEC;  // x / dy rows [token][p]
     static constexpr int GR = N + VEC;  // G / H rows [p][n]
-    static constexpr int PR = P + VEC;  // G^T / H^T rows [n][p]
     static constexpr int TR = Q + VEC;  // B^T / C^T rows [n][token]
     // Z rows in LDS for dC: row tile a keeps columns [0, cw(a)) (whole k steps)
     __host__ __device__ static constexpr int cw(int a) { return KS * (a / TPK + 1); }
@@ -67,9 +85,9 @@ struct ChunkBwdHB {
     // head loop: x, dy, G, H of the head and the per-wave row sums
     static constexpr int O_D = Q * XR, O_G = 2 * Q * XR, O_H = O_G + P * GR, O_RW = O_H + P * GR;
     static constexpr int E_HEAD = O_RW + NW * Q * 4 / (int)sizeof(T);
-    // final phase: Z rows and C^T (then G^T of HG heads), later B^T and H^T
+    // final phase: Z rows and C^T (then G of HG heads), later B^T and H
     static constexpr int HG = 4;  // heads per round of state terms
-    static constexpr int O_BT = zoff(QT), E_FIN = O_BT + N * TR, E_FS = O_BT + HG * N * PR;
+    static constexpr int O_BT = zoff(QT), E_FIN = O_BT + N * TR, E_FS = O_BT + HG * P * GR;
     static constexpr int E_U = cmax(E_HEAD, cmax(E_FIN, E_FS));
     static constexpr size_t LDS =
         (size_t)E_U * sizeof(T) + (size_t)Q * 20 + (size_t)QT * QT * 4 + (size_t)NW * 4 + 64;
@@ -81,8 +99,8 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
     Dims d, SegTab tab, int hbs, const T* __restrict__ xc, const T* __restrict__ dy,
     const T* __restrict__ gramT, const T* __restrict__ bct, const float* __restrict__ Dp,
     const float* __restrict__ dt_ws, const float* __restrict__ cs_ws,
-    const int32_t* __restrict__ seq, const T* __restrict__ gpn, const T* __restrict__ gnp,
-    const T* __restrict__ hpn, const T* __restrict__ hnp, T* __restrict__ dv,
+    const int32_t* __restrict__ seq, const T* __restrict__ gpn, const T* __restrict__ hpn,
+    T* __restrict__ dv,
     T* __restrict__ dbcp, float* __restrict__ rpart, float* __restrict__ tokp,
     float* __restrict__ red4) {
     typedef ChunkBwdHB<T, P, N, Q> K;
@@ -102,7 +120,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
     float* const s_rw = (float*)(U + K::O_RW);  // per-wave row sums of F [NW][Q]
     T* const sZ = U;                            // final phase: Z rows, strip per row tile
     T* const sBT = U + K::O_BT;                 // final phase: C^T, then B^T [N][TR]
-    constexpr int GR = K::GR, PR = K::PR, TR = K::TR;
+    constexpr int GR = K::GR, TR = K::TR;
     __shared__ __attribute__((aligned(16))) float scs[Q];
     __shared__ __attribute__((aligned(16))) float sdt[Q];
     __shared__ __attribute__((aligned(16))) float sea[Q];  // exp(cs_t - F(t))
@@ -495,10 +513,11 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
         }
     };
     // the state terms of one part over the heads: ab[c] += S^T (scaled rows of
-    // tile c), S^T = G^T (dB, rows of x scaled by dt g) or H^T (dC, rows of dy
-    // scaled by f); HG heads per round, their S^T staged at sS
+    // tile c), S = G (dB, rows of x scaled by dt g) or H (dC, rows of dy scaled
+    // by f); HG heads per round, their S staged at sS as [p][n] rows and read
+    // transposed (XT), the rows in the matching k order
     constexpr int HG = K::HG;
-    constexpr int V_GT = (N * (P / VEC) + NTH - 1) / NTH;
+    constexpr int V_GT = (P * (N / VEC) + NTH - 1) / NTH;
     auto state_terms = [&](bool dB, T* sS) {
         for (int hf = 0; hf < hbs; hf += HG) {
             vt rs[HG][V_GT];
@@ -509,11 +528,11 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
                 if (hf + q < hbs) {
                     const int h = h0 + hf + q;
                     const int64_t hl = hl_of(h), so = st_of(h);
-                    const T* src = (dB ? gnp : hnp) + so;
+                    const T* src = (dB ? gpn : hpn) + so;
 #pragma unroll
                     for (int v = 0; v < V_GT; ++v) {
                         const int idx = threadIdx.x + v * NTH;
-                        if (idx < N * (P / VEC)) rs[q][v] = *(const vt*)(src + (int64_t)idx * VEC);
+                        if (idx < P * (N / VEC)) rs[q][v] = *(const vt*)(src + (int64_t)idx * VEC);
                     }
                     const float cse = cs_ws[hl + Q - 1];
 #pragma unroll
@@ -521,8 +540,8 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
                         const int t = (c == 0 ? j0 : j1) * 16 + lr2;
 #pragma unroll
                         for (int kp = 0; kp < KP; ++kp)
-                            rr[q][c][kp] = dB ? M::load(xc + (rb + t0 + t) * d.C + (int64_t)h * P + kp * KS + SL * lg2)
-                                              : M::load(dy + (rb + t0 + t) * HPd + (int64_t)h * P + kp * KS + SL * lg2);
+                            rr[q][c][kp] = dB ? KPermRow<T>::load(xc + (rb + t0 + t) * d.C + (int64_t)h * P + kp * KS, lg2)
+                                              : KPermRow<T>::load(dy + (rb + t0 + t) * HPd + (int64_t)h * P + kp * KS, lg2);
                         const float cst = cs_ws[hl + t];
                         sc[q][c] = dB ? ((ssq[t] == seq_e) ? dt_ws[hl + t] * __expf(cse - cst) : 0.f)
                                       : ((ssq[t] == seq_refc) ? __expf(cst) : 0.f);
@@ -536,9 +555,9 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
 #pragma unroll
                     for (int v = 0; v < V_GT; ++v) {
                         const int idx = threadIdx.x + v * NTH;
-                        if (idx < N * (P / VEC)) {
-                            const int n = idx / (P / VEC), pv = idx % (P / VEC);
-                            *(vt*)&sS[q * N * PR + n * PR + pv * VEC] = rs[q][v];
+                        if (idx < P * (N / VEC)) {
+                            const int p = idx / (N / VEC), nv = idx % (N / VEC);
+                            *(vt*)&sS[q * P * GR + p * GR + nv * VEC] = rs[q][v];
                         }
                     }
                 }
@@ -547,7 +566,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
 #pragma unroll
             for (int q = 0; q < HG; ++q) {
                 if (hf + q < hbs) {
-                    const T* sq_ = sS + q * N * PR;
+                    const T* sq_ = sS + q * P * GR;
 #pragma unroll
                     for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -557,8 +576,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
                             for (int e = 0; e < SL; ++e) sf[e] = (E)((float)rr[q][c][kp][e] * sc[q][c]);
 #pragma unroll
                             for (int nt = 0; nt < NT; ++nt)
-                                ab[c][nt] = M::mma(M::load(&sq_[(nt * 16 + lr2) * PR + kp * KS + SL * lg2]),
-                                                   sf, ab[c][nt]);
+                                ab[c][nt] = M::mma(XT<T>::load(sq_, GR, kp * KS, nt * 16, lane2), sf, ab[c][nt]);
                         }
                     }
                 }

@@ -40,6 +40,7 @@
 #include "chunk_bwd.h"
 #include "gram.h"
 #include "ssd_internal.h"
+#include "xt.h"
 
 namespace ssd {
 
@@ -117,8 +118,8 @@ __global__ void __launch_bounds__(256) k_bc_transpose(Dims d, const T* __restric
 //          chunk adds to the state leaving it),
 //   Zg_c = sum_i exp(cs_i) [seq_i = seq of the entering state] dy_i C_i^T
 //          (the gradient its outputs send to the state entering it),
-// both P x N in FP32, and the chunk's dy transposed to [p][token] (permuted
-// token order) for the chunk kernel.
+// both P x N in FP32, and (for the per-head chunk kernel only) the chunk's dy
+// transposed to [p][token] in the permuted token order.
 template <typename T, int P, int N>
 __global__ void __launch_bounds__(256) k_bwd_chunk_states(
     Dims d, SegTab tab, const T* __restrict__ xc, const T* __restrict__ bct,
@@ -127,13 +128,15 @@ __global__ void __launch_bounds__(256) k_bwd_chunk_states(
     T* __restrict__ dyT) {
     typedef Mma<T> M;
     typedef typename M::Frag Frag;
-    constexpr int SL = M::SL, KS = M::KS;
+    constexpr int SL = M::SL, KS = M::KS, TPK = KS / 16;
     constexpr int KT = 64;               // tokens per LDS slice
     constexpr int VEC = 16 / sizeof(T);
-    constexpr int PITCH = KT + VEC;
+    constexpr int XR = P + VEC;          // [token][p] row pitch
     constexpr int PT = P / 16, NT = N / 16, NTW = (NT + 3) / 4;
-    __shared__ __attribute__((aligned(16))) T sX[P * PITCH];
-    __shared__ __attribute__((aligned(16))) T sY[P * PITCH];
+    // x rows scaled by their state weight, and dy rows, natural layout; the MFMA
+    // A operands (k = token) come from transposed reads (XT)
+    __shared__ __attribute__((aligned(16))) T sX[KT * XR];
+    __shared__ __attribute__((aligned(16))) T sY[KT * XR];
     __shared__ __attribute__((aligned(16))) float wz[KT];
     typedef T vt __attribute__((ext_vector_type(VEC)));
 
@@ -154,7 +157,6 @@ __global__ void __launch_bounds__(256) k_bwd_chunk_states(
     const float cs_e = cs_ws[hl + Q - 1];
     const T* bctB = bct + ((((int64_t)b * d.nchunk + cm) * d.G + g) * 2) * (int64_t)N * Q;
     const T* bctC = bctB + (int64_t)N * Q;
-    T* yT = dyT + (((int64_t)b * d.nchunk + cm) * d.H + h) * (int64_t)P * Q;
 
     f32x4 ah[PT][NTW], ag[PT][NTW];
 #pragma unroll
@@ -165,49 +167,50 @@ __global__ void __launch_bounds__(256) k_bwd_chunk_states(
     for (int sl = 0; sl < Q / KT; ++sl) {
         const int tb = sl * KT;
         __syncthreads();
-        // token-fastest mapping: the transposed LDS stores of a wave hit
-        // consecutive 16-bit positions of one row
         for (int idx = threadIdx.x; idx < KT * (P / VEC); idx += blockDim.x) {
-            const int pv = idx / KT, jj = idx % KT;
+            const int jj = idx / (P / VEC), pv = idx % (P / VEC);
             const int64_t tok = rb + t0 + tb + jj;
             const bool same = !seq || seq[tok] == seq_e;
             const float w = same ? __expf(cs_e - cs_ws[hl + tb + jj]) * dt_ws[hl + tb + jj] : 0.f;
             const vt xv = *(const vt*)(xc + tok * d.C + (int64_t)h * P + pv * VEC);
-            const vt yv = *(const vt*)(dy + tok * HPd + (int64_t)h * P + pv * VEC);
-            const int q = tpos<T>(jj);
+            vt xs;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                sX[(pv * VEC + e) * PITCH + q] = (T)((float)xv[e] * w);
-                sY[(pv * VEC + e) * PITCH + q] = yv[e];
-            }
+            for (int e = 0; e < VEC; ++e) xs[e] = (T)((float)xv[e] * w);
+            *(vt*)&sX[jj * XR + pv * VEC] = xs;
+            *(vt*)&sY[jj * XR + pv * VEC] = *(const vt*)(dy + tok * HPd + (int64_t)h * P + pv * VEC);
         }
         if (threadIdx.x < KT) {
             const int jj = threadIdx.x;
             const bool same = !seq || seq[rb + t0 + tb + jj] == seq_ref;
-            wz[tpos<T>(jj)] = same ? __expf(cs_ws[hl + tb + jj]) : 0.f;
+            wz[jj] = same ? __expf(cs_ws[hl + tb + jj]) : 0.f;
         }
         __syncthreads();
-        for (int idx = threadIdx.x; idx < P * (KT / VEC); idx += blockDim.x) {
-            const int p = idx / (KT / VEC), v = idx % (KT / VEC);
-            *(vt*)(yT + (int64_t)p * Q + tb + v * VEC) = *(const vt*)(sY + p * PITCH + v * VEC);
+        if (dyT) {  // dy as [p][token] in the permuted token order (per-head chunk kernel)
+            T* yT = dyT + (((int64_t)b * d.nchunk + cm) * d.H + h) * (int64_t)P * Q;
+            for (int idx = threadIdx.x; idx < P * KT; idx += blockDim.x) {
+                const int p = idx / KT, jj = idx % KT;
+                yT[(int64_t)p * Q + tb + tpos<T>(jj)] = sY[jj * XR + p];
+            }
         }
 #pragma unroll
         for (int kk = 0; kk < KT / KS; ++kk) {
-            const int jl = kk * KS + SL * lg;
+            const int jb = kk * KS;
             Frag ax[PT], ay[PT];
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                ax[pt] = M::load(&sX[(pt * 16 + lr) * PITCH + jl]);
-                ay[pt] = M::load(&sY[(pt * 16 + lr) * PITCH + jl]);
+                ax[pt] = XT<T>::load(sX, XR, jb, pt * 16, lane);
+                ay[pt] = XT<T>::load(sY, XR, jb, pt * 16, lane);
             }
+            // weight of k slot s: the token XT puts there
             float wl[SL];
 #pragma unroll
-            for (int s = 0; s < SL; ++s) wl[s] = wz[jl + s];
+            for (int s2 = 0; s2 < SL; ++s2)
+                wl[s2] = wz[jb + (TPK == 2 ? 16 * (s2 / 4) + 4 * lg + s2 % 4 : 4 * lg + s2)];
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 const int nt = wave + 4 * j;
                 if (nt < NT) {
-                    const int64_t o = (int64_t)(nt * 16 + lr) * Q + tb + jl;
+                    const int64_t o = (int64_t)(nt * 16 + lr) * Q + tb + jb + SL * lg;
                     const Frag bB = M::load(bctB + o);
                     const Frag bC = M::load_scaled(bctC + o, wl);
 #pragma unroll
@@ -245,9 +248,10 @@ __global__ void __launch_bounds__(256) k_bwd_chunk_states(
 //   PASS_SUMMARY: G <- alpha_c G + Zg_c from the last chunk with zero final
 //                 gradient; leaves L_k (dL/dS_in of the segment's own outputs)
 //                 and a_k = prod alpha_c in the summary layout.
-//   PASS_TRUE:    G from dS_out backwards, storing every G_c as [p][n] and
-//                 [n][p]; then H from S_in forwards, storing every H_c as
-//                 [n][p] and <G_c, H_c> per chunk.
+//   PASS_TRUE:    G from dS_out backwards, storing every G_c as [p][n] (and
+//                 [n][p] if gnp is given); then H from S_in forwards, storing
+//                 every H_c as [p][n] and / or [n][p] (whichever of hpn, hnp
+//                 is given) and <G_c, H_c> per chunk.
 enum PassMode { PASS_SUMMARY = 0, PASS_TRUE = 1 };
 
 template <typename T, int P, int N, int MODE>
@@ -303,20 +307,24 @@ __global__ void __launch_bounds__(256) k_state_pass(
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = (T)acc[q][e];
                     *(vt4*)(gpn + so + 4 * i4) = v;
-                    const int p = (4 * i4) / N, n = (4 * i4) % N;
+                    if (gnp) {
+                        const int p = (4 * i4) / N, n = (4 * i4) % N;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) tile[p * TP + n + e] = acc[q][e];
+                        for (int e = 0; e < 4; ++e) tile[p * TP + n + e] = acc[q][e];
+                    }
                 }
             }
-            __syncthreads();
-            for (int idx = threadIdx.x; idx < N * (P / VEC); idx += 256) {
-                const int n = idx / (P / VEC), p0 = (idx % (P / VEC)) * VEC;
-                vt v;
+            if (gnp) {
+                __syncthreads();
+                for (int idx = threadIdx.x; idx < N * (P / VEC); idx += 256) {
+                    const int n = idx / (P / VEC), p0 = (idx % (P / VEC)) * VEC;
+                    vt v;
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) v[e] = (T)tile[(p0 + e) * TP + n];
-                *(vt*)(gnp + so + (int64_t)n * P + p0) = v;
+                    for (int e = 0; e < VEC; ++e) v[e] = (T)tile[(p0 + e) * TP + n];
+                    *(vt*)(gnp + so + (int64_t)n * P + p0) = v;
+                }
+                __syncthreads();
             }
-            __syncthreads();
         }
         const float a = alpha_of(c);
         ablk *= a;
@@ -361,7 +369,7 @@ __global__ void __launch_bounds__(256) k_state_pass(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     dot += (float)gv[e] * acc[q][e];
-                    tile[p * TP + n + e] = acc[q][e];
+                    if (hnp) tile[p * TP + n + e] = acc[q][e];
                     hv[e] = (T)acc[q][e];
                 }
                 if (hpn) *(vt4*)(hpn + so + 4 * i4) = hv;
@@ -371,12 +379,14 @@ __global__ void __launch_bounds__(256) k_state_pass(
         for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
         if (lane == 0) sred[wave] = dot;
         __syncthreads();
-        for (int idx = threadIdx.x; idx < N * (P / VEC); idx += 256) {
-            const int n = idx / (P / VEC), p0 = (idx % (P / VEC)) * VEC;
-            vt v;
+        if (hnp) {
+            for (int idx = threadIdx.x; idx < N * (P / VEC); idx += 256) {
+                const int n = idx / (P / VEC), p0 = (idx % (P / VEC)) * VEC;
+                vt v;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) v[e] = (T)tile[(p0 + e) * TP + n];
-            *(vt*)(hnp + so + (int64_t)n * P + p0) = v;
+                for (int e = 0; e < VEC; ++e) v[e] = (T)tile[(p0 + e) * TP + n];
+                *(vt*)(hnp + so + (int64_t)n * P + p0) = v;
+            }
         }
         if (threadIdx.x == 0)
             dotgh[((int64_t)b * d.nchunk + cm0 + c) * d.H + h] = sred[0] + sred[1] + sred[2] + sred[3];
@@ -1462,8 +1472,8 @@ static void launch_chunk_bwd(const Dims& d, const SegTab& t, const BwdArgs& a, c
                            (const T*)(ws + L.xc), (const T*)a.dy, (const T*)(ws + L.gramt),
                            (const T*)(ws + L.bct), a.D, (const float*)(ws + L.dt),
                            (const float*)(ws + L.cs), a.seq, (const T*)(ws + L.gpn),
-                           (const T*)(ws + L.gnp), (const T*)(ws + L.hpn), (const T*)(ws + L.hnp),
-                           (T*)(ws + L.dv), (T*)(ws + L.dbc), (float*)(ws + L.rpart),
+                           (const T*)(ws + L.hpn), (T*)(ws + L.dv), (T*)(ws + L.dbc),
+                           (float*)(ws + L.rpart),
                            (float*)(ws + L.tokp), (float*)(ws + L.red4));
     } else if constexpr (chunk_bwd_fits<T, P, N, Q>()) {
         constexpr int TPW = chunk_bwd_tpw<T, Q>();
@@ -1520,7 +1530,8 @@ static void bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a, floa
     hipLaunchKernelGGL((k_bwd_chunk_states<T, P, N>), chunk_head_grid(d), dim3(256), 0, s,
                        d, t, (const T*)xc, (const T*)(ws + L.bct), (const T*)a.dy,
                        (const float*)(ws + L.dt), (const float*)(ws + L.cs), a.seq,
-                       (float*)(ws + L.zh), (float*)(ws + L.zg), (T*)(ws + L.dyT));
+                       (float*)(ws + L.zh), (float*)(ws + L.zg),
+                       hb_path<T, P, N>(d.Q) ? (T*)nullptr : (T*)(ws + L.dyT));
     hipLaunchKernelGGL((k_state_pass<T, P, N, PASS_SUMMARY>),
                        dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0, s,
                        d, t, (const float*)(ws + L.ctot), a.seq, (const float*)(ws + L.zg),
@@ -1531,14 +1542,17 @@ static void bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a, floa
 template <typename T, int P, int N>
 static void bwd_pass_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* ws_,
                        hipStream_t s) {
+    // the head-blocked chunk kernel reads G and H as [p][n] only; the per-head
+    // one reads G as [p][n] and [n][p] and H as [n][p]
+    const bool hb = hb_path<T, P, N>(d.Q);
     const BwdWs L = bwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
     char* ws = (char*)ws_;
     hipLaunchKernelGGL((k_state_pass<T, P, N, PASS_TRUE>),
                        dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0, s,
                        d, t, (const float*)(ws + L.ctot), a.seq, (const float*)(ws + L.zg),
                        (const float*)(ws + L.zh), a.S_in, a.dS_out, (float*)nullptr,
-                       (T*)(ws + L.gpn), (T*)(ws + L.gnp), (T*)(ws + L.hnp),
-                       hb_path<T, P, N>(d.Q) ? (T*)(ws + L.hpn) : (T*)nullptr,
+                       (T*)(ws + L.gpn), hb ? (T*)nullptr : (T*)(ws + L.gnp),
+                       hb ? (T*)nullptr : (T*)(ws + L.hnp), hb ? (T*)(ws + L.hpn) : (T*)nullptr,
                        (float*)(ws + L.dotgh));
 }
 
