@@ -154,6 +154,15 @@ def measured_traffic(workload, kernel):
     return hits[0]["hbm_bytes"] if len(hits) == 1 else None
 
 
+def head_block(wl):
+    """Heads per workgroup of the head-blocked chunk backward (largest divisor of the
+    heads per group up to 8); 1 when the per-head kernel runs (headdim above 64)."""
+    if wl.headdim > 64:
+        return 1
+    hpg = wl.nheads // wl.ngroups
+    return max(c for c in range(1, 9) if hpg % c == 0)
+
+
 def algorithmic_bytes(wl):
     """Bytes each call must move at minimum: its own inputs and outputs, with every
     workspace intermediate counted once where one pass writes it and another reads
@@ -176,6 +185,9 @@ def algorithmic_bytes(wl):
     dtcs = 2 * BL * H * 4
     dy = BL * H * P * e
     x, bc = BL * H * P * e, BL * 2 * G * N * e
+    nhb = H // head_block(wl)
+    dbc_part = BL * nhb * 2 * N * e  # dB, dC per head block
+    tokp = 5 * BL * H * 4            # per-token ddt partial sums
     return {
         "ssd_conv1d_fwd": 2 * BL * C * e + C * wl.conv_width * 4 + seq,
         # dt prep (dt_raw in, dt and cumsum out), the walk (x, B in; entering states and
@@ -186,21 +198,23 @@ def algorithmic_bytes(wl):
         "ssd_segment_output_fused": x + bc // 2 + gram + hst + states + dtcs + x + seq,
         "ssd_segment_output": x + bc // 2 + gram + hst + dtcs + BL * H * P * 4 + seq,
         "ssd_apply_init_state": BL * H * P * 4 + x + bc // 2 + BL * H * 4 + states + x + seq,
-        # conv recompute, dt prep, chunk contributions to state and state gradient
-        # (FP32 out), the summary walk
-        "ssd_segment_bwd_summary": BL * C * e + BL * C * e + BL * H * e + dtcs + x + dy + bc
-                                   + 2 * st_all * 4 + summary + seq,
+        # conv recompute (xBC in, conv output out), dt prep, the transposed Gram tiles,
+        # every chunk's contributions to the state and its gradient (x, B, C, dy in;
+        # FP32 out), the summary walk
+        "ssd_segment_bwd_summary": BL * C * e + BL * C * e + BL * H * e + dtcs + bc + gram
+                                   + x + dy + 2 * st_all * 4 + summary + seq,
         "ssd_boundary_scan(reverse)": summary + states,
-        # chunk contributions and the two boundary states in; entering state and exit
-        # gradient per chunk out
+        # chunk contributions and the two boundary states in; exit gradient and
+        # entering state of every chunk out
         "ssd_segment_bwd_pass": 2 * st_all * 4 + 2 * states + 2 * st_all * e,
-        # x, B, C, dy, decays, entering state and exit gradient per chunk in; dx (FP32),
-        # dB and dC (FP32, summed over heads), per-token d(dt) partials out
-        "ssd_segment_bwd_chunks": BL * C * e + dy + dtcs + 2 * st_all * e + BL * H * P * 4
-                                  + BL * 2 * G * N * 4 + BL * H * 4 * 4 + seq,
-        # xBC and d(conv output) in, dxBC out; d(dt) partials and dt_raw in, ddt_raw out
-        "ssd_conv1d_bwd": BL * C * e + BL * C * 4 + BL * C * e + BL * H * 4 * 4 + 2 * BL * H * e
-                          + seq,
+        # x, B, C, dy, decays, exit gradient and entering state per chunk, Gram tiles
+        # in; d(conv output) of x, dB and dC per head block, ddt partial sums out
+        "ssd_segment_bwd_chunks": BL * C * e + dy + dtcs + 2 * st_all * e + gram + x
+                                  + dbc_part + tokp + seq,
+        # ddt partials and dt_raw in, ddt_raw out; dB / dC partials summed per group;
+        # xBC and d(conv output) in, dxBC out
+        "ssd_conv1d_bwd": tokp + 2 * BL * H * e + dbc_part + bc + BL * C * e + x + bc
+                          + BL * C * e + seq,
     }
 
 
@@ -212,12 +226,15 @@ def output_flops(wl):
 
 
 def chunk_bwd_flops(wl):
-    """MFMA flops of ssd_segment_bwd_chunks: C B^T, dy x^T (twice), their products with
-    dy, C and B, and the three entering/exit-state products (causal pairs only)."""
+    """MFMA flops of ssd_segment_bwd_chunks over causal pairs only: per head dy x^T and
+    its weighted product with dy (dx), the four state products (G B, H C, G^T x,
+    H^T dy); per head block the products of the head-summed weights with C (dB) and
+    B (dC)."""
     b, L, H, P, N, Q = wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.chunk
     pairs = Q * (Q + 1) // 2
-    per_chunk_head = 2 * pairs * (3 * N + 3 * P) + 6 * Q * P * N
-    return b * (L // Q) * H * per_chunk_head
+    per_head = 2 * pairs * 2 * P + 4 * 2 * Q * P * N
+    per_block = 2 * pairs * 2 * N
+    return b * (L // Q) * (H * per_head + H // head_block(wl) * per_block)
 
 
 def cpu_baseline(wl, runs, backward):
