@@ -1,38 +1,31 @@
-// Per-segment walk of chunk states (forward) or state gradients (backward).
+// Per-segment walk of chunk states (forward).
 //
 // One workgroup per (row, segment, head) visits the segment's chunks in causal
-// order (forward) or reverse causal order (backward).  The running P x N matrix
-// lives in MFMA accumulators (FP32).  For every chunk it first stores the
-// running value, then applies the chunk's decay alpha_c = exp(cs_end) (exactly
-// 0 when a packed sequence starts inside the chunk) and accumulates the chunk's
-// own contribution A^T diag(w) B with MFMA:
+// order.  The running P x N state lives in MFMA accumulators (FP32).  For every
+// chunk it first stores the running value (the state entering the chunk, zero
+// initial state), then applies the chunk's decay alpha_c = exp(cs_end)
+// (exactly 0 when a packed sequence starts inside the chunk) and accumulates
+// the chunk's own contribution x^T diag(w) B with MFMA,
+//   w_j = exp(cs_end - cs_j) dt_j [seq_j = seq_end].
+// The final value is the segment's S_ext and the product of the alphas its
+// block decay a_block.  This is the decay-weighted sum over earlier chunk
+// states that state-spaces/mamba #482 (second comment) identifies as the part
+// of the scan that must cross devices; Megatron-LM #6808 ships its
+// segment-level result as the FP32 summary.
 //
-//   forward : A = x, B = B channels, w_j = exp(cs_end - cs_j) dt_j [seq_j = seq_end]
-//             stored value = state entering the chunk (zero initial state),
-//             final value = the segment's S_ext.
-//   backward: A = dy, B = C channels, w_i = exp(cs_i) [seq_i = seq of the state
-//             entering the chunk]; walked from the last chunk, the stored value is
-//             the gradient of the state leaving the chunk (zero final-state
-//             gradient) and the final value is dL/dS_in of the segment's own
-//             outputs.
-//
-// The product of the alphas is the segment's block decay a_block in both
-// directions.  This is the decay-weighted sum over earlier chunk states that
-// state-spaces/mamba #482 (second comment) identifies as the part of the scan
-// that must cross devices; Megatron-LM #6808 ships its segment-level result as
-// the FP32 summary.
+// The chunk is read in 64-token slices: x rows (scaled by w) and B rows go to
+// LDS in their natural [token][.] layout and both MFMA operands come from
+// transposed LDS reads (XT); the next slice is loaded into registers while the
+// current one is multiplied.
 #pragma once
 
 #include "ssd_internal.h"
+#include "xt.h"
 
 namespace ssd {
 
-enum WalkMode { WALK_FWD_PN = 0, WALK_FWD_NP = 1, WALK_BWD_PN = 2 };
-
-template <typename T, int P, int N, int MODE>
-__global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T* __restrict__ a_src,
-                                                   int64_t a_stride, const T* __restrict__ xc,
-                                                   int64_t b_chan0,
+template <typename T, int P, int N>
+__global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T* __restrict__ xc,
                                                    const float* __restrict__ dt_ws,
                                                    const float* __restrict__ cs_ws,
                                                    const int32_t* __restrict__ seq,
@@ -40,15 +33,16 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
                                                    float* __restrict__ summary) {
     typedef Mma<T> M;
     typedef typename M::Frag Frag;
-    constexpr int SL = M::SL, KS = M::KS;
+    constexpr int KS = M::KS;
     constexpr int KT = 64;               // tokens per LDS slice
+    constexpr int NTH = 256;
     constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
-    constexpr int PITCH = KT + VEC;      // padded LDS row (keeps 16-byte alignment)
+    constexpr int XR = P + VEC, BR = N + VEC;
     constexpr int PT = P / 16, NTT = N / 16, NTW = (NTT + 3) / 4;
-    constexpr bool BWD = MODE == WALK_BWD_PN;
-    __shared__ __attribute__((aligned(16))) T At[P * PITCH];
-    __shared__ __attribute__((aligned(16))) T Bt[N * PITCH];
-    __shared__ float wv[KT];
+    constexpr int VX = (KT * (P / VEC) + NTH - 1) / NTH;  // x vectors per thread and slice
+    constexpr int VB = (KT * (N / VEC) + NTH - 1) / NTH;  // B vectors per thread and slice
+    __shared__ __attribute__((aligned(16))) T sX[KT * XR];
+    __shared__ __attribute__((aligned(16))) T sB[KT * BR];
     typedef T vt __attribute__((ext_vector_type(VEC)));
 
     const int h = blockIdx.x, k = blockIdx.y;
@@ -59,11 +53,62 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
     const int64_t rb = b * d.L;
     const int64_t s0 = tab.start[k];
     const int nc = (int)(tab.len[k] / Q);
+    const int spc = Q / KT;  // slices per chunk
+    const int ns = nc * spc;
     const int64_t pred = seg_pred_token(tab, k);
     const float* dtp = dt_ws + ((int64_t)b * d.H + h) * d.L;
     const float* csp = cs_ws + ((int64_t)b * d.H + h) * d.L;
-    const T* arow = a_src + rb * a_stride + (int64_t)h * P;
-    const T* brow = xc + rb * d.C + b_chan0 + (int64_t)g * N;
+    const T* xrow = xc + rb * d.C + (int64_t)h * P;
+    const T* brow = xc + rb * d.C + (int64_t)d.H * P + (int64_t)g * N;
+
+    // ---- one slice: registers, then LDS (x scaled by its token's weight)
+    vt rx[VX], rbv[VB];
+    float rcs[VX], rdt[VX];
+    int rsq[VX];
+    auto fetch = [&](int si) {
+        const int64_t tb = s0 + (int64_t)si * KT;
+#pragma unroll
+        for (int q = 0; q < VX; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (idx < KT * (P / VEC)) {
+                const int jj = idx / (P / VEC), pv = idx % (P / VEC);
+                rx[q] = *(const vt*)(xrow + (tb + jj) * d.C + pv * VEC);
+                rcs[q] = csp[tb + jj];
+                rdt[q] = dtp[tb + jj];
+                rsq[q] = seq ? seq[rb + tb + jj] : 0;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < VB; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (idx < KT * (N / VEC)) {
+                const int jj = idx / (N / VEC), nv = idx % (N / VEC);
+                rbv[q] = *(const vt*)(brow + (tb + jj) * d.C + nv * VEC);
+            }
+        }
+    };
+    auto stash = [&](float cs_e, int seq_e) {
+#pragma unroll
+        for (int q = 0; q < VX; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (idx < KT * (P / VEC)) {
+                const int jj = idx / (P / VEC), pv = idx % (P / VEC);
+                const float w = (rsq[q] == seq_e) ? __expf(cs_e - rcs[q]) * rdt[q] : 0.f;
+                vt v;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) v[e] = (T)((float)rx[q][e] * w);
+                *(vt*)&sX[jj * XR + pv * VEC] = v;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < VB; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (idx < KT * (N / VEC)) {
+                const int jj = idx / (N / VEC), nv = idx % (N / VEC);
+                *(vt*)&sB[jj * BR + nv * VEC] = rbv[q];
+            }
+        }
+    };
 
     f32x4 acc[PT][NTW];
 #pragma unroll
@@ -71,89 +116,61 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
 #pragma unroll
         for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     float ablk = 1.f;
+    float cs_e = 0.f;
+    int seq_e = 0;
 
-    for (int step = 0; step < nc; ++step) {
-        const int c = BWD ? nc - 1 - step : step;
-        const int64_t t0 = s0 + (int64_t)c * Q;
-        const int cm = (int)(t0 / Q);
-        const float cs_e = csp[t0 + Q - 1];
-        const int seq_e = seq ? seq[rb + t0 + Q - 1] : 0;
-        // The state entering chunk c belongs to the sequence of the token just
-        // before it; for a row's first segment that is the sequence of the
-        // row's first token (an initial state feeds the first sequence).
-        const int64_t ptok = c > 0 ? t0 - 1 : (pred >= 0 ? pred : s0);
-        const int seq_ref = seq ? seq[rb + ptok] : 0;
-        const float alpha = (seq_ref == seq_e) ? expf(cs_e) : 0.f;
-        ablk *= alpha;
-        if (step > 0) {
-            T* hp = store + (((int64_t)b * d.nchunk + cm) * d.H + h) * (P * N);
+    fetch(0);
+    for (int si = 0; si < ns; ++si) {
+        const int c = si / spc;
+        if (si % spc == 0) {
+            const int64_t t0 = s0 + (int64_t)c * Q;
+            const int cm = (int)(t0 / Q);
+            cs_e = csp[t0 + Q - 1];
+            seq_e = seq ? seq[rb + t0 + Q - 1] : 0;
+            // The state entering chunk c belongs to the sequence of the token just
+            // before it; for a row's first segment that is the sequence of the
+            // row's first token (an initial state feeds the first sequence).
+            const int64_t ptok = c > 0 ? t0 - 1 : (pred >= 0 ? pred : s0);
+            const int seq_ref = seq ? seq[rb + ptok] : 0;
+            const float alpha = (seq_ref == seq_e) ? expf(cs_e) : 0.f;
+            ablk *= alpha;
+            if (c > 0) {
+                T* hp = store + (((int64_t)b * d.nchunk + cm) * d.H + h) * (P * N);
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                    for (int j = 0; j < NTW; ++j) {
+                        const int nt = wave + 4 * j;
+                        if (nt < NTT) {
+                            const int n = nt * 16 + lr;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                hp[(pt * 16 + 4 * lg + r) * N + n] = (T)acc[pt][j][r];
+                        }
+                    }
+            }
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-                for (int j = 0; j < NTW; ++j) {
-                    const int nt = wave + 4 * j;
-                    if (nt < NTT) {
-                        const int n = nt * 16 + lr;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int p = pt * 16 + 4 * lg + r;
-                            if (MODE == WALK_FWD_NP) hp[n * P + p] = (T)acc[pt][j][r];
-                            else hp[p * N + n] = (T)acc[pt][j][r];
-                        }
-                    }
-                }
+                for (int j = 0; j < NTW; ++j) acc[pt][j] *= alpha;
         }
+        __syncthreads();  // the previous slice's products are done with the LDS
+        stash(cs_e, seq_e);
+        __syncthreads();
+        if (si + 1 < ns) fetch(si + 1);
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
+        for (int kk = 0; kk < KT / KS; ++kk) {
+            const int jb = kk * KS;
+            Frag a[PT];
 #pragma unroll
-            for (int j = 0; j < NTW; ++j) acc[pt][j] *= alpha;
-
-        for (int sl = 0; sl < Q / KT; ++sl) {
-            const int64_t tb = t0 + (int64_t)sl * KT;
-            __syncthreads();
-            for (int idx = threadIdx.x; idx < KT * (P / VEC); idx += blockDim.x) {
-                const int jj = idx / (P / VEC), pv = idx % (P / VEC);
-                const vt v = *(const vt*)(arow + (tb + jj) * a_stride + pv * VEC);
+            for (int pt = 0; pt < PT; ++pt) a[pt] = XT<T>::load(sX, XR, jb, pt * 16, lane);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) At[(pv * VEC + e) * PITCH + jj] = v[e];
-            }
-            for (int idx = threadIdx.x; idx < KT * (N / VEC); idx += blockDim.x) {
-                const int jj = idx / (N / VEC), nv = idx % (N / VEC);
-                const vt v = *(const vt*)(brow + (tb + jj) * d.C + nv * VEC);
+            for (int j = 0; j < NTW; ++j) {
+                const int nt = wave + 4 * j;
+                if (nt < NTT) {
+                    const Frag bb = XT<T>::load(sB, BR, jb, nt * 16, lane);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) Bt[(nv * VEC + e) * PITCH + jj] = v[e];
-            }
-            if (threadIdx.x < KT) {
-                const int64_t tok = tb + threadIdx.x;
-                float w;
-                if (BWD) {
-                    const bool same = !seq || seq[rb + tok] == seq_ref;
-                    w = same ? expf(csp[tok]) : 0.f;
-                } else {
-                    const bool same = !seq || seq[rb + tok] == seq_e;
-                    w = same ? expf(cs_e - csp[tok]) * dtp[tok] : 0.f;
-                }
-                wv[threadIdx.x] = w;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int kk = 0; kk < KT / KS; ++kk) {
-                const int jl = kk * KS + SL * lg;
-                float wl[SL];
-#pragma unroll
-                for (int s = 0; s < SL; ++s) wl[s] = wv[jl + s];
-                Frag a[PT];
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-                    a[pt] = M::load_scaled(&At[(pt * 16 + lr) * PITCH + jl], wl);
-#pragma unroll
-                for (int j = 0; j < NTW; ++j) {
-                    const int nt = wave + 4 * j;
-                    if (nt < NTT) {
-                        const Frag bb = M::load(&Bt[(nt * 16 + lr) * PITCH + jl]);
-#pragma unroll
-                        for (int pt = 0; pt < PT; ++pt) acc[pt][j] = M::mma(a[pt], bb, acc[pt][j]);
-                    }
+                    for (int pt = 0; pt < PT; ++pt) acc[pt][j] = M::mma(a[pt], bb, acc[pt][j]);
                 }
             }
         }
