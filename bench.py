@@ -311,7 +311,7 @@ def main():
             ("ssd_boundary_scan(reverse)", lambda: ssd.ssd_boundary_scan(
                 p, segs.n, bb.summary, None, True, bb.dS_out)),
             ("ssd_segment_bwd_pass", lambda: ssd.ssd_segment_bwd_pass(
-                p, segs, seq, bufs.S_in, bb.dS_out, bb.ws)),
+                p, segs, seq, dy, bufs.S_in, bb.dS_out, bb.ws)),
             ("ssd_segment_bwd_chunks", lambda: ssd.ssd_segment_bwd_chunks(
                 p, segs, D, seq, dy, bb.ws)),
             ("ssd_conv1d_bwd", lambda: ssd.ssd_conv1d_bwd(

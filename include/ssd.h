@@ -248,7 +248,8 @@ int ssd_segment_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t
 /* The three phases of ssd_segment_bwd, in this order (calling them is the same
  * as ssd_segment_bwd; each reads the workspace ssd_segment_bwd_summary filled):
  *  ssd_segment_bwd_pass    walks every segment's chunks from S_in forward and
- *                          from dS_out backward, leaving in `ws` the true
+ *                          from dS_out backward (reading dy for the chunks'
+ *                          gradient contributions), leaving in `ws` the true
  *                          entering state and exit-state gradient of every chunk.
  *  ssd_segment_bwd_chunks  per chunk and head: dx, dB, dC (into `ws`, the
  *                          buffers the conv backward consumes, as #6808's first
@@ -262,8 +263,8 @@ int ssd_segment_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t
  *                          dA_log and dD (fixed order, deterministic).
  * Arguments mean what they mean for ssd_segment_bwd. */
 int ssd_segment_bwd_pass(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
-                         const int32_t* seq_idx, const float* S_in, const float* dS_out, void* ws,
-                         size_t ws_bytes, void* stream);
+                         const int32_t* seq_idx, const void* dy, const float* S_in,
+                         const float* dS_out, void* ws, size_t ws_bytes, void* stream);
 int ssd_segment_bwd_chunks(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
                            const float* D, const int32_t* seq_idx, const void* dy, void* ws,
                            size_t ws_bytes, void* stream);

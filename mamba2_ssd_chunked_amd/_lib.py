@@ -57,8 +57,8 @@ SIGNATURES = {
     "ssd_segment_bwd": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _vp, _vp, ctypes.c_size_t, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _vp]),
-    "ssd_segment_bwd_pass": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, _vp, ctypes.c_size_t,
-                                            _vp]),
+    "ssd_segment_bwd_pass": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, _vp, _vp,
+                                            ctypes.c_size_t, _vp]),
     "ssd_segment_bwd_chunks": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                               _vp]),
     "ssd_conv1d_bwd": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,

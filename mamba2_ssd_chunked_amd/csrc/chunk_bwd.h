@@ -18,7 +18,8 @@
 // g_j = exp(cs_e - cs_j) [j in the last token's sequence].  The ddt terms are
 // the ones the per-head kernel produced (see k_ddt): row and column sums of
 // F = S W L dt, u_i = f_i dy_i . (H C_i), v_j = dt_j x_j . (g_j G B_j),
-// q_j = x_j . (dx_j / dt_j without the D term), and the dD partial.
+// q_j = x_j . (dx_j / dt_j without the D term), the dD partial, and <G, H>
+// of every chunk and head.
 //
 // Work split: NW = Q/32 waves; wave w owns the 16-token tiles w and QT-1-w,
 // as columns j (dx, column sums, v, q, dB) and as rows i (u, dC).  For a
@@ -102,7 +103,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
     const int32_t* __restrict__ seq, const T* __restrict__ gpn, const T* __restrict__ hpn,
     T* __restrict__ dv,
     T* __restrict__ dbcp, float* __restrict__ rpart, float* __restrict__ tokp,
-    float* __restrict__ red4) {
+    float* __restrict__ red4, float* __restrict__ dotgh) {
     typedef ChunkBwdHB<T, P, N, Q> K;
     typedef Mma<T> M;
     typedef typename M::Frag Frag;
@@ -128,6 +129,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
     __shared__ __attribute__((aligned(16))) int ssq[Q];
     __shared__ float stab[QT * QT];  // exp(F_a - L_b), a >= b
     __shared__ float s_dd[NW];
+    __shared__ float s_gh[NW];  // per-wave parts of <G, H> of the current head
 
     // block -> (head block, chunk, row); the head blocks of a chunk are adjacent
     // items, and consecutive items go to one XCD
@@ -201,6 +203,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
                 *(vt*)&sD[j * XR + pv * VEC] = rd[q];
             }
         }
+        float gh = 0.f;  // this thread's part of <G, H>
 #pragma unroll
         for (int q = 0; q < V_S; ++q) {
             const int idx = threadIdx.x + q * NTH;
@@ -208,8 +211,13 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
                 const int p = idx / (N / VEC), nv = idx % (N / VEC);
                 *(vt*)&sG[p * GR + nv * VEC] = rg[q];
                 *(vt*)&sH[p * GR + nv * VEC] = rh[q];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) gh += (float)rg[q][e] * (float)rh[q][e];
             }
         }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) gh += __shfl_xor(gh, off, 64);
+        if (threadIdx.x % 64 == 0) s_gh[wave] = gh;
     };
 
     f32x4 Z[NB][TPK];
@@ -468,10 +476,14 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
             rpart[hl + t] = rsum;
         }
         if (threadIdx.x == 0) {
-            float dd = 0.f;
+            float dd = 0.f, gh = 0.f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) dd += s_dd[w];
+            for (int w = 0; w < NW; ++w) {
+                dd += s_dd[w];
+                gh += s_gh[w];
+            }
             red4[((int64_t)b * d.nchunk + cm) * d.H + h] = dd;
+            dotgh[((int64_t)b * d.nchunk + cm) * d.H + h] = gh;
         }
     }
 

@@ -104,7 +104,7 @@ const char* ssd_status_string(int status) {
     }
 }
 
-int32_t ssd_abi_version(void) { return 2; }
+int32_t ssd_abi_version(void) { return 3; }
 
 int32_t ssd_supported(int32_t headdim, int32_t dstate, int32_t act_dtype) {
     return kernels_supported(headdim, dstate, act_dtype) ? 1 : 0;
@@ -314,16 +314,18 @@ int check_bwd(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
 }  // namespace
 
 int ssd_segment_bwd_pass(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
-                         const int32_t* seq_idx, const float* S_in, const float* dS_out, void* ws,
-                         size_t ws_bytes, void* stream) {
+                         const int32_t* seq_idx, const void* dy, const float* S_in,
+                         const float* dS_out, void* ws, size_t ws_bytes, void* stream) {
     Dims d;
     SegTab t;
     int rc = check_bwd(problem, segs, nseg, &d, &t, ws, ws_bytes);
     if (rc) return rc;
-    if (!S_in || !dS_out) return SSD_ERR_NULL;
-    if (!aligned16(seq_idx) || !aligned16(S_in) || !aligned16(dS_out)) return SSD_ERR_ALIGN;
+    if (!dy || !S_in || !dS_out) return SSD_ERR_NULL;
+    if (!aligned16(seq_idx) || !aligned16(dy) || !aligned16(S_in) || !aligned16(dS_out))
+        return SSD_ERR_ALIGN;
     BwdArgs ar = {};
     ar.seq = seq_idx;
+    ar.dy = dy;
     ar.S_in = S_in;
     ar.dS_out = dS_out;
     return hip_status(launch_bwd_pass(d, t, problem->act_dtype, ar, ws, (hipStream_t)stream));

@@ -40,6 +40,7 @@
 #include "chunk_bwd.h"
 #include "gram.h"
 #include "ssd_internal.h"
+#include "state_walk.h"
 #include "xt.h"
 
 namespace ssd {
@@ -1474,7 +1475,7 @@ static void launch_chunk_bwd(const Dims& d, const SegTab& t, const BwdArgs& a, c
                            (const float*)(ws + L.cs), a.seq, (const T*)(ws + L.gpn),
                            (const T*)(ws + L.hpn), (T*)(ws + L.dv), (T*)(ws + L.dbc),
                            (float*)(ws + L.rpart),
-                           (float*)(ws + L.tokp), (float*)(ws + L.red4));
+                           (float*)(ws + L.tokp), (float*)(ws + L.red4), (float*)(ws + L.dotgh));
     } else if constexpr (chunk_bwd_fits<T, P, N, Q>()) {
         constexpr int TPW = chunk_bwd_tpw<T, Q>();
         constexpr int NW = ChunkBwd<T, P, N, Q, TPW>::NW;
@@ -1527,6 +1528,16 @@ static void bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a, floa
     launch_dt_prep(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32, a.dt_raw, a.dt_bias,
                    a.A_log, a.seq, (float*)(ws + L.dt), (float*)(ws + L.cs),
                    (float*)(ws + L.ctot), s);
+    if (hb_path<T, P, N>(d.Q)) {
+        // the reverse walk from a zero final gradient: dL/dS_in of each segment's
+        // own outputs and its block decay
+        hipLaunchKernelGGL((k_state_walk<T, P, N, true>),
+                           dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0,
+                           s, d, t, (const T*)xc, (const T*)a.dy, (const float*)(ws + L.dt),
+                           (const float*)(ws + L.cs), a.seq, (const float*)nullptr, (T*)nullptr,
+                           (const T*)nullptr, (float*)nullptr, summary);
+        return;
+    }
     hipLaunchKernelGGL((k_bwd_chunk_states<T, P, N>), chunk_head_grid(d), dim3(256), 0, s,
                        d, t, (const T*)xc, (const T*)(ws + L.bct), (const T*)a.dy,
                        (const float*)(ws + L.dt), (const float*)(ws + L.cs), a.seq,
@@ -1547,6 +1558,20 @@ static void bwd_pass_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* w
     const bool hb = hb_path<T, P, N>(d.Q);
     const BwdWs L = bwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
     char* ws = (char*)ws_;
+    if (hb) {
+        // G of every chunk: the reverse walk from dS_out; then H of every chunk:
+        // the forward walk from S_in (<G_c, H_c> comes from the chunk kernel)
+        const dim3 grid((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch);
+        hipLaunchKernelGGL((k_state_walk<T, P, N, true>), grid, dim3(256), 0, s, d, t,
+                           (const T*)(ws + L.xc), (const T*)a.dy, (const float*)(ws + L.dt),
+                           (const float*)(ws + L.cs), a.seq, a.dS_out, (T*)(ws + L.gpn),
+                           (const T*)nullptr, (float*)nullptr, (float*)nullptr);
+        hipLaunchKernelGGL((k_state_walk<T, P, N, false>), grid, dim3(256), 0, s, d, t,
+                           (const T*)(ws + L.xc), (const T*)nullptr, (const float*)(ws + L.dt),
+                           (const float*)(ws + L.cs), a.seq, a.S_in, (T*)(ws + L.hpn),
+                           (const T*)nullptr, (float*)nullptr, (float*)nullptr);
+        return;
+    }
     hipLaunchKernelGGL((k_state_pass<T, P, N, PASS_TRUE>),
                        dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0, s,
                        d, t, (const float*)(ws + L.ctot), a.seq, (const float*)(ws + L.zg),

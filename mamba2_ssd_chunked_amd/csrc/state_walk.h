@@ -1,20 +1,33 @@
-// Per-segment walk of chunk states (forward).
+// Per-segment walk of chunk states (forward) or state gradients (backward).
 //
 // One workgroup per (row, segment, head) visits the segment's chunks in causal
-// order.  The running P x N state lives in MFMA accumulators (FP32).  For every
-// chunk it first stores the running value (the state entering the chunk, zero
-// initial state), then applies the chunk's decay alpha_c = exp(cs_end)
+// order (forward) or reverse causal order (backward).  The running P x N
+// matrix lives in MFMA accumulators (FP32).  For every chunk it first stores
+// the running value, then applies the chunk's decay alpha_c = exp(cs_end)
 // (exactly 0 when a packed sequence starts inside the chunk) and accumulates
-// the chunk's own contribution x^T diag(w) B with MFMA,
-//   w_j = exp(cs_end - cs_j) dt_j [seq_j = seq_end].
-// The final value is the segment's S_ext and the product of the alphas its
-// block decay a_block.  This is the decay-weighted sum over earlier chunk
-// states that state-spaces/mamba #482 (second comment) identifies as the part
-// of the scan that must cross devices; Megatron-LM #6808 ships its
-// segment-level result as the FP32 summary.
+// the chunk's own contribution A^T diag(w) B with MFMA:
 //
-// The chunk is read in 64-token slices: x rows (scaled by w) and B rows go to
-// LDS in their natural [token][.] layout and both MFMA operands come from
+//   forward : A = x, B = B channels, w_j = exp(cs_end - cs_j) dt_j [seq_j = seq_end];
+//             the stored value is the state entering the chunk.
+//   backward: A = dy, B = C channels, w_i = exp(cs_i) [seq_i = seq of the state
+//             entering the chunk]; the stored value is the gradient of the
+//             state leaving the chunk.
+//
+// The walk starts from `init` ([S][b][H][P][N] FP32: S_in forward, dS_out
+// backward) or from zero; from zero, the forward walk stores nothing for a
+// segment's first chunk (its entering state is zero).  The final value is
+// S_ext (forward) or dL/dS_in of the segment's own outputs (backward), and the
+// product of the alphas the block decay a_block, both written to `summary` if
+// given.  With `gdot`, the forward walk also writes <G_c, H_c> per chunk, G_c
+// read from gdot in the stored layout.
+//
+// This is the decay-weighted sum over earlier chunk states that
+// state-spaces/mamba #482 (second comment) identifies as the part of the scan
+// that must cross devices; Megatron-LM #6808 ships its segment-level result as
+// the FP32 summary.
+//
+// A chunk is read in 64-token slices: A rows (scaled by w) and B rows go to LDS
+// in their natural [token][.] layout and both MFMA operands come from
 // transposed LDS reads (XT); the next slice is loaded into registers while the
 // current one is multiplied.
 #pragma once
@@ -24,12 +37,16 @@
 
 namespace ssd {
 
-template <typename T, int P, int N>
+template <typename T, int P, int N, bool BWD>
 __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T* __restrict__ xc,
+                                                   const T* __restrict__ dy,
                                                    const float* __restrict__ dt_ws,
                                                    const float* __restrict__ cs_ws,
                                                    const int32_t* __restrict__ seq,
+                                                   const float* __restrict__ init,
                                                    T* __restrict__ store,
+                                                   const T* __restrict__ gdot,
+                                                   float* __restrict__ dotgh,
                                                    float* __restrict__ summary) {
     typedef Mma<T> M;
     typedef typename M::Frag Frag;
@@ -39,10 +56,11 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
     constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
     constexpr int XR = P + VEC, BR = N + VEC;
     constexpr int PT = P / 16, NTT = N / 16, NTW = (NTT + 3) / 4;
-    constexpr int VX = (KT * (P / VEC) + NTH - 1) / NTH;  // x vectors per thread and slice
+    constexpr int VX = (KT * (P / VEC) + NTH - 1) / NTH;  // A vectors per thread and slice
     constexpr int VB = (KT * (N / VEC) + NTH - 1) / NTH;  // B vectors per thread and slice
     __shared__ __attribute__((aligned(16))) T sX[KT * XR];
     __shared__ __attribute__((aligned(16))) T sB[KT * BR];
+    __shared__ float sdot[4];
     typedef T vt __attribute__((ext_vector_type(VEC)));
 
     const int h = blockIdx.x, k = blockIdx.y;
@@ -58,23 +76,25 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
     const int64_t pred = seg_pred_token(tab, k);
     const float* dtp = dt_ws + ((int64_t)b * d.H + h) * d.L;
     const float* csp = cs_ws + ((int64_t)b * d.H + h) * d.L;
-    const T* xrow = xc + rb * d.C + (int64_t)h * P;
-    const T* brow = xc + rb * d.C + (int64_t)d.H * P + (int64_t)g * N;
+    const int64_t astr = BWD ? (int64_t)d.H * P : (int64_t)d.C;
+    const T* arow = (BWD ? dy + rb * astr : xc + rb * astr) + (int64_t)h * P;
+    const T* brow = xc + rb * d.C + (int64_t)d.H * P + (BWD ? (int64_t)d.G * N : 0) + (int64_t)g * N;
+    auto chunk_of = [&](int si) { return BWD ? nc - 1 - si / spc : si / spc; };
 
-    // ---- one slice: registers, then LDS (x scaled by its token's weight)
+    // ---- one slice: registers, then LDS (A scaled by its token's weight)
     vt rx[VX], rbv[VB];
     float rcs[VX], rdt[VX];
     int rsq[VX];
     auto fetch = [&](int si) {
-        const int64_t tb = s0 + (int64_t)si * KT;
+        const int64_t tb = s0 + (int64_t)chunk_of(si) * Q + (int64_t)(si % spc) * KT;
 #pragma unroll
         for (int q = 0; q < VX; ++q) {
             const int idx = threadIdx.x + q * NTH;
             if (idx < KT * (P / VEC)) {
                 const int jj = idx / (P / VEC), pv = idx % (P / VEC);
-                rx[q] = *(const vt*)(xrow + (tb + jj) * d.C + pv * VEC);
+                rx[q] = *(const vt*)(arow + (tb + jj) * astr + pv * VEC);
                 rcs[q] = csp[tb + jj];
-                rdt[q] = dtp[tb + jj];
+                rdt[q] = BWD ? 0.f : dtp[tb + jj];
                 rsq[q] = seq ? seq[rb + tb + jj] : 0;
             }
         }
@@ -87,13 +107,16 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
             }
         }
     };
-    auto stash = [&](float cs_e, int seq_e) {
+    // sref: seq_end (forward) or the entering state's sequence (backward)
+    auto stash = [&](float cs_e, int sref) {
 #pragma unroll
         for (int q = 0; q < VX; ++q) {
             const int idx = threadIdx.x + q * NTH;
             if (idx < KT * (P / VEC)) {
                 const int jj = idx / (P / VEC), pv = idx % (P / VEC);
-                const float w = (rsq[q] == seq_e) ? __expf(cs_e - rcs[q]) * rdt[q] : 0.f;
+                const float w = rsq[q] != sref ? 0.f
+                                : BWD      ? __expf(rcs[q])
+                                           : __expf(cs_e - rcs[q]) * rdt[q];
                 vt v;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) v[e] = (T)((float)rx[q][e] * w);
@@ -110,32 +133,46 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
         }
     };
 
+    const int64_t per = (int64_t)d.batch * d.H * P * N;
+    const int64_t sg = ((int64_t)k * d.batch + b) * d.H + h;
     f32x4 acc[PT][NTW];
 #pragma unroll
-    for (int i = 0; i < PT; ++i)
+    for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NTW; ++j) {
+            const int nt = wave + 4 * j;
+            if (init && nt < NTT) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[pt][j][r] = init[sg * (P * N) + (pt * 16 + 4 * lg + r) * N + nt * 16 + lr];
+            } else {
+                acc[pt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
     float ablk = 1.f;
     float cs_e = 0.f;
-    int seq_e = 0;
+    int sref = 0;
+    int64_t dot_at = -1;  // dotgh index of the chunk whose <G, H> sits in sdot
 
     fetch(0);
     for (int si = 0; si < ns; ++si) {
-        const int c = si / spc;
+        const int c = chunk_of(si);
         if (si % spc == 0) {
             const int64_t t0 = s0 + (int64_t)c * Q;
             const int cm = (int)(t0 / Q);
             cs_e = csp[t0 + Q - 1];
-            seq_e = seq ? seq[rb + t0 + Q - 1] : 0;
+            const int seq_e = seq ? seq[rb + t0 + Q - 1] : 0;
             // The state entering chunk c belongs to the sequence of the token just
             // before it; for a row's first segment that is the sequence of the
             // row's first token (an initial state feeds the first sequence).
             const int64_t ptok = c > 0 ? t0 - 1 : (pred >= 0 ? pred : s0);
             const int seq_ref = seq ? seq[rb + ptok] : 0;
+            sref = BWD ? seq_ref : seq_e;
             const float alpha = (seq_ref == seq_e) ? expf(cs_e) : 0.f;
             ablk *= alpha;
-            if (c > 0) {
-                T* hp = store + (((int64_t)b * d.nchunk + cm) * d.H + h) * (P * N);
+            const int64_t so = (((int64_t)b * d.nchunk + cm) * d.H + h) * (P * N);
+            if (store && (init || BWD || c > 0)) {
+                T* hp = store + so;
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
@@ -149,13 +186,36 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
                         }
                     }
             }
+            if (gdot) {
+                float dot = 0.f;
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                    for (int j = 0; j < NTW; ++j) {
+                        const int nt = wave + 4 * j;
+                        if (nt < NTT) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                dot += (float)gdot[so + (pt * 16 + 4 * lg + r) * N + nt * 16 + lr] *
+                                       acc[pt][j][r];
+                        }
+                    }
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+                if (lane == 0) sdot[wave] = dot;
+                dot_at = ((int64_t)b * d.nchunk + cm) * d.H + h;
+            }
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
                 for (int j = 0; j < NTW; ++j) acc[pt][j] *= alpha;
         }
         __syncthreads();  // the previous slice's products are done with the LDS
-        stash(cs_e, seq_e);
+        if (dot_at >= 0 && threadIdx.x == 0) {
+            dotgh[dot_at] = sdot[0] + sdot[1] + sdot[2] + sdot[3];
+        }
+        dot_at = -1;
+        stash(cs_e, sref);
         __syncthreads();
         if (si + 1 < ns) fetch(si + 1);
 #pragma unroll
@@ -177,7 +237,6 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
     }
 
     if (!summary) return;
-    const int64_t per = (int64_t)d.batch * d.H * P * N;
     float* sx = summary + (int64_t)k * per + ((int64_t)b * d.H + h) * (P * N);
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)

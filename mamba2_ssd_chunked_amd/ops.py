@@ -239,11 +239,14 @@ def ssd_segment_bwd(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log,
         ctypes.byref(problem), s.ptr(), s.n, *ins, ws_p, nbytes, *outs, _stream(stream)))
 
 
-def ssd_segment_bwd_pass(problem: Problem, segs, seq_idx, S_in, dS_out, ws, stream=None):
+def ssd_segment_bwd_pass(problem: Problem, segs, seq_idx, dy, S_in, dS_out, ws, stream=None):
     s = _segs(segs)
     st = s.n * problem.batch * problem.nheads * problem.headdim * problem.dstate
     f32 = torch.float32
-    ins = (_need(seq_idx, "seq_idx", problem.batch * problem.seqlen, torch.int32, optional=True),
+    act = _TORCH_ACT[problem.act_dtype]
+    BL = problem.batch * problem.seqlen
+    ins = (_need(seq_idx, "seq_idx", BL, torch.int32, optional=True),
+           _need(dy, "dy", BL * problem.nheads * problem.headdim, act),
            _need(S_in, "S_in", st, f32), _need(dS_out, "dS_out", st, f32))
     ws_p, nbytes = _ws(ws)
     _check("ssd_segment_bwd_pass", _lib.load().ssd_segment_bwd_pass(

@@ -130,7 +130,7 @@ def test_backward_phases_equal_composite(bwd_run):
     ssd.ssd_segment_bwd_summary(p, s, x["xBC"], x["conv_w"], x["dt_raw"], x["dt_bias"],
                                 x["A_log"], x["seq_idx"], x["dy"], b2.summary, b2.ws)
     ssd.ssd_boundary_scan(p, s.n, b2.summary, None, True, b2.dS_out)
-    ssd.ssd_segment_bwd_pass(p, s, x["seq_idx"], fb.S_in, b2.dS_out, b2.ws)
+    ssd.ssd_segment_bwd_pass(p, s, x["seq_idx"], x["dy"], fb.S_in, b2.dS_out, b2.ws)
     ssd.ssd_segment_bwd_chunks(p, s, x["D"], x["seq_idx"], x["dy"], b2.ws)
     ssd.ssd_conv1d_bwd(p, s, x["xBC"], x["conv_w"], x["dt_raw"], x["dt_bias"], x["A_log"],
                        x["seq_idx"], b2.ws, b2.dxBC, b2.ddt_raw, b2.dconv_w, b2.ddt_bias,
