@@ -1276,21 +1276,27 @@ __global__ void __launch_bounds__(256) k_conv_bwd(Dims d, SegTab tab, const T* _
 #pragma unroll
         for (int kk = 0; kk < W; ++kk) wr[e][kk] = active ? w[(c + e) * W + kk] : 0.f;
 
-    // x row r is the token r - (W-1) places after t0 in causal order
-    vt xs[RX];
+    // x row r is the token r - (W-1) places after t0 in causal order.  Rows,
+    // their positions and sequence ids are the same for the whole wave (t0 is),
+    // so the tap masks are scalar.
+    float xs[RX][4];
     int mem[RX];  // position in the row (< 2^31), -1 outside
     int sq[RX];
 #pragma unroll
     for (int r = 0; r < RX; ++r) {
         const int o = r - (W - 1);
-        mem[r] = (int)((o >= 0 && o < TPT) ? t0 + o : conv_row(tab, k, t0, o));
-        sq[r] = (mem[r] >= 0 && seq) ? seq[rb + mem[r]] : 0;
+        mem[r] = __builtin_amdgcn_readfirstlane(
+            (int)((o >= 0 && o < TPT) ? t0 + o : conv_row(tab, k, t0, o)));
+        sq[r] = __builtin_amdgcn_readfirstlane((mem[r] >= 0 && seq) ? seq[rb + mem[r]] : 0);
+        vt v;
         if (mem[r] >= 0 && active) {
-            xs[r] = *(const vt*)(xBC + (rb + mem[r]) * d.C + c);
+            v = *(const vt*)(xBC + (rb + mem[r]) * d.C + c);
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) xs[r][e] = (T)0.f;
+            for (int e = 0; e < 4; ++e) v[e] = (T)0.f;
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xs[r][e] = (float)v[e];
     }
     auto tap = [&](int src, int dst) { return mem[src] >= 0 && mem[dst] >= 0 && sq[src] == sq[dst]; };
 
@@ -1313,7 +1319,7 @@ __global__ void __launch_bounds__(256) k_conv_bwd(Dims d, SegTab tab, const T* _
         for (int kk = 0; kk < W; ++kk) {
             if (tap(o + kk, r)) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) u[e] += wr[e][kk] * (float)xs[o + kk][e];
+                for (int e = 0; e < 4; ++e) u[e] += wr[e][kk] * xs[o + kk][e];
             }
         }
         float g[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1330,7 +1336,7 @@ __global__ void __launch_bounds__(256) k_conv_bwd(Dims d, SegTab tab, const T* _
             for (int kk = 0; kk < W; ++kk) {
                 if (tap(o + kk, r)) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) dw[e][kk] += g[e] * (float)xs[o + kk][e];
+                    for (int e = 0; e < 4; ++e) dw[e][kk] += g[e] * xs[o + kk][e];
                 }
             }
         }

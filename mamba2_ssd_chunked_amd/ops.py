@@ -296,6 +296,7 @@ class ForwardBuffers:
     S_in: torch.Tensor
     ws: torch.Tensor
     y: torch.Tensor
+    final_state: torch.Tensor  # [b][H][P][N] float32, the state after each row's last token
 
     @staticmethod
     def allocate(problem: Problem, segs, device) -> "ForwardBuffers":
@@ -313,18 +314,21 @@ class ForwardBuffers:
             summary=torch.empty(summary_numel(problem, s.n), dtype=torch.float32, device=device),
             S_in=torch.empty((s.n, b, H, P, N), dtype=torch.float32, device=device),
             ws=torch.empty(wsb, dtype=torch.uint8, device=device),
-            y=torch.empty((b, L, H, P), dtype=act, device=device))
+            y=torch.empty((b, L, H, P), dtype=act, device=device),
+            final_state=torch.empty((b, H, P, N), dtype=torch.float32, device=device))
 
 
 def forward(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log, D, seq_idx=None,
             init=None, bufs: Optional[ForwardBuffers] = None, stream=None,
-            fused: bool = True) -> ForwardBuffers:
+            fused: bool = True, want_final: bool = False) -> ForwardBuffers:
     """The forward path; returns the buffers.
 
     fused=True : conv1d -> segment states -> boundary scan -> fused output pass
                  (y only; bufs.y_zero is left untouched).
     fused=False: conv1d -> segment-local SSD (states and y_zero) -> boundary scan
                  -> correction pass.
+    init       : optional [b][H][P][N] float32 state before each row's first token.
+    want_final : also write bufs.final_state (the boundary scan's final state).
     """
     s = _segs(segs)
     if bufs is None:
@@ -333,13 +337,15 @@ def forward(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log, D, seq_
     if fused:
         ssd_segment_states(problem, s, bufs.xBC_conv, dt_raw, dt_bias, A_log, seq_idx,
                            bufs.summary, bufs.ws, stream)
-        ssd_boundary_scan(problem, s.n, bufs.summary, init, False, bufs.S_in, None, stream)
+        ssd_boundary_scan(problem, s.n, bufs.summary, init, False, bufs.S_in,
+                          bufs.final_state if want_final else None, stream)
         ssd_segment_output_fused(problem, s, bufs.xBC_conv, D, seq_idx, bufs.S_in, bufs.ws,
                                  bufs.y, stream)
         return bufs
     ssd_segment_fwd(problem, s, bufs.xBC_conv, dt_raw, dt_bias, A_log, seq_idx, bufs.y_zero,
                     bufs.summary, bufs.ws, stream)
-    ssd_boundary_scan(problem, s.n, bufs.summary, init, False, bufs.S_in, None, stream)
+    ssd_boundary_scan(problem, s.n, bufs.summary, init, False, bufs.S_in,
+                      bufs.final_state if want_final else None, stream)
     ssd_apply_init_state(problem, s, bufs.y_zero, bufs.xBC_conv, D, seq_idx, bufs.S_in, bufs.ws,
                          bufs.y, stream)
     return bufs
@@ -356,6 +362,7 @@ class BackwardBuffers:
     ddt_bias: torch.Tensor
     dA_log: torch.Tensor
     dD: torch.Tensor
+    dinit: torch.Tensor  # [b][H][P][N] float32, gradient of the initial state
 
     @staticmethod
     def allocate(problem: Problem, segs, device) -> "BackwardBuffers":
@@ -377,21 +384,27 @@ class BackwardBuffers:
             dconv_w=torch.empty((C, W), dtype=f32, device=device),
             ddt_bias=torch.empty(H, dtype=f32, device=device),
             dA_log=torch.empty(H, dtype=f32, device=device),
-            dD=torch.empty(H, dtype=f32, device=device))
+            dD=torch.empty(H, dtype=f32, device=device),
+            dinit=torch.empty((b, H, P, N), dtype=f32, device=device))
 
 
 def backward(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log, D, dy, S_in,
-             seq_idx=None, bufs: Optional[BackwardBuffers] = None, stream=None) -> BackwardBuffers:
+             seq_idx=None, bufs: Optional[BackwardBuffers] = None, stream=None,
+             dfinal=None, want_dinit: bool = False) -> BackwardBuffers:
     """Summary phase -> reverse boundary scan -> segment phase; returns the buffers.
 
     ``S_in`` is the forward boundary scan's output (ForwardBuffers.S_in).
+    dfinal     : optional [b][H][P][N] float32 gradient of the final state (the
+                 reverse scan starts from it).
+    want_dinit : also write bufs.dinit, the gradient of the forward's initial state.
     """
     s = _segs(segs)
     if bufs is None:
         bufs = BackwardBuffers.allocate(problem, s, xBC.device)
     ssd_segment_bwd_summary(problem, s, xBC, conv_w, dt_raw, dt_bias, A_log, seq_idx, dy,
                             bufs.summary, bufs.ws, stream)
-    ssd_boundary_scan(problem, s.n, bufs.summary, None, True, bufs.dS_out, None, stream)
+    ssd_boundary_scan(problem, s.n, bufs.summary, dfinal, True, bufs.dS_out,
+                      bufs.dinit if want_dinit else None, stream)
     ssd_segment_bwd(problem, s, xBC, conv_w, dt_raw, dt_bias, A_log, D, seq_idx, dy, S_in,
                     bufs.dS_out, bufs.ws, bufs.dxBC, bufs.ddt_raw, bufs.dconv_w, bufs.ddt_bias,
                     bufs.dA_log, bufs.dD, stream)
