@@ -30,7 +30,8 @@
 // H of a head sit in LDS in their natural rows: row reads for the W and state
 // products, transposed reads (XT) of dy for dx; the Gram tiles come from L2 one
 // k step ahead of their use.  After the heads, Z goes to LDS as rows for dC,
-// the chunk's C^T and B^T are staged in turn for the Z products, and each
+// the chunk's C and B rows are staged in turn for the Z products (read
+// transposed), and each
 // head's G and H for its state terms (read transposed); dB is finished before
 // dC starts.
 #pragma once
@@ -73,7 +74,7 @@ struct ChunkBwdHB {
     static constexpr int PT = P / 16, NT = N / 16, KP = P / KS, KN = N / KS;
     static constexpr int XR = P + VEC;  // x / dy rows [token][p]
     static constexpr int GR = N + VEC;  // G / H rows [p][n]
-    static constexpr int TR = Q + VEC;  // B^T / C^T rows [n][token]
+    static constexpr int BR = N + VEC;  // B / C rows [token][n]
     // Z rows in LDS for dC: row tile a keeps columns [0, cw(a)) (whole k steps)
     __host__ __device__ static constexpr int cw(int a) { return KS * (a / TPK + 1); }
     __host__ __device__ static constexpr int zpitch(int a) { return cw(a) + VEC; }
@@ -88,7 +89,7 @@ struct ChunkBwdHB {
     static constexpr int E_HEAD = O_RW + NW * Q * 4 / (int)sizeof(T);
     // final phase: Z rows and C^T (then G of HG heads), later B^T and H
     static constexpr int HG = 4;  // heads per round of state terms
-    static constexpr int O_BT = zoff(QT), E_FIN = O_BT + N * TR, E_FS = O_BT + HG * P * GR;
+    static constexpr int O_BT = zoff(QT), E_FIN = O_BT + Q * BR, E_FS = O_BT + HG * P * GR;
     static constexpr int E_U = cmax(E_HEAD, cmax(E_FIN, E_FS));
     static constexpr size_t LDS =
         (size_t)E_U * sizeof(T) + (size_t)Q * 20 + (size_t)QT * QT * 4 + (size_t)NW * 4 + 64;
@@ -98,7 +99,7 @@ struct ChunkBwdHB {
 template <typename T, int P, int N, int Q>
 __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
     Dims d, SegTab tab, int hbs, const T* __restrict__ xc, const T* __restrict__ dy,
-    const T* __restrict__ gramT, const T* __restrict__ bct, const float* __restrict__ Dp,
+    const T* __restrict__ gramT, const float* __restrict__ Dp,
     const float* __restrict__ dt_ws, const float* __restrict__ cs_ws,
     const int32_t* __restrict__ seq, const T* __restrict__ gpn, const T* __restrict__ hpn,
     T* __restrict__ dv,
@@ -120,8 +121,8 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
     T* const sH = U + K::O_H;                   // entering state H [P][GR]
     float* const s_rw = (float*)(U + K::O_RW);  // per-wave row sums of F [NW][Q]
     T* const sZ = U;                            // final phase: Z rows, strip per row tile
-    T* const sBT = U + K::O_BT;                 // final phase: C^T, then B^T [N][TR]
-    constexpr int GR = K::GR, TR = K::TR;
+    T* const sBT = U + K::O_BT;                 // final phase: C rows, then B rows [Q][BR]
+    constexpr int GR = K::GR, BR = K::BR;
     __shared__ __attribute__((aligned(16))) float scs[Q];
     __shared__ __attribute__((aligned(16))) float sdt[Q];
     __shared__ __attribute__((aligned(16))) float sea[Q];  // exp(cs_t - F(t))
@@ -160,8 +161,6 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
     const int64_t boff = HPd + (int64_t)g * N;
     const int64_t coff = HPd + (int64_t)d.G * N + (int64_t)g * N;
     const int64_t cg = ((int64_t)b * d.nchunk + cm) * d.G + g;
-    const T* bctB = bct + (cg * 2 + 0) * (int64_t)N * Q;
-    const T* bctC = bctB + (int64_t)N * Q;
     const T* gT0 = gramT + cg * (int64_t)gram_tiles(QT) * 256 + lane * 4;
     const int j0 = wave, j1 = QT - 1 - wave;  // the wave's tiles
     const int ks0 = j0 / TPK, ks1 = j1 / TPK;  // first k step of each as a column
@@ -495,14 +494,10 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
     asm volatile("s_mov_b32 %0, 0" : "=s"(opq));
     const int lane2 = threadIdx.x % 64 + opq, lr2 = lane2 % 16, lg2 = lane2 / 16;
     constexpr int V_T = (N * (Q / VEC) + NTH - 1) / NTH;
-    auto stage_bt = [&](const T* src) {  // [N][Q] -> sBT
-#pragma unroll
-        for (int q = 0; q < V_T; ++q) {
-            const int idx = threadIdx.x + q * NTH;
-            if (idx < N * (Q / VEC)) {
-                const int n = idx / (Q / VEC), tv = idx % (Q / VEC);
-                *(vt*)&sBT[n * TR + tv * VEC] = *(const vt*)(src + (int64_t)n * Q + tv * VEC);
-            }
+    auto stage_rows = [&](int64_t choff) {  // B or C rows of the chunk -> sBT [Q][BR]
+        for (int idx = threadIdx.x; idx < Q * (N / VEC); idx += NTH) {
+            const int j = idx / (N / VEC), nv = idx % (N / VEC);
+            *(vt*)&sBT[j * BR + nv * VEC] = *(const vt*)(xc + (rb + t0 + j) * d.C + choff + nv * VEC);
         }
     };
     T* const dbp = dbcp + (int64_t)hbi * 2 * N;
@@ -597,7 +592,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
     };
 
     __syncthreads();  // every wave is done with the head loop's LDS
-    // Z into LDS as natural rows (strip per row tile) for dC; C^T for dB
+    // Z into LDS as natural rows (strip per row tile) for dC; C rows for dB
     auto zstore = [&](const f32x4 (&z)[TPK], int jc, int ks) {
 #pragma unroll
         for (int it = 0; it < TPK; ++it) {
@@ -614,7 +609,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
         if (ks >= ks0) zstore(Z[ks + 1], j0, ks);
-    stage_bt(bctC);
+    stage_rows(coff);
     __syncthreads();
 
     auto zfrag = [&](const f32x4 (&z)[TPK]) {
@@ -625,7 +620,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
             for (int r = 0; r < 4; ++r) f[it * 4 + r] = (E)z[it][r];
         return f;
     };
-    // ---- dB^T [n][j] = sum_i C^T[n][i] Z[i][j] + state terms
+    // ---- dB^T [n][j] = sum_i C^T[n][i] Z[i][j] + state terms (C^T read transposed)
     ab_zero();
 #pragma unroll
     for (int m = 0; m < MAXA; ++m) {
@@ -634,7 +629,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
             const int ks = ks1 + m;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
-                ab[1][nt] = M::mma(M::load(&sBT[(nt * 16 + lr2) * TR + ks * KS + SL * lg2]), zf, ab[1][nt]);
+                ab[1][nt] = M::mma(XT<T>::load(sBT, BR, ks * KS, nt * 16, lane2), zf, ab[1][nt]);
         }
     }
 #pragma unroll
@@ -643,15 +638,15 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
             const Frag zf = zfrag(Z[ks + 1]);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
-                ab[0][nt] = M::mma(M::load(&sBT[(nt * 16 + lr2) * TR + ks * KS + SL * lg2]), zf, ab[0][nt]);
+                ab[0][nt] = M::mma(XT<T>::load(sBT, BR, ks * KS, nt * 16, lane2), zf, ab[0][nt]);
         }
     }
-    state_terms(true, sBT);  // G^T goes where C^T was (the Z rows stay)
+    state_terms(true, sBT);  // G goes where the C rows were (the Z rows stay)
     ab_store(0);
 
-    // ---- dC^T [n][i] = sum_j B^T[n][j] Z[i][j] + state terms
+    // ---- dC^T [n][i] = sum_j B^T[n][j] Z[i][j] + state terms (B^T read transposed)
     __syncthreads();  // every wave is done with sBT
-    stage_bt(bctB);
+    stage_rows(boff);
     __syncthreads();
     ab_zero();
 #pragma unroll
@@ -669,7 +664,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
             }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
-                ab[it][nt] = M::mma(M::load(&sBT[(nt * 16 + lr2) * TR + ks * KS + SL * lg2]), zf, ab[it][nt]);
+                ab[it][nt] = M::mma(XT<T>::load(sBT, BR, ks * KS, nt * 16, lane2), zf, ab[it][nt]);
         }
     }
     state_terms(false, sZ);  // H^T goes where the Z rows were (after the first sync)

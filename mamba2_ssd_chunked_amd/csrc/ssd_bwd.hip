@@ -1476,8 +1476,7 @@ static void launch_chunk_bwd(const Dims& d, const SegTab& t, const BwdArgs& a, c
         const unsigned nblk = (unsigned)((int64_t)d.nchunk * (d.H / hbs) * d.batch);
         hipLaunchKernelGGL((k_chunk_bwd_hb<T, P, N, Q>), dim3(nblk),
                            dim3(ChunkBwdHB<T, P, N, Q>::NTH), 0, s, d, t, hbs,
-                           (const T*)(ws + L.xc), (const T*)a.dy, (const T*)(ws + L.gramt),
-                           (const T*)(ws + L.bct), a.D, (const float*)(ws + L.dt),
+                           (const T*)(ws + L.xc), (const T*)a.dy, (const T*)(ws + L.gramt), a.D, (const float*)(ws + L.dt),
                            (const float*)(ws + L.cs), a.seq, (const T*)(ws + L.gpn),
                            (const T*)(ws + L.hpn), (T*)(ws + L.dv), (T*)(ws + L.dbc),
                            (float*)(ws + L.rpart),
@@ -1528,9 +1527,12 @@ static void bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a, floa
     T* xc = (T*)(ws + L.xc);
     launch_conv1d_fwd(d, t, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32, a.xBC, a.conv_w,
                       a.seq, xc, s);
-    hipLaunchKernelGGL(k_bc_transpose<T>, dim3((unsigned)d.nchunk, (unsigned)d.G, (unsigned)d.batch),
-                       dim3(256), 0, s, d, (const T*)xc, (T*)(ws + L.bct));
-    if (hb_path<T, P, N>(d.Q)) launch_gram<T, N, true>(d, xc, (T*)(ws + L.gramt), s);
+    if (hb_path<T, P, N>(d.Q))
+        launch_gram<T, N, true>(d, xc, (T*)(ws + L.gramt), s);
+    else
+        hipLaunchKernelGGL(k_bc_transpose<T>,
+                           dim3((unsigned)d.nchunk, (unsigned)d.G, (unsigned)d.batch), dim3(256), 0,
+                           s, d, (const T*)xc, (T*)(ws + L.bct));
     launch_dt_prep(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32, a.dt_raw, a.dt_bias,
                    a.A_log, a.seq, (float*)(ws + L.dt), (float*)(ws + L.cs),
                    (float*)(ws + L.ctot), s);
