@@ -34,21 +34,27 @@ __global__ void __launch_bounds__(256) k_conv1d_silu(Dims d, SegTab tab, const T
 #pragma unroll
         for (int kk = 0; kk < W; ++kk) wr[e][kk] = w[(c + e) * W + kk];
 
-    // row r is the token r - (W-1) places after t0
-    vt xs[R];
+    // row r is the token r - (W-1) places after t0; rows, their positions and
+    // sequence ids are the same for the whole wave (t0 is), so the tap masks are
+    // scalar
+    float xs[R][CONV_VEC];
     int sq[R];
     bool ok[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int mem = (int)(r >= W - 1 ? t0 + (r - (W - 1)) : conv_row(tab, k, t0, r - (W - 1)));
+        const int mem = __builtin_amdgcn_readfirstlane(
+            (int)(r >= W - 1 ? t0 + (r - (W - 1)) : conv_row(tab, k, t0, r - (W - 1))));
         ok[r] = mem >= 0;
-        sq[r] = (ok[r] && seq) ? seq[rb + mem] : 0;
+        sq[r] = __builtin_amdgcn_readfirstlane((ok[r] && seq) ? seq[rb + mem] : 0);
+        vt v;
         if (ok[r]) {
-            xs[r] = *(const vt*)(xBC + (rb + mem) * d.C + c);
+            v = *(const vt*)(xBC + (rb + mem) * d.C + c);
         } else {
 #pragma unroll
-            for (int e = 0; e < CONV_VEC; ++e) xs[r][e] = (T)0.f;
+            for (int e = 0; e < CONV_VEC; ++e) v[e] = (T)0.f;
         }
+#pragma unroll
+        for (int e = 0; e < CONV_VEC; ++e) xs[r][e] = (float)v[e];
     }
 #pragma unroll
     for (int t = 0; t < CONV_TPT; ++t) {
@@ -59,12 +65,14 @@ __global__ void __launch_bounds__(256) k_conv1d_silu(Dims d, SegTab tab, const T
             const int r = t + kk;
             if (ok[r] && sq[r] == sq[ro]) {
 #pragma unroll
-                for (int e = 0; e < CONV_VEC; ++e) acc[e] += wr[e][kk] * (float)xs[r][e];
+                for (int e = 0; e < CONV_VEC; ++e) acc[e] += wr[e][kk] * xs[r][e];
             }
         }
+        // SiLU with the hardware reciprocal (1 ulp)
         vt o;
 #pragma unroll
-        for (int e = 0; e < CONV_VEC; ++e) o[e] = (T)(acc[e] / (1.f + __expf(-acc[e])));
+        for (int e = 0; e < CONV_VEC; ++e)
+            o[e] = (T)(acc[e] * __builtin_amdgcn_rcpf(1.f + __expf(-acc[e])));
         *(vt*)(out + (rb + t0 + t) * d.C + c) = o;
     }
 }

@@ -1327,7 +1327,7 @@ __global__ void __launch_bounds__(256) k_conv_bwd(Dims d, SegTab tab, const T* _
             const f32x4 dv4 = grad4(rb + mem[r]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float sg = 1.f / (1.f + __expf(-u[e]));
+                const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-u[e]));
                 g[e] = dv4[e] * sg * (1.f + u[e] * (1.f - sg));
             }
         }
