@@ -9,6 +9,8 @@
 // consecutive channels of the same tokens, so every load and store of a wave is
 // one contiguous run.  Taps that reach before the row start or across a packed
 // sequence start are zero.  HBM-bound: 2*C*sizeof(act) bytes per token.
+#include <type_traits>
+
 #include "ssd_internal.h"
 
 namespace ssd {
@@ -56,25 +58,35 @@ __global__ void __launch_bounds__(256) k_conv1d_silu(Dims d, SegTab tab, const T
 #pragma unroll
         for (int e = 0; e < CONV_VEC; ++e) xs[r][e] = (float)v[e];
     }
+    // almost every wave sees neither a row start nor a sequence start in its rows:
+    // then no tap is masked and the loop runs without selects
+    bool clean = true;
 #pragma unroll
-    for (int t = 0; t < CONV_TPT; ++t) {
-        const int ro = t + W - 1;
-        float acc[CONV_VEC] = {};
+    for (int r = 0; r < R; ++r) clean = clean && ok[r] && sq[r] == sq[0];
+    auto run = [&](auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-        for (int kk = 0; kk < W; ++kk) {
-            const int r = t + kk;
-            if (ok[r] && sq[r] == sq[ro]) {
+        for (int t = 0; t < CONV_TPT; ++t) {
+            const int ro = t + W - 1;
+            float acc[CONV_VEC] = {};
 #pragma unroll
-                for (int e = 0; e < CONV_VEC; ++e) acc[e] += wr[e][kk] * xs[r][e];
+            for (int kk = 0; kk < W; ++kk) {
+                const int r = t + kk;
+                if (!MASKED || (ok[r] && sq[r] == sq[ro])) {
+#pragma unroll
+                    for (int e = 0; e < CONV_VEC; ++e) acc[e] += wr[e][kk] * xs[r][e];
+                }
             }
-        }
-        // SiLU with the hardware reciprocal (1 ulp)
-        vt o;
+            // SiLU with the hardware reciprocal (1 ulp)
+            vt o;
 #pragma unroll
-        for (int e = 0; e < CONV_VEC; ++e)
-            o[e] = (T)(acc[e] * __builtin_amdgcn_rcpf(1.f + __expf(-acc[e])));
-        *(vt*)(out + (rb + t0 + t) * d.C + c) = o;
-    }
+            for (int e = 0; e < CONV_VEC; ++e)
+                o[e] = (T)(acc[e] * __builtin_amdgcn_rcpf(1.f + __expf(-acc[e])));
+            *(vt*)(out + (rb + t0 + t) * d.C + c) = o;
+        }
+    };
+    if (clean) run(std::false_type{});
+    else run(std::true_type{});
 }
 
 template <typename T, int W>
