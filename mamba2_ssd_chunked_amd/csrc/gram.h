@@ -21,7 +21,10 @@ namespace ssd {
 __host__ __device__ constexpr int gram_tiles(int qt) { return qt * (qt + 1) / 2; }
 __host__ __device__ constexpr int gram_index(int a, int b) { return a * (a + 1) / 2 + b; }
 
-// One wave per (output tiles w and QT-1-w, chunk, group, row).
+// One wave per (output tiles w and QT-1-w, every GSPLIT-th source tile, chunk,
+// group, row): 2048 waves at the mixer shard's shape, each with a few
+// independent tile products to keep loads in flight.
+constexpr int GSPLIT = 4;
 template <typename T, int N, bool TRANS = false>
 __global__ void __launch_bounds__(64) k_gram(Dims d, const T* __restrict__ xc, T* __restrict__ gram) {
     typedef Mma<T> M;
@@ -29,7 +32,7 @@ __global__ void __launch_bounds__(64) k_gram(Dims d, const T* __restrict__ xc, T
     constexpr int SL = M::SL, KS = M::KS, NKF = N / KS;
     typedef T t4 __attribute__((ext_vector_type(4)));
     const int QT = d.Q / 16;
-    const int w = blockIdx.x;
+    const int w = blockIdx.x / GSPLIT, part = blockIdx.x % GSPLIT;
     const int g = blockIdx.y % d.G, cm = blockIdx.y / d.G;
     const int64_t b = blockIdx.z;
     const int lane = threadIdx.x, lr = lane % 16, lg = lane / 16;
@@ -44,7 +47,8 @@ __global__ void __launch_bounds__(64) k_gram(Dims d, const T* __restrict__ xc, T
 #pragma unroll
         for (int kn = 0; kn < NKF; ++kn)
             cf[kn] = M::load(xc + (t0 + a * 16 + lr) * d.C + coff + kn * KS + SL * lg);
-        for (int bt = 0; bt <= a; ++bt) {
+#pragma unroll 2
+        for (int bt = part; bt <= a; bt += GSPLIT) {
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kn = 0; kn < NKF; ++kn) {
@@ -60,7 +64,7 @@ __global__ void __launch_bounds__(64) k_gram(Dims d, const T* __restrict__ xc, T
 template <typename T, int N, bool TRANS = false>
 inline void launch_gram(const Dims& d, const T* xc, T* gram, hipStream_t s) {
     const int QT = d.Q / 16;
-    hipLaunchKernelGGL((k_gram<T, N, TRANS>), dim3((unsigned)(QT / 2), (unsigned)(d.nchunk * d.G),
+    hipLaunchKernelGGL((k_gram<T, N, TRANS>), dim3((unsigned)(QT / 2 * GSPLIT), (unsigned)(d.nchunk * d.G),
                                             (unsigned)d.batch),
                        dim3(64), 0, s, d, xc, gram);
 }
