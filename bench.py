@@ -63,7 +63,6 @@ CALL_KERNEL = {
     "ssd_segment_output_fused": r"k_chunk_y<",
     "ssd_boundary_scan": r"k_boundary_scan<",
     "ssd_boundary_scan(reverse)": r"k_boundary_scan<",
-    "ssd_segment_bwd_pass": r"k_state_pass<.*Li1E?>",
     "ssd_segment_bwd_chunks": r"k_chunk_bwd(_hb)?<",
 }
 CSRC = os.path.join(ROOT, "mamba2_ssd_chunked_amd", "csrc")
@@ -198,15 +197,16 @@ def algorithmic_bytes(wl):
         "ssd_segment_output_fused": x + bc // 2 + gram + hst + states + dtcs + x + seq,
         "ssd_segment_output": x + bc // 2 + gram + hst + dtcs + BL * H * P * 4 + seq,
         "ssd_apply_init_state": BL * H * P * 4 + x + bc // 2 + BL * H * 4 + states + x + seq,
-        # conv recompute (xBC in, conv output out), dt prep, the transposed Gram tiles,
-        # every chunk's contributions to the state and its gradient (x, B, C, dy in;
-        # FP32 out), the summary walk
+        # conv recompute (xBC in, conv output out), dt prep, the transposed Gram tiles
+        # (B, C in), the reverse walk of every segment from zero (dy, C, cumsum in;
+        # summary out)
         "ssd_segment_bwd_summary": BL * C * e + BL * C * e + BL * H * e + dtcs + bc + gram
-                                   + x + dy + 2 * st_all * 4 + summary + seq,
+                                   + dy + bc // 2 + dtcs // 2 + summary + seq,
         "ssd_boundary_scan(reverse)": summary + states,
-        # chunk contributions and the two boundary states in; exit gradient and
-        # entering state of every chunk out
-        "ssd_segment_bwd_pass": 2 * st_all * 4 + 2 * states + 2 * st_all * e,
+        # the reverse walk from dS_out (dy, C, cumsum in; exit gradient of every chunk
+        # out) and the forward walk from S_in (x, B, dt, cumsum in; entering state of
+        # every chunk out)
+        "ssd_segment_bwd_pass": dy + x + bc + dtcs + 2 * states + 2 * st_all * e + seq,
         # x, B, C, dy, decays, exit gradient and entering state per chunk, Gram tiles
         # in; d(conv output) of x, dB and dC per head block, ddt partial sums out
         "ssd_segment_bwd_chunks": BL * C * e + dy + dtcs + 2 * st_all * e + gram + x
@@ -319,8 +319,7 @@ def main():
                 bb.dconv_w, bb.ddt_bias, bb.dA_log, bb.dD)),
         ]
     single_kernel = {"ssd_conv1d_fwd", "ssd_segment_output_fused", "ssd_boundary_scan",
-                     "ssd_boundary_scan(reverse)", "ssd_segment_bwd_pass",
-                     "ssd_segment_bwd_chunks"}
+                     "ssd_boundary_scan(reverse)", "ssd_segment_bwd_chunks"}
 
     def step(events=None):
         for i, (_, fn) in enumerate(calls):

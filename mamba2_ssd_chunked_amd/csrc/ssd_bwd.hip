@@ -1561,8 +1561,9 @@ static void bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a, floa
 template <typename T, int P, int N>
 static void bwd_pass_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* ws_,
                        hipStream_t s) {
-    // the head-blocked chunk kernel reads G and H as [p][n] only; the per-head
-    // one reads G as [p][n] and [n][p] and H as [n][p]
+    // the head-blocked chunk kernel reads G and H as [p][n] only (written by the
+    // two walks); the per-head one reads G as [p][n] and [n][p] and H as [n][p]
+    // (written by the pass kernel from the chunk contributions)
     const bool hb = hb_path<T, P, N>(d.Q);
     const BwdWs L = bwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
     char* ws = (char*)ws_;
@@ -1584,8 +1585,7 @@ static void bwd_pass_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* w
                        dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0, s,
                        d, t, (const float*)(ws + L.ctot), a.seq, (const float*)(ws + L.zg),
                        (const float*)(ws + L.zh), a.S_in, a.dS_out, (float*)nullptr,
-                       (T*)(ws + L.gpn), hb ? (T*)nullptr : (T*)(ws + L.gnp),
-                       hb ? (T*)nullptr : (T*)(ws + L.hnp), hb ? (T*)(ws + L.hpn) : (T*)nullptr,
+                       (T*)(ws + L.gpn), (T*)(ws + L.gnp), (T*)(ws + L.hnp), (T*)nullptr,
                        (float*)(ws + L.dotgh));
 }
 

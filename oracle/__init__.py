@@ -224,21 +224,40 @@ def forward(wl, heads: Optional[Sequence[int]] = None, rows: Optional[Sequence[i
                    dt_min=wl.dt_min, dt_max=wl.dt_max, seq_idx=seq)
 
 
-def backward(wl):
+def backward(wl, heads: Optional[Sequence[int]] = None):
     """All gradients for a workload with ``dy``; causal token order, float64.
 
     Returns dict: y, dxBC [b, L, C], dconv_w [C, W], ddt_raw [b, L, H],
     ddt_bias, dA_log, dD [H].
+
+    ``heads`` restricts the problem to those heads and their groups' B and C
+    channels.  The gradients that belong to a head alone are then exactly those
+    of the full problem: dxBC and dconv_w of the head's x channels (returned as
+    [b, L, H' * P] and [H' * P, W]), ddt_raw [b, L, H'], ddt_bias, dA_log and
+    dD [H'].  B and C channel gradients sum over every head of a group and are
+    not returned for a subset.
     """
     xBC = wl.to_causal(wl.xBC)
     dt_raw = wl.to_causal(wl.dt_raw)
     dy = wl.to_causal(wl.dy)
     seq = wl.causal_seq_idx()
-    kw = dict(nheads=wl.nheads, headdim=wl.headdim, dstate=wl.dstate, ngroups=wl.ngroups,
+    H, P, G = wl.nheads, wl.headdim, wl.ngroups
+    conv_w, dt_bias, A_log, D = wl.conv_w, wl.dt_bias, wl.A_log, wl.D
+    if heads is not None:
+        new_heads, groups, ch = _select_heads(wl, heads)
+        xBC = xBC[:, :, ch]
+        conv_w = conv_w[ch]
+        dt_raw = dt_raw[:, :, new_heads]
+        dy = dy[:, :, new_heads]
+        dt_bias, A_log, D = dt_bias[new_heads], A_log[new_heads], D[new_heads]
+        H, G = len(new_heads), len(groups)
+    kw = dict(nheads=H, headdim=P, dstate=wl.dstate, ngroups=G,
               dt_min=wl.dt_min, dt_max=wl.dt_max, seq_idx=seq)
-    _, v = conv_silu(xBC, wl.conv_w, seq)
-    y = ssd_fwd(v, dt_raw, wl.dt_bias, wl.A_log, wl.D, **kw)
-    g = ssd_bwd(v, dt_raw, wl.dt_bias, wl.A_log, wl.D, dy, **kw)
-    dxBC, dw = conv_silu_bwd(xBC, wl.conv_w, g["dv"], seq)
+    _, v = conv_silu(xBC, conv_w, seq)
+    y = ssd_fwd(v, dt_raw, dt_bias, A_log, D, **kw)
+    g = ssd_bwd(v, dt_raw, dt_bias, A_log, D, dy, **kw)
+    dxBC, dw = conv_silu_bwd(xBC, conv_w, g["dv"], seq)
+    if heads is not None:
+        dxBC, dw = dxBC[:, :, :H * P], dw[:H * P]
     return dict(y=y, dxBC=dxBC, dconv_w=dw, ddt_raw=g["ddt_raw"], ddt_bias=g["ddt_bias"],
                 dA_log=g["dA_log"], dD=g["dD"])

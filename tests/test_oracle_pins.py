@@ -297,6 +297,25 @@ def test_head_subset_matches_full_run():
     np.testing.assert_array_equal(ys, y[:, :, [2, 3, 6, 7]])
 
 
+def test_head_subset_backward_matches_full_run():
+    """Gradients that belong to one head alone are unchanged when the problem is
+    restricted to a subset of heads (with their groups' B and C channels)."""
+    wl = W.make_workload("sub_bwd", batch=2, seqlen=64, nheads=8, headdim=4, dstate=4,
+                         ngroups=4, chunk=16, act="bf16", seed=22, lengths=[20, 1, 43],
+                         with_dy=True)
+    heads = [2, 3, 6, 7]
+    full = oracle.backward(wl)
+    sub = oracle.backward(wl, heads=heads)
+    P = wl.headdim
+    ch = np.concatenate([np.arange(h * P, (h + 1) * P) for h in heads])
+    np.testing.assert_allclose(sub["dxBC"], full["dxBC"][:, :, ch], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(sub["dconv_w"], full["dconv_w"][ch], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(sub["ddt_raw"], full["ddt_raw"][:, :, heads], rtol=1e-12,
+                               atol=1e-14)
+    for k in ("ddt_bias", "dA_log", "dD"):
+        np.testing.assert_allclose(sub[k], full[k][heads], rtol=1e-12, atol=1e-14)
+
+
 # ---------------------------------------------------------------- gradients
 
 
