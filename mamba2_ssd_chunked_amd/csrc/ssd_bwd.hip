@@ -1539,11 +1539,9 @@ static void bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a, floa
     if (hb_path<T, P, N>(d.Q)) {
         // the reverse walk from a zero final gradient: dL/dS_in of each segment's
         // own outputs and its block decay
-        hipLaunchKernelGGL((k_state_walk<T, P, N, true>),
-                           dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0,
-                           s, d, t, (const T*)xc, (const T*)a.dy, (const float*)(ws + L.dt),
-                           (const float*)(ws + L.cs), a.seq, (const float*)nullptr, (T*)nullptr,
-                           (const T*)nullptr, (float*)nullptr, summary);
+        launch_state_walk<T, P, N, true>(d, t, (const T*)xc, (const T*)a.dy,
+                                         (const float*)(ws + L.dt), (const float*)(ws + L.cs),
+                                         a.seq, nullptr, (T*)nullptr, summary, s);
         return;
     }
     hipLaunchKernelGGL((k_bwd_chunk_states<T, P, N>), chunk_head_grid(d), dim3(256), 0, s,
@@ -1570,15 +1568,12 @@ static void bwd_pass_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* w
     if (hb) {
         // G of every chunk: the reverse walk from dS_out; then H of every chunk:
         // the forward walk from S_in (<G_c, H_c> comes from the chunk kernel)
-        const dim3 grid((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch);
-        hipLaunchKernelGGL((k_state_walk<T, P, N, true>), grid, dim3(256), 0, s, d, t,
-                           (const T*)(ws + L.xc), (const T*)a.dy, (const float*)(ws + L.dt),
-                           (const float*)(ws + L.cs), a.seq, a.dS_out, (T*)(ws + L.gpn),
-                           (const T*)nullptr, (float*)nullptr, (float*)nullptr);
-        hipLaunchKernelGGL((k_state_walk<T, P, N, false>), grid, dim3(256), 0, s, d, t,
-                           (const T*)(ws + L.xc), (const T*)nullptr, (const float*)(ws + L.dt),
-                           (const float*)(ws + L.cs), a.seq, a.S_in, (T*)(ws + L.hpn),
-                           (const T*)nullptr, (float*)nullptr, (float*)nullptr);
+        launch_state_walk<T, P, N, true>(d, t, (const T*)(ws + L.xc), (const T*)a.dy,
+                                         (const float*)(ws + L.dt), (const float*)(ws + L.cs),
+                                         a.seq, a.dS_out, (T*)(ws + L.gpn), nullptr, s);
+        launch_state_walk<T, P, N, false>(d, t, (const T*)(ws + L.xc), (const T*)nullptr,
+                                          (const float*)(ws + L.dt), (const float*)(ws + L.cs),
+                                          a.seq, a.S_in, (T*)(ws + L.hpn), nullptr, s);
         return;
     }
     hipLaunchKernelGGL((k_state_pass<T, P, N, PASS_TRUE>),

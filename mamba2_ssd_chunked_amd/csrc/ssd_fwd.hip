@@ -576,10 +576,8 @@ static void segment_states_t(const Dims& d, const SegTab& t, const void* xc_, co
     T* hst = (T*)(w + L.hst);
     launch_dt_prep(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32, dt_raw, dt_bias, A_log,
                    seq, dtw, csw, ctot, s);
-    hipLaunchKernelGGL((k_state_walk<T, P, N, false>),
-                       dim3((unsigned)d.H, (unsigned)d.nseg, (unsigned)d.batch), dim3(256), 0, s,
-                       d, t, xc, (const T*)nullptr, dtw, csw, seq, (const float*)nullptr, hst,
-                       (const T*)nullptr, (float*)nullptr, summary);
+    launch_state_walk<T, P, N, false>(d, t, xc, (const T*)nullptr, dtw, csw, seq, nullptr, hst,
+                                      summary, s);
     // the group Gram tiles the output pass reads (local work a multi-GPU caller
     // overlaps with the summary exchange, like the walk above)
     launch_gram<T, N>(d, xc, (T*)(w + L.gram), s);

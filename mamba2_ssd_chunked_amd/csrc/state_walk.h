@@ -18,18 +18,20 @@
 // segment's first chunk (its entering state is zero).  The final value is
 // S_ext (forward) or dL/dS_in of the segment's own outputs (backward), and the
 // product of the alphas the block decay a_block, both written to `summary` if
-// given.  With `gdot`, the forward walk also writes <G_c, H_c> per chunk, G_c
-// read from gdot in the stored layout.
+// given.
 //
 // This is the decay-weighted sum over earlier chunk states that
 // state-spaces/mamba #482 (second comment) identifies as the part of the scan
 // that must cross devices; Megatron-LM #6808 ships its segment-level result as
 // the FP32 summary.
 //
-// A chunk is read in 64-token slices: A rows (scaled by w) and B rows go to LDS
-// in their natural [token][.] layout and both MFMA operands come from
-// transposed LDS reads (XT); the next slice is loaded into registers while the
-// current one is multiplied.
+// A segment is read in slices of KT = 64 tokens (a chunk holds Q / KT of
+// them).  Each slice passes through registers (loaded two slices ahead of its
+// use, with the decay and sequence values of its chunk) into one of two LDS
+// buffers: A rows scaled by w and B rows, both in their natural [token][.]
+// layout, and both MFMA operands come from transposed LDS reads (XT).  While
+// the waves multiply slice s from one buffer they write slice s + 1 into the
+// other, so one barrier per slice suffices.
 #pragma once
 
 #include "ssd_internal.h"
@@ -37,7 +39,7 @@
 
 namespace ssd {
 
-template <typename T, int P, int N, bool BWD>
+template <typename T, int P, int N, bool BWD, bool SEQ>
 __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T* __restrict__ xc,
                                                    const T* __restrict__ dy,
                                                    const float* __restrict__ dt_ws,
@@ -45,26 +47,40 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
                                                    const int32_t* __restrict__ seq,
                                                    const float* __restrict__ init,
                                                    T* __restrict__ store,
-                                                   const T* __restrict__ gdot,
-                                                   float* __restrict__ dotgh,
                                                    float* __restrict__ summary) {
     typedef Mma<T> M;
     typedef typename M::Frag Frag;
     constexpr int KS = M::KS;
-    constexpr int KT = 64;               // tokens per LDS slice
+    constexpr int KT = 64;               // tokens per slice
     constexpr int NTH = 256;
     constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
     constexpr int XR = P + VEC, BR = N + VEC;
     constexpr int PT = P / 16, NTT = N / 16, NTW = (NTT + 3) / 4;
     constexpr int VX = (KT * (P / VEC) + NTH - 1) / NTH;  // A vectors per thread and slice
     constexpr int VB = (KT * (N / VEC) + NTH - 1) / NTH;  // B vectors per thread and slice
-    __shared__ __attribute__((aligned(16))) T sX[KT * XR];
-    __shared__ __attribute__((aligned(16))) T sB[KT * BR];
-    __shared__ float sdot[4];
+    // index checks that hold for every thread of the shape compile away (a
+    // check the compiler cannot drop splits the loop body into small blocks
+    // and forces full waits for the outstanding loads at their joins)
+    constexpr bool XFULL = KT * (P / VEC) % NTH == 0, BFULL = KT * (N / VEC) % NTH == 0;
+    constexpr bool NFULL = NTT % 4 == 0;
+    __shared__ __attribute__((aligned(16))) T sX[2][KT * XR];
+    __shared__ __attribute__((aligned(16))) T sB[2][KT * BR];
     typedef T vt __attribute__((ext_vector_type(VEC)));
 
-    const int h = blockIdx.x, k = blockIdx.y;
-    const int64_t b = blockIdx.z;
+    // block -> (row, segment, head): the walks of one (row, segment) are
+    // consecutive items and consecutive items go to one XCD, so they share that
+    // XCD's L2 for the B (or C) rows they all read
+    int h, k;
+    int64_t b;
+    {
+        constexpr int NXCD = 8;
+        const int64_t n = gridDim.x, i = blockIdx.x;
+        int64_t item = (n % NXCD == 0) ? (i % NXCD) * (n / NXCD) + i / NXCD : i;
+        h = (int)(item % d.H);
+        item /= d.H;
+        k = (int)(item % d.nseg);
+        b = item / d.nseg;
+    }
     const int wave = wave_id(), lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
     const int g = h / d.hpg;
     const int Q = d.Q;
@@ -81,54 +97,70 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
     const T* brow = xc + rb * d.C + (int64_t)d.H * P + (BWD ? (int64_t)d.G * N : 0) + (int64_t)g * N;
     auto chunk_of = [&](int si) { return BWD ? nc - 1 - si / spc : si / spc; };
 
-    // ---- one slice: registers, then LDS (A scaled by its token's weight)
-    vt rx[VX], rbv[VB];
-    float rcs[VX], rdt[VX];
-    int rsq[VX];
-    auto fetch = [&](int si) {
-        const int64_t tb = s0 + (int64_t)chunk_of(si) * Q + (int64_t)(si % spc) * KT;
+    // ---- one slice in registers, with the values of its chunk
+    struct Slice {
+        vt x[VX], b[VB];
+        float cs[VX], dt[VX];
+        int sq[VX];
+        float cse;       // cumulative log decay at the chunk's last token
+        int seqe, seqr;  // sequence of the chunk's last token / of the state entering it
+    };
+    auto fetch = [&](Slice& r, int si) {
+        const int c = chunk_of(si);
+        const int64_t t0 = s0 + (int64_t)c * Q;
+        const int64_t tb = t0 + (int64_t)(si % spc) * KT;
+        r.cse = csp[t0 + Q - 1];
+        // The state entering chunk c belongs to the sequence of the token just
+        // before it; for a row's first segment that is the sequence of the
+        // row's first token (an initial state feeds the first sequence).
+        const int64_t ptok = c > 0 ? t0 - 1 : (pred >= 0 ? pred : s0);
+        r.seqe = SEQ ? seq[rb + t0 + Q - 1] : 0;
+        r.seqr = SEQ ? seq[rb + ptok] : 0;
 #pragma unroll
         for (int q = 0; q < VX; ++q) {
             const int idx = threadIdx.x + q * NTH;
-            if (idx < KT * (P / VEC)) {
+            if (XFULL || idx < KT * (P / VEC)) {
                 const int jj = idx / (P / VEC), pv = idx % (P / VEC);
-                rx[q] = *(const vt*)(arow + (tb + jj) * astr + pv * VEC);
-                rcs[q] = csp[tb + jj];
-                rdt[q] = BWD ? 0.f : dtp[tb + jj];
-                rsq[q] = seq ? seq[rb + tb + jj] : 0;
+                r.x[q] = *(const vt*)(arow + (tb + jj) * astr + pv * VEC);
+                r.cs[q] = csp[tb + jj];
+                r.dt[q] = BWD ? 0.f : dtp[tb + jj];
+                r.sq[q] = SEQ ? seq[rb + tb + jj] : 0;
             }
         }
 #pragma unroll
         for (int q = 0; q < VB; ++q) {
             const int idx = threadIdx.x + q * NTH;
-            if (idx < KT * (N / VEC)) {
+            if (BFULL || idx < KT * (N / VEC)) {
                 const int jj = idx / (N / VEC), nv = idx % (N / VEC);
-                rbv[q] = *(const vt*)(brow + (tb + jj) * d.C + nv * VEC);
+                r.b[q] = *(const vt*)(brow + (tb + jj) * d.C + nv * VEC);
             }
         }
     };
-    // sref: seq_end (forward) or the entering state's sequence (backward)
-    auto stash = [&](float cs_e, int sref) {
+    // A rows scaled by their weights, and B rows, into LDS buffer u; the weight
+    // is zero for tokens of another sequence than seq_end (forward) or than the
+    // entering state's (backward)
+    auto stash = [&](const Slice& r, int u) {
+        const int sref = BWD ? r.seqr : r.seqe;
 #pragma unroll
         for (int q = 0; q < VX; ++q) {
             const int idx = threadIdx.x + q * NTH;
-            if (idx < KT * (P / VEC)) {
+            if (XFULL || idx < KT * (P / VEC)) {
                 const int jj = idx / (P / VEC), pv = idx % (P / VEC);
-                const float w = rsq[q] != sref ? 0.f
-                                : BWD      ? __expf(rcs[q])
-                                           : __expf(cs_e - rcs[q]) * rdt[q];
+                const float w = r.sq[q] != sref ? 0.f
+                                : BWD          ? __expf(r.cs[q])
+                                               : __expf(r.cse - r.cs[q]) * r.dt[q];
                 vt v;
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) v[e] = (T)((float)rx[q][e] * w);
-                *(vt*)&sX[jj * XR + pv * VEC] = v;
+                for (int e = 0; e < VEC; ++e) v[e] = (T)((float)r.x[q][e] * w);
+                *(vt*)&sX[u][jj * XR + pv * VEC] = v;
             }
         }
 #pragma unroll
         for (int q = 0; q < VB; ++q) {
             const int idx = threadIdx.x + q * NTH;
-            if (idx < KT * (N / VEC)) {
+            if (BFULL || idx < KT * (N / VEC)) {
                 const int jj = idx / (N / VEC), nv = idx % (N / VEC);
-                *(vt*)&sB[jj * BR + nv * VEC] = rbv[q];
+                *(vt*)&sB[u][jj * BR + nv * VEC] = r.b[q];
             }
         }
     };
@@ -141,7 +173,7 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
             const int nt = wave + 4 * j;
-            if (init && nt < NTT) {
+            if (init && (NFULL || nt < NTT)) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     acc[pt][j][r] = init[sg * (P * N) + (pt * 16 + 4 * lg + r) * N + nt * 16 + lr];
@@ -150,90 +182,80 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
             }
         }
     float ablk = 1.f;
-    float cs_e = 0.f;
-    int sref = 0;
-    int64_t dot_at = -1;  // dotgh index of the chunk whose <G, H> sits in sdot
 
-    fetch(0);
-    for (int si = 0; si < ns; ++si) {
+    // At a chunk's first slice (held by r): store the running value, then
+    // apply the chunk's decay.
+    auto chunk_start = [&](const Slice& r, int si) {
         const int c = chunk_of(si);
-        if (si % spc == 0) {
-            const int64_t t0 = s0 + (int64_t)c * Q;
-            const int cm = (int)(t0 / Q);
-            cs_e = csp[t0 + Q - 1];
-            const int seq_e = seq ? seq[rb + t0 + Q - 1] : 0;
-            // The state entering chunk c belongs to the sequence of the token just
-            // before it; for a row's first segment that is the sequence of the
-            // row's first token (an initial state feeds the first sequence).
-            const int64_t ptok = c > 0 ? t0 - 1 : (pred >= 0 ? pred : s0);
-            const int seq_ref = seq ? seq[rb + ptok] : 0;
-            sref = BWD ? seq_ref : seq_e;
-            const float alpha = (seq_ref == seq_e) ? expf(cs_e) : 0.f;
-            ablk *= alpha;
-            const int64_t so = (((int64_t)b * d.nchunk + cm) * d.H + h) * (P * N);
-            if (store && (init || BWD || c > 0)) {
-                T* hp = store + so;
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                    for (int j = 0; j < NTW; ++j) {
-                        const int nt = wave + 4 * j;
-                        if (nt < NTT) {
-                            const int n = nt * 16 + lr;
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                hp[(pt * 16 + 4 * lg + r) * N + n] = (T)acc[pt][j][r];
-                        }
-                    }
-            }
-            if (gdot) {
-                float dot = 0.f;
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                    for (int j = 0; j < NTW; ++j) {
-                        const int nt = wave + 4 * j;
-                        if (nt < NTT) {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                dot += (float)gdot[so + (pt * 16 + 4 * lg + r) * N + nt * 16 + lr] *
-                                       acc[pt][j][r];
-                        }
-                    }
-#pragma unroll
-                for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
-                if (lane == 0) sdot[wave] = dot;
-                dot_at = ((int64_t)b * d.nchunk + cm) * d.H + h;
-            }
+        const int cm = (int)((s0 + (int64_t)c * Q) / Q);
+        const float alpha = (r.seqr == r.seqe) ? expf(r.cse) : 0.f;
+        ablk *= alpha;
+        if (store && (init || BWD || c > 0)) {
+            T* hp = store + (((int64_t)b * d.nchunk + cm) * d.H + h) * (P * N);
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-                for (int j = 0; j < NTW; ++j) acc[pt][j] *= alpha;
+                for (int j = 0; j < NTW; ++j) {
+                    const int nt = wave + 4 * j;
+                    if (NFULL || nt < NTT) {
+                        const int n = nt * 16 + lr;
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+                            hp[(pt * 16 + 4 * lg + rr) * N + n] = (T)acc[pt][j][rr];
+                    }
+                }
         }
-        __syncthreads();  // the previous slice's products are done with the LDS
-        if (dot_at >= 0 && threadIdx.x == 0) {
-            dotgh[dot_at] = sdot[0] + sdot[1] + sdot[2] + sdot[3];
-        }
-        dot_at = -1;
-        stash(cs_e, sref);
-        __syncthreads();
-        if (si + 1 < ns) fetch(si + 1);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) acc[pt][j] *= alpha;
+    };
+    // products of the slice in LDS buffer u
+    auto multiply = [&](int u) {
 #pragma unroll
         for (int kk = 0; kk < KT / KS; ++kk) {
             const int jb = kk * KS;
             Frag a[PT];
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) a[pt] = XT<T>::load(sX, XR, jb, pt * 16, lane);
+            for (int pt = 0; pt < PT; ++pt) a[pt] = XT<T>::load(sX[u], XR, jb, pt * 16, lane);
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 const int nt = wave + 4 * j;
-                if (nt < NTT) {
-                    const Frag bb = XT<T>::load(sB, BR, jb, nt * 16, lane);
+                if (NFULL || nt < NTT) {
+                    const Frag bb = XT<T>::load(sB[u], BR, jb, nt * 16, lane);
 #pragma unroll
                     for (int pt = 0; pt < PT; ++pt) acc[pt][j] = M::mma(a[pt], bb, acc[pt][j]);
                 }
             }
         }
+    };
+    // Slice si: `cur` holds it (already in LDS buffer u), `nxt` holds slice
+    // si + 1 (not yet in LDS).  After the barrier every wave is done with the
+    // products of slice si - 1, whose buffer 1 - u takes slice si + 1; `cur`
+    // then takes slice si + 2.  Past the last slice the loads repeat it and its
+    // copy goes to a buffer nobody reads any more: the loads and LDS writes of
+    // every step are unconditional, so they stay in the step's straight-line
+    // code, ahead of the products.
+    Slice r0, r1;
+    auto step = [&](Slice& cur, Slice& nxt, int si, int u, bool live) {
+        __syncthreads();
+        if (live && si % spc == 0) chunk_start(cur, si);
+        fetch(cur, min(si + 2, ns - 1));
+        // the loads stay ahead of the LDS writes, whose waits then cover only
+        // the loads of the slice before
+        __builtin_amdgcn_sched_barrier(0);
+        stash(nxt, 1 - u);
+        if (live) multiply(u);
+    };
+
+    if (ns > 0) {
+        fetch(r0, 0);
+        fetch(r1, min(1, ns - 1));
+        stash(r0, 0);
+    }
+    for (int si = 0; si < ns; si += 2) {
+        step(r0, r1, si, 0, true);
+        step(r1, r0, si + 1, 1, si + 1 < ns);
     }
 
     if (!summary) return;
@@ -243,7 +265,7 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
             const int nt = wave + 4 * j;
-            if (nt < NTT) {
+            if (NFULL || nt < NTT) {
                 const int n = nt * 16 + lr;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sx[(pt * 16 + 4 * lg + r) * N + n] = acc[pt][j][r];
@@ -251,6 +273,21 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
         }
     if (threadIdx.x == 0)
         summary[(int64_t)d.nseg * per + ((int64_t)k * d.batch + b) * d.H + h] = ablk;
+}
+
+// One walk per (row, segment, head), see k_state_walk; A = x (forward) or dy
+// (backward).
+template <typename T, int P, int N, bool BWD>
+inline void launch_state_walk(const Dims& d, const SegTab& t, const T* xc, const T* dy,
+                              const float* dt_ws, const float* cs_ws, const int32_t* seq,
+                              const float* init, T* store, float* summary, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)d.H * d.nseg * d.batch));
+    if (seq)
+        hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, true>), grid, dim3(256), 0, s, d, t, xc, dy,
+                           dt_ws, cs_ws, seq, init, store, summary);
+    else
+        hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, false>), grid, dim3(256), 0, s, d, t, xc,
+                           dy, dt_ws, cs_ws, seq, init, store, summary);
 }
 
 }  // namespace ssd

@@ -51,11 +51,15 @@ def _bwd_small(name):
     if name == "bf16_q128":
         return mk(name, batch=2, seqlen=1024, nheads=2, headdim=32, dstate=64, ngroups=1,
                   chunk=128, act="bf16", seed=307, nseg=2, packed=(60, 300), **kw)
+    if name == "bf16_blocks":
+        # 16 heads in one group: two head blocks of 8 per group, summed per group
+        return mk(name, batch=1, seqlen=1024, nheads=16, headdim=64, dstate=128, ngroups=1,
+                  chunk=256, act="bf16", seed=308, nseg=2, packed=(100, 700), **kw)
     raise KeyError(name)
 
 
 SMALL = ["tiny_f32", "slow_tiny_f32", "f32_head_thd", "f32_virtual", "bf16_small", "bf16_virtual", "bf16_thd",
-         "bf16_q64", "bf16_q128"]
+         "bf16_q64", "bf16_q128", "bf16_blocks"]
 
 
 def run_fwd_bwd(wl, inputs=None):
