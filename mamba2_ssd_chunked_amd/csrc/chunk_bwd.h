@@ -88,7 +88,9 @@ struct ChunkBwdHB {
     static constexpr int O_D = Q * XR, O_G = 2 * Q * XR, O_H = O_G + P * GR, O_RW = O_H + P * GR;
     static constexpr int E_HEAD = O_RW + NW * Q * 4 / (int)sizeof(T);
     // final phase: Z rows and C^T (then G of HG heads), later B^T and H
-    static constexpr int HG = 4;  // heads per round of state terms
+    // heads per round of state terms: 2 below Q = 256 keeps the LDS of a
+    // workgroup within half a CU's, so two workgroups share a CU
+    static constexpr int HG = Q >= 256 ? 4 : 2;
     static constexpr int O_BT = zoff(QT), E_FIN = O_BT + Q * BR, E_FS = O_BT + HG * P * GR;
     static constexpr int E_U = cmax(E_HEAD, cmax(E_FIN, E_FS));
     static constexpr size_t LDS =
@@ -97,7 +99,7 @@ struct ChunkBwdHB {
 };
 
 template <typename T, int P, int N, int Q>
-__global__ void __launch_bounds__(Q / 32 * 64, 1) k_chunk_bwd_hb(
+__global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     Dims d, SegTab tab, int hbs, const T* __restrict__ xc, const T* __restrict__ dy,
     const T* __restrict__ gramT, const float* __restrict__ Dp,
     const float* __restrict__ dt_ws, const float* __restrict__ cs_ws,

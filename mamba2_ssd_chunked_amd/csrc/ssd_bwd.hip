@@ -1395,15 +1395,26 @@ __global__ void __launch_bounds__(256) k_bwd_reduce(Dims d, const float* __restr
     const int nout = CW + 3 * d.H;
     const int col = threadIdx.x % 32, gq = threadIdx.x / 32;
     const int o = blockIdx.x * 32 + col;
-    float s = 0.f;
+    // each group sums its partials in four interleaved chains, so four loads
+    // are in flight at a time; the order of the additions is fixed
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
     if (o < CW) {
         const int64_t ntot = d.batch * (d.L / 64);
-        for (int64_t t = gq; t < ntot; t += 8) s += dwp[t * CW + o];
+        int64_t t = gq;
+        for (; t + 24 < ntot; t += 32)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s4[u] += dwp[(t + 8 * u) * CW + o];
+        for (; t < ntot; t += 8) s4[0] += dwp[t * CW + o];
     } else if (o < nout) {
         const int j = o - CW, h = j / 3, q = j % 3;
         const int64_t ntot = d.batch * d.nchunk;
-        for (int64_t bc = gq; bc < ntot; bc += 8) s += red[(bc * d.H + h) * 3 + q];
+        int64_t bc = gq;
+        for (; bc + 24 < ntot; bc += 32)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s4[u] += red[((bc + 8 * u) * d.H + h) * 3 + q];
+        for (; bc < ntot; bc += 8) s4[0] += red[(bc * d.H + h) * 3 + q];
     }
+    const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     part[gq][col] = s;
     __syncthreads();
     if (gq == 0 && o < nout) {
