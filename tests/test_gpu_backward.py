@@ -165,6 +165,22 @@ def test_backward_packed_thd_full():
         assert_close(got[name], ref[name], wl.act, f"packed thd {name}")
 
 
+def test_maximum_segment_count():
+    """SSD_MAX_SEGMENTS (64) segments of one 64-token chunk each, with packed
+    sequences crossing them: y and every gradient against the oracle.  Each walk
+    then covers a single slice."""
+    wl = W.make_workload("max_segments", batch=1, seqlen=4096, nheads=2, headdim=64,
+                         dstate=64, ngroups=1, chunk=64, act="bf16", seed=309, nseg=64,
+                         packed=(30, 400), with_dy=True)
+    log(f"[backward] {wl.name}: {len(wl.segments)} segments")
+    _, _, fb, bb = run_fwd_bwd(wl)
+    ref = oracle.backward(wl)
+    assert_close(wl.to_causal(to_np(fb.y)), ref["y"], wl.act, "y, 64 segments")
+    got = gpu_grads(wl, bb)
+    for name in GRADS:
+        assert_close(got[name], ref[name], wl.act, f"{name}, 64 segments")
+
+
 @pytest.mark.parametrize("cfg", ["long_context_bf16", "long_context_virtual_bf16"])
 def test_backward_long_context_sampled_heads(cfg):
     """131072 tokens, 64 heads in 8 groups: the full backward on the GPU; the gradients
