@@ -34,13 +34,15 @@
 // other, so one barrier per slice suffices.
 #pragma once
 
+#include <type_traits>
+
 #include "ssd_internal.h"
 #include "xt.h"
 
 namespace ssd {
 
-template <typename T, int P, int N, bool BWD, bool SEQ>
-__global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T* __restrict__ xc,
+template <typename T, int P, int N, bool BWD, bool SEQ, int HW>
+__global__ void __launch_bounds__(256 * HW) k_state_walk(Dims d, SegTab tab, const T* __restrict__ xc,
                                                    const T* __restrict__ dy,
                                                    const float* __restrict__ dt_ws,
                                                    const float* __restrict__ cs_ws,
@@ -52,36 +54,40 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
     typedef typename M::Frag Frag;
     constexpr int KS = M::KS;
     constexpr int KT = 64;               // tokens per slice
-    constexpr int NTH = 256;
+    constexpr int NTH = 256 * HW, HTH = 256;  // threads of the block / of one head
     constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
     constexpr int XR = P + VEC, BR = N + VEC;
     constexpr int PT = P / 16, NTT = N / 16, NTW = (NTT + 3) / 4;
-    constexpr int VX = (KT * (P / VEC) + NTH - 1) / NTH;  // A vectors per thread and slice
+    constexpr int VX = (KT * (P / VEC) + HTH - 1) / HTH;  // A vectors per thread and slice
     constexpr int VB = (KT * (N / VEC) + NTH - 1) / NTH;  // B vectors per thread and slice
     // index checks that hold for every thread of the shape compile away (a
     // check the compiler cannot drop splits the loop body into small blocks
     // and forces full waits for the outstanding loads at their joins)
-    constexpr bool XFULL = KT * (P / VEC) % NTH == 0, BFULL = KT * (N / VEC) % NTH == 0;
+    constexpr bool XFULL = KT * (P / VEC) % HTH == 0, BFULL = KT * (N / VEC) % NTH == 0;
     constexpr bool NFULL = NTT % 4 == 0;
-    __shared__ __attribute__((aligned(16))) T sX[2][KT * XR];
+    __shared__ __attribute__((aligned(16))) T sX[2][HW][KT * XR];
     __shared__ __attribute__((aligned(16))) T sB[2][KT * BR];
     typedef T vt __attribute__((ext_vector_type(VEC)));
 
-    // block -> (row, segment, head): the walks of one (row, segment) are
-    // consecutive items and consecutive items go to one XCD, so they share that
-    // XCD's L2 for the B (or C) rows they all read
+    // block -> (row, segment, HW heads of one group): the walks of one (row,
+    // segment) are consecutive items and consecutive items go to one XCD, so
+    // they share that XCD's L2 for the B (or C) rows they all read.  The HW
+    // heads of a block share its B (or C) rows in LDS; threads hs*256 ..
+    // hs*256+255 (four waves) walk head h0 + hs.
+    const int hs = threadIdx.x / HTH;
     int h, k;
     int64_t b;
     {
         constexpr int NXCD = 8;
         const int64_t n = gridDim.x, i = blockIdx.x;
         int64_t item = (n % NXCD == 0) ? (i % NXCD) * (n / NXCD) + i / NXCD : i;
-        h = (int)(item % d.H);
-        item /= d.H;
+        h = (int)(item % (d.H / HW)) * HW + hs;
+        item /= d.H / HW;
         k = (int)(item % d.nseg);
         b = item / d.nseg;
     }
-    const int wave = wave_id(), lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
+    const int wave = wave_id() % 4, lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
+    const int ht = threadIdx.x % HTH;  // thread index within the head
     const int g = h / d.hpg;
     const int Q = d.Q;
     const int64_t rb = b * d.L;
@@ -118,7 +124,7 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
         r.seqr = SEQ ? seq[rb + ptok] : 0;
 #pragma unroll
         for (int q = 0; q < VX; ++q) {
-            const int idx = threadIdx.x + q * NTH;
+            const int idx = ht + q * HTH;
             if (XFULL || idx < KT * (P / VEC)) {
                 const int jj = idx / (P / VEC), pv = idx % (P / VEC);
                 r.x[q] = *(const vt*)(arow + (tb + jj) * astr + pv * VEC);
@@ -143,7 +149,7 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
         const int sref = BWD ? r.seqr : r.seqe;
 #pragma unroll
         for (int q = 0; q < VX; ++q) {
-            const int idx = threadIdx.x + q * NTH;
+            const int idx = ht + q * HTH;
             if (XFULL || idx < KT * (P / VEC)) {
                 const int jj = idx / (P / VEC), pv = idx % (P / VEC);
                 const float w = r.sq[q] != sref ? 0.f
@@ -152,7 +158,7 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
                 vt v;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) v[e] = (T)((float)r.x[q][e] * w);
-                *(vt*)&sX[u][jj * XR + pv * VEC] = v;
+                *(vt*)&sX[u][hs][jj * XR + pv * VEC] = v;
             }
         }
 #pragma unroll
@@ -217,7 +223,7 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
             const int jb = kk * KS;
             Frag a[PT];
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) a[pt] = XT<T>::load(sX[u], XR, jb, pt * 16, lane);
+            for (int pt = 0; pt < PT; ++pt) a[pt] = XT<T>::load(sX[u][hs], XR, jb, pt * 16, lane);
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 const int nt = wave + 4 * j;
@@ -271,7 +277,7 @@ __global__ void __launch_bounds__(256) k_state_walk(Dims d, SegTab tab, const T*
                 for (int r = 0; r < 4; ++r) sx[(pt * 16 + 4 * lg + r) * N + n] = acc[pt][j][r];
             }
         }
-    if (threadIdx.x == 0)
+    if (ht == 0)
         summary[(int64_t)d.nseg * per + ((int64_t)k * d.batch + b) * d.H + h] = ablk;
 }
 
@@ -281,12 +287,24 @@ template <typename T, int P, int N, bool BWD>
 inline void launch_state_walk(const Dims& d, const SegTab& t, const T* xc, const T* dy,
                               const float* dt_ws, const float* cs_ws, const int32_t* seq,
                               const float* init, T* store, float* summary, hipStream_t s) {
+    // two heads of a group per block where they exist (bf16: the float32
+    // accumulators of two heads would not fit two waves per SIMD)
+    if (std::is_same<T, bf16>::value && d.hpg % 2 == 0) {
+        const dim3 grid((unsigned)((int64_t)(d.H / 2) * d.nseg * d.batch));
+        if (seq)
+            hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, true, 2>), grid, dim3(512), 0, s, d, t,
+                               xc, dy, dt_ws, cs_ws, seq, init, store, summary);
+        else
+            hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, false, 2>), grid, dim3(512), 0, s, d, t,
+                               xc, dy, dt_ws, cs_ws, seq, init, store, summary);
+        return;
+    }
     const dim3 grid((unsigned)((int64_t)d.H * d.nseg * d.batch));
     if (seq)
-        hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, true>), grid, dim3(256), 0, s, d, t, xc, dy,
-                           dt_ws, cs_ws, seq, init, store, summary);
+        hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, true, 1>), grid, dim3(256), 0, s, d, t, xc,
+                           dy, dt_ws, cs_ws, seq, init, store, summary);
     else
-        hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, false>), grid, dim3(256), 0, s, d, t, xc,
+        hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, false, 1>), grid, dim3(256), 0, s, d, t, xc,
                            dy, dt_ws, cs_ws, seq, init, store, summary);
 }
 
