@@ -2,7 +2,7 @@
 // block of HB heads of one group).
 //
 // Per chunk, with S_ij = C_i . B_j (the group's causal Gram tiles, transposed
-// orientation from k_gram<TRANS>), W^h_ij = dy^h_i . x^h_j, the decay
+// orientation from the Gram pass with TRANS), W^h_ij = dy^h_i . x^h_j, the decay
 // L^h_ij = exp(cs_i - cs_j) [j <= i, same sequence] and
 //   Z_ij = sum over the block's heads of W^h_ij L^h_ij dt^h_j,
 // the gradients of the intra-chunk term are

@@ -14,6 +14,7 @@
 // chunk backward consumes.
 #pragma once
 
+#include "dt_prep.h"
 #include "ssd_internal.h"
 
 namespace ssd {
@@ -25,16 +26,18 @@ __host__ __device__ constexpr int gram_index(int a, int b) { return a * (a + 1) 
 // group, row): 2048 waves at the mixer shard's shape, each with a few
 // independent tile products to keep loads in flight.
 constexpr int GSPLIT = 4;
-template <typename T, int N, bool TRANS = false>
-__global__ void __launch_bounds__(64) k_gram(Dims d, const T* __restrict__ xc, T* __restrict__ gram) {
+// One block of the Gram pass: bx = (tile pair, source-tile part), by =
+// (chunk, group), b = row.
+template <typename T, int N, bool TRANS>
+__device__ __forceinline__ void gram_block(const Dims& d, const T* __restrict__ xc,
+                                           T* __restrict__ gram, int bx, int by, int64_t b) {
     typedef Mma<T> M;
     typedef typename M::Frag Frag;
     constexpr int SL = M::SL, KS = M::KS, NKF = N / KS;
     typedef T t4 __attribute__((ext_vector_type(4)));
     const int QT = d.Q / 16;
-    const int w = blockIdx.x / GSPLIT, part = blockIdx.x % GSPLIT;
-    const int g = blockIdx.y % d.G, cm = blockIdx.y / d.G;
-    const int64_t b = blockIdx.z;
+    const int w = bx / GSPLIT, part = bx % GSPLIT;
+    const int g = by % d.G, cm = by / d.G;
     const int lane = threadIdx.x, lr = lane % 16, lg = lane / 16;
     const int64_t t0 = b * d.L + (int64_t)cm * d.Q;
     const int64_t boff = (int64_t)d.H * d.P + (int64_t)g * N;
@@ -61,12 +64,40 @@ __global__ void __launch_bounds__(64) k_gram(Dims d, const T* __restrict__ xc, T
     }
 }
 
+// The Gram pass and dt prep in one launch: the first blocks are Gram blocks,
+// the rest one wave per (row, chunk, head) of dt prep.  The two read different
+// inputs (B, C and dt_raw) and have no order between them, so their blocks
+// share the chip instead of running one kernel after the other.
+template <typename T, int N, bool TRANS>
+__global__ void __launch_bounds__(64) k_gram_dt(Dims d, const T* __restrict__ xc,
+                                               T* __restrict__ gram, int64_t ngram,
+                                               const T* __restrict__ dt_raw,
+                                               const float* __restrict__ dt_bias,
+                                               const float* __restrict__ A_log,
+                                               const int32_t* __restrict__ seq,
+                                               float* __restrict__ dt_ws,
+                                               float* __restrict__ cs_ws,
+                                               float* __restrict__ ctot) {
+    const int64_t i = blockIdx.x;
+    if (i < ngram) {
+        const int gx = d.Q / 16 / 2 * GSPLIT, gy = d.nchunk * d.G;
+        gram_block<T, N, TRANS>(d, xc, gram, (int)(i % gx), (int)((i / gx) % gy), i / gx / gy);
+    } else {
+        const int64_t j = i - ngram;
+        dt_prep_wave<T>(d, dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot,
+                        (int)((j / d.H) % d.nchunk), (int)(j % d.H), j / d.H / d.nchunk,
+                        threadIdx.x);
+    }
+}
+
 template <typename T, int N, bool TRANS = false>
-inline void launch_gram(const Dims& d, const T* xc, T* gram, hipStream_t s) {
-    const int QT = d.Q / 16;
-    hipLaunchKernelGGL((k_gram<T, N, TRANS>), dim3((unsigned)(QT / 2 * GSPLIT), (unsigned)(d.nchunk * d.G),
-                                            (unsigned)d.batch),
-                       dim3(64), 0, s, d, xc, gram);
+inline void launch_gram_dt(const Dims& d, const T* xc, T* gram, const void* dt_raw,
+                           const float* dt_bias, const float* A_log, const int32_t* seq,
+                           float* dt_ws, float* cs_ws, float* ctot, hipStream_t s) {
+    const int64_t ngram = (int64_t)(d.Q / 16 / 2 * GSPLIT) * d.nchunk * d.G * d.batch;
+    const int64_t ndt = (int64_t)d.nchunk * d.H * d.batch;
+    hipLaunchKernelGGL((k_gram_dt<T, N, TRANS>), dim3((unsigned)(ngram + ndt)), dim3(64), 0, s, d,
+                       xc, gram, ngram, (const T*)dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot);
 }
 
 }  // namespace ssd

@@ -1538,15 +1538,19 @@ static void bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a, floa
     T* xc = (T*)(ws + L.xc);
     launch_conv1d_fwd(d, t, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32, a.xBC, a.conv_w,
                       a.seq, xc, s);
-    if (hb_path<T, P, N>(d.Q))
-        launch_gram<T, N, true>(d, xc, (T*)(ws + L.gramt), s);
-    else
+    if (hb_path<T, P, N>(d.Q)) {
+        // the transposed Gram tiles and dt prep in one launch
+        launch_gram_dt<T, N, true>(d, xc, (T*)(ws + L.gramt), a.dt_raw, a.dt_bias, a.A_log, a.seq,
+                                   (float*)(ws + L.dt), (float*)(ws + L.cs),
+                                   (float*)(ws + L.ctot), s);
+    } else {
         hipLaunchKernelGGL(k_bc_transpose<T>,
                            dim3((unsigned)d.nchunk, (unsigned)d.G, (unsigned)d.batch), dim3(256), 0,
                            s, d, (const T*)xc, (T*)(ws + L.bct));
-    launch_dt_prep(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32, a.dt_raw, a.dt_bias,
-                   a.A_log, a.seq, (float*)(ws + L.dt), (float*)(ws + L.cs),
-                   (float*)(ws + L.ctot), s);
+        launch_dt_prep(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32, a.dt_raw, a.dt_bias,
+                       a.A_log, a.seq, (float*)(ws + L.dt), (float*)(ws + L.cs),
+                       (float*)(ws + L.ctot), s);
+    }
     if (hb_path<T, P, N>(d.Q)) {
         // the reverse walk from a zero final gradient: dL/dS_in of each segment's
         // own outputs and its block decay

@@ -27,16 +27,13 @@
 //                  callers that keep y_zero.
 #include <type_traits>
 
+#include "dt_prep.h"
 #include "gram.h"
 #include "ssd_internal.h"
 #include "state_walk.h"
 #include "xt.h"
 
 namespace ssd {
-
-__device__ __forceinline__ float softplus_f(float z) {
-    return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
-}
 
 // Operand whose k slots follow the layout of an MFMA output tile reused as the
 // B operand: with 16x16 output tiles stacked along k, slot s of lane group g
@@ -54,11 +51,7 @@ template <> struct KPerm<float> {
 };
 
 // ---------------------------------------------------------------------------
-// dt prep, one wave per (row, chunk, head), four heads per workgroup; lane l
-// owns the Q/64 consecutive tokens l*Q/64 ...  The cumsum restarts at every
-// packed-sequence start inside the chunk (a segmented scan), so a sequence's
-// decays are computed from its own tokens only and perturbing one sequence
-// cannot change another's bits.
+// dt prep on its own (the paths without Gram tiles), four heads per workgroup.
 template <typename T>
 __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ dt_raw,
                                                 const float* __restrict__ dt_bias,
@@ -66,63 +59,10 @@ __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ d
                                                 const int32_t* __restrict__ seq,
                                                 float* __restrict__ dt_ws, float* __restrict__ cs_ws,
                                                 float* __restrict__ ctot) {
-    const int cm = blockIdx.x, h = blockIdx.y * 4 + wave_id();
-    const int64_t b = blockIdx.z;
+    const int h = blockIdx.y * 4 + wave_id();
     if (h >= d.H) return;
-    const int lane = threadIdx.x % 64;
-    const int Q = d.Q;
-    const int E = Q / 64;  // tokens per lane (1, 2 or 4)
-    const int64_t tok0 = b * d.L + (int64_t)cm * Q + lane * E;
-    const float A = -expf(A_log[h]);
-    const float bias = dt_bias[h];
-    float dtv[4], csl[4];
-    bool rs[4];  // a sequence starts at or before this token, inside this lane
-    bool lflag = false;
-    float run = 0.f;
-    int sprev = (seq && lane * E > 0) ? seq[tok0 - 1] : 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        if (e < E) {
-            const int j = lane * E + e;
-            const int sj = seq ? seq[tok0 + e] : 0;
-            const bool start = j > 0 && sj != sprev;
-            sprev = sj;
-            lflag = lflag || start;
-            rs[e] = lflag;
-            if (start) run = 0.f;
-            const float z = to_f(dt_raw[(tok0 + e) * d.H + h]) + bias;
-            const float dt = fminf(fmaxf(softplus_f(z), d.dt_min), d.dt_max);
-            dtv[e] = dt;
-            run += dt * A;
-            csl[e] = run;
-        }
-    }
-    // Segmented inclusive scan of (flag, sum) across the wave:
-    // (f1, v1) then (f2, v2) -> (f1 | f2, f2 ? v2 : v1 + v2).
-    float iv = run;
-    bool ifl = lflag;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float v = __shfl_up(iv, off, 64);
-        const int f = __shfl_up((int)ifl, off, 64);
-        if (lane >= off) {
-            if (!ifl) iv += v;
-            ifl = ifl || f;
-        }
-    }
-    float ev = __shfl_up(iv, 1, 64);
-    if (lane == 0) ev = 0.f;
-    const int64_t o = ((int64_t)b * d.H + h) * d.L + (int64_t)cm * Q + lane * E;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        if (e < E) {
-            dt_ws[o + e] = dtv[e];
-            cs_ws[o + e] = rs[e] ? csl[e] : ev + csl[e];
-        }
-    }
-    // the chunk total is the last token's cumulative sum, bit for bit
-    if (lane == 63)
-        ctot[((int64_t)b * d.H + h) * d.nchunk + cm] = rs[E - 1] ? csl[E - 1] : ev + csl[E - 1];
+    dt_prep_wave<T>(d, dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot, blockIdx.x, h, blockIdx.z,
+                    threadIdx.x % 64);
 }
 
 // ---------------------------------------------------------------------------
@@ -132,7 +72,7 @@ __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ d
 //
 // For output token i and source token j <= i of the same packed sequence the
 // intra-chunk weight is (C_i . B_j) exp(cs_i - cs_j) dt_j.  C_i . B_j comes
-// from the group's Gram tiles (k_gram); every load the workgroup needs (X of the
+// from the group's Gram tiles (k_gram_dt); every load the workgroup needs (X of the
 // head in its natural layout, the entering state, the Gram tiles of the wave's
 // two output tiles, the decays) is issued up front, so one memory latency is
 // paid per workgroup and about 58 KB of LDS lets two workgroups share a CU.
@@ -574,13 +514,11 @@ static void segment_states_t(const Dims& d, const SegTab& t, const void* xc_, co
     float* csw = (float*)(w + L.cs);
     float* ctot = (float*)(w + L.ctot);
     T* hst = (T*)(w + L.hst);
-    launch_dt_prep(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32, dt_raw, dt_bias, A_log,
-                   seq, dtw, csw, ctot, s);
+    // the group Gram tiles the output pass reads and dt prep share one launch
+    // (independent inputs); the walk then needs dt and the cumulative sums
+    launch_gram_dt<T, N>(d, xc, (T*)(w + L.gram), dt_raw, dt_bias, A_log, seq, dtw, csw, ctot, s);
     launch_state_walk<T, P, N, false>(d, t, xc, (const T*)nullptr, dtw, csw, seq, nullptr, hst,
                                       summary, s);
-    // the group Gram tiles the output pass reads (local work a multi-GPU caller
-    // overlaps with the summary exchange, like the walk above)
-    launch_gram<T, N>(d, xc, (T*)(w + L.gram), s);
 }
 
 // y_zero (FINAL = false) or the corrected y (FINAL = true), from the workspace
