@@ -16,7 +16,7 @@
 //   dC_i += sum_h f_i H^T dy_i,
 // with f_i = exp(cs_i) [i in the entering state's sequence] and
 // g_j = exp(cs_e - cs_j) [j in the last token's sequence].  The ddt terms are
-// the ones the per-head kernel produced (see k_ddt): row and column sums of
+// the ones the per-head kernel produced (see ddt_wave): row and column sums of
 // F = S W L dt, u_i = f_i dy_i . (H C_i), v_j = dt_j x_j . (g_j G B_j),
 // q_j = x_j . (dx_j / dt_j without the D term), the dD partial, and <G, H>
 // of every chunk and head.
@@ -422,7 +422,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
             const float Kj = sum_groups(kacc);
             if (lg == 0) {
                 float* tp = tokp + (hl + j) * 4;
-                tp[0] = ui - Kj;  // R_j is added by k_ddt from the row sums
+                tp[0] = ui - Kj;  // R_j is added by the ddt assembly from the row sums
                 tp[1] = qj;
                 tp[2] = vj;
             }

@@ -15,14 +15,15 @@
 //   reverse boundary scan (ssd_boundary_scan, reverse = 1) -> the gradient of
 //     every segment's final state.
 //   pass phase (ssd_segment_bwd_pass): the true exit gradient and entering
-//     state of every chunk (k_state_pass from dS_out and S_in).
+//     state of every chunk (the reverse walk from dS_out and the forward walk
+//     from S_in; k_state_pass on the headdim-128 path).
 //   chunk phase (ssd_segment_bwd_chunks): k_chunk_bwd per chunk and head: dx,
 //     dB, dC and the ddt partial sums, written into the buffers the conv
 //     backward consumes.
-//   conv phase (ssd_conv1d_bwd): k_ddt (ddt per token), k_bc_blocksum (dB, dC
-//     summed over head blocks), k_conv_bwd
-//     (SiLU' and the transposed conv, with a right halo from the causal
-//     successor segment) and k_bwd_reduce (deterministic parameter gradients).
+//   conv phase (ssd_conv1d_bwd): k_bc_blocksum (dB, dC summed over head
+//     blocks), k_conv_bwd_ddt (SiLU' and the transposed conv, with a right halo
+//     from the causal successor segment, and in the same launch the ddt
+//     assembly per token) and k_bwd_reduce (deterministic parameter gradients).
 //
 // ddt without recomputing y.  dL/d(dt_t A) sums, over every (source j, output
 // i) pair with j < t <= i, the derivative of their decay.  Per chunk that is
@@ -425,7 +426,7 @@ __global__ void __launch_bounds__(256) k_state_pass(
 // and j-blocks (phase A) of KS tokens are
 // staged once per workgroup in LDS, double buffered; transposed operands come
 // pre-transposed in the permuted token order.  Per-token partial sums for ddt
-// go to the workspace; k_ddt assembles ddt per chunk.
+// go to the workspace; the ddt assembly (ddt_wave) combines them per chunk.
 template <typename T, int P, int N, int Q, int TPW>
 struct ChunkBwd {
     typedef Mma<T> M;
@@ -1058,7 +1059,7 @@ __global__ void __launch_bounds__(Q / (16 * TPW) * 64) k_chunk_bwd(
         const float K_j = dt_j[jt] * sum_groups(kq[jt]);
         if (lg == 0) {
             float* tp = tokp + (hl + tj) * 4;
-            tp[0] = u_t[jt] - K_j;  // R_i is added by k_ddt from the row sums
+            tp[0] = u_t[jt] - K_j;  // R_i is added by the ddt assembly from the row sums
             tp[1] = q_t[jt];
             tp[2] = v_t[jt];
         }
@@ -1087,22 +1088,32 @@ __global__ void __launch_bounds__(Q / (16 * TPW) * 64) k_chunk_bwd(
 //                  + sum_{j < t} v_j + exp(cs_end) <G_exit, H_enter>,
 // exactly 0 at a token that starts a packed sequence; then
 // ddt_t = q_t + A dL/d(dt_t A) and the chain through clamp and softplus.
+// The arguments of the ddt assembly, passed whole to the kernels that run it.
 template <typename T>
-__global__ void __launch_bounds__(64) k_ddt(Dims d, SegTab tab,
-                                           const T* __restrict__ dt_raw,
-                                           const float* __restrict__ dt_bias,
-                                           const float* __restrict__ A_log,
-                                           const float* __restrict__ dt_ws,
-                                           const float* __restrict__ cs_ws,
-                                           const int32_t* __restrict__ seq,
-                                           const float* __restrict__ rpart,
-                                           const float* __restrict__ tokp,
-                                           const float* __restrict__ dotgh,
-                                           const float* __restrict__ red4, T* __restrict__ ddt_raw,
-                                           float* __restrict__ red) {
-    const int cm = blockIdx.x, h = blockIdx.y;
-    const int64_t b = blockIdx.z;
-    const int lane = threadIdx.x;
+struct DdtArgs {
+    const T* dt_raw;
+    const float *dt_bias, *A_log, *dt_ws, *cs_ws;
+    const int32_t* seq;
+    const float *rpart, *tokp, *dotgh, *red4;
+    T* ddt_raw;
+    float* red;
+};
+
+template <typename T>
+__device__ __forceinline__ void ddt_wave(const Dims& d, const SegTab& tab, const DdtArgs<T>& g,
+                                         int cm, int h, int64_t b, int lane) {
+    const T* __restrict__ dt_raw = g.dt_raw;
+    const float* __restrict__ dt_bias = g.dt_bias;
+    const float* __restrict__ A_log = g.A_log;
+    const float* __restrict__ dt_ws = g.dt_ws;
+    const float* __restrict__ cs_ws = g.cs_ws;
+    const int32_t* __restrict__ seq = g.seq;
+    const float* __restrict__ rpart = g.rpart;
+    const float* __restrict__ tokp = g.tokp;
+    const float* __restrict__ dotgh = g.dotgh;
+    const float* __restrict__ red4 = g.red4;
+    T* __restrict__ ddt_raw = g.ddt_raw;
+    float* __restrict__ red = g.red;
     const int Q = d.Q, E = Q / 64;
     const int64_t rb = b * d.L, t0 = (int64_t)cm * Q;
     const int64_t hl = ((int64_t)b * d.H + h) * d.L + t0;
@@ -1239,21 +1250,23 @@ __global__ void __launch_bounds__(256) k_bc_blocksum(Dims d, int nblk, int bpg,
 // read from dvx (x channels, [token][H*P]) or dbc (B and C channels,
 // [token][G][2N]).  dconv_w is written per 64-token block and reduced later.
 template <typename T, int W>
-__global__ void __launch_bounds__(256) k_conv_bwd(Dims d, SegTab tab, const T* __restrict__ xBC,
-                                                 const float* __restrict__ w,
-                                                 const int32_t* __restrict__ seq,
-                                                 const T* __restrict__ dvx,
-                                                 const T* __restrict__ dbc,
-                                                 T* __restrict__ dxBC, float* __restrict__ dwp) {
+__device__ __forceinline__ void conv_bwd_block(const Dims& d, const SegTab& tab,
+                                               const T* __restrict__ xBC,
+                                               const float* __restrict__ w,
+                                               const int32_t* __restrict__ seq,
+                                               const T* __restrict__ dvx,
+                                               const T* __restrict__ dbc, T* __restrict__ dxBC,
+                                               float* __restrict__ dwp, int bx, int by,
+                                               int64_t bz) {
     constexpr int TPT = CONV_TPT;
     constexpr int RX = TPT + 2 * (W - 1);  // x rows: offsets -(W-1) .. TPT+W-2
     constexpr int RD = TPT + W - 1;        // du rows: offsets 0 .. TPT+W-2
     typedef T vt __attribute__((ext_vector_type(4)));
     __shared__ float wred[4][64][4 * W];
     const int lane = threadIdx.x % 64, wave = wave_id();
-    const int c = (blockIdx.x * 64 + lane) * 4;
-    const int64_t b = blockIdx.z;
-    const int64_t t0 = (int64_t)blockIdx.y * CONV_TT + wave * TPT;
+    const int c = (bx * 64 + lane) * 4;
+    const int64_t b = bz;
+    const int64_t t0 = (int64_t)by * CONV_TT + wave * TPT;
     const int64_t rb = b * d.L;
     const bool active = c < d.C;
     const int k = conv_seg(tab, t0);
@@ -1373,10 +1386,36 @@ __global__ void __launch_bounds__(256) k_conv_bwd(Dims d, SegTab tab, const T* _
     __syncthreads();
     for (int q = threadIdx.x; q < 64 * 4 * W; q += blockDim.x) {
         const int ln = q / (4 * W), j = q % (4 * W);
-        const int cc = (blockIdx.x * 64 + ln) * 4 + j / W;
+        const int cc = (bx * 64 + ln) * 4 + j / W;
         const float sum = wred[0][ln][j] + wred[1][ln][j] + wred[2][ln][j] + wred[3][ln][j];
-        if (cc < d.C) dwp[(((int64_t)b * (d.L / CONV_TT) + blockIdx.y) * d.C + cc) * W + (j % W)] = sum;
+        if (cc < d.C) dwp[(((int64_t)b * (d.L / CONV_TT) + by) * d.C + cc) * W + (j % W)] = sum;
     }
+}
+
+// The conv backward blocks, then the ddt assembly, one wave per (row, chunk,
+// head), in the same launch: the two are independent (only the final
+// reduction needs both), and the ddt waves fill the last, partial round of
+// conv blocks.
+template <typename T, int W>
+__global__ void __launch_bounds__(256) k_conv_bwd_ddt(Dims d, SegTab tab, const T* __restrict__ xBC,
+                                                     const float* __restrict__ w,
+                                                     const int32_t* __restrict__ seq,
+                                                     const T* __restrict__ dvx,
+                                                     const T* __restrict__ dbc,
+                                                     T* __restrict__ dxBC,
+                                                     float* __restrict__ dwp, DdtArgs<T> g) {
+    const int gx = (d.C + 255) / 256, gy = d.L / CONV_TT;
+    const int64_t nconv = (int64_t)gx * gy * d.batch;
+    const int64_t i = blockIdx.x;
+    if (i < nconv) {
+        conv_bwd_block<T, W>(d, tab, xBC, w, seq, dvx, dbc, dxBC, dwp, (int)(i % gx),
+                             (int)((i / gx) % gy), i / gx / gy);
+        return;
+    }
+    const int64_t item = (i - nconv) * 4 + wave_id();
+    if (item >= (int64_t)d.nchunk * d.H * d.batch) return;
+    ddt_wave<T>(d, tab, g, (int)((item / d.H) % d.nchunk), (int)(item % d.H),
+                item / d.H / d.nchunk, threadIdx.x % 64);
 }
 
 // ---------------------------------------------------------------------------
@@ -1508,11 +1547,18 @@ static void launch_chunk_bwd(const Dims& d, const SegTab& t, const BwdArgs& a, c
 template <typename T, int W>
 static void launch_conv_bwd_w(const Dims& d, const SegTab& t, const BwdArgs& a, const BwdWs& L,
                               int hbs, char* ws, hipStream_t s) {
-    dim3 grid((d.C + 255) / 256, (unsigned)(d.L / CONV_TT), (unsigned)d.batch);
+    const int64_t nconv = (int64_t)((d.C + 255) / 256) * (d.L / CONV_TT) * d.batch;
+    const int64_t nddt = ((int64_t)d.nchunk * d.H * d.batch + 3) / 4;
     // one head block per group: its partials are already [token][G][2N]
     const T* dbc = (const T*)(ws + (d.hpg / hbs == 1 ? L.dbc : L.dbcs));
-    hipLaunchKernelGGL((k_conv_bwd<T, W>), grid, dim3(256), 0, s, d, t, (const T*)a.xBC, a.conv_w,
-                       a.seq, (const T*)(ws + L.dv), dbc, (T*)a.dxBC, (float*)(ws + L.dwp));
+
+    const DdtArgs<T> g = {(const T*)a.dt_raw, a.dt_bias, a.A_log, (const float*)(ws + L.dt),
+                          (const float*)(ws + L.cs), a.seq, (const float*)(ws + L.rpart),
+                          (const float*)(ws + L.tokp), (const float*)(ws + L.dotgh),
+                          (const float*)(ws + L.red4), (T*)a.ddt_raw, (float*)(ws + L.red)};
+    hipLaunchKernelGGL((k_conv_bwd_ddt<T, W>), dim3((unsigned)(nconv + nddt)), dim3(256), 0, s, d, t,
+                       (const T*)a.xBC, a.conv_w, a.seq, (const T*)(ws + L.dv), dbc, (T*)a.dxBC,
+                       (float*)(ws + L.dwp), g);
 }
 
 template <typename T>
@@ -1616,12 +1662,6 @@ static void conv_bwd_t(const Dims& d, const SegTab& t, const BwdArgs& a, int hbs
                        hipStream_t s) {
     const BwdWs L = bwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
     char* ws = (char*)ws_;
-    hipLaunchKernelGGL((k_ddt<T>), dim3((unsigned)d.nchunk, (unsigned)d.H, (unsigned)d.batch),
-                       dim3(64), 0, s, d, t, (const T*)a.dt_raw, a.dt_bias, a.A_log,
-                       (const float*)(ws + L.dt), (const float*)(ws + L.cs), a.seq,
-                       (const float*)(ws + L.rpart), (const float*)(ws + L.tokp),
-                       (const float*)(ws + L.dotgh), (const float*)(ws + L.red4), (T*)a.ddt_raw,
-                       (float*)(ws + L.red));
     if (d.hpg / hbs > 1) {
         const int64_t nv = d.batch * d.L * d.G * 2 * d.N / (16 / sizeof(T));
         hipLaunchKernelGGL(k_bc_blocksum<T>, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, s, d,
