@@ -55,11 +55,15 @@ def _bwd_small(name):
         # 16 heads in one group: two head blocks of 8 per group, summed per group
         return mk(name, batch=1, seqlen=1024, nheads=16, headdim=64, dstate=128, ngroups=1,
                   chunk=256, act="bf16", seed=308, nseg=2, packed=(100, 700), **kw)
+    if name == "bf16_odd_hpg":
+        # three heads per group: one head per walk block, head blocks of three
+        return mk(name, batch=1, seqlen=1024, nheads=6, headdim=64, dstate=128, ngroups=2,
+                  chunk=256, act="bf16", seed=310, nseg=2, packed=(90, 600), **kw)
     raise KeyError(name)
 
 
 SMALL = ["tiny_f32", "slow_tiny_f32", "f32_head_thd", "f32_virtual", "bf16_small", "bf16_virtual", "bf16_thd",
-         "bf16_q64", "bf16_q128", "bf16_blocks"]
+         "bf16_q64", "bf16_q128", "bf16_blocks", "bf16_odd_hpg"]
 
 
 def run_fwd_bwd(wl, inputs=None):
