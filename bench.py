@@ -12,9 +12,11 @@ chunk 256, conv width 4, bf16 activations with FP32 state, cut into 8
 contiguous causal segments of 1024 tokens (one device's context-parallel
 shard each).  Inputs are resident in HBM before timing starts.
 
-Prints ONE JSON line (rank 0).  Per-call durations come from HIP events
-recorded around every call inside the timed region; the roofline entry uses
-the call whose single kernel takes the most time.
+Prints ONE JSON line (rank 0).  Per-call durations ("calls") come from a
+breakdown pass of K steps with HIP events around every call.  The timed region
+(K further steps, the headline value) records events around one call only:
+the call whose single kernel takes the most time, whose duration there gives
+the roofline entry.
 """
 from __future__ import annotations
 
@@ -322,13 +324,20 @@ def main():
     single_kernel = {"ssd_conv1d_fwd", "ssd_segment_output_fused", "ssd_boundary_scan",
                      "ssd_boundary_scan(reverse)", "ssd_segment_bwd_chunks"}
 
-    def step(events=None):
+    def step(events=None, only=None):
+        """One pass of every call; with `events`, record [start, end] around each call
+        (or, with `only`, around that call alone)."""
         for i, (_, fn) in enumerate(calls):
-            if events is not None:
-                events[i][0].record(stream)
+            rec = events is not None and (only is None or i == only)
+            if rec:
+                events[i if only is None else 0][0].record(stream)
             fn()
-            if events is not None:
-                events[i][1].record(stream)
+            if rec:
+                events[i if only is None else 0][1].record(stream)
+
+    def new_events(n):
+        return [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+                for _ in range(args.steps)]
 
     if args.copy_probe_mb:
         nb = args.copy_probe_mb * (1 << 20)
@@ -346,22 +355,13 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in calls]
-          for _ in range(args.steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record(stream)
+    # Breakdown pass (not the timed region): events around every call give the
+    # per-call times.  Each event record adds a few microseconds between calls,
+    # so the step is timed separately below with events around one call only.
+    ev = new_events(len(calls))
     for k in range(args.steps):
         step(ev[k])
-    t1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    gc.enable()
-    ms_total = t0.elapsed_time(t1)
-    ms_step = ms_total / args.steps
-
     abytes = algorithmic_bytes(wl)
     per_call = {}
     for i, (name, _) in enumerate(calls):
@@ -371,12 +371,32 @@ def main():
                           "algorithmic_MB": round(abytes[name] / 1e6, 2),
                           "GB_per_s": round(abytes[name] / (ms * 1e-3) / 1e9, 1)}
     dom = max(single_kernel, key=lambda n: per_call[n]["ms"])
-    achieved = per_call[dom]["GB_per_s"]
+    dom_i = [name for name, _ in calls].index(dom)
+
+    # Timed region: K whole steps, with HIP events on the launch stream around the
+    # dominant kernel's call only (its duration for the roofline line).
+    evd = new_events(1)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for k in range(args.steps):
+        step(evd[k], only=dom_i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gc.enable()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    dom_ms = statistics.mean(evd[k][0][0].elapsed_time(evd[k][0][1]) for k in range(args.steps))
+    achieved = round(abytes[dom] / (dom_ms * 1e-3) / 1e9, 1)
     mfma_peak = BF16_PEAK_TFLOPS if wl.act == "bf16" else F32_PEAK_TFLOPS
     mfma = {}
     for name, fl in [("ssd_segment_output_fused", output_flops(wl))] + \
             ([("ssd_segment_bwd_chunks", chunk_bwd_flops(wl))] if do_bwd else []):
-        tf = fl / (per_call[name]["ms"] * 1e-3) / 1e12
+        ms = dom_ms if name == dom else per_call[name]["ms"]
+        tf = fl / (ms * 1e-3) / 1e12
         mfma[name] = {"achieved": round(tf, 2), "peak": mfma_peak, "unit": "TFLOP/s",
                       "frac": round(tf / mfma_peak, 4), "algorithmic_GFLOP": round(fl / 1e9, 2)}
 
@@ -400,9 +420,11 @@ def main():
                    "layout": wl.layout, "packed": wl.seq_idx is not None},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(wl.name, CALL_KERNEL[dom])},
+                     "traffic": measured_traffic(wl.name, CALL_KERNEL[dom]),
+                     "kernel_ms": round(dom_ms, 5),
+                     "algorithmic_MB": round(abytes[dom] / 1e6, 2)},
         "mfma": mfma,
-        "calls": per_call,
+        "calls": per_call,  # from the breakdown pass, events around every call
         "wall_s_timed_region": round(wall, 4),
     }
     if not args.no_cpu_baseline:
