@@ -1600,9 +1600,9 @@ static void bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a, floa
     if (hb_path<T, P, N>(d.Q)) {
         // the reverse walk from a zero final gradient: dL/dS_in of each segment's
         // own outputs and its block decay
-        launch_state_walk<T, P, N, true>(d, t, (const T*)xc, (const T*)a.dy,
-                                         (const float*)(ws + L.dt), (const float*)(ws + L.cs),
-                                         a.seq, nullptr, (T*)nullptr, summary, s);
+        const WalkArgs<T> wa = {(const T*)xc, (const T*)a.dy, (const float*)(ws + L.dt),
+                                (const float*)(ws + L.cs), a.seq, nullptr, nullptr, summary};
+        launch_state_walk<T, P, N, true>(d, t, wa, s);
         return;
     }
     hipLaunchKernelGGL((k_bwd_chunk_states<T, P, N>), chunk_head_grid(d), dim3(256), 0, s,
@@ -1627,14 +1627,16 @@ static void bwd_pass_t(const Dims& d, const SegTab& t, const BwdArgs& a, void* w
     const BwdWs L = bwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
     char* ws = (char*)ws_;
     if (hb) {
-        // G of every chunk: the reverse walk from dS_out; then H of every chunk:
-        // the forward walk from S_in (<G_c, H_c> comes from the chunk kernel)
-        launch_state_walk<T, P, N, true>(d, t, (const T*)(ws + L.xc), (const T*)a.dy,
-                                         (const float*)(ws + L.dt), (const float*)(ws + L.cs),
-                                         a.seq, a.dS_out, (T*)(ws + L.gpn), nullptr, s);
-        launch_state_walk<T, P, N, false>(d, t, (const T*)(ws + L.xc), (const T*)nullptr,
-                                          (const float*)(ws + L.dt), (const float*)(ws + L.cs),
-                                          a.seq, a.S_in, (T*)(ws + L.hpn), nullptr, s);
+        // G of every chunk: the reverse walk from dS_out; H of every chunk: the
+        // forward walk from S_in; both in one launch (<G_c, H_c> comes from the
+        // chunk kernel)
+        const WalkArgs<T> bwd = {(const T*)(ws + L.xc), (const T*)a.dy, (const float*)(ws + L.dt),
+                                 (const float*)(ws + L.cs), a.seq, a.dS_out, (T*)(ws + L.gpn),
+                                 nullptr};
+        const WalkArgs<T> fwd = {(const T*)(ws + L.xc), nullptr, (const float*)(ws + L.dt),
+                                 (const float*)(ws + L.cs), a.seq, a.S_in, (T*)(ws + L.hpn),
+                                 nullptr};
+        launch_state_walk_pair<T, P, N>(d, t, bwd, fwd, s);
         return;
     }
     hipLaunchKernelGGL((k_state_pass<T, P, N, PASS_TRUE>),

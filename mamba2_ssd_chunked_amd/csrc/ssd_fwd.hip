@@ -517,8 +517,8 @@ static void segment_states_t(const Dims& d, const SegTab& t, const void* xc_, co
     // the group Gram tiles the output pass reads and dt prep share one launch
     // (independent inputs); the walk then needs dt and the cumulative sums
     launch_gram_dt<T, N>(d, xc, (T*)(w + L.gram), dt_raw, dt_bias, A_log, seq, dtw, csw, ctot, s);
-    launch_state_walk<T, P, N, false>(d, t, xc, (const T*)nullptr, dtw, csw, seq, nullptr, hst,
-                                      summary, s);
+    const WalkArgs<T> wa = {xc, nullptr, dtw, csw, seq, nullptr, hst, summary};
+    launch_state_walk<T, P, N, false>(d, t, wa, s);
 }
 
 // y_zero (FINAL = false) or the corrected y (FINAL = true), from the workspace

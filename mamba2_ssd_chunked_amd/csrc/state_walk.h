@@ -41,19 +41,44 @@
 
 namespace ssd {
 
+// The pointers of one walk launch.
+template <typename T>
+struct WalkArgs {
+    const T* xc;           // conv output [b][L][C]
+    const T* dy;           // output gradient [b][L][H][P] (backward)
+    const float* dt_ws;    // dt [b][H][L]
+    const float* cs_ws;    // chunk-local cumulative sums [b][H][L]
+    const int32_t* seq;    // packed sequence ids or null
+    const float* init;     // starting value [S][b][H][P][N] or null (zero)
+    T* store;              // value at every chunk start, or null
+    float* summary;        // final value and block decay, or null
+};
+
+constexpr int WALK_KT = 64;  // tokens per slice
+// LDS of a walk block (elements of T): two slice buffers of HW heads' A rows
+// and of the shared B rows.
+template <typename T, int P, int N, int HW>
+constexpr int walk_lds() {
+    return 2 * HW * WALK_KT * (P + 16 / (int)sizeof(T)) + 2 * WALK_KT * (N + 16 / (int)sizeof(T));
+}
+
+// One walk block: block `blk` of `nblk` (the XCD-aware item mapping is over
+// this range), its slice buffers at `lds`.
 template <typename T, int P, int N, bool BWD, bool SEQ, int HW>
-__global__ void __launch_bounds__(256 * HW) k_state_walk(Dims d, SegTab tab, const T* __restrict__ xc,
-                                                   const T* __restrict__ dy,
-                                                   const float* __restrict__ dt_ws,
-                                                   const float* __restrict__ cs_ws,
-                                                   const int32_t* __restrict__ seq,
-                                                   const float* __restrict__ init,
-                                                   T* __restrict__ store,
-                                                   float* __restrict__ summary) {
+__device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, const WalkArgs<T>& wa,
+                                           T* lds, int64_t blk, int64_t nblk) {
+    const T* __restrict__ xc = wa.xc;
+    const T* __restrict__ dy = wa.dy;
+    const float* __restrict__ dt_ws = wa.dt_ws;
+    const float* __restrict__ cs_ws = wa.cs_ws;
+    const int32_t* __restrict__ seq = wa.seq;
+    const float* __restrict__ init = wa.init;
+    T* __restrict__ store = wa.store;
+    float* __restrict__ summary = wa.summary;
     typedef Mma<T> M;
     typedef typename M::Frag Frag;
     constexpr int KS = M::KS;
-    constexpr int KT = 64;               // tokens per slice
+    constexpr int KT = WALK_KT;          // tokens per slice
     constexpr int NTH = 256 * HW, HTH = 256;  // threads of the block / of one head
     constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
     constexpr int XR = P + VEC, BR = N + VEC;
@@ -65,8 +90,8 @@ __global__ void __launch_bounds__(256 * HW) k_state_walk(Dims d, SegTab tab, con
     // and forces full waits for the outstanding loads at their joins)
     constexpr bool XFULL = KT * (P / VEC) % HTH == 0, BFULL = KT * (N / VEC) % NTH == 0;
     constexpr bool NFULL = NTT % 4 == 0;
-    __shared__ __attribute__((aligned(16))) T sX[2][HW][KT * XR];
-    __shared__ __attribute__((aligned(16))) T sB[2][KT * BR];
+    auto sX = reinterpret_cast<T(*)[HW][KT * XR]>(lds);
+    auto sB = reinterpret_cast<T(*)[KT * BR]>(lds + 2 * HW * KT * XR);
     typedef T vt __attribute__((ext_vector_type(VEC)));
 
     // block -> (row, segment, HW heads of one group): the walks of one (row,
@@ -79,7 +104,7 @@ __global__ void __launch_bounds__(256 * HW) k_state_walk(Dims d, SegTab tab, con
     int64_t b;
     {
         constexpr int NXCD = 8;
-        const int64_t n = gridDim.x, i = blockIdx.x;
+        const int64_t n = nblk, i = blk;
         int64_t item = (n % NXCD == 0) ? (i % NXCD) * (n / NXCD) + i / NXCD : i;
         h = (int)(item % (d.H / HW)) * HW + hs;
         item /= d.H / HW;
@@ -281,31 +306,74 @@ __global__ void __launch_bounds__(256 * HW) k_state_walk(Dims d, SegTab tab, con
         summary[(int64_t)d.nseg * per + ((int64_t)k * d.batch + b) * d.H + h] = ablk;
 }
 
-// One walk per (row, segment, head), see k_state_walk; A = x (forward) or dy
-// (backward).
-template <typename T, int P, int N, bool BWD>
-inline void launch_state_walk(const Dims& d, const SegTab& t, const T* xc, const T* dy,
-                              const float* dt_ws, const float* cs_ws, const int32_t* seq,
-                              const float* init, T* store, float* summary, hipStream_t s) {
-    // two heads of a group per block where they exist (bf16: the float32
-    // accumulators of two heads would not fit two waves per SIMD)
-    if (std::is_same<T, bf16>::value && d.hpg % 2 == 0) {
-        const dim3 grid((unsigned)((int64_t)(d.H / 2) * d.nseg * d.batch));
-        if (seq)
-            hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, true, 2>), grid, dim3(512), 0, s, d, t,
-                               xc, dy, dt_ws, cs_ws, seq, init, store, summary);
-        else
-            hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, false, 2>), grid, dim3(512), 0, s, d, t,
-                               xc, dy, dt_ws, cs_ws, seq, init, store, summary);
-        return;
-    }
-    const dim3 grid((unsigned)((int64_t)d.H * d.nseg * d.batch));
-    if (seq)
-        hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, true, 1>), grid, dim3(256), 0, s, d, t, xc,
-                           dy, dt_ws, cs_ws, seq, init, store, summary);
+// Two heads per block: four waves per SIMD, so that two blocks (of one walk or
+// of the two walks of k_state_walk_pair) share a CU.
+template <typename T, int P, int N, bool BWD, bool SEQ, int HW>
+__global__ void __launch_bounds__(256 * HW, HW == 2 ? 4 : 1) k_state_walk(Dims d, SegTab tab,
+                                                                         WalkArgs<T> wa) {
+    __shared__ __attribute__((aligned(16))) T lds[walk_lds<T, P, N, HW>()];
+    walk_block<T, P, N, BWD, SEQ, HW>(d, tab, wa, lds, blockIdx.x, gridDim.x);
+}
+
+// The reverse walk (blocks 0 .. n-1) and the forward walk (n .. 2n-1) in one
+// launch: the two have no order between them, and their blocks share the CUs.
+template <typename T, int P, int N, bool SEQ, int HW>
+__global__ void __launch_bounds__(256 * HW, HW == 2 ? 4 : 1) k_state_walk_pair(Dims d, SegTab tab,
+                                                                              WalkArgs<T> bwd,
+                                                                              WalkArgs<T> fwd) {
+    __shared__ __attribute__((aligned(16))) T lds[walk_lds<T, P, N, HW>()];
+    const int64_t n = gridDim.x / 2;
+    if ((int64_t)blockIdx.x < n)
+        walk_block<T, P, N, true, SEQ, HW>(d, tab, bwd, lds, blockIdx.x, n);
     else
-        hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, false, 1>), grid, dim3(256), 0, s, d, t, xc,
-                           dy, dt_ws, cs_ws, seq, init, store, summary);
+        walk_block<T, P, N, false, SEQ, HW>(d, tab, fwd, lds, blockIdx.x - n, n);
+}
+
+// One walk per (row, segment, head), see walk_block; A = x (forward) or dy
+// (backward).  Two heads of a group per block where they exist (bf16: the
+// float32 accumulators of two heads would not fit four waves per SIMD).
+template <typename T>
+inline int walk_heads(const Dims& d) {
+    return (std::is_same<T, bf16>::value && d.hpg % 2 == 0) ? 2 : 1;
+}
+
+template <typename T, int P, int N, bool BWD>
+inline void launch_state_walk(const Dims& d, const SegTab& t, const WalkArgs<T>& wa,
+                              hipStream_t s) {
+    const int hw = walk_heads<T>(d);
+    const dim3 grid((unsigned)((int64_t)(d.H / hw) * d.nseg * d.batch));
+    const dim3 block(256 * hw);
+    if (hw == 2) {
+        if (wa.seq)
+            hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, true, 2>), grid, block, 0, s, d, t, wa);
+        else
+            hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, false, 2>), grid, block, 0, s, d, t, wa);
+    } else {
+        if (wa.seq)
+            hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, true, 1>), grid, block, 0, s, d, t, wa);
+        else
+            hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, false, 1>), grid, block, 0, s, d, t, wa);
+    }
+}
+
+// The reverse and the forward walk of the backward pass in one launch.
+template <typename T, int P, int N>
+inline void launch_state_walk_pair(const Dims& d, const SegTab& t, const WalkArgs<T>& bwd,
+                                   const WalkArgs<T>& fwd, hipStream_t s) {
+    const int hw = walk_heads<T>(d);
+    const dim3 grid((unsigned)(2 * (int64_t)(d.H / hw) * d.nseg * d.batch));
+    const dim3 block(256 * hw);
+    if (hw == 2) {
+        if (bwd.seq)
+            hipLaunchKernelGGL((k_state_walk_pair<T, P, N, true, 2>), grid, block, 0, s, d, t, bwd, fwd);
+        else
+            hipLaunchKernelGGL((k_state_walk_pair<T, P, N, false, 2>), grid, block, 0, s, d, t, bwd, fwd);
+    } else {
+        if (bwd.seq)
+            hipLaunchKernelGGL((k_state_walk_pair<T, P, N, true, 1>), grid, block, 0, s, d, t, bwd, fwd);
+        else
+            hipLaunchKernelGGL((k_state_walk_pair<T, P, N, false, 1>), grid, block, 0, s, d, t, bwd, fwd);
+    }
 }
 
 }  // namespace ssd
