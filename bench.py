@@ -370,7 +370,7 @@ def main():
         per_call[name] = {"ms": round(ms, 5), "max_ms": round(max(each), 5),
                           "algorithmic_MB": round(abytes[name] / 1e6, 2),
                           "GB_per_s": round(abytes[name] / (ms * 1e-3) / 1e9, 1)}
-    dom = max(single_kernel, key=lambda n: per_call[n]["ms"])
+    dom = max((n for n in single_kernel if n in per_call), key=lambda n: per_call[n]["ms"])
     dom_i = [name for name, _ in calls].index(dom)
 
     # Timed region: K whole steps, with HIP events on the launch stream around the
