@@ -154,7 +154,20 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
     const bool inter = FINAL || !first;
     const int a0 = wave, a1 = QT - 1 - wave;
 
-    // ---- issue every global load of the workgroup
+    // ---- issue every global load of the workgroup.  First the C rows of the
+    // wave's two output tiles for the inter-chunk term's first k step (each
+    // later k step's are loaded a step ahead of their use)
+    int i0[2];
+    i0[0] = a0 * 16;
+    i0[1] = a1 * 16;
+    auto cload = [&](int it, int kn) {
+        return M::load(xc + (rb + t0 + i0[it] + lr) * d.C + coff + kn * KS + SL * lg);
+    };
+    Frag cfc[2];
+    if (inter) {
+        cfc[0] = cload(0, 0);
+        cfc[1] = cload(1, 0);
+    }
     constexpr int V_X = (Q * (P / VEC) + NTH - 1) / NTH;
     vt rx[V_X];
 #pragma unroll
@@ -268,9 +281,6 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
         if (q < NKS) fetch_gram(q, cgr[q]);
 
     // ---- inter-chunk term of the wave's two output tiles (C_i H^T, rows p, columns i)
-    int i0[2];
-    i0[0] = a0 * 16;
-    i0[1] = a1 * 16;
     f32x4 acc[2][PT];
     float rsc_i[2], cs_i[2];
     int sq_i[2];
@@ -282,15 +292,28 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
         rsc_i[it] = exact ? 0.f : sea[i];
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[it][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (inter) {
+    }
+    if (inter) {
 #pragma unroll
-            for (int kn = 0; kn < NKF; ++kn) {
-                const Frag cf = M::load(xc + (rb + t0 + i) * d.C + coff + kn * KS + SL * lg);
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-                    acc[it][pt] = M::mma(M::load(&sH[(pt * 16 + lr) * HP + kn * KS + SL * lg]), cf,
-                                         acc[it][pt]);
+        for (int kn = 0; kn < NKF; ++kn) {
+            Frag cfn[2];
+            if (kn + 1 < NKF) {
+                cfn[0] = cload(0, kn + 1);
+                cfn[1] = cload(1, kn + 1);
             }
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const Frag hf = M::load(&sH[(pt * 16 + lr) * HP + kn * KS + SL * lg]);
+                acc[0][pt] = M::mma(hf, cfc[0], acc[0][pt]);
+                acc[1][pt] = M::mma(hf, cfc[1], acc[1][pt]);
+            }
+            if (kn + 1 < NKF) {
+                cfc[0] = cfn[0];
+                cfc[1] = cfn[1];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
             const float f = (sq_i[it] == seq_prev) ? expf(cs_i[it]) : 0.f;
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) acc[it][pt] *= f;
