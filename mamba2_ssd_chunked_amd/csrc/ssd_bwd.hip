@@ -1278,10 +1278,13 @@ __device__ __forceinline__ void conv_bwd_block(const Dims& d, const SegTab& tab,
         const int o = (int)(c - HP), part = o / (d.G * d.N), gn = o % (d.G * d.N);
         return (int64_t)(gn / d.N) * 2 * d.N + part * d.N + gn % d.N;
     }();
-    auto grad4 = [&](int64_t tok) {
-        const vt v = xch ? *(const vt*)(dvx + tok * HP + c) : *(const vt*)(dbc + tok * GN2 + bco);
-        return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-    };
+    // The output gradients of the rows are loaded GD rows ahead of their use
+    // (a load right before its use costs a memory round trip per row).  Each
+    // load is unconditional: a lane past the channels reads channel 0, a row
+    // outside the sequence reads row 0, and the products drop those values.
+    constexpr int GD = 6;
+    const T* gsrc = xch ? dvx + (active ? c : 0) : dbc + bco;
+    const int64_t gstr = xch ? HP : GN2;
 
     float wr[4][W];
 #pragma unroll
@@ -1318,6 +1321,13 @@ __device__ __forceinline__ void conv_bwd_block(const Dims& d, const SegTab& tab,
     for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int kk = 0; kk < W; ++kk) dw[e][kk] = 0.f;
+    auto gload = [&](int o) {
+        return *(const vt*)(gsrc + (rb + max(mem[o + W - 1], 0)) * gstr);
+    };
+    vt gbuf[GD];
+#pragma unroll
+    for (int q = 0; q < GD; ++q)
+        if (q < RD) gbuf[q] = gload(q);
     float win[W][4];  // du of offsets o-(W-1) .. o
 #pragma unroll
     for (int q = 0; q < W; ++q)
@@ -1335,13 +1345,14 @@ __device__ __forceinline__ void conv_bwd_block(const Dims& d, const SegTab& tab,
                 for (int e = 0; e < 4; ++e) u[e] += wr[e][kk] * xs[o + kk][e];
             }
         }
+        const vt dv4 = gbuf[o % GD];
+        if (o + GD < RD) gbuf[o % GD] = gload(o + GD);
         float g[4] = {0.f, 0.f, 0.f, 0.f};
         if (mem[r] >= 0 && active) {
-            const f32x4 dv4 = grad4(rb + mem[r]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-u[e]));
-                g[e] = dv4[e] * sg * (1.f + u[e] * (1.f - sg));
+                g[e] = (float)dv4[e] * sg * (1.f + u[e] * (1.f - sg));
             }
         }
         if (o < TPT) {  // dconv_w from this thread's own outputs
