@@ -174,8 +174,13 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     constexpr int V_X = (Q * (P / VEC) + NTH - 1) / NTH;
     constexpr int V_S = (P * (N / VEC) + NTH - 1) / NTH;
     vt rx[V_X], rd[V_X], rg[V_S], rh[V_S];
+    float rcs = 0.f, rdt = 0.f;  // cumulative sum and dt of token threadIdx.x (< Q)
     auto fetch = [&](int h) {
         const int64_t so = st_of(h);
+        if (threadIdx.x < Q) {
+            rcs = cs_ws[hl_of(h) + threadIdx.x];
+            rdt = dt_ws[hl_of(h) + threadIdx.x];
+        }
 #pragma unroll
         for (int q = 0; q < V_X; ++q) {
             const int idx = threadIdx.x + q * NTH;
@@ -251,9 +256,9 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
         }
         __syncthreads();  // the previous head is done with the LDS
         stash();
-        for (int j = threadIdx.x; j < Q; j += NTH) {
-            scs[j] = cs_ws[hl + j];
-            sdt[j] = dt_ws[hl + j];
+        if (threadIdx.x < Q) {  // loaded with the head's rows
+            scs[threadIdx.x] = rcs;
+            sdt[threadIdx.x] = rdt;
         }
         for (int j = threadIdx.x; j < NW * Q; j += NTH) s_rw[j] = 0.f;
         __syncthreads();
