@@ -1127,7 +1127,27 @@ __device__ __forceinline__ void ddt_wave(const Dims& d, const SegTab& tab, const
     const float cs_e = cs_ws[hl + Q - 1];
     const float const4 = (seq_refc == seq_e ? expf(cs_e) : 0.f) *
                          dotgh[((int64_t)b * d.nchunk + cm) * d.H + h];
-    auto sq = [&](int t) { return seq ? seq[rb + t0 + t] : 0; };
+    // every per-token input of the lane's tokens lane*E .. lane*E+E-1 up front
+    // (one memory round trip), with the sequence ids of the tokens on either side
+    f32x4 tp[4];
+    float rp[4], dtr[4], dtw[4];
+    int sqv[6];  // sequence ids of tokens lane*E-1 .. lane*E+E
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (e < E) {
+            const int t = lane * E + e;
+            tp[e] = *(const f32x4*)&tokp[(hl + t) * 4];
+            rp[e] = rpart[hl + t];
+            dtr[e] = (float)dt_raw[(rb + t0 + t) * d.H + h];
+            dtw[e] = dt_ws[hl + t];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 6; ++e) {
+        const int t = lane * E + e - 1;
+        sqv[e] = (seq && e <= E + 1 && t >= 0 && t < Q) ? seq[rb + t0 + t] : 0;
+    }
+    auto sq = [&](int e) { return sqv[e + 1]; };  // id of token lane*E + e
 
     // segmented suffix of s (runs end where the sequence changes), lanes hold
     // tokens lane*E .. lane*E+E-1
@@ -1137,10 +1157,10 @@ __device__ __forceinline__ void ddt_wave(const Dims& d, const SegTab& tab, const
     for (int e = 3; e >= 0; --e) {
         if (e < E) {
             const int t = lane * E + e;
-            const bool cut = t < Q - 1 && sq(t + 1) != sq(t);
+            const bool cut = t < Q - 1 && sq(e + 1) != sq(e);
             if (cut) run = 0.f;
             cut_any = cut_any || cut;
-            const float s = tokp[(hl + t) * 4 + 0] + rpart[hl + t];
+            const float s = tp[e][0] + rp[e];
             run += s;
             sl[e] = run;
             rs[e] = cut_any;
@@ -1166,7 +1186,7 @@ __device__ __forceinline__ void ddt_wave(const Dims& d, const SegTab& tab, const
     for (int e = 0; e < 4; ++e) {
         if (e < E) {
             vl[e] = vrun;
-            vrun += tokp[(hl + lane * E + e) * 4 + 2];
+            vrun += tp[e][2];
         }
     }
     float vin = vrun;
@@ -1183,16 +1203,16 @@ __device__ __forceinline__ void ddt_wave(const Dims& d, const SegTab& tab, const
         if (e < E) {
             const int t = lane * E + e;
             // the decay of a token that starts a sequence is the constant 0
-            const bool starts = t > 0 ? sq(t) != sq(t - 1) : sq(0) != seq_refc;
+            const bool starts = t > 0 ? sq(e) != sq(e - 1) : sq(e) != seq_refc;
             const float dl = starts ? 0.f : sl[e] + (rs[e] ? 0.f : carry) + vbefore + vl[e] + const4;
-            const float ddt = tokp[(hl + t) * 4 + 1] + A * dl;
-            const float z = (float)dt_raw[(rb + t0 + t) * d.H + h] + bias;
+            const float ddt = tp[e][1] + A * dl;
+            const float z = dtr[e] + bias;
             const float sp = softplus_b(z);
             const bool pass = sp >= d.dt_min && sp <= d.dt_max;
             const float gr = pass ? ddt / (1.f + expf(-z)) : 0.f;
             ddt_raw[(rb + t0 + t) * d.H + h] = (T)gr;
             s_db += gr;
-            s_da += dt_ws[hl + t] * dl;
+            s_da += dtw[e] * dl;
         }
     }
 #pragma unroll
