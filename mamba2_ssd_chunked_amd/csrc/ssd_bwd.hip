@@ -1129,23 +1129,27 @@ __device__ __forceinline__ void ddt_wave(const Dims& d, const SegTab& tab, const
                          dotgh[((int64_t)b * d.nchunk + cm) * d.H + h];
     // every per-token input of the lane's tokens lane*E .. lane*E+E-1 up front
     // (one memory round trip), with the sequence ids of the tokens on either side
-    f32x4 tp[4];
+    // (three of tokp's four floats per token: a loaded register that is never
+    // read gets reused at once, and the reuse waits for that load)
+    typedef float f32x3 __attribute__((ext_vector_type(3)));
+    f32x3 tp[4];
     float rp[4], dtr[4], dtw[4];
     int sqv[6];  // sequence ids of tokens lane*E-1 .. lane*E+E
+    // (slots e >= E load token lane*E+E-1 again, unused: no branch around the loads)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        if (e < E) {
-            const int t = lane * E + e;
-            tp[e] = *(const f32x4*)&tokp[(hl + t) * 4];
-            rp[e] = rpart[hl + t];
-            dtr[e] = (float)dt_raw[(rb + t0 + t) * d.H + h];
-            dtw[e] = dt_ws[hl + t];
-        }
+        const int t = lane * E + min(e, E - 1);
+        tp[e] = *(const f32x3*)&tokp[(hl + t) * 4];
+        rp[e] = rpart[hl + t];
+        dtr[e] = (float)dt_raw[(rb + t0 + t) * d.H + h];
+        dtw[e] = dt_ws[hl + t];
     }
+    if (seq) {
 #pragma unroll
-    for (int e = 0; e < 6; ++e) {
-        const int t = lane * E + e - 1;
-        sqv[e] = (seq && e <= E + 1 && t >= 0 && t < Q) ? seq[rb + t0 + t] : 0;
+        for (int e = 0; e < 6; ++e) sqv[e] = seq[rb + t0 + min(max(lane * E + e - 1, 0), Q - 1)];
+    } else {
+#pragma unroll
+        for (int e = 0; e < 6; ++e) sqv[e] = 0;
     }
     auto sq = [&](int e) { return sqv[e + 1]; };  // id of token lane*E + e
 
@@ -1302,15 +1306,20 @@ __device__ __forceinline__ void conv_bwd_block(const Dims& d, const SegTab& tab,
     // (a load right before its use costs a memory round trip per row).  Each
     // load is unconditional: a lane past the channels reads channel 0, a row
     // outside the sequence reads row 0, and the products drop those values.
+    // Every other access of the loop is a bounded buffer access without a
+    // branch, so the wait for a row's gradient counts the stores issued since
+    // (a store under a branch might not have been issued, and the wait would
+    // then also take the loads of the rows after it).
     constexpr int GD = 6;
-    const T* gsrc = xch ? dvx + (active ? c : 0) : dbc + bco;
-    const int64_t gstr = xch ? HP : GN2;
+    const T* gsrc = !active ? dvx : xch ? dvx + c : dbc + bco;
+    const int64_t gstr = (!active || xch) ? HP : GN2;
 
     float wr[4][W];
+    const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(w, d.C * W * (int)sizeof(float));
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int kk = 0; kk < W; ++kk) wr[e][kk] = active ? w[(c + e) * W + kk] : 0.f;
+        for (int kk = 0; kk < W; ++kk) wr[e][kk] = buf_load<float>(wrs, ((c + e) * W + kk) * 4);
 
     // x row r is the token r - (W-1) places after t0 in causal order.  Rows,
     // their positions and sequence ids are the same for the whole wave (t0 is),
@@ -1324,13 +1333,10 @@ __device__ __forceinline__ void conv_bwd_block(const Dims& d, const SegTab& tab,
         mem[r] = __builtin_amdgcn_readfirstlane(
             (int)((o >= 0 && o < TPT) ? t0 + o : conv_row(tab, k, t0, o)));
         sq[r] = __builtin_amdgcn_readfirstlane((mem[r] >= 0 && seq) ? seq[rb + mem[r]] : 0);
-        vt v;
-        if (mem[r] >= 0 && active) {
-            v = *(const vt*)(xBC + (rb + mem[r]) * d.C + c);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (T)0.f;
-        }
+        // a row outside the sequence gets an empty resource (reads zeros)
+        const vt v = buf_load<vt>(buf_rsrc(xBC + (rb + max(mem[r], 0)) * d.C,
+                                           mem[r] >= 0 ? d.C * (int)sizeof(T) : 0),
+                                  c * (int)sizeof(T));
 #pragma unroll
         for (int e = 0; e < 4; ++e) xs[r][e] = (float)v[e];
     }
@@ -1367,13 +1373,16 @@ __device__ __forceinline__ void conv_bwd_block(const Dims& d, const SegTab& tab,
         }
         const vt dv4 = gbuf[o % GD];
         if (o + GD < RD) gbuf[o % GD] = gload(o + GD);
-        float g[4] = {0.f, 0.f, 0.f, 0.f};
-        if (mem[r] >= 0 && active) {
+        // zero outside the sequence (that row's gradient load read row 0); a
+        // lane past the channels has zero x and weights, so its g only meets
+        // zeros and its stores are dropped.  A factor, not a branch: the load
+        // of the gradient stays where it was issued.
+        const float gm = mem[r] >= 0 ? 1.f : 0.f;
+        float g[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-u[e]));
-                g[e] = (float)dv4[e] * sg * (1.f + u[e] * (1.f - sg));
-            }
+        for (int e = 0; e < 4; ++e) {
+            const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-u[e]));
+            g[e] = gm * (float)dv4[e] * sg * (1.f + u[e] * (1.f - sg));
         }
         if (o < TPT) {  // dconv_w from this thread's own outputs
 #pragma unroll
@@ -1402,12 +1411,11 @@ __device__ __forceinline__ void conv_bwd_block(const Dims& d, const SegTab& tab,
                     for (int e = 0; e < 4; ++e) acc[e] += wr[e][kk] * win[ot - s][e];
                 }
             }
-            if (active) {
-                vt ov;
+            vt ov;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ov[e] = (T)acc[e];
-                *(vt*)(dxBC + (rb + t0 + s) * d.C + c) = ov;
-            }
+            for (int e = 0; e < 4; ++e) ov[e] = (T)acc[e];
+            buf_store(ov, buf_rsrc(dxBC + (rb + t0 + s) * d.C, d.C * (int)sizeof(T)),
+                      c * (int)sizeof(T));
         }
     }
 #pragma unroll

@@ -110,6 +110,34 @@ __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / 64));
 }
 
+// Raw buffer access (gfx9 resource word 3): a resource spans `bytes` bytes from
+// `base`; a load at or past that end returns zeros and a store there is
+// dropped by the hardware, so lanes outside a row's channels need no branch.
+// Offsets are 32-bit: a resource covers one token row at a time.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+template <typename V>
+__device__ __forceinline__ V buf_load(__amdgpu_buffer_rsrc_t r, int off) {
+    static_assert(sizeof(V) == 4 || sizeof(V) == 8 || sizeof(V) == 16, "buffer access width");
+    if constexpr (sizeof(V) == 4)
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    else if constexpr (sizeof(V) == 8)
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    else
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+template <typename V>
+__device__ __forceinline__ void buf_store(V v, __amdgpu_buffer_rsrc_t r, int off) {
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    static_assert(sizeof(V) == 8 || sizeof(V) == 16, "buffer access width");
+    if constexpr (sizeof(V) == 8)
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, v), r, off, 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // MFMA fragments.
 //
