@@ -16,7 +16,10 @@ Prints ONE JSON line (rank 0).  Per-call durations ("calls") come from a
 breakdown pass of K steps with HIP events around every call.  The timed region
 (K further steps, the headline value) records events around one call only:
 the call whose single kernel takes the most time, whose duration there gives
-the roofline entry.
+the roofline entry.  After the timed region, two probe kernels (a 1 GiB copy and
+a bf16 MFMA loop, libssd_probe.so) measure the achievable HBM and MFMA rates;
+the roofline and MFMA entries give fractions of those beside the fractions of
+the published peaks.
 """
 from __future__ import annotations
 
@@ -53,6 +56,12 @@ def parse():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one device-to-device copy of this many MB before timing, so that "
                          "hardware byte counters can be calibrated against a known size")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the achievable-peak probes (copy kernel, MFMA loop) run after timing")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DB",
+                    help="no GPU work: read a rocprofv3 --pmc database with SQ_VALU_MFMA_BUSY_CYCLES, "
+                         "GRBM_GUI_ACTIVE and SQ_INSTS_VALU_MFMA_MOPS_BF16 of a run with the peak "
+                         "probes, and print every kernel's MFMA-busy fraction as JSON")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="no GPU work: read two rocprofv3 --pmc databases (FETCH_SIZE, then "
                          "WRITE_SIZE) of a run made with --copy-probe-mb, and print the per-launch "
@@ -76,7 +85,8 @@ def source_digest():
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h", ".cpp")):
+        # the peak probes are measurement kernels, not kernels of the path
+        if name.endswith((".hip", ".h", ".cpp")) and not name.startswith("peak_probes"):
             h.update(name.encode())
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(f.read())
@@ -139,6 +149,98 @@ def summarize_traffic(fetch_db, write_db, probe_mb):
         e["hbm_bytes"] = e.get("FETCH_SIZE_bytes", 0) + e.get("WRITE_SIZE_bytes", 0)
     out["source_sha256"] = source_digest()
     return out
+
+
+SIMDS = 256 * 4  # MI355X: 256 CUs of 4 SIMDs
+
+
+def summarize_mfma(db):
+    """Per kernel, the mean over its dispatches of
+      busy = sum of SQ_VALU_MFMA_BUSY_CYCLES / (max GRBM_GUI_ACTIVE * SIMDS)
+    (the counters' own MfmaUtil formula) and of the executed MFMA flops
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts 512 flops).  The absolute busy figure depends on
+    how the counter's instances map to SIMDs, so every kernel's figure is also given as a
+    fraction of that of the busier MFMA-loop probe (k_probe_mfma16 / k_probe_mfma32, waves
+    of independent products only): the matrix-core time a plain kernel reaches."""
+    import collections
+    import re
+    import sqlite3
+    cur = sqlite3.connect(db).cursor()
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    names = {}
+    for disp, kname, cname, val in cur.execute(
+            "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+        acc[disp][cname].append(val)
+        names[disp] = kname
+    per_k = collections.defaultdict(lambda: {"busy": [], "gflop": []})
+    for disp, cs in acc.items():
+        gui = max(cs.get("GRBM_GUI_ACTIVE", [0]))
+        if gui <= 0 or "SQ_VALU_MFMA_BUSY_CYCLES" not in cs:
+            continue
+        m = re.search(r"k_probe_\w+", names[disp])
+        e = per_k[m.group(0) if m else kernel_short(names[disp])]
+        e["busy"].append(sum(cs["SQ_VALU_MFMA_BUSY_CYCLES"]) / (gui * SIMDS))
+        e["gflop"].append(sum(cs.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [0])) * 512 / 1e9)
+    out = {"simds": SIMDS, "kernels": {}}
+    for kn, e in per_k.items():
+        out["kernels"][kn] = {"mfma_busy": round(statistics.mean(e["busy"]), 4),
+                              "executed_bf16_GFLOP": round(statistics.mean(e["gflop"]), 3),
+                              "dispatches": len(e["busy"])}
+    probes = [k for k in out["kernels"] if k.startswith("k_probe_mfma")]
+    if probes:
+        ref = max(probes, key=lambda k: out["kernels"][k]["mfma_busy"])
+        out["probe"] = ref
+        for e in out["kernels"].values():
+            e["busy_vs_probe"] = round(e["mfma_busy"] / out["kernels"][ref]["mfma_busy"], 4)
+    out["source_sha256"] = source_digest()
+    return out
+
+
+def measure_peaks(torch, dev, stream):
+    """Achievable peaks of plain kernels on this GPU (libssd_probe.so): HBM GB/s of a
+    1 GiB device copy (read + write bytes / time, median of 10), and bf16 MFMA TFLOP/s
+    of the MFMA loop (2048 workgroups of 4 waves, median of 5), checked against its
+    closed-form output."""
+    from mamba2_ssd_chunked_amd import probes
+    nb = 1 << 30
+    src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    ts = []
+    for rep in range(12):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        probes.probe_copy(src, dst)
+        b.record(stream)
+        if rep >= 2:
+            ts.append((a, b))
+    torch.cuda.synchronize()
+    copy_ms = statistics.median(a.elapsed_time(b) for a, b in ts)
+    if not bool(torch.equal(src, dst)):
+        raise RuntimeError("copy probe produced wrong bytes")
+    del src, dst
+    blocks, iters = 2048, 4096
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    rate = {}
+    for shape in (16, 32):
+        ts = []
+        for rep in range(7):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            flops = probes.probe_mfma(out, blocks, iters, shape)
+            b.record(stream)
+            if rep >= 2:
+                ts.append((a, b))
+        torch.cuda.synchronize()
+        mfma_ms = statistics.median(a.elapsed_time(b) for a, b in ts)
+        if not bool(torch.all(out == probes.mfma_expected(iters, shape))):
+            raise RuntimeError(f"MFMA probe ({shape}) output differs from its closed form")
+        rate[shape] = round(flops / (mfma_ms * 1e-3) / 1e12, 1)
+    return {"hbm_GBps": round(2 * nb / (copy_ms * 1e-3) / 1e9, 1),
+            "bf16_mfma_TFLOPs": max(rate.values()),
+            "bf16_mfma_TFLOPs_by_shape": {f"{s}x{s}": v for s, v in rate.items()},
+            "probes": "1 GiB device copy, 64-thread workgroups of 4 KiB (read + write bytes); "
+                      "bf16 MFMA loops of 16x16x32 (8 independent chains per wave) and "
+                      f"32x32x16 (4 chains), 2048 x 256 threads, {iters} rounds; the faster"}
 
 
 def measured_traffic(workload, kernel):
@@ -222,9 +324,11 @@ def algorithmic_bytes(wl):
 
 
 def output_flops(wl):
-    """MFMA flops of the output pass: causal C B^T, its product with X, and C H^T."""
+    """MFMA flops of the output pass: the decay-weighted Gram tiles times X over causal
+    pairs, and C H^T.  The Gram tiles C B^T themselves are formed once per group by the
+    Gram pass of ssd_segment_states, not here."""
     b, L, H, P, N, Q = wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.chunk
-    per_chunk_head = Q * (Q + 1) // 2 * 2 * (N + P) + 2 * Q * P * N
+    per_chunk_head = Q * (Q + 1) // 2 * 2 * P + 2 * Q * P * N
     return b * (L // Q) * H * per_chunk_head
 
 
@@ -260,6 +364,9 @@ def cpu_baseline(wl, runs, backward):
 
 def main():
     args = parse()
+    if args.summarize_mfma:
+        print(json.dumps(summarize_mfma(args.summarize_mfma), indent=1))
+        return
     if args.summarize_traffic:
         if not args.copy_probe_mb:
             raise SystemExit("--summarize-traffic needs the --copy-probe-mb of the profiled run")
@@ -387,6 +494,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     gc.enable()
+    peaks = None if args.no_peaks else measure_peaks(torch, dev, stream)
     ms_total = t0.elapsed_time(t1)
     ms_step = ms_total / args.steps
     dom_ms = statistics.mean(evd[k][0][0].elapsed_time(evd[k][0][1]) for k in range(args.steps))
@@ -399,6 +507,9 @@ def main():
         tf = fl / (ms * 1e-3) / 1e12
         mfma[name] = {"achieved": round(tf, 2), "peak": mfma_peak, "unit": "TFLOP/s",
                       "frac": round(tf / mfma_peak, 4), "algorithmic_GFLOP": round(fl / 1e9, 2)}
+        if peaks and wl.act == "bf16":
+            mfma[name]["achievable_peak"] = peaks["bf16_mfma_TFLOPs"]
+            mfma[name]["achievable_frac"] = round(tf / peaks["bf16_mfma_TFLOPs"], 4)
 
     result = {
         "metric": METRIC,
@@ -423,10 +534,14 @@ def main():
                      "traffic": measured_traffic(wl.name, CALL_KERNEL[dom]),
                      "kernel_ms": round(dom_ms, 5),
                      "algorithmic_MB": round(abytes[dom] / 1e6, 2)},
+        "achievable_peaks": peaks,
         "mfma": mfma,
         "calls": per_call,  # from the breakdown pass, events around every call
         "wall_s_timed_region": round(wall, 4),
     }
+    if peaks:
+        result["roofline"]["achievable_peak"] = peaks["hbm_GBps"]
+        result["roofline"]["achievable_frac"] = round(achieved / peaks["hbm_GBps"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_runs, do_bwd)
     print(json.dumps(result), flush=True)

@@ -1,4 +1,5 @@
-"""Build libssd.so (gfx950) in-tree with hipcc.
+"""Build libssd.so (gfx950) in-tree with hipcc, and beside it libssd_probe.so,
+the achievable-peak probes that the roofline figures are also quoted against.
 
 All HIP sources are compiled for gfx950 only, with packed-FP32 instructions
 disabled (-Xclang -target-feature -Xclang -packed-fp32-ops).
@@ -14,11 +15,18 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssd.so")
+PROBE_LIB = os.path.join(HERE, "libssd_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["ssd_api.cpp", "conv1d.hip", "ssd_fwd.hip", "scan.hip", "ssd_bwd.hip"]
+PROBE_SOURCES = ["peak_probes.hip"]
+# The probes' MFMA loops keep their accumulators in ordinary VGPRs, updated in
+# place: with accumulation registers the allocator copies every chain's
+# accumulator between registers each round, and the copies wait for the
+# products.  (The SSD kernels get the in-place VGPR form without the flag.)
+EXTRA_FLAGS = {"peak_probes.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -28,26 +36,33 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA_FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libssd.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link failed for {os.path.basename(lib)}:\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link libssd.so and libssd_probe.so; returns the
+    path of libssd.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {os.path.basename(PROBE_LIB)}")
     return LIB
 
 
