@@ -425,3 +425,36 @@ def test_adjoint_matches_finite_differences():
             if field in ("dt_raw", "dt_bias") and _near_clamp(wl, field, fi, 2 * eps):
                 continue  # the clamp has a kink there; a central difference straddles it
             assert abs(fd - an) <= 2e-3 * max(1.0, abs(an)), (name, fi, fd, an)
+
+
+def test_adjoint_dot_product_identity():
+    """The dot-product test of an adjoint: along one random direction v over every input
+    at once, <dy, y(x + d+)> - <dy, y(x - d-)> = <J^T dy, d+ + d-> up to third order in
+    the step, with J^T dy the oracle's gradients and d+-, the float32-representable steps
+    of size 1e-4 v.  Entries of dt_raw near a clamp bound (a kink of the dt path) get no
+    step, and neither does dt_bias (it moves every token of its head)."""
+    import copy
+    wl = W.make_workload("dot", batch=1, seqlen=64, nheads=2, headdim=4, dstate=4, ngroups=1,
+                         chunk=16, act="f32", seed=43, with_dy=True, lengths=[30, 34])
+    g = oracle.backward(wl)
+    rng = np.random.default_rng(44)
+    eps = 1e-4
+    fields = [("dxBC", "xBC"), ("dconv_w", "conv_w"), ("ddt_raw", "dt_raw"),
+              ("dA_log", "A_log"), ("dD", "D")]
+    plus, minus = copy.copy(wl), copy.copy(wl)
+    predicted = 0.0
+    for gname, field in fields:
+        base = getattr(wl, field).astype(np.float64)
+        v = rng.standard_normal(base.shape)
+        if field == "dt_raw":
+            keep = np.array([not _near_clamp(wl, "dt_raw", i, 4 * eps) for i in range(base.size)])
+            v = v * keep.reshape(base.shape)
+        p32 = (base + eps * v).astype(np.float32)
+        m32 = (base - eps * v).astype(np.float32)
+        setattr(plus, field, p32)
+        setattr(minus, field, m32)
+        step = p32.astype(np.float64) - m32.astype(np.float64)
+        predicted += float((g[gname].astype(np.float64) * step).sum())
+    measured = float((oracle.forward(plus) * wl.dy).sum() - (oracle.forward(minus) * wl.dy).sum())
+    assert abs(predicted) > 1e-6
+    assert abs(measured - predicted) <= 1e-5 * abs(predicted), (measured, predicted)
