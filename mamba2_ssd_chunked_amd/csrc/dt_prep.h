@@ -33,17 +33,31 @@ __device__ __forceinline__ void dt_prep_wave(const Dims& d, const T* __restrict_
     bool lflag = false;
     float run = 0.f;
     int sprev = (seq && lane * E > 0) ? seq[tok0 - 1] : 0;
+    // every input of the lane's tokens first, in one memory round trip (slots
+    // e >= E repeat the last token and are not used): a load under the e < E
+    // branch would be waited for before the next slot's load is issued
+    float raw[4];
+    int sqs[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) raw[e] = to_f(dt_raw[(tok0 + min(e, E - 1)) * d.H + h]);
+    if (seq) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sqs[e] = seq[tok0 + min(e, E - 1)];
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sqs[e] = 0;
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         if (e < E) {
             const int j = lane * E + e;
-            const int sj = seq ? seq[tok0 + e] : 0;
+            const int sj = sqs[e];
             const bool start = j > 0 && sj != sprev;
             sprev = sj;
             lflag = lflag || start;
             rs[e] = lflag;
             if (start) run = 0.f;
-            const float z = to_f(dt_raw[(tok0 + e) * d.H + h]) + bias;
+            const float z = raw[e] + bias;
             const float dt = fminf(fmaxf(softplus_f(z), d.dt_min), d.dt_max);
             dtv[e] = dt;
             run += dt * A;

@@ -262,7 +262,11 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
     __syncthreads();
 
     // Gram tiles of the wave's output tiles, DEPTH k steps ahead of their use
-    // (the first ones overlap the inter-chunk term)
+    // (the first ones overlap the inter-chunk term).  A source tile past the
+    // output tile (not used: its weights are zero) loads the diagonal tile
+    // instead, so the loads need no branch: under a branch a load might not have
+    // been issued, and the wait for an older one would then also take the
+    // loads issued after it.
     constexpr int TPK = KS / 16;  // source tiles per k step
     constexpr int NKS = Q / KS;
     constexpr int DEPTH = 3;
@@ -272,8 +276,8 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
 #pragma unroll
         for (int st = 0; st < TPK; ++st) {
             const int bt = ks * TPK + st;
-            if (bt <= a0) dst[0][st] = *(const t4*)(gb + (int64_t)gram_index(a0, bt) * 256);
-            if (bt <= a1) dst[1][st] = *(const t4*)(gb + (int64_t)gram_index(a1, bt) * 256);
+            dst[0][st] = *(const t4*)(gb + (int64_t)gram_index(a0, min(bt, a0)) * 256);
+            dst[1][st] = *(const t4*)(gb + (int64_t)gram_index(a1, min(bt, a1)) * 256);
         }
     };
 #pragma unroll
