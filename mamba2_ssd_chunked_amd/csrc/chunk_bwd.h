@@ -537,31 +537,41 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
             vt rs[HG][V_GT];
             Frag rr[HG][2][KP];
             float sc[HG][2];
+            // Every load of the round first, then the row scales from the loaded
+            // cumulative sums: computed under each head's branch, a scale waited
+            // for its head's loads before the next head's were issued.  Slots past
+            // the block's last head repeat it and are not used.
+            float cse_r[HG], cst_r[HG][2], dt_r[HG][2];
 #pragma unroll
             for (int q = 0; q < HG; ++q) {
-                if (hf + q < hbs) {
-                    const int h = h0 + hf + q;
-                    const int64_t hl = hl_of(h), so = st_of(h);
-                    const T* src = (dB ? gpn : hpn) + so;
+                const int h = h0 + min(hf + q, hbs - 1);
+                const int64_t hl = hl_of(h), so = st_of(h);
+                const T* src = (dB ? gpn : hpn) + so;
 #pragma unroll
-                    for (int v = 0; v < V_GT; ++v) {
-                        const int idx = threadIdx.x + v * NTH;
-                        if (idx < P * (N / VEC)) rs[q][v] = *(const vt*)(src + (int64_t)idx * VEC);
-                    }
-                    const float cse = cs_ws[hl + Q - 1];
+                for (int v = 0; v < V_GT; ++v) {
+                    const int idx = threadIdx.x + v * NTH;
+                    if (idx < P * (N / VEC)) rs[q][v] = *(const vt*)(src + (int64_t)idx * VEC);
+                }
+                cse_r[q] = cs_ws[hl + Q - 1];
 #pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        const int t = (c == 0 ? j0 : j1) * 16 + lr2;
+                for (int c = 0; c < 2; ++c) {
+                    const int t = (c == 0 ? j0 : j1) * 16 + lr2;
 #pragma unroll
-                        for (int kp = 0; kp < KP; ++kp)
-                            rr[q][c][kp] = dB ? KPermRow<T>::load(xc + (rb + t0 + t) * d.C + (int64_t)h * P + kp * KS, lg2)
-                                              : KPermRow<T>::load(dy + (rb + t0 + t) * HPd + (int64_t)h * P + kp * KS, lg2);
-                        const float cst = cs_ws[hl + t];
-                        sc[q][c] = dB ? ((ssq[t] == seq_e) ? dt_ws[hl + t] * __expf(cse - cst) : 0.f)
-                                      : ((ssq[t] == seq_refc) ? __expf(cst) : 0.f);
-                    }
+                    for (int kp = 0; kp < KP; ++kp)
+                        rr[q][c][kp] = dB ? KPermRow<T>::load(xc + (rb + t0 + t) * d.C + (int64_t)h * P + kp * KS, lg2)
+                                          : KPermRow<T>::load(dy + (rb + t0 + t) * HPd + (int64_t)h * P + kp * KS, lg2);
+                    cst_r[q][c] = cs_ws[hl + t];
+                    dt_r[q][c] = dB ? dt_ws[hl + t] : 0.f;
                 }
             }
+#pragma unroll
+            for (int q = 0; q < HG; ++q)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int t = (c == 0 ? j0 : j1) * 16 + lr2;
+                    sc[q][c] = dB ? ((ssq[t] == seq_e) ? dt_r[q][c] * __expf(cse_r[q] - cst_r[q][c]) : 0.f)
+                                  : ((ssq[t] == seq_refc) ? __expf(cst_r[q][c]) : 0.f);
+                }
             __syncthreads();  // the previous round's products are done with sS
 #pragma unroll
             for (int q = 0; q < HG; ++q) {
