@@ -373,7 +373,7 @@ def main():
         print(json.dumps(summarize_traffic(*args.summarize_traffic, args.copy_probe_mb), indent=1))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

@@ -68,7 +68,7 @@ typedef enum {
     SSD_OK = 0,
     SSD_ERR_NULL = -1,        /* a required pointer is NULL                       */
     SSD_ERR_SHAPE = -2,       /* inconsistent sizes                               */
-    SSD_ERR_UNSUPPORTED = -3, /* valid problem this build has no kernel for        */
+    SSD_ERR_UNSUPPORTED = -3, /* valid problem the library has no kernel for      */
     SSD_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned           */
     SSD_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required        */
     SSD_ERR_HIP = -6,         /* the HIP runtime reported an error at launch       */
