@@ -234,8 +234,10 @@ def backward(wl, heads: Optional[Sequence[int]] = None):
     channels.  The gradients that belong to a head alone are then exactly those
     of the full problem: dxBC and dconv_w of the head's x channels (returned as
     [b, L, H' * P] and [H' * P, W]), ddt_raw [b, L, H'], ddt_bias, dA_log and
-    dD [H'].  B and C channel gradients sum over every head of a group and are
-    not returned for a subset.
+    dD [H'].  B and C channel gradients sum over every head of a group: they are
+    returned only when ``heads`` holds every head of each group it touches, and
+    then dxBC and dconv_w also cover those groups' B and C channels.  The key
+    ``channels`` lists the channel of the full problem behind each returned one.
     """
     xBC = wl.to_causal(wl.xBC)
     dt_raw = wl.to_causal(wl.dt_raw)
@@ -257,7 +259,11 @@ def backward(wl, heads: Optional[Sequence[int]] = None):
     y = ssd_fwd(v, dt_raw, dt_bias, A_log, D, **kw)
     g = ssd_bwd(v, dt_raw, dt_bias, A_log, D, dy, **kw)
     dxBC, dw = conv_silu_bwd(xBC, conv_w, g["dv"], seq)
+    channels = np.arange(wl.conv_dim)
     if heads is not None:
-        dxBC, dw = dxBC[:, :, :H * P], dw[:H * P]
+        hpg = wl.nheads // wl.ngroups
+        whole = all(sum(1 for h in new_heads if h // hpg == gg) == hpg for gg in groups)
+        keep = dxBC.shape[2] if whole else H * P
+        dxBC, dw, channels = dxBC[:, :, :keep], dw[:keep], ch[:keep]
     return dict(y=y, dxBC=dxBC, dconv_w=dw, ddt_raw=g["ddt_raw"], ddt_bias=g["ddt_bias"],
-                dA_log=g["dA_log"], dD=g["dD"])
+                dA_log=g["dA_log"], dD=g["dD"], channels=channels)

@@ -297,17 +297,25 @@ def test_head_subset_matches_full_run():
     np.testing.assert_array_equal(ys, y[:, :, [2, 3, 6, 7]])
 
 
-def test_head_subset_backward_matches_full_run():
+@pytest.mark.parametrize("heads", [[2, 3, 6, 7], [2, 6]])
+def test_head_subset_backward_matches_full_run(heads):
     """Gradients that belong to one head alone are unchanged when the problem is
-    restricted to a subset of heads (with their groups' B and C channels)."""
+    restricted to a subset of heads (with their groups' B and C channels); with
+    every head of each touched group ([2, 3, 6, 7]: groups 1 and 3) the groups'
+    B and C channel gradients are whole and come back too."""
     wl = W.make_workload("sub_bwd", batch=2, seqlen=64, nheads=8, headdim=4, dstate=4,
                          ngroups=4, chunk=16, act="bf16", seed=22, lengths=[20, 1, 43],
                          with_dy=True)
-    heads = [2, 3, 6, 7]
     full = oracle.backward(wl)
     sub = oracle.backward(wl, heads=heads)
-    P = wl.headdim
+    P, N, H, G = wl.headdim, wl.dstate, wl.nheads, wl.ngroups
     ch = np.concatenate([np.arange(h * P, (h + 1) * P) for h in heads])
+    if len(heads) == 4:
+        for g in (1, 3):
+            ch = np.concatenate([ch, H * P + g * N + np.arange(N)])
+        for g in (1, 3):
+            ch = np.concatenate([ch, H * P + G * N + g * N + np.arange(N)])
+    np.testing.assert_array_equal(sub["channels"], ch)
     np.testing.assert_allclose(sub["dxBC"], full["dxBC"][:, :, ch], rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(sub["dconv_w"], full["dconv_w"][ch], rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(sub["ddt_raw"], full["ddt_raw"][:, :, heads], rtol=1e-12,
@@ -458,3 +466,172 @@ def test_adjoint_dot_product_identity():
     measured = float((oracle.forward(plus) * wl.dy).sum() - (oracle.forward(minus) * wl.dy).sum())
     assert abs(predicted) > 1e-6
     assert abs(measured - predicted) <= 1e-5 * abs(predicted), (measured, predicted)
+
+
+# ---------------------------------------------------------------- initial state in the adjoint
+#
+# The boundary scan hands every segment an initial state S_in and the reverse scan
+# hands back dL/dS_in (Megatron-LM #6808, first commit: S_out = a_block S_in + S_ext,
+# and the backward mirrors it with a reverse scan).  The oracle's adjoint with a
+# non-zero initial state (its t = 0 terms and the gradient of the initial state
+# itself) is pinned here at the level of the post-conv recurrence.
+
+
+def _init_problem(seed, lengths=None):
+    """A small post-conv problem with a random initial state and upstream gradient."""
+    rng = np.random.default_rng(seed)
+    b, L, H, P, N, G = 2, 40, 4, 3, 4, 2
+    C = H * P + 2 * G * N
+    v = rng.standard_normal((b, L, C))
+    dt_raw = rng.standard_normal((b, L, H)).astype(np.float32)
+    dt_bias = (rng.standard_normal(H) * 0.5 - 2.5).astype(np.float32)
+    A_log = rng.uniform(0.0, math.log(4.0), H).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    init = rng.standard_normal((b, H, P, N))
+    dy = rng.standard_normal((b, L, H, P)).astype(np.float32)
+    seq = None
+    if lengths is not None:
+        seq = np.ascontiguousarray(np.broadcast_to(
+            np.repeat(np.arange(len(lengths)), lengths).astype(np.int32), (b, L)))
+    kw = dict(nheads=H, headdim=P, dstate=N, ngroups=G, dt_min=1e-3, dt_max=0.1, seq_idx=seq)
+    return dict(v=v, dt_raw=dt_raw, dt_bias=dt_bias, A_log=A_log, D=D, init=init, dy=dy), kw
+
+
+def _torch_loss_with_init(v, dt_raw, dt_bias, A_log, D, init, dy, H, P, N, G, seq):
+    """<dy, y> with y from the quadratic (SSD-matrix) form plus the initial-state term
+    exp(cs_i) C_i . init[p, :] for tokens i of the row's first sequence, where cs is the
+    inclusive cumulative sum of dt A from the row start (the state before the first
+    token decays by that token's factor).  Written independently of the oracle."""
+    b, L, _ = v.shape
+    hpg = H // G
+    idx = torch.arange(L)
+    causal = idx[:, None] >= idx[None, :]
+    first = torch.ones(b, L, dtype=torch.bool)
+    if seq is not None:
+        s = torch.from_numpy(np.asarray(seq))
+        causal = causal[None] & (s[:, :, None] == s[:, None, :])
+        first = s == s[:, :1]
+    else:
+        causal = causal[None].expand(b, L, L)
+    lo, hi = float(np.float32(1e-3)), float(np.float32(0.1))
+    loss = 0
+    for h in range(H):
+        g = h // hpg
+        x = v[:, :, h * P:(h + 1) * P]
+        Bm = v[:, :, H * P + g * N:H * P + (g + 1) * N]
+        Cm = v[:, :, H * P + G * N + g * N:H * P + G * N + (g + 1) * N]
+        dt = torch.clamp(torch.nn.functional.softplus(dt_raw[:, :, h] + dt_bias[h]), lo, hi)
+        cs = torch.cumsum(dt * (-torch.exp(A_log[h])), dim=1)
+        seg = cs[:, :, None] - cs[:, None, :]
+        lam = torch.where(causal, torch.exp(torch.where(causal, seg, torch.zeros_like(seg))),
+                          torch.zeros_like(seg))
+        y = (lam * (Cm @ Bm.transpose(1, 2))) @ (dt[:, :, None] * x) + D[h] * x
+        dec = torch.where(first, torch.exp(cs), torch.zeros_like(cs))
+        y = y + dec[:, :, None] * (Cm @ init[:, h].transpose(1, 2))
+        loss = loss + (y * dy[:, :, h, :]).sum()
+    return loss
+
+
+@pytest.mark.parametrize("lengths", [None, [13, 27]])
+def test_adjoint_with_initial_state_matches_autograd(lengths):
+    """Every gradient of the oracle's adjoint under a non-zero initial state, dinit
+    included, against torch autograd of the quadratic form with the initial-state term."""
+    a, kw = _init_problem(51, lengths)
+    g = oracle.ssd_bwd(a["v"], a["dt_raw"], a["dt_bias"], a["A_log"], a["D"], a["dy"],
+                       init=a["init"], want_dinit=True, **kw)
+    t = lambda z: torch.tensor(np.asarray(z, np.float64), requires_grad=True)
+    v, dtr, dtb, al, D, ini = (t(a["v"]), t(a["dt_raw"]), t(a["dt_bias"]), t(a["A_log"]),
+                               t(a["D"]), t(a["init"]))
+    loss = _torch_loss_with_init(v, dtr, dtb, al, D, ini, torch.from_numpy(a["dy"].astype(np.float64)),
+                                 kw["nheads"], kw["headdim"], kw["dstate"], kw["ngroups"],
+                                 kw["seq_idx"])
+    loss.backward()
+    # the forward itself under the initial state
+    y = oracle.ssd_fwd(a["v"], a["dt_raw"], a["dt_bias"], a["A_log"], a["D"], init=a["init"], **kw)
+    np.testing.assert_allclose(float((y * a["dy"]).sum()), loss.item(), rtol=1e-11)
+    for name, ref in [("dv", v), ("ddt_raw", dtr), ("ddt_bias", dtb), ("dA_log", al),
+                      ("dD", D), ("dinit", ini)]:
+        np.testing.assert_allclose(g[name], ref.grad.numpy(), rtol=1e-9, atol=1e-10, err_msg=name)
+    if lengths is not None:
+        # tokens after the first reset cannot see the initial state
+        assert np.any(g["dinit"] != 0.0)
+
+
+def test_initial_state_gradient_matches_finite_differences():
+    """dL/dinit and, under a non-zero initial state, dL/d(dt_raw) and dL/dA_log by
+    central differences of the oracle forward (the loss is linear in init, so those
+    differences are exact up to rounding)."""
+    a, kw = _init_problem(52, [22, 18])
+    g = oracle.ssd_bwd(a["v"], a["dt_raw"], a["dt_bias"], a["A_log"], a["D"], a["dy"],
+                       init=a["init"], want_dinit=True, **kw)
+
+    def loss(**over):
+        z = dict(a, **over)
+        y = oracle.ssd_fwd(z["v"], z["dt_raw"], z["dt_bias"], z["A_log"], z["D"],
+                           init=z["init"], **kw)
+        return float((y * a["dy"]).sum())
+
+    eps = 1e-5
+    base = a["init"]
+    for fi in range(base.size):
+        p, m = base.copy().reshape(-1), base.copy().reshape(-1)
+        p[fi] += eps
+        m[fi] -= eps
+        fd = (loss(init=p.reshape(base.shape)) - loss(init=m.reshape(base.shape))) / (2 * eps)
+        an = g["dinit"].reshape(-1)[fi]
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), ("dinit", fi, fd, an)
+    # t = 0 of every row: the only token whose dt term sees the initial state directly
+    rng = np.random.default_rng(53)
+    checks = [("ddt_raw", "dt_raw", (r, 0, h)) for r in range(2) for h in range(4)]
+    checks += [("ddt_raw", "dt_raw", tuple(rng.integers(0, s) for s in a["dt_raw"].shape))
+               for _ in range(6)]
+    checks += [("dA_log", "A_log", (h,)) for h in range(4)]
+    sp = np.logaddexp(0.0, a["dt_raw"].astype(np.float64) + a["dt_bias"][None, None, :])
+    for gname, field, ix in checks:
+        if field == "dt_raw" and min(abs(sp[ix] - float(np.float32(1e-3))),
+                                     abs(sp[ix] - float(np.float32(0.1)))) < 1e-3:
+            continue  # at a clamp kink a central difference straddles it
+        base32 = a[field]
+        h = 1e-3
+        p, m = base32.copy(), base32.copy()
+        p[ix] = np.float32(p[ix] + h)
+        m[ix] = np.float32(m[ix] - h)
+        step = float(p[ix]) - float(m[ix])
+        fd = (loss(**{field: p}) - loss(**{field: m})) / step
+        an = g[gname][ix]
+        assert abs(fd - an) <= 2e-4 * max(1.0, abs(an)), (gname, ix, fd, an)
+
+
+def test_adjoint_dot_product_identity_with_initial_state():
+    """The dot-product test of the adjoint along one random direction over every input
+    of the recurrence and the initial state at once."""
+    a, kw = _init_problem(54, [19, 21])
+    g = oracle.ssd_bwd(a["v"], a["dt_raw"], a["dt_bias"], a["A_log"], a["D"], a["dy"],
+                       init=a["init"], want_dinit=True, **kw)
+    rng = np.random.default_rng(55)
+    eps = 1e-4
+    sp = np.logaddexp(0.0, a["dt_raw"].astype(np.float64) + a["dt_bias"][None, None, :])
+    far = (np.minimum(np.abs(sp - float(np.float32(1e-3))), np.abs(sp - float(np.float32(0.1))))
+           > 4 * eps)
+    plus, minus = dict(a), dict(a)
+    predicted = 0.0
+    for gname, field in [("dv", "v"), ("ddt_raw", "dt_raw"), ("dA_log", "A_log"), ("dD", "D"),
+                         ("dinit", "init")]:
+        base = a[field].astype(np.float64)
+        d = rng.standard_normal(base.shape)
+        if field == "dt_raw":
+            d = d * far
+        dt = a[field].dtype
+        pz = (base + eps * d).astype(dt)
+        mz = (base - eps * d).astype(dt)
+        plus[field], minus[field] = pz, mz
+        predicted += float((g[gname] * (pz.astype(np.float64) - mz.astype(np.float64))).sum())
+
+    def lval(z):
+        y = oracle.ssd_fwd(z["v"], z["dt_raw"], z["dt_bias"], z["A_log"], z["D"],
+                           init=z["init"], **kw)
+        return float((y * a["dy"]).sum())
+
+    measured = lval(plus) - lval(minus)
+    assert abs(predicted) > 1e-6
+    assert abs(measured - predicted) <= 1e-6 * abs(predicted), (measured, predicted)
