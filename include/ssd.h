@@ -45,9 +45,12 @@
  *    problem->act_dtype; parameters, states, summaries, y_zero and every
  *    parameter gradient are float32.
  *  - Outputs are overwritten, never accumulated.
- *  - Errors: all arguments are checked on the host before anything is
- *    enqueued.  On error the function returns a negative ssd_status and
- *    enqueues nothing.  A failed launch returns SSD_ERR_HIP.
+ *  - Errors: all arguments, and every launch grid the call will need, are
+ *    checked on the host before anything is enqueued; on such an error the
+ *    function returns a negative ssd_status and enqueues nothing.  A launch
+ *    that the HIP runtime refuses returns SSD_ERR_HIP.  A call made of several
+ *    launches stops at the first refused one: the launches before it stay
+ *    enqueued, so the outputs are then undefined.
  *  - Calls are re-entrant and hold no global state.
  */
 #ifndef MI355X_SSD_H
@@ -103,7 +106,12 @@ const char* ssd_status_string(int status);
 /* Library ABI version (increments on incompatible changes). */
 int32_t ssd_abi_version(void);
 
-/* Returns 1 when (headdim, dstate, act_dtype) has compiled kernels, else 0. */
+/* Returns 1 when (headdim, dstate, act_dtype) has compiled kernels, else 0:
+ * float32 (16, 16), (32, 32), (64, 64), (64, 128); bf16 (32, 64), (64, 64),
+ * (64, 128).  Every chunk length runs the forward; the backward runs every
+ * bf16 pair at every chunk length and the float32 pairs at chunks 64 and 128
+ * (ssd_workspace_bytes(..., SSD_WS_BACKWARD) is 0 for the rest, and the
+ * backward calls return SSD_ERR_UNSUPPORTED). */
 int32_t ssd_supported(int32_t headdim, int32_t dstate, int32_t act_dtype);
 
 /* Bytes of device workspace the forward (SSD_WS_FORWARD: ssd_segment_fwd, read
@@ -175,7 +183,9 @@ int ssd_boundary_scan(const ssd_problem* problem, int32_t nseg, const float* sum
                       const float* init, int32_t reverse, float* out, float* final_state,
                       void* stream);
 
-/* Correction and output pass: y = y_zero + decay_t * C_t S_in^T + D x_t.
+/* Correction and output pass: y = y_zero + decay_t * C_t S_in^T + D x_t, the
+ * correction of Megatron-LM #6808's first commit (a segment's outputs gain the
+ * term C_t * decay * S_in once the boundary scan has produced its S_in).
  * decay_t = exp(sum of dt*A from the segment start through t), and 0 once a
  * packed sequence starts inside the segment; for the first segment of a row,
  * S_in is the state before the row's first token.
@@ -209,7 +219,11 @@ int ssd_segment_output_fused(const ssd_problem* problem, const ssd_segment* segs
                              const float* S_in, const void* ws, size_t ws_bytes, void* y,
                              void* stream);
 
-/* Backward, summary phase.  Recomputes the conv output, dt and the
+/* Backward, summary phase (Megatron-LM #6808, first commit: the backward
+ * mirrors the forward, each segment summarising the gradient its own outputs
+ * send to its initial state, gathered and reverse-scanned like the forward
+ * summaries; sequence-length-sized intermediates are recomputed, not stored).
+ * Recomputes the conv output, dt and the
  * cumulative decays into `ws` (sequence-length-sized intermediates are
  * recomputed, never saved from the forward), then walks every segment's chunks
  * in reverse causal order carrying the state gradient.  Writes, in the summary
@@ -228,7 +242,11 @@ int ssd_segment_bwd_summary(const ssd_problem* problem, const ssd_segment* segs,
                             const void* dy, float* summary, void* ws, size_t ws_bytes,
                             void* stream);
 
-/* Backward, segment phase: every gradient of the path.
+/* Backward, segment phase: every gradient of the path (Megatron-LM #6808,
+ * first commit: with its initial state from the forward scan and its
+ * final-state gradient from the reverse scan, each segment runs the SSD
+ * backward locally and writes its gradients straight into the buffers the
+ * convolution backward consumes).
  *   S_in      [nseg][batch][H][P][N] float32: initial states from the forward
  *             boundary scan (segment-count sized, so it may be kept)         (in)
  *   dS_out    [nseg][batch][H][P][N] float32: final-state gradients from the

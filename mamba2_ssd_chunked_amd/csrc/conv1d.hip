@@ -90,34 +90,33 @@ __global__ void __launch_bounds__(256) k_conv1d_silu(Dims d, SegTab tab, const T
 }
 
 template <typename T, int W>
-static void launch_w(const Dims& d, const SegTab& t, const void* xBC, const float* w,
-                     const int32_t* seq, void* out, hipStream_t s) {
+static hipError_t launch_w(const Dims& d, const SegTab& t, const void* xBC, const float* w,
+                           const int32_t* seq, void* out, hipStream_t s) {
     dim3 grid((d.C + 64 * CONV_VEC - 1) / (64 * CONV_VEC), (unsigned)(d.L / CONV_TT),
               (unsigned)d.batch);
-    hipLaunchKernelGGL((k_conv1d_silu<T, W>), grid, dim3(256), 0, s, d, t, (const T*)xBC, w, seq,
-                       (T*)out);
+    return launch(k_conv1d_silu<T, W>, grid, dim3(256), s, d, t, (const T*)xBC, w, seq, (T*)out);
 }
 
 template <typename T>
-static void launch_t(const Dims& d, const SegTab& t, const void* xBC, const float* w,
-                     const int32_t* seq, void* out, hipStream_t s) {
+static hipError_t launch_t(const Dims& d, const SegTab& t, const void* xBC, const float* w,
+                           const int32_t* seq, void* out, hipStream_t s) {
     switch (d.W) {
-        case 1: launch_w<T, 1>(d, t, xBC, w, seq, out, s); break;
-        case 2: launch_w<T, 2>(d, t, xBC, w, seq, out, s); break;
-        case 3: launch_w<T, 3>(d, t, xBC, w, seq, out, s); break;
-        case 4: launch_w<T, 4>(d, t, xBC, w, seq, out, s); break;
-        case 5: launch_w<T, 5>(d, t, xBC, w, seq, out, s); break;
-        case 6: launch_w<T, 6>(d, t, xBC, w, seq, out, s); break;
-        case 7: launch_w<T, 7>(d, t, xBC, w, seq, out, s); break;
-        default: launch_w<T, 8>(d, t, xBC, w, seq, out, s); break;
+        case 1: return launch_w<T, 1>(d, t, xBC, w, seq, out, s);
+        case 2: return launch_w<T, 2>(d, t, xBC, w, seq, out, s);
+        case 3: return launch_w<T, 3>(d, t, xBC, w, seq, out, s);
+        case 4: return launch_w<T, 4>(d, t, xBC, w, seq, out, s);
+        case 5: return launch_w<T, 5>(d, t, xBC, w, seq, out, s);
+        case 6: return launch_w<T, 6>(d, t, xBC, w, seq, out, s);
+        case 7: return launch_w<T, 7>(d, t, xBC, w, seq, out, s);
+        case 8: return launch_w<T, 8>(d, t, xBC, w, seq, out, s);
+        default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_conv1d_fwd(const Dims& d, const SegTab& t, int act, const void* xBC,
                              const float* w, const int32_t* seq, void* out, hipStream_t s) {
-    if (act == SSD_BF16) launch_t<bf16>(d, t, xBC, w, seq, out, s);
-    else launch_t<float>(d, t, xBC, w, seq, out, s);
-    return hipGetLastError();
+    if (act == SSD_BF16) return launch_t<bf16>(d, t, xBC, w, seq, out, s);
+    return launch_t<float>(d, t, xBC, w, seq, out, s);
 }
 
 }  // namespace ssd

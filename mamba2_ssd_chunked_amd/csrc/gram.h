@@ -91,13 +91,13 @@ __global__ void __launch_bounds__(64) k_gram_dt(Dims d, const T* __restrict__ xc
 }
 
 template <typename T, int N, bool TRANS = false>
-inline void launch_gram_dt(const Dims& d, const T* xc, T* gram, const void* dt_raw,
-                           const float* dt_bias, const float* A_log, const int32_t* seq,
-                           float* dt_ws, float* cs_ws, float* ctot, hipStream_t s) {
+inline hipError_t launch_gram_dt(const Dims& d, const T* xc, T* gram, const void* dt_raw,
+                                 const float* dt_bias, const float* A_log, const int32_t* seq,
+                                 float* dt_ws, float* cs_ws, float* ctot, hipStream_t s) {
     const int64_t ngram = (int64_t)(d.Q / 16 / 2 * GSPLIT) * d.nchunk * d.G * d.batch;
     const int64_t ndt = (int64_t)d.nchunk * d.H * d.batch;
-    hipLaunchKernelGGL((k_gram_dt<T, N, TRANS>), dim3((unsigned)(ngram + ndt)), dim3(64), 0, s, d,
-                       xc, gram, ngram, (const T*)dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot);
+    return launch(k_gram_dt<T, N, TRANS>, dim3((unsigned)(ngram + ndt)), dim3(64), s, d, xc, gram,
+                  ngram, (const T*)dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot);
 }
 
 }  // namespace ssd

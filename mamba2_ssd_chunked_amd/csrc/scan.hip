@@ -45,9 +45,8 @@ hipError_t launch_boundary_scan(const Dims& d, int nseg, const float* summary, c
     const int64_t BH = d.batch * d.H;
     const int PN = d.P * d.N;
     const int64_t nq = BH * (PN / 4);
-    hipLaunchKernelGGL(k_boundary_scan, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, BH,
-                       PN, nseg, reverse, summary, init, out, final_state);
-    return hipGetLastError();
+    return launch(k_boundary_scan, dim3((unsigned)((nq + 255) / 256)), dim3(256), s, BH, PN, nseg,
+                  reverse, summary, init, out, final_state);
 }
 
 }  // namespace ssd

@@ -19,6 +19,34 @@ namespace {
 
 bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 
+// Every launch grid of the library fits the dispatch limits: at most 2^32 - 1
+// work-items and 2^31 - 1 workgroups along x, at most 65535 workgroups along y
+// and z.  The grids are those of the launchers (conv1d.hip, gram.h, state_walk.h,
+// ssd_fwd.hip, scan.hip, ssd_bwd.hip), computed here in 128-bit arithmetic so
+// that no product overflows; a problem whose grids do not fit is rejected
+// before anything is enqueued.
+bool grids_fit(const ssd_problem* p, int64_t C) {
+    typedef unsigned __int128 u128;
+    const u128 b = (u128)p->batch, L = (u128)p->seqlen, H = (u128)p->nheads;
+    const u128 G = (u128)p->ngroups, Q = (u128)p->chunk, nc = L / Q;
+    const u128 nseg = SSD_MAX_SEGMENTS;
+    const u128 PN = (u128)p->headdim * (u128)p->dstate, CC = (u128)C;
+    auto x_ok = [](u128 blocks, u128 threads) {
+        return blocks <= 0x7fffffffu && blocks * threads <= 0xffffffffu;
+    };
+    const u128 cx = (CC + 255) / 256;  // conv workgroups along channels
+    bool ok = x_ok(cx, 256) && L / 64 <= 65535 && b <= 65535;                   // conv forward
+    ok = ok && x_ok((Q / 32 * 4) * nc * G * b + nc * H * b, 64);                   // Gram + dt prep
+    ok = ok && x_ok(2 * H * nseg * b, 512);                                        // state walks
+    ok = ok && x_ok(nc * H * b, 512);                                              // output passes
+    ok = ok && x_ok((b * H * PN / 4 + 255) / 256, 256);                            // boundary scan
+    ok = ok && nc <= 0x7fffffffu && (H + 3) / 4 <= 65535;                         // dt prep alone
+    ok = ok && x_ok((b * L * G * 2 * (u128)p->dstate / 4 + 255) / 256, 256);       // dB, dC sums
+    ok = ok && x_ok(cx * (L / 64) * b + (nc * H * b + 3) / 4, 256);                // conv backward
+    ok = ok && x_ok((CC * (u128)p->conv_width + 3 * H + 31) / 32, 256);            // reductions
+    return ok;
+}
+
 // Validates the problem and fills Dims.  Returns SSD_OK or an error.
 int check_problem(const ssd_problem* p, Dims* d) {
     if (!p) return SSD_ERR_NULL;
@@ -33,12 +61,13 @@ int check_problem(const ssd_problem* p, Dims* d) {
     if (p->seqlen % p->chunk != 0) return SSD_ERR_SHAPE;
     if (!kernels_supported(p->headdim, p->dstate, p->act_dtype)) return SSD_ERR_UNSUPPORTED;
     if (!chunk_supported(p->headdim, p->dstate, p->chunk, p->act_dtype)) return SSD_ERR_UNSUPPORTED;
+    if (p->batch > 65535 || p->nheads > 65535 || p->seqlen > INT32_MAX) return SSD_ERR_SHAPE;
     const int64_t C = (int64_t)p->nheads * p->headdim + 2LL * p->ngroups * p->dstate;
-    // token positions inside a row are 32-bit in the kernels; the per-(chunk,
-    // head) kernels use one 1-D grid of at most 2^32 work-items
-    if (C > (1LL << 30) || p->seqlen > INT32_MAX || p->batch > 65535 || p->nheads > 65535 ||
-        (p->seqlen / p->chunk) * p->nheads * p->batch * 512 >= (1LL << 32))
-        return SSD_ERR_SHAPE;
+    const int64_t esz = p->act_dtype == SSD_BF16 ? 2 : 4;
+    // a token row of xBC must be addressable with 32-bit byte offsets (the conv
+    // backward's buffer accesses), and every launch grid must fit
+    if (C * esz > INT32_MAX) return SSD_ERR_SHAPE;
+    if (!grids_fit(p, C)) return SSD_ERR_SHAPE;
     d->batch = p->batch;
     d->L = p->seqlen;
     d->H = p->nheads;

@@ -520,18 +520,19 @@ static bool shape_ok(int Q) {
 }
 
 template <typename T, int P, int N, int Q, bool FINAL>
-static void launch_chunk_y(const Dims& d, const SegTab& t, const T* xc, const T* gram,
-                           const float* dtw, const float* csw, const float* ctot,
-                           const int32_t* seq, const T* hst, const float* S_in, const float* D,
-                           float* y_zero, T* y, hipStream_t s) {
+static hipError_t launch_chunk_y(const Dims& d, const SegTab& t, const T* xc, const T* gram,
+                                 const float* dtw, const float* csw, const float* ctot,
+                                 const int32_t* seq, const T* hst, const float* S_in,
+                                 const float* D, float* y_zero, T* y, hipStream_t s) {
     if constexpr (chunk_y_lds<T, P, N, Q>() <= LDS_LIMIT) {
-        hipLaunchKernelGGL((k_chunk_y<T, P, N, Q, FINAL>), chunk_head_grid(d), dim3(Q / 32 * 64), 0,
-                           s, d, t, xc, gram, dtw, csw, ctot, seq, hst, S_in, D, y_zero, y);
+        return launch(k_chunk_y<T, P, N, Q, FINAL>, chunk_head_grid(d), dim3(Q / 32 * 64), s, d, t,
+                      xc, gram, dtw, csw, ctot, seq, hst, S_in, D, y_zero, y);
     }
+    return hipErrorInvalidValue;
 }
 
 template <typename T, int P, int N>
-static void segment_states_t(const Dims& d, const SegTab& t, const void* xc_, const void* dt_raw,
+static hipError_t segment_states_t(const Dims& d, const SegTab& t, const void* xc_, const void* dt_raw,
                              const float* dt_bias, const float* A_log, const int32_t* seq,
                              float* summary, void* ws, hipStream_t s) {
     const T* xc = (const T*)xc_;
@@ -543,15 +544,16 @@ static void segment_states_t(const Dims& d, const SegTab& t, const void* xc_, co
     T* hst = (T*)(w + L.hst);
     // the group Gram tiles the output pass reads and dt prep share one launch
     // (independent inputs); the walk then needs dt and the cumulative sums
-    launch_gram_dt<T, N>(d, xc, (T*)(w + L.gram), dt_raw, dt_bias, A_log, seq, dtw, csw, ctot, s);
+    SSD_TRY(launch_gram_dt<T, N>(d, xc, (T*)(w + L.gram), dt_raw, dt_bias, A_log, seq, dtw, csw,
+                                 ctot, s));
     const WalkArgs<T> wa = {xc, nullptr, dtw, csw, seq, nullptr, hst, summary};
-    launch_state_walk<T, P, N, false>(d, t, wa, s);
+    return launch_state_walk<T, P, N, false>(d, t, wa, s);
 }
 
 // y_zero (FINAL = false) or the corrected y (FINAL = true), from the workspace
 // that segment_states_t filled (decays, entering states, Gram tiles).
 template <typename T, int P, int N, bool FINAL>
-static void segment_output_t(const Dims& d, const SegTab& t, const void* xc_, const int32_t* seq,
+static hipError_t segment_output_t(const Dims& d, const SegTab& t, const void* xc_, const int32_t* seq,
                              const void* ws, const float* S_in, const float* D, float* y_zero,
                              void* y, hipStream_t s) {
     const T* xc = (const T*)xc_;
@@ -565,29 +567,28 @@ static void segment_output_t(const Dims& d, const SegTab& t, const void* xc_, co
     T* yo = (T*)y;
     switch (d.Q) {
         case 64:
-            launch_chunk_y<T, P, N, 64, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst, S_in, D,
-                                               y_zero, yo, s);
-            break;
+            return launch_chunk_y<T, P, N, 64, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst, S_in,
+                                                      D, y_zero, yo, s);
         case 128:
-            launch_chunk_y<T, P, N, 128, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst, S_in, D,
-                                                y_zero, yo, s);
-            break;
+            return launch_chunk_y<T, P, N, 128, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst,
+                                                       S_in, D, y_zero, yo, s);
+        case 256:
+            return launch_chunk_y<T, P, N, 256, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst,
+                                                       S_in, D, y_zero, yo, s);
         default:
-            launch_chunk_y<T, P, N, 256, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst, S_in, D,
-                                                y_zero, yo, s);
-            break;
+            return hipErrorInvalidValue;
     }
 }
 
 template <typename T, int P, int N>
-static void apply_init_t(const Dims& d, const SegTab& t, const float* y_zero, const void* xc,
-                         const float* D, const int32_t* seq, const float* S_in, const void* ws,
-                         void* y, hipStream_t s) {
+static hipError_t apply_init_t(const Dims& d, const SegTab& t, const float* y_zero, const void* xc,
+                               const float* D, const int32_t* seq, const float* S_in,
+                               const void* ws, void* y, hipStream_t s) {
     const FwdWs L = fwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
     const char* w = (const char*)ws;
-    hipLaunchKernelGGL((k_apply_init<T, P, N>), chunk_head_grid(d),
-                       dim3(256), 0, s, d, t, y_zero, (const T*)xc, D, seq, S_in,
-                       (const float*)(w + L.cs), (const float*)(w + L.ctot), (T*)y);
+    return launch(k_apply_init<T, P, N>, chunk_head_grid(d), dim3(256), s, d, t, y_zero,
+                  (const T*)xc, D, seq, S_in, (const float*)(w + L.cs),
+                  (const float*)(w + L.ctot), (T*)y);
 }
 
 hipError_t launch_dt_prep(const Dims& d, int act, const void* dt_raw, const float* dt_bias,
@@ -595,17 +596,11 @@ hipError_t launch_dt_prep(const Dims& d, int act, const void* dt_raw, const floa
                           float* ctot, hipStream_t s) {
     const dim3 grid((unsigned)d.nchunk, (unsigned)((d.H + 3) / 4), (unsigned)d.batch);
     if (act == SSD_BF16)
-        hipLaunchKernelGGL(k_dt_prep<bf16>, grid, dim3(256), 0, s, d, (const bf16*)dt_raw, dt_bias,
-                           A_log, seq, dt_ws, cs_ws, ctot);
-    else
-        hipLaunchKernelGGL(k_dt_prep<float>, grid, dim3(256), 0, s, d, (const float*)dt_raw,
-                           dt_bias, A_log, seq, dt_ws, cs_ws, ctot);
-    return hipGetLastError();
+        return launch(k_dt_prep<bf16>, grid, dim3(256), s, d, (const bf16*)dt_raw, dt_bias, A_log,
+                      seq, dt_ws, cs_ws, ctot);
+    return launch(k_dt_prep<float>, grid, dim3(256), s, d, (const float*)dt_raw, dt_bias, A_log,
+                  seq, dt_ws, cs_ws, ctot);
 }
-
-// (P, N) pairs with kernels.  bf16 needs N % 32 == 0 (one MFMA consumes 32 of k).
-#define SSD_F32_SHAPES(X) X(16, 16) X(32, 32) X(64, 64) X(64, 128)
-#define SSD_BF16_SHAPES(X) X(32, 64) X(64, 64) X(64, 128) X(128, 128)
 
 bool kernels_supported(int P, int N, int act) {
 #define X(p, n) if (P == p && N == n) return true;
@@ -633,8 +628,7 @@ hipError_t launch_segment_states(const Dims& d, const SegTab& t, int act, const 
                                  const int32_t* seq, float* summary, void* ws, hipStream_t s) {
 #define X(p, n)                                                                               \
     if (d.P == p && d.N == n) {                                                               \
-        segment_states_t<T, p, n>(d, t, xBC_conv, dt_raw, dt_bias, A_log, seq, summary, ws, s); \
-        return hipGetLastError();                                                             \
+        return segment_states_t<T, p, n>(d, t, xBC_conv, dt_raw, dt_bias, A_log, seq, summary, ws, s); \
     }
     if (act == SSD_F32) {
         typedef float T;
@@ -652,9 +646,8 @@ hipError_t launch_segment_output(const Dims& d, const SegTab& t, int act, const 
                                  hipStream_t s) {
 #define X(p, n)                                                                                 \
     if (d.P == p && d.N == n) {                                                                 \
-        segment_output_t<T, p, n, false>(d, t, xBC_conv, seq, ws, nullptr, nullptr, y_zero,     \
-                                         nullptr, s);                                           \
-        return hipGetLastError();                                                               \
+        return segment_output_t<T, p, n, false>(d, t, xBC_conv, seq, ws, nullptr, nullptr, y_zero, \
+                                                nullptr, s);                                  \
     }
     if (act == SSD_F32) {
         typedef float T;
@@ -672,8 +665,7 @@ hipError_t launch_segment_output_fused(const Dims& d, const SegTab& t, int act,
                                        const float* S_in, const void* ws, void* y, hipStream_t s) {
 #define X(p, n)                                                                                 \
     if (d.P == p && d.N == n) {                                                                 \
-        segment_output_t<T, p, n, true>(d, t, xBC_conv, seq, ws, S_in, D, nullptr, y, s);       \
-        return hipGetLastError();                                                               \
+        return segment_output_t<T, p, n, true>(d, t, xBC_conv, seq, ws, S_in, D, nullptr, y, s); \
     }
     if (act == SSD_F32) {
         typedef float T;
@@ -691,8 +683,7 @@ hipError_t launch_apply_init_state(const Dims& d, const SegTab& t, int act, cons
                                    const float* S_in, const void* ws, void* y, hipStream_t s) {
 #define X(p, n)                                                                     \
     if (d.P == p && d.N == n) {                                                     \
-        apply_init_t<T, p, n>(d, t, y_zero, xBC_conv, D, seq, S_in, ws, y, s);     \
-        return hipGetLastError();                                                   \
+        return apply_init_t<T, p, n>(d, t, y_zero, xBC_conv, D, seq, S_in, ws, y, s); \
     }
     if (act == SSD_F32) {
         typedef float T;

@@ -8,6 +8,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <array>
+#include <tuple>
+#include <utility>
+
 #include "../../include/ssd.h"
 
 namespace ssd {
@@ -25,6 +29,28 @@ struct Dims {
     int nseg;
     float dt_min, dt_max;
 };
+
+// Kernel launch that returns the launch's own status (hipLaunchKernel), so a
+// call made of several launches stops at the first that fails.  The arguments
+// are converted to the kernel's parameter types first.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
+                         Args&&... args) {
+    std::tuple<KArgs...> a(std::forward<Args>(args)...);
+    return std::apply(
+        [&](auto&... v) {
+            std::array<void*, sizeof...(KArgs) + 1> p = {(void*)&v..., nullptr};
+            return hipLaunchKernel((const void*)kernel, grid, block, p.data(), 0, s);
+        },
+        a);
+}
+
+// Stops a host launcher at the first failed launch.
+#define SSD_TRY(...)                              \
+    do {                                          \
+        const hipError_t ssd_e_ = (__VA_ARGS__);  \
+        if (ssd_e_ != hipSuccess) return ssd_e_;  \
+    } while (0)
 
 // Segment table in causal order; start and len in tokens (memory offsets).
 struct SegTab {
@@ -196,6 +222,12 @@ template <> struct Mma<float> {
     }
 };
 
+// (P, N) pairs with compiled kernels, per activation type.  bf16 needs
+// N % 32 == 0 (one MFMA consumes 32 of k).  The chunk length and the backward
+// narrow this further (chunk_supported, bwd_supported).
+#define SSD_F32_SHAPES(X) X(16, 16) X(32, 32) X(64, 64) X(64, 128)
+#define SSD_BF16_SHAPES(X) X(32, 64) X(64, 64) X(64, 128)
+
 // Host-side launchers (defined in the .hip files).  Each returns hipSuccess or
 // the launch error.
 hipError_t launch_conv1d_fwd(const Dims& d, const SegTab& t, int act, const void* xBC,
@@ -260,11 +292,21 @@ inline FwdWs fwd_ws_layout(const Dims& d, int act) {
     return w;
 }
 
-// Backward workspace layout (byte offsets).  Filled by the summary phase
-// (xc, bct, dt, cs, ctot, zh, zg, dyT) and used by the segment phase.
+// Heads per workgroup of the head-blocked chunk backward: the largest divisor of
+// the heads per group up to eight.
+inline int head_block(const Dims& d) {
+    int hb = 1;
+    for (int c = 1; c <= 8; ++c)
+        if (d.hpg % c == 0) hb = c;
+    return hb;
+}
+
+// Backward workspace layout (byte offsets).  The summary phase fills xc, gramt,
+// dt, cs and ctot; the pass phase gpn and hpn; the chunk phase dv, dbc, rpart,
+// tokp, dotgh and red4; the conv phase dbcs, red and dwp.
 struct BwdWs {
-    size_t xc, bct, gramt, dt, cs, ctot, zh, zg, gpn, gnp, hnp, hpn, dyT, dv, dbc, dbcs, rpart,
-        tokp, dotgh, red4, red, dwp, total;
+    size_t xc, gramt, dt, cs, ctot, gpn, hpn, dv, dbc, dbcs, rpart, tokp, dotgh, red4, red, dwp,
+        total;
 };
 inline BwdWs bwd_ws_layout(const Dims& d, int act) {
     BwdWs w;
@@ -274,22 +316,16 @@ inline BwdWs bwd_ws_layout(const Dims& d, int act) {
     const size_t bhl = (size_t)d.batch * d.H * d.L;
     size_t o = 0;
     w.xc = o;   o = align256(o + BL * d.C * e);
-    w.bct = o;  o = align256(o + (size_t)d.batch * d.nchunk * d.G * 2 * d.N * d.Q * e);
     // causal C_i . B_j tiles per (row, chunk, group), 256 elements each
     const size_t qt = (size_t)d.Q / 16;
     w.gramt = o; o = align256(o + (size_t)d.batch * d.nchunk * d.G * (qt * (qt + 1) / 2) * 256 * e);
     w.dt = o;   o = align256(o + bhl * 4);
     w.cs = o;   o = align256(o + bhl * 4);
     w.ctot = o; o = align256(o + (size_t)d.batch * d.H * d.nchunk * 4);
-    w.zh = o;   o = align256(o + st * 4);  // chunk contributions to the state, FP32
-    w.zg = o;   o = align256(o + st * 4);  // chunk contributions to the state gradient, FP32
     w.gpn = o;  o = align256(o + st * e);  // exit gradient per chunk, [p][n]
-    w.gnp = o;  o = align256(o + st * e);  // the same, [n][p]
-    w.hnp = o;  o = align256(o + st * e);  // entering state per chunk, [n][p]
-    w.hpn = o;  o = align256(o + st * e);  // the same, [p][n]
-    w.dyT = o;  o = align256(o + bhl * d.P * e);  // dy per chunk and head, [p][token]
+    w.hpn = o;  o = align256(o + st * e);  // entering state per chunk, [p][n]
     w.dv = o;   o = align256(o + BL * d.H * d.P * e);  // d(conv output), x channels
-    w.dbc = o;  o = align256(o + BL * d.H * 2 * d.N * e);  // dB, dC per head or head block
+    w.dbc = o;  o = align256(o + BL * (d.H / head_block(d)) * 2 * d.N * e);  // dB, dC per head block
     w.dbcs = o; o = align256(o + BL * d.G * 2 * d.N * e);  // the same, summed per group
     w.rpart = o; o = align256(o + bhl * 4);
     w.tokp = o; o = align256(o + bhl * 4 * 4);

@@ -338,42 +338,33 @@ inline int walk_heads(const Dims& d) {
 }
 
 template <typename T, int P, int N, bool BWD>
-inline void launch_state_walk(const Dims& d, const SegTab& t, const WalkArgs<T>& wa,
-                              hipStream_t s) {
+inline hipError_t launch_state_walk(const Dims& d, const SegTab& t, const WalkArgs<T>& wa,
+                                    hipStream_t s) {
     const int hw = walk_heads<T>(d);
     const dim3 grid((unsigned)((int64_t)(d.H / hw) * d.nseg * d.batch));
     const dim3 block(256 * hw);
     if (hw == 2) {
-        if (wa.seq)
-            hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, true, 2>), grid, block, 0, s, d, t, wa);
-        else
-            hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, false, 2>), grid, block, 0, s, d, t, wa);
-    } else {
-        if (wa.seq)
-            hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, true, 1>), grid, block, 0, s, d, t, wa);
-        else
-            hipLaunchKernelGGL((k_state_walk<T, P, N, BWD, false, 1>), grid, block, 0, s, d, t, wa);
+        if (wa.seq) return launch(k_state_walk<T, P, N, BWD, true, 2>, grid, block, s, d, t, wa);
+        return launch(k_state_walk<T, P, N, BWD, false, 2>, grid, block, s, d, t, wa);
     }
+    if (wa.seq) return launch(k_state_walk<T, P, N, BWD, true, 1>, grid, block, s, d, t, wa);
+    return launch(k_state_walk<T, P, N, BWD, false, 1>, grid, block, s, d, t, wa);
 }
 
 // The reverse and the forward walk of the backward pass in one launch.
 template <typename T, int P, int N>
-inline void launch_state_walk_pair(const Dims& d, const SegTab& t, const WalkArgs<T>& bwd,
-                                   const WalkArgs<T>& fwd, hipStream_t s) {
+inline hipError_t launch_state_walk_pair(const Dims& d, const SegTab& t, const WalkArgs<T>& bwd,
+                                         const WalkArgs<T>& fwd, hipStream_t s) {
     const int hw = walk_heads<T>(d);
     const dim3 grid((unsigned)(2 * (int64_t)(d.H / hw) * d.nseg * d.batch));
     const dim3 block(256 * hw);
     if (hw == 2) {
         if (bwd.seq)
-            hipLaunchKernelGGL((k_state_walk_pair<T, P, N, true, 2>), grid, block, 0, s, d, t, bwd, fwd);
-        else
-            hipLaunchKernelGGL((k_state_walk_pair<T, P, N, false, 2>), grid, block, 0, s, d, t, bwd, fwd);
-    } else {
-        if (bwd.seq)
-            hipLaunchKernelGGL((k_state_walk_pair<T, P, N, true, 1>), grid, block, 0, s, d, t, bwd, fwd);
-        else
-            hipLaunchKernelGGL((k_state_walk_pair<T, P, N, false, 1>), grid, block, 0, s, d, t, bwd, fwd);
+            return launch(k_state_walk_pair<T, P, N, true, 2>, grid, block, s, d, t, bwd, fwd);
+        return launch(k_state_walk_pair<T, P, N, false, 2>, grid, block, s, d, t, bwd, fwd);
     }
+    if (bwd.seq) return launch(k_state_walk_pair<T, P, N, true, 1>, grid, block, s, d, t, bwd, fwd);
+    return launch(k_state_walk_pair<T, P, N, false, 1>, grid, block, s, d, t, bwd, fwd);
 }
 
 }  // namespace ssd

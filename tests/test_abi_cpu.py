@@ -142,3 +142,75 @@ def test_binding_rejects_wrong_sizes_before_the_library():
     x = torch.zeros(10)
     with pytest.raises(ValueError):
         ssd.ssd_conv1d_fwd(p, [(0, 256)], x, x, None, x)
+
+
+# Every (activation, headdim, dstate, chunk) the library accepts, forward and
+# backward.  tests/test_gpu_shapes.py runs each accepted combination on the GPU
+# against the oracle, so a shape cannot be accepted without being exercised.
+FWD_SHAPES = {(a, p, n, q) for a, p, n in [("f32", 16, 16), ("f32", 32, 32), ("f32", 64, 64),
+                                           ("f32", 64, 128), ("bf16", 32, 64), ("bf16", 64, 64),
+                                           ("bf16", 64, 128)]
+              for q in (64, 128, 256)}
+BWD_SHAPES = {s for s in FWD_SHAPES if s[0] == "bf16" or s[3] != 256}
+
+
+def accepted_shapes():
+    """(forward set, backward set) of the combinations ssd_workspace_bytes accepts, over a
+    grid wider than the compiled one."""
+    fwd, bwd = set(), set()
+    for act in ("f32", "bf16"):
+        for P in (8, 16, 32, 48, 64, 128, 256):
+            for N in (8, 16, 32, 64, 96, 128, 256):
+                for Q in (32, 64, 128, 256, 512):
+                    p = _p(batch=1, seqlen=2 * 512, nheads=2, headdim=P, dstate=N, chunk=Q,
+                           act=act)
+                    segs = [(0, 1024)]
+                    if ssd.ssd_workspace_bytes(p, segs, ssd.SSD_WS_FORWARD):
+                        fwd.add((act, P, N, Q))
+                    if ssd.ssd_workspace_bytes(p, segs, ssd.SSD_WS_BACKWARD):
+                        bwd.add((act, P, N, Q))
+    return fwd, bwd
+
+
+def test_support_table_is_the_tested_one():
+    fwd, bwd = accepted_shapes()
+    assert fwd == FWD_SHAPES
+    assert bwd == BWD_SHAPES
+    lib = _lib.load()
+    for act, P, N, Q in FWD_SHAPES:
+        assert lib.ssd_supported(P, N, 0 if act == "f32" else 1) == 1
+    assert lib.ssd_supported(128, 128, 1) == 0
+
+
+def test_backward_refuses_unsupported_shape_before_launching():
+    p = _p(batch=1, seqlen=1024, nheads=2, headdim=64, dstate=128, chunk=256, act="f32")
+    s = ssd.Segments([(0, 1024)])
+    lib = _lib.load()
+    rc = lib.ssd_segment_bwd_summary(ctypes.byref(p), s.ptr(), s.n, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     None, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert rc == -3
+
+
+def test_over_long_row_is_refused_before_launching():
+    """A row of 2^23 tokens needs 2^17 conv workgroups along the grid's y dimension
+    (beyond 65535): validation refuses it, for the conv alone and for the multi-kernel
+    backward summary, before anything is launched (no GPU here, so a launch would fail
+    with SSD_ERR_HIP instead)."""
+    L = 1 << 23
+    p = _p(batch=1, seqlen=L, nheads=2, headdim=64, dstate=128, chunk=256)
+    segs = [(0, L)]
+    assert _conv(p, segs) == -2
+    assert ssd.ssd_workspace_bytes(p, segs, ssd.SSD_WS_BACKWARD) == 0
+    s = ssd.Segments(segs)
+    rc = _lib.load().ssd_segment_bwd_summary(ctypes.byref(p), s.ptr(), s.n, FAKE, FAKE, FAKE, FAKE,
+                                             FAKE, None, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert rc == -2
+    # the longest row the conv grid takes is accepted by validation
+    ok = _p(batch=1, seqlen=65535 * 64 // 256 * 256, nheads=2, headdim=64, dstate=128, chunk=256)
+    assert ssd.ssd_workspace_bytes(ok, [(0, ok.seqlen)], ssd.SSD_WS_FORWARD) > 0
+
+
+def test_grid_overflow_is_refused():
+    """batch x heads x P x N beyond 2^32 work-items of the boundary scan's grid."""
+    p = _p(batch=4096, seqlen=256, nheads=4096, headdim=64, dstate=128, chunk=256)
+    assert _conv(p, [(0, 256)]) == -2

@@ -186,25 +186,29 @@ def test_maximum_segment_count():
 
 
 @pytest.mark.parametrize("cfg", ["long_context_bf16", "long_context_virtual_bf16"])
-def test_backward_long_context_sampled_heads(cfg):
-    """131072 tokens, 64 heads in 8 groups: the full backward on the GPU; the gradients
-    that belong to heads 0, 7, 57 and 63 alone (their x channels' dxBC and dconv_w,
-    ddt_raw, ddt_bias, dA_log, dD) against the oracle restricted to those heads."""
+def test_backward_long_context_whole_groups(cfg):
+    """131072 tokens, 64 heads in 8 groups: the full backward on the GPU; every gradient
+    of the first and the last group (heads 0-7 and 56-63: their x channels and the
+    groups' B and C channels in dxBC and dconv_w, ddt_raw, ddt_bias, dA_log, dD)
+    against the oracle restricted to that group."""
     wl = W.make_workload(cfg.replace("_bf16", "_bwd_bf16"), **W.WORKLOADS[cfg], with_dy=True)
-    log(f"[backward] {wl.name} sampled heads")
+    log(f"[backward] {wl.name} whole groups")
     _, _, _, bb = run_fwd_bwd(wl)
-    heads = [0, 7, 57, 63]
-    P = wl.headdim
-    ch = torch.cat([torch.arange(h * P, (h + 1) * P) for h in heads]).to(bb.dxBC.device)
-    hs = torch.tensor(heads, device=bb.dxBC.device)
-    got = dict(dxBC=wl.to_causal(to_np(bb.dxBC.index_select(2, ch))),
-               dconv_w=to_np(bb.dconv_w.index_select(0, ch)),
-               ddt_raw=wl.to_causal(to_np(bb.ddt_raw.index_select(2, hs))),
-               ddt_bias=to_np(bb.ddt_bias)[heads], dA_log=to_np(bb.dA_log)[heads],
-               dD=to_np(bb.dD)[heads])
-    ref = oracle.backward(wl, heads=heads)
-    for name in GRADS:
-        assert_close(got[name], ref[name], wl.act, f"{cfg} {name} heads {heads}")
+    hpg = wl.nheads // wl.ngroups
+    for g in (0, wl.ngroups - 1):
+        heads = list(range(g * hpg, (g + 1) * hpg))
+        ref = oracle.backward(wl, heads=heads)
+        ch = torch.from_numpy(ref["channels"]).to(bb.dxBC.device)
+        hs = torch.tensor(heads, device=bb.dxBC.device)
+        got = dict(dxBC=wl.to_causal(to_np(bb.dxBC.index_select(2, ch))),
+                   dconv_w=to_np(bb.dconv_w.index_select(0, ch)),
+                   ddt_raw=wl.to_causal(to_np(bb.ddt_raw.index_select(2, hs))),
+                   ddt_bias=to_np(bb.ddt_bias)[heads], dA_log=to_np(bb.dA_log)[heads],
+                   dD=to_np(bb.dD)[heads])
+        assert ref["dxBC"].shape[2] == hpg * wl.headdim + 2 * wl.dstate
+        for name in GRADS:
+            assert_close(got[name], ref[name], wl.act, f"{cfg} {name} group {g}")
+        del ref
 
 
 def test_tiny_gradients_against_finite_differences():

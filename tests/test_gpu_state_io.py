@@ -138,7 +138,8 @@ def test_final_state_gradient_finite_differences():
 def test_graph_replay_is_bitwise():
     """Forward (with initial and final state) and backward captured in one HIP graph;
     every replay, with eager work and synchronisation between replays, gives outputs
-    bit-identical to the eager run."""
+    bit-identical to the eager run, and after new values are written into the
+    captured input buffers the replay's outputs follow them."""
     import mamba2_ssd_chunked_amd as ssd
     wl = _bwd_small("bf16_thd")
     log(f"[state io] graph replay {wl.name}")
@@ -185,3 +186,16 @@ def test_graph_replay_is_bitwise():
             assert torch.equal(a, b), (rep, i)
         run(fe, be)  # eager work between replays
         torch.cuda.synchronize()
+    # new values in the captured input buffers: the replay reads them (its outputs
+    # follow the eager run on the new inputs and differ from the old ones)
+    with torch.no_grad():
+        x["xBC"].mul_(-0.75).add_(0.125)
+        x["dy"].mul_(1.5)
+    run(fe, be)
+    torch.cuda.synchronize()
+    fresh = [t.clone() for t in outputs(fe, be)]
+    graph.replay()
+    torch.cuda.synchronize()
+    for i, (a, b, c) in enumerate(zip(outputs(fg, bg), fresh, eager)):
+        assert torch.equal(a, b), ("new inputs", i)
+        assert not torch.equal(a, c), ("unchanged after new inputs", i)
