@@ -75,7 +75,8 @@ typedef enum {
     SSD_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned           */
     SSD_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required        */
     SSD_ERR_HIP = -6,         /* the HIP runtime reported an error at launch       */
-    SSD_ERR_SEGMENTS = -7     /* the segment table does not tile the sequence      */
+    SSD_ERR_SEGMENTS = -7,    /* the segment table does not tile the sequence      */
+    SSD_ERR_SCRATCH = -8      /* the problem needs more than the fixed scratch     */
 } ssd_status;
 
 typedef struct {
@@ -152,6 +153,26 @@ int ssd_segment_fwd(const ssd_problem* problem, const ssd_segment* segs, int32_t
                     const void* xBC_conv, const void* dt_raw, const float* dt_bias,
                     const float* A_log, const int32_t* seq_idx, float* y_zero, float* summary,
                     void* ws, size_t ws_bytes, void* stream);
+
+/* ssd_segment_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same outputs from the same kernels, with the workspace in a fixed device
+ * array of the library (SSD_SCRATCH_BYTES = 64 MiB per GPU, held until the
+ * process ends) instead of a `ws` argument.  The call allocates nothing.
+ * Problems whose forward workspace (ssd_workspace_bytes(..., SSD_WS_FORWARD))
+ * exceeds SSD_SCRATCH_BYTES return SSD_ERR_SCRATCH before anything is enqueued.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a GPU
+ * (on different streams, or from different threads) race and give wrong
+ * results.  The scratch keeps the last call's contents; nothing in it needs
+ * clearing, since each call reads only what it wrote.  The workspace stays
+ * internal, so ssd_apply_init_state cannot follow this call (the fused output
+ * path or ssd_segment_fwd serve callers that need the corrected y).
+ * Arguments as for ssd_segment_fwd, without ws and ws_bytes. */
+#define SSD_SCRATCH_BYTES (64u << 20)
+int ssd_segment_fwd_noalloc(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                            const void* xBC_conv, const void* dt_raw, const float* dt_bias,
+                            const float* A_log, const int32_t* seq_idx, float* y_zero,
+                            float* summary, void* stream);
 
 /* The two phases of ssd_segment_fwd, for callers that overlap the summary
  * exchange with the local intra-chunk work (#6808's first commit issues the

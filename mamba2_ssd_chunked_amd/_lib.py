@@ -18,6 +18,7 @@ SSD_BF16 = 1
 SSD_WS_FORWARD = 0
 SSD_WS_BACKWARD = 1
 SSD_MAX_SEGMENTS = 64
+SSD_SCRATCH_BYTES = 64 << 20
 
 
 class Problem(ctypes.Structure):
@@ -67,6 +68,8 @@ SIGNATURES = {
                                             ctypes.c_size_t, _vp, _vp]),
     "ssd_segment_output_fused": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, _vp, _vp,
                                                 ctypes.c_size_t, _vp, _vp]),
+    "ssd_segment_fwd_noalloc": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                               _vp]),
 }
 
 _lib = None

@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["ssd_api.cpp", "conv1d.hip", "ssd_fwd.hip", "scan.hip", "ssd_bwd.hip"]
+SOURCES = ["ssd_api.cpp", "conv1d.hip", "ssd_fwd.hip", "scan.hip", "ssd_bwd.hip", "noalloc.hip"]
 PROBE_SOURCES = ["peak_probes.hip"]
 # The probes' MFMA loops keep their accumulators in ordinary VGPRs, updated in
 # place: with accumulation registers the allocator copies every chain's

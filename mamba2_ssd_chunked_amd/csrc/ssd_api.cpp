@@ -129,6 +129,7 @@ const char* ssd_status_string(int status) {
         case SSD_ERR_WORKSPACE: return "workspace missing or too small";
         case SSD_ERR_HIP: return "HIP launch error";
         case SSD_ERR_SEGMENTS: return "segment table does not tile the sequence in chunk units";
+        case SSD_ERR_SCRATCH: return "problem needs more workspace than the fixed 64 MiB device scratch";
         default: return "unknown status";
     }
 }
@@ -237,6 +238,31 @@ int ssd_segment_fwd(const ssd_problem* problem, const ssd_segment* segs, int32_t
     if ((rc = check_output_args(problem, segs, nseg, xBC_conv, seq_idx, ws, ws_bytes, y_zero, &d,
                                 &t)))
         return rc;
+    rc = hip_status(launch_segment_states(d, t, problem->act_dtype, xBC_conv, dt_raw, dt_bias,
+                                          A_log, seq_idx, summary, ws, (hipStream_t)stream));
+    if (rc) return rc;
+    return hip_status(launch_segment_output(d, t, problem->act_dtype, xBC_conv, seq_idx, ws, y_zero,
+                                            (hipStream_t)stream));
+}
+
+int ssd_segment_fwd_noalloc(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                            const void* xBC_conv, const void* dt_raw, const float* dt_bias,
+                            const float* A_log, const int32_t* seq_idx, float* y_zero,
+                            float* summary, void* stream) {
+    Dims d;
+    SegTab t;
+    int rc = check_problem(problem, &d);
+    if (rc) return rc;
+    if ((rc = check_segments(segs, nseg, &d, &t))) return rc;
+    if (!xBC_conv || !dt_raw || !dt_bias || !A_log || !summary || !y_zero) return SSD_ERR_NULL;
+    if (!aligned16(xBC_conv) || !aligned16(dt_raw) || !aligned16(dt_bias) || !aligned16(A_log) ||
+        !aligned16(seq_idx) || !aligned16(summary) || !aligned16(y_zero))
+        return SSD_ERR_ALIGN;
+    if (fwd_ws_layout(d, problem->act_dtype).total > SCRATCH_BYTES) return SSD_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return SSD_ERR_HIP;
+    // every byte of the workspace the two phases read is written earlier in the
+    // same call, so the scratch needs no clearing
     rc = hip_status(launch_segment_states(d, t, problem->act_dtype, xBC_conv, dt_raw, dt_bias,
                                           A_log, seq_idx, summary, ws, (hipStream_t)stream));
     if (rc) return rc;

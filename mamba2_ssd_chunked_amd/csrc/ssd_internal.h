@@ -228,6 +228,11 @@ template <> struct Mma<float> {
 #define SSD_F32_SHAPES(X) X(16, 16) X(32, 32) X(64, 64) X(64, 128)
 #define SSD_BF16_SHAPES(X) X(32, 64) X(64, 64) X(64, 128)
 
+// Size of the fixed device scratch of ssd_segment_fwd_noalloc (noalloc.hip),
+// and its device address on the current device (taken once per device).
+constexpr size_t SCRATCH_BYTES = SSD_SCRATCH_BYTES;
+hipError_t scratch_address(void** out);
+
 // Host-side launchers (defined in the .hip files).  Each returns hipSuccess or
 // the launch error.
 hipError_t launch_conv1d_fwd(const Dims& d, const SegTab& t, int act, const void* xBC,

@@ -126,6 +126,23 @@ def ssd_segment_fwd(problem: Problem, segs, xBC_conv, dt_raw, dt_bias, A_log, se
         _stream(stream)))
 
 
+def ssd_segment_fwd_noalloc(problem: Problem, segs, xBC_conv, dt_raw, dt_bias, A_log, seq_idx,
+                            y_zero, summary, stream=None):
+    """ssd_segment_fwd with the workspace in the library's fixed device scratch
+    (nothing is allocated; overlapping calls on one GPU race)."""
+    s = _segs(segs)
+    act = _TORCH_ACT[problem.act_dtype]
+    BL, C, H = problem.batch * problem.seqlen, _conv_dim(problem), problem.nheads
+    f32 = torch.float32
+    args = (_need(xBC_conv, "xBC_conv", BL * C, act), _need(dt_raw, "dt_raw", BL * H, act),
+            _need(dt_bias, "dt_bias", H, f32), _need(A_log, "A_log", H, f32),
+            _need(seq_idx, "seq_idx", BL, torch.int32, optional=True),
+            _need(y_zero, "y_zero", BL * H * problem.headdim, f32),
+            _need(summary, "summary", summary_numel(problem, s.n), f32))
+    _check("ssd_segment_fwd_noalloc", _lib.load().ssd_segment_fwd_noalloc(
+        ctypes.byref(problem), s.ptr(), s.n, *args, _stream(stream)))
+
+
 def ssd_segment_states(problem: Problem, segs, xBC_conv, dt_raw, dt_bias, A_log, seq_idx,
                        summary, ws, stream=None):
     s = _segs(segs)

@@ -128,7 +128,7 @@ def test_boundary_scan_validation():
 
 def test_status_strings_and_support():
     lib = _lib.load()
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert lib.ssd_status_string(code)
     assert lib.ssd_supported(64, 128, 1) == 1
     assert lib.ssd_supported(16, 16, 0) == 1
