@@ -39,6 +39,7 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 F32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 MFMA, published
 
 METRIC = "SSD fwd(+bwd) tokens/s on 1 MI355X; % of MFMA peak and HBM GB/s"
+DEFAULT_WORKLOAD = "mixer_shard_bwd_bf16"
 
 
 def parse():
@@ -46,12 +47,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixer_shard_bwd_bf16",
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="a name from ssd_workloads.WORKLOADS (default: the mixer shard with dy, "
                          "forward+backward)")
     ap.add_argument("--pass", dest="which", default=None, choices=["fwd", "fwd+bwd"],
                     help="default: fwd+bwd when the workload has dy, else fwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="time only the chosen workload (by default the headline run also times "
+                         "the forward of every other configuration)")
     ap.add_argument("--cpu-runs", type=int, default=8)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one device-to-device copy of this many MB before timing, so that "
@@ -344,51 +348,68 @@ def chunk_bwd_flops(wl):
     return b * (L // Q) * (H * per_head + H // head_block(wl) * per_block)
 
 
-def cpu_baseline(wl, runs, backward):
+def path_floor_bytes(wl):
+    """Method floors of the whole path (bytes), each pass counting its own inputs and
+    outputs once:
+      survey_fwd: conv, segment-local SSD with an FP32 y_zero and the summary, boundary
+                  scan, correction pass (the passes of the unfused order);
+      f1_fwd    : the states-first order (conv, states and summary, scan, one output pass
+                  writing y): no y_zero;
+      bwd       : the backward's summary phase and segment phase each reading xBC, dt_raw
+                  and dy once, the summaries and scanned states of both scans, dxBC and
+                  ddt written once (chunk states kept on chip)."""
+    e = 2 if wl.act == "bf16" else 4
+    b, L, H, P, N, G = wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.ngroups
+    S = len(wl.segments)
+    BL, C = b * L, H * P + 2 * G * N
+    summ = S * b * H * (P * N + 1) * 4
+    st = S * b * H * P * N * 4
+    conv = 2 * BL * C * e
+    scan = summ + st
+    survey = (conv + (BL * C * e + BL * H * e + BL * H * P * 4 + summ) + scan
+              + (BL * H * P * 4 + BL * (H * P + G * N) * e + st + BL * H * P * e + BL * H * 4))
+    f1 = (conv + (BL * (H * P + G * N) * e + BL * H * e + summ) + scan
+          + (BL * (H * P + G * N) * e + st + BL * H * e + BL * H * P * e))
+    bwd = (2 * BL * C * e + 2 * BL * H * e + 2 * BL * H * P * e + 2 * summ + 2 * st
+           + BL * C * e + BL * H * e)
+    return {"survey_fwd": survey, "f1_fwd": f1, "bwd": bwd}
+
+
+def cpu_baseline(wl, runs, backward, heads=None):
+    """The oracle timed on this host.  `heads` restricts it to a sample of heads (the
+    value is then scaled to all heads: the oracle's work is per head)."""
     import oracle
     threads = oracle.num_threads()
     times = []
     for _ in range(runs):
         t = time.perf_counter()
         if backward:
-            oracle.backward(wl)  # runs the forward too
+            oracle.backward(wl, heads=heads)  # runs the forward too
         else:
-            oracle.forward(wl)
+            oracle.forward(wl, heads=heads)
         times.append(time.perf_counter() - t)
     med = statistics.median(times)
     what = "forward + backward (adjoint)" if backward else "forward"
-    return {"value": wl.tokens / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole workload ({wl.tokens} tokens, all heads), float64 token-by-token "
-                      f"recurrence, {what}, median of {runs} runs ({med:.2f} s each)"}
+    frac = 1.0 if heads is None else len(heads) / wl.nheads
+    sample = (f"the whole workload ({wl.tokens} tokens, all heads)" if heads is None else
+              f"heads {heads[0]}-{heads[-1]} of {wl.nheads} over all {wl.tokens} tokens, "
+              f"scaled to all heads")
+    return {"value": round(wl.tokens * frac / med, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{sample}, float64 token-by-token recurrence, {what}, median of {runs} "
+                      f"runs ({med:.2f} s each)"}
 
 
-def main():
-    args = parse()
-    if args.summarize_mfma:
-        print(json.dumps(summarize_mfma(args.summarize_mfma), indent=1))
-        return
-    if args.summarize_traffic:
-        if not args.copy_probe_mb:
-            raise SystemExit("--summarize-traffic needs the --copy-probe-mb of the profiled run")
-        print(json.dumps(summarize_traffic(*args.summarize_traffic, args.copy_probe_mb), indent=1))
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
-
+def run_workload(wl, which, steps, warmup, dev, copy_probe_mb=0):
+    """Times one workload: a breakdown pass with events around every call, then
+    `steps` whole steps with events around the dominant single-kernel call only.
+    Returns the measurements (no JSON formatting)."""
     import numpy as np
     import torch
 
     import mamba2_ssd_chunked_amd as ssd
-    import ssd_workloads as W
 
-    wl = W.config(args.workload)
-    which = args.which or ("fwd+bwd" if wl.dy is not None else "fwd")
-    if which == "fwd+bwd" and wl.dy is None:
-        raise SystemExit("this workload has no dy; use --pass fwd")
     do_bwd = which == "fwd+bwd"
-    dev = torch.device("cuda:0")
     act = torch.bfloat16 if wl.act == "bf16" else torch.float32
     f32 = torch.float32
     t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
@@ -428,8 +449,7 @@ def main():
                 p, segs, xBC, conv_w, dt_raw, dt_bias, A_log, seq, bb.ws, bb.dxBC, bb.ddt_raw,
                 bb.dconv_w, bb.ddt_bias, bb.dA_log, bb.dD)),
         ]
-    single_kernel = {"ssd_conv1d_fwd", "ssd_segment_output_fused", "ssd_boundary_scan",
-                     "ssd_boundary_scan(reverse)", "ssd_segment_bwd_chunks"}
+    single_kernel = set(CALL_KERNEL)
 
     def step(events=None, only=None):
         """One pass of every call; with `events`, record [start, end] around each call
@@ -444,10 +464,10 @@ def main():
 
     def new_events(n):
         return [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
-                for _ in range(args.steps)]
+                for _ in range(steps)]
 
-    if args.copy_probe_mb:
-        nb = args.copy_probe_mb * (1 << 20)
+    if copy_probe_mb:
+        nb = copy_probe_mb * (1 << 20)
         src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
@@ -458,58 +478,114 @@ def main():
     # the collector off until the timing is done.
     gc.collect()
     gc.disable()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    try:
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
 
-    # Breakdown pass (not the timed region): events around every call give the
-    # per-call times.  Each event record adds a few microseconds between calls,
-    # so the step is timed separately below with events around one call only.
-    ev = new_events(len(calls))
-    for k in range(args.steps):
-        step(ev[k])
-    torch.cuda.synchronize()
-    abytes = algorithmic_bytes(wl)
-    per_call = {}
-    for i, (name, _) in enumerate(calls):
-        each = [ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]
-        ms = statistics.mean(each)
-        per_call[name] = {"ms": round(ms, 5), "max_ms": round(max(each), 5),
-                          "algorithmic_MB": round(abytes[name] / 1e6, 2),
-                          "GB_per_s": round(abytes[name] / (ms * 1e-3) / 1e9, 1)}
-    dom = max((n for n in single_kernel if n in per_call), key=lambda n: per_call[n]["ms"])
-    dom_i = [name for name, _ in calls].index(dom)
+        # Breakdown pass (not the timed region): events around every call give the
+        # per-call times.  Each event record adds a few microseconds between calls,
+        # so the step is timed separately below with events around one call only.
+        ev = new_events(len(calls))
+        for k in range(steps):
+            step(ev[k])
+        torch.cuda.synchronize()
+        abytes = algorithmic_bytes(wl)
+        per_call = {}
+        for i, (name, _) in enumerate(calls):
+            each = [ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(steps)]
+            ms = statistics.mean(each)
+            per_call[name] = {"ms": round(ms, 5), "max_ms": round(max(each), 5),
+                              "algorithmic_MB": round(abytes[name] / 1e6, 2),
+                              "GB_per_s": round(abytes[name] / (ms * 1e-3) / 1e9, 1)}
+        dom = max((n for n in single_kernel if n in per_call), key=lambda n: per_call[n]["ms"])
+        dom_i = [name for name, _ in calls].index(dom)
 
-    # Timed region: K whole steps, with HIP events on the launch stream around the
-    # dominant kernel's call only (its duration for the roofline line).
-    evd = new_events(1)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    for k in range(args.steps):
-        step(evd[k], only=dom_i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    gc.enable()
-    peaks = None if args.no_peaks else measure_peaks(torch, dev, stream)
-    ms_total = t0.elapsed_time(t1)
-    ms_step = ms_total / args.steps
-    dom_ms = statistics.mean(evd[k][0][0].elapsed_time(evd[k][0][1]) for k in range(args.steps))
-    achieved = round(abytes[dom] / (dom_ms * 1e-3) / 1e9, 1)
+        # Timed region: K whole steps, with HIP events on the launch stream around the
+        # dominant kernel's call only (its duration for the roofline line).
+        evd = new_events(1)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t0.record(stream)
+        for k in range(steps):
+            step(evd[k], only=dom_i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+    finally:
+        gc.enable()
+    ms_step = t0.elapsed_time(t1) / steps
+    dom_ms = statistics.mean(evd[k][0][0].elapsed_time(evd[k][0][1]) for k in range(steps))
+    return {"ms_step": ms_step, "dom": dom, "dom_ms": dom_ms, "abytes": abytes,
+            "per_call": per_call, "wall": wall}
+
+
+def flops_entries(wl, m, do_bwd, peaks=None):
     mfma_peak = BF16_PEAK_TFLOPS if wl.act == "bf16" else F32_PEAK_TFLOPS
     mfma = {}
     for name, fl in [("ssd_segment_output_fused", output_flops(wl))] + \
             ([("ssd_segment_bwd_chunks", chunk_bwd_flops(wl))] if do_bwd else []):
-        ms = dom_ms if name == dom else per_call[name]["ms"]
+        ms = m["dom_ms"] if name == m["dom"] else m["per_call"][name]["ms"]
         tf = fl / (ms * 1e-3) / 1e12
         mfma[name] = {"achieved": round(tf, 2), "peak": mfma_peak, "unit": "TFLOP/s",
                       "frac": round(tf / mfma_peak, 4), "algorithmic_GFLOP": round(fl / 1e9, 2)}
         if peaks and wl.act == "bf16":
             mfma[name]["achievable_peak"] = peaks["bf16_mfma_TFLOPs"]
             mfma[name]["achievable_frac"] = round(tf / peaks["bf16_mfma_TFLOPs"], 4)
+    return mfma
+
+
+def path_entry(wl, ms_step, do_bwd):
+    """t_floor / t_measured of the whole path at the published HBM peak."""
+    fl = path_floor_bytes(wl)
+    out = {}
+    for key, fwd in (("survey", fl["survey_fwd"]), ("states_first", fl["f1_fwd"])):
+        total = fwd + (fl["bwd"] if do_bwd else 0)
+        t_floor = total / (HBM_PEAK_GBS * 1e9)
+        out[key] = {"floor_MB": round(total / 1e6, 1), "t_floor_ms": round(t_floor * 1e3, 5),
+                    "frac": round(t_floor / (ms_step * 1e-3), 4)}
+    return out
+
+
+# Configurations measured beside the headline (forward of each; the headline is the
+# forward + backward of the mixer shard), and the head sample their oracle baseline uses.
+EXTRA_CONFIGS = [("tiny_f32", None), ("mixer_shard_bf16", None), ("packed_thd_bf16", None),
+                 ("long_context_bf16", list(range(8))),
+                 ("long_context_virtual_bf16", list(range(8)))]
+
+
+def main():
+    args = parse()
+    if args.summarize_mfma:
+        print(json.dumps(summarize_mfma(args.summarize_mfma), indent=1))
+        return
+    if args.summarize_traffic:
+        if not args.copy_probe_mb:
+            raise SystemExit("--summarize-traffic needs the --copy-probe-mb of the profiled run")
+        print(json.dumps(summarize_traffic(*args.summarize_traffic, args.copy_probe_mb), indent=1))
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import ssd_workloads as W
+
+    wl = W.config(args.workload)
+    which = args.which or ("fwd+bwd" if wl.dy is not None else "fwd")
+    if which == "fwd+bwd" and wl.dy is None:
+        raise SystemExit("this workload has no dy; use --pass fwd")
+    do_bwd = which == "fwd+bwd"
+    dev = torch.device("cuda:0")
+    m = run_workload(wl, which, args.steps, args.warmup, dev, args.copy_probe_mb)
+    torch.cuda.empty_cache()
+    peaks = None if args.no_peaks else measure_peaks(torch, dev, torch.cuda.current_stream())
+    ms_step, dom, dom_ms, abytes = m["ms_step"], m["dom"], m["dom_ms"], m["abytes"]
+    achieved = round(abytes[dom] / (dom_ms * 1e-3) / 1e9, 1)
 
     result = {
         "metric": METRIC,
@@ -534,16 +610,47 @@ def main():
                      "traffic": measured_traffic(wl.name, CALL_KERNEL[dom]),
                      "kernel_ms": round(dom_ms, 5),
                      "algorithmic_MB": round(abytes[dom] / 1e6, 2)},
+        "path_roofline": path_entry(wl, ms_step, do_bwd),
         "achievable_peaks": peaks,
-        "mfma": mfma,
-        "calls": per_call,  # from the breakdown pass, events around every call
-        "wall_s_timed_region": round(wall, 4),
+        "mfma": flops_entries(wl, m, do_bwd, peaks),
+        "calls": m["per_call"],  # from the breakdown pass, events around every call
+        "wall_s_timed_region": round(m["wall"], 4),
     }
     if peaks:
         result["roofline"]["achievable_peak"] = peaks["hbm_GBps"]
         result["roofline"]["achievable_frac"] = round(achieved / peaks["hbm_GBps"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_runs, do_bwd)
+
+    # the other configurations, forward, one line each inside the same JSON object
+    if not args.no_extra_configs and args.workload == DEFAULT_WORKLOAD:
+        extra = {}
+        for name, heads in EXTRA_CONFIGS:
+            xw = W.config(name)
+            xm = run_workload(xw, "fwd", args.steps, args.warmup, dev)
+            torch.cuda.empty_cache()
+            xd = xm["dom"]
+            xa = xm["abytes"][xd] / (xm["dom_ms"] * 1e-3) / 1e9
+            e = {"value": round(xw.tokens / (xm["ms_step"] * 1e-3), 1), "unit": "tokens/s",
+                 "ms_per_step": round(xm["ms_step"], 5), "pass": "fwd", "dtype": xw.act,
+                 "config": {"batch": xw.batch, "seq_len": xw.seqlen, "nheads": xw.nheads,
+                            "headdim": xw.headdim, "dstate": xw.dstate, "ngroups": xw.ngroups,
+                            "chunk": xw.chunk, "segments": len(xw.segments),
+                            "layout": xw.layout, "packed": xw.seq_idx is not None},
+                 "roofline": {"bound": "hbm", "kernel": xd, "achieved": round(xa, 1),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(xa / HBM_PEAK_GBS, 4),
+                              "kernel_ms": round(xm["dom_ms"], 5),
+                              "algorithmic_MB": round(xm["abytes"][xd] / 1e6, 2)},
+                 "path_roofline": path_entry(xw, xm["ms_step"], False),
+                 "mfma": flops_entries(xw, xm, False),
+                 "calls": {k: v["ms"] for k, v in xm["per_call"].items()}}
+            if not args.no_cpu_baseline:
+                e["cpu_baseline"] = cpu_baseline(xw, 1, False, heads=heads)
+            extra[name] = e
+            del xw, xm
+            gc.collect()
+        result["configs"] = extra
     print(json.dumps(result), flush=True)
 
 
