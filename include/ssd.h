@@ -181,13 +181,16 @@ int ssd_segment_fwd_noalloc(const ssd_problem* problem, const ssd_segment* segs,
  * state, the segment summaries (into `summary` and `ws`) and the causal C B^T
  * Gram tiles of every chunk and group (into `ws`); ssd_segment_output then
  * computes y_zero from the same inputs and `ws`.  Calling both in this
- * order is the same as ssd_segment_fwd.  */
+ * order is the same as ssd_segment_fwd.  When the state walk splits long
+ * segments into spans (see ssd_workspace_bytes), ssd_segment_output also
+ * writes the states entering the spans into `ws`, so the output calls take a
+ * writable workspace.  */
 int ssd_segment_states(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
                        const void* xBC_conv, const void* dt_raw, const float* dt_bias,
                        const float* A_log, const int32_t* seq_idx, float* summary, void* ws,
                        size_t ws_bytes, void* stream);
 int ssd_segment_output(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
-                       const void* xBC_conv, const int32_t* seq_idx, const void* ws,
+                       const void* xBC_conv, const int32_t* seq_idx, void* ws,
                        size_t ws_bytes, float* y_zero, void* stream);
 
 /* Affine scan over segment summaries, in causal segment order (#6808's first
@@ -233,11 +236,12 @@ int ssd_apply_init_state(const ssd_problem* problem, const ssd_segment* segs, in
  *   xBC_conv, D, seq_idx   as for ssd_apply_init_state                         (in)
  *   S_in      [nseg][batch][H][P][N] float32 (ssd_boundary_scan output)         (in)
  *   ws        the workspace ssd_segment_states filled for the same problem,
- *             segments and inputs (read only)                                   (in)
+ *             segments and inputs; the states entering the spans of long
+ *             segments are written into it                                      (in/out)
  *   y         [batch][seqlen][H][P] act_dtype                                   (out) */
 int ssd_segment_output_fused(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
                              const void* xBC_conv, const float* D, const int32_t* seq_idx,
-                             const float* S_in, const void* ws, size_t ws_bytes, void* y,
+                             const float* S_in, void* ws, size_t ws_bytes, void* y,
                              void* stream);
 
 /* Backward, summary phase (Megatron-LM #6808, first commit: the backward

@@ -80,6 +80,7 @@ int check_problem(const ssd_problem* p, Dims* d) {
     d->hpg = p->nheads / p->ngroups;
     d->nchunk = (int)(p->seqlen / p->chunk);
     d->nseg = 0;
+    d->act = p->act_dtype;
     d->dt_min = p->dt_min;
     d->dt_max = p->dt_max;
     return SSD_OK;
@@ -146,7 +147,7 @@ size_t ssd_workspace_bytes(const ssd_problem* problem, const ssd_segment* segs, 
     SegTab t;
     if (check_problem(problem, &d) != SSD_OK) return 0;
     if (check_segments(segs, nseg, &d, &t) != SSD_OK) return 0;
-    if (kind == SSD_WS_FORWARD) return fwd_ws_layout(d, problem->act_dtype).total;
+    if (kind == SSD_WS_FORWARD) return fwd_ws_layout(d, t, problem->act_dtype).total;
     if (kind == SSD_WS_BACKWARD) {
         if (!bwd_supported(d.P, d.N, d.Q, problem->act_dtype)) return 0;
         return bwd_ws_layout(d, problem->act_dtype).total;
@@ -179,7 +180,7 @@ int check_states_args(const ssd_problem* problem, const ssd_segment* segs, int32
     if ((rc = check_segments(segs, nseg, d, t))) return rc;
     if (!xBC_conv || !dt_raw || !dt_bias || !A_log || !summary) return SSD_ERR_NULL;
     if (!ws) return SSD_ERR_WORKSPACE;
-    if (ws_bytes < fwd_ws_layout(*d, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
+    if (ws_bytes < fwd_ws_layout(*d, *t, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
     if (!aligned16(xBC_conv) || !aligned16(dt_raw) || !aligned16(dt_bias) || !aligned16(A_log) ||
         !aligned16(seq_idx) || !aligned16(summary) || !aligned16(ws))
         return SSD_ERR_ALIGN;
@@ -194,7 +195,7 @@ int check_output_args(const ssd_problem* problem, const ssd_segment* segs, int32
     if ((rc = check_segments(segs, nseg, d, t))) return rc;
     if (!xBC_conv || !y_zero) return SSD_ERR_NULL;
     if (!ws) return SSD_ERR_WORKSPACE;
-    if (ws_bytes < fwd_ws_layout(*d, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
+    if (ws_bytes < fwd_ws_layout(*d, *t, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
     if (!aligned16(xBC_conv) || !aligned16(seq_idx) || !aligned16(ws) || !aligned16(y_zero))
         return SSD_ERR_ALIGN;
     return SSD_OK;
@@ -215,7 +216,7 @@ int ssd_segment_states(const ssd_problem* problem, const ssd_segment* segs, int3
 }
 
 int ssd_segment_output(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
-                       const void* xBC_conv, const int32_t* seq_idx, const void* ws,
+                       const void* xBC_conv, const int32_t* seq_idx, void* ws,
                        size_t ws_bytes, float* y_zero, void* stream) {
     Dims d;
     SegTab t;
@@ -258,7 +259,7 @@ int ssd_segment_fwd_noalloc(const ssd_problem* problem, const ssd_segment* segs,
     if (!aligned16(xBC_conv) || !aligned16(dt_raw) || !aligned16(dt_bias) || !aligned16(A_log) ||
         !aligned16(seq_idx) || !aligned16(summary) || !aligned16(y_zero))
         return SSD_ERR_ALIGN;
-    if (fwd_ws_layout(d, problem->act_dtype).total > SCRATCH_BYTES) return SSD_ERR_SCRATCH;
+    if (fwd_ws_layout(d, t, problem->act_dtype).total > SCRATCH_BYTES) return SSD_ERR_SCRATCH;
     void* ws = nullptr;
     if (scratch_address(&ws) != hipSuccess) return SSD_ERR_HIP;
     // every byte of the workspace the two phases read is written earlier in the
@@ -296,7 +297,7 @@ int ssd_apply_init_state(const ssd_problem* problem, const ssd_segment* segs, in
     if ((rc = check_segments(segs, nseg, &d, &t))) return rc;
     if (!y_zero || !xBC_conv || !D || !S_in || !y) return SSD_ERR_NULL;
     if (!ws) return SSD_ERR_WORKSPACE;
-    if (ws_bytes < fwd_ws_layout(d, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
+    if (ws_bytes < fwd_ws_layout(d, t, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
     if (!aligned16(y_zero) || !aligned16(xBC_conv) || !aligned16(D) || !aligned16(seq_idx) ||
         !aligned16(S_in) || !aligned16(ws) || !aligned16(y))
         return SSD_ERR_ALIGN;
@@ -306,7 +307,7 @@ int ssd_apply_init_state(const ssd_problem* problem, const ssd_segment* segs, in
 
 int ssd_segment_output_fused(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
                              const void* xBC_conv, const float* D, const int32_t* seq_idx,
-                             const float* S_in, const void* ws, size_t ws_bytes, void* y,
+                             const float* S_in, void* ws, size_t ws_bytes, void* y,
                              void* stream) {
     Dims d;
     SegTab t;
@@ -315,7 +316,7 @@ int ssd_segment_output_fused(const ssd_problem* problem, const ssd_segment* segs
     if ((rc = check_segments(segs, nseg, &d, &t))) return rc;
     if (!xBC_conv || !D || !S_in || !y) return SSD_ERR_NULL;
     if (!ws) return SSD_ERR_WORKSPACE;
-    if (ws_bytes < fwd_ws_layout(d, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
+    if (ws_bytes < fwd_ws_layout(d, t, problem->act_dtype).total) return SSD_ERR_WORKSPACE;
     if (!aligned16(xBC_conv) || !aligned16(D) || !aligned16(seq_idx) || !aligned16(S_in) ||
         !aligned16(ws) || !aligned16(y))
         return SSD_ERR_ALIGN;

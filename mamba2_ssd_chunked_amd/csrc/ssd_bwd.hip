@@ -560,7 +560,8 @@ static hipError_t bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a
     // the reverse walk from a zero final gradient: dL/dS_in of each segment's own
     // outputs and its block decay
     const WalkArgs<T> wa = {(const T*)xc, (const T*)a.dy, (const float*)(ws + L.dt),
-                            (const float*)(ws + L.cs), a.seq, nullptr, nullptr, summary};
+                            (const float*)(ws + L.cs), a.seq, nullptr, nullptr, summary,
+                            span_plan(d, t, false)};
     return launch_state_walk<T, P, N, true>(d, t, wa, s);
 }
 
@@ -571,12 +572,13 @@ static hipError_t bwd_pass_t(const Dims& d, const SegTab& t, const BwdArgs& a, v
     char* ws = (char*)ws_;
     // G of every chunk: the reverse walk from dS_out; H of every chunk: the forward
     // walk from S_in; both in one launch (<G_c, H_c> comes from the chunk kernel)
+    const SpanPlan one = span_plan(d, t, false);  // one span per segment
     const WalkArgs<T> bwd = {(const T*)(ws + L.xc), (const T*)a.dy, (const float*)(ws + L.dt),
                              (const float*)(ws + L.cs), a.seq, a.dS_out, (T*)(ws + L.gpn),
-                             nullptr};
+                             nullptr, one};
     const WalkArgs<T> fwd = {(const T*)(ws + L.xc), nullptr, (const float*)(ws + L.dt),
                              (const float*)(ws + L.cs), a.seq, a.S_in, (T*)(ws + L.hpn),
-                             nullptr};
+                             nullptr, one};
     return launch_state_walk_pair<T, P, N>(d, t, bwd, fwd, s);
 }
 

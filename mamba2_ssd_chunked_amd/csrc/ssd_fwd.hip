@@ -90,7 +90,10 @@ __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ d
 // FINAL = true:  y = the same with H_c replaced by the true entering state
 //                H_c + eps S_in (eps = exp(sum of dt A from the segment start to
 //                the chunk), 0 once a packed sequence started in between), plus
-//                D x, in the activation type.  This is the zero-state output and
+//                D x, in the activation type.
+// With spans (SpanPlan), H_c and eps run from the chunk's span start and S_st
+// holds the state entering each span (zero-initial-state or true): the
+// entering state is H_c + eps S_st[span].  This is the zero-state output and
 //                the correction pass of #6808 in one pass: y_zero never goes to
 //                memory and x and C are read once.  D is folded into the
 //                diagonal of the weight matrix (j = i), so D x comes out of the
@@ -103,7 +106,8 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
                                                         const float* __restrict__ ctot,
                                                         const int32_t* __restrict__ seq,
                                                         const T* __restrict__ hst,
-                                                        const float* __restrict__ S_in,
+                                                        SpanPlan sp,
+                                                        const float* __restrict__ S_st,
                                                         const float* __restrict__ Dp,
                                                         float* __restrict__ y_zero,
                                                         T* __restrict__ y) {
@@ -142,11 +146,20 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
     const int64_t rb = b * d.L, t0 = (int64_t)cm * Q;
     const int k = seg_of_chunk(tab, cm, Q);
     const int64_t s0 = tab.start[k];
-    const bool first = (t0 == s0);
+    const bool first = (t0 == s0);  // first chunk of the segment
+    // the chunk's span (SpanPlan): the walk left the zero-state entering state of
+    // every chunk but a span's first; S_st holds the state entering each span
+    const int cseg0 = (int)(s0 / Q);
+    const int jsp = (cm - cseg0) / sp.cps;
+    const int cspan0 = cseg0 + jsp * sp.cps;
+    const bool sfirst = (cm == cspan0);  // first chunk of its span
+    const bool use_st = S_st != nullptr && (FINAL || jsp > 0);
     const int64_t pred = seg_pred_token(tab, k);
-    // sequence of the state entering the segment, and of the one entering the chunk
+    // sequence of the state entering the segment, of the one entering the
+    // chunk, and of the one entering the chunk's span
     const int seq_ref = seq ? seq[rb + (pred >= 0 ? pred : s0)] : 0;
     const int seq_prev = (seq && !first) ? seq[rb + t0 - 1] : seq_ref;
+    const int seq_span = (seq && jsp > 0) ? seq[rb + (int64_t)cspan0 * Q - 1] : seq_ref;
     const bool split = seq && seq[rb + t0] != seq[rb + t0 + Q - 1];
     const int64_t xoff = (int64_t)h * P;
     const int64_t coff = (int64_t)d.H * P + (int64_t)d.G * N + (int64_t)g * N;
@@ -182,23 +195,24 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
     vt rh[V_H];
     f32x4 rs[V_H][VEC / 4];
     const T* hp = hst + (((int64_t)b * d.nchunk + cm) * d.H + h) * (P * N);
-    const float* sp = S_in + (((int64_t)k * d.batch + b) * d.H + h) * (P * N);
+    const float* stp = use_st ? S_st + (((int64_t)(sp.first[k] + jsp) * d.batch + b) * d.H + h) * (P * N)
+                              : nullptr;
     if (inter) {
 #pragma unroll
         for (int q = 0; q < V_H; ++q) {
             const int idx = threadIdx.x + q * NTH;
             if (idx < P * (N / VEC)) {
                 const int p = idx / (N / VEC), nv = idx % (N / VEC);
-                if (!first) {
+                if (!sfirst) {
                     rh[q] = *(const vt*)(hp + (int64_t)p * N + nv * VEC);
                 } else {
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) rh[q][e] = (T)0.f;
                 }
-                if (FINAL) {
+                if (use_st) {
 #pragma unroll
                     for (int e = 0; e < VEC / 4; ++e)
-                        rs[q][e] = *(const f32x4*)(sp + (int64_t)p * N + nv * VEC + 4 * e);
+                        rs[q][e] = *(const f32x4*)(stp + (int64_t)p * N + nv * VEC + 4 * e);
                 }
             }
         }
@@ -208,16 +222,15 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
         sdt[j] = dt_ws[hl + j];
         ssq[j] = seq ? seq[rb + t0 + j] : 0;
     }
-    if (FINAL && wave == 0) {
-        // eps = exp(sum of the segment's earlier chunk totals), if no sequence
-        // started between the segment start and this chunk
-        const int cseg0 = (int)(s0 / Q);
+    if (use_st && wave == 0) {
+        // eps = exp(sum of the span's earlier chunk totals), if no sequence
+        // started between the span start and this chunk
         const float* ct = ctot + ((int64_t)b * d.H + h) * d.nchunk;
         float part = 0.f;
-        for (int c = cseg0 + lane; c < cm; c += 64) part += ct[c];
+        for (int c = cspan0 + lane; c < cm; c += 64) part += ct[c];
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-        if (lane == 0) s_eps = (seq_prev == seq_ref) ? expf(part) : 0.f;
+        if (lane == 0) s_eps = (seq_prev == seq_span) ? expf(part) : 0.f;
     }
 #pragma unroll
     for (int q = 0; q < V_X; ++q) {
@@ -232,14 +245,15 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
     for (int a = threadIdx.x; a < QT; a += NTH) wide |= (scs[16 * a] - scs[16 * a + 15] > 80.f);
     const bool exact = __syncthreads_or(wide) || split;
     if (inter) {
-        // entering state [p][n]: zero-state part (non-first chunks) + eps S_in
-        const float eps = FINAL ? s_eps : 0.f;
+        // entering state [p][n]: zero-state part from the span's own chunks + eps
+        // times the state entering the span
+        const float eps = use_st ? s_eps : 0.f;
 #pragma unroll
         for (int q = 0; q < V_H; ++q) {
             const int idx = threadIdx.x + q * NTH;
             if (idx < P * (N / VEC)) {
                 vt v = rh[q];
-                if (FINAL) {
+                if (use_st) {
 #pragma unroll
                     for (int e = 0; e < VEC; ++e)
                         v[e] = (T)((float)v[e] + eps * rs[q][e / 4][e % 4]);
@@ -522,21 +536,22 @@ static bool shape_ok(int Q) {
 template <typename T, int P, int N, int Q, bool FINAL>
 static hipError_t launch_chunk_y(const Dims& d, const SegTab& t, const T* xc, const T* gram,
                                  const float* dtw, const float* csw, const float* ctot,
-                                 const int32_t* seq, const T* hst, const float* S_in,
-                                 const float* D, float* y_zero, T* y, hipStream_t s) {
+                                 const int32_t* seq, const T* hst, const SpanPlan& sp,
+                                 const float* S_st, const float* D, float* y_zero, T* y,
+                                 hipStream_t s) {
     if constexpr (chunk_y_lds<T, P, N, Q>() <= LDS_LIMIT) {
         return launch(k_chunk_y<T, P, N, Q, FINAL>, chunk_head_grid(d), dim3(Q / 32 * 64), s, d, t,
-                      xc, gram, dtw, csw, ctot, seq, hst, S_in, D, y_zero, y);
+                      xc, gram, dtw, csw, ctot, seq, hst, sp, S_st, D, y_zero, y);
     }
     return hipErrorInvalidValue;
 }
 
 template <typename T, int P, int N>
-static hipError_t segment_states_t(const Dims& d, const SegTab& t, const void* xc_, const void* dt_raw,
-                             const float* dt_bias, const float* A_log, const int32_t* seq,
-                             float* summary, void* ws, hipStream_t s) {
+static hipError_t segment_states_t(const Dims& d, const SegTab& t, const void* xc_,
+                                   const void* dt_raw, const float* dt_bias, const float* A_log,
+                                   const int32_t* seq, float* summary, void* ws, hipStream_t s) {
     const T* xc = (const T*)xc_;
-    const FwdWs L = fwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
+    const FwdWs L = fwd_ws_layout(d, t, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
     char* w = (char*)ws;
     float* dtw = (float*)(w + L.dt);
     float* csw = (float*)(w + L.cs);
@@ -546,35 +561,51 @@ static hipError_t segment_states_t(const Dims& d, const SegTab& t, const void* x
     // (independent inputs); the walk then needs dt and the cumulative sums
     SSD_TRY(launch_gram_dt<T, N>(d, xc, (T*)(w + L.gram), dt_raw, dt_bias, A_log, seq, dtw, csw,
                                  ctot, s));
-    const WalkArgs<T> wa = {xc, nullptr, dtw, csw, seq, nullptr, hst, summary};
-    return launch_state_walk<T, P, N, false>(d, t, wa, s);
+    const SpanPlan sp = span_plan(d, t, true);
+    if (plan_trivial(sp, t)) {
+        const WalkArgs<T> wa = {xc, nullptr, dtw, csw, seq, nullptr, hst, summary, sp};
+        return launch_state_walk<T, P, N, false>(d, t, wa, s);
+    }
+    // long segments: walk their spans, then compose the span summaries
+    float* spsum = (float*)(w + L.spsum);
+    const WalkArgs<T> wa = {xc, nullptr, dtw, csw, seq, nullptr, hst, spsum, sp};
+    SSD_TRY(launch_state_walk<T, P, N, false>(d, t, wa, s));
+    return launch_span_combine(d, sp, spsum, summary, s);
 }
 
 // y_zero (FINAL = false) or the corrected y (FINAL = true), from the workspace
 // that segment_states_t filled (decays, entering states, Gram tiles).
 template <typename T, int P, int N, bool FINAL>
-static hipError_t segment_output_t(const Dims& d, const SegTab& t, const void* xc_, const int32_t* seq,
-                             const void* ws, const float* S_in, const float* D, float* y_zero,
-                             void* y, hipStream_t s) {
+static hipError_t segment_output_t(const Dims& d, const SegTab& t, const void* xc_,
+                                   const int32_t* seq, void* ws, const float* S_in,
+                                   const float* D, float* y_zero, void* y, hipStream_t s) {
     const T* xc = (const T*)xc_;
-    const FwdWs L = fwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
-    const char* w = (const char*)ws;
+    const FwdWs L = fwd_ws_layout(d, t, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
+    char* w = (char*)ws;
     const float* dtw = (const float*)(w + L.dt);
     const float* csw = (const float*)(w + L.cs);
     const float* ctot = (const float*)(w + L.ctot);
     const T* hst = (const T*)(w + L.hst);
     const T* gram = (const T*)(w + L.gram);
     T* yo = (T*)y;
+    const SpanPlan sp = span_plan(d, t, true);
+    const float* S_st = FINAL ? S_in : nullptr;
+    if (!plan_trivial(sp, t)) {
+        // the state entering every span: from S_in (y) or from zero (y_zero)
+        float* spst = (float*)(w + L.spst);
+        SSD_TRY(launch_span_scan(d, sp, (const float*)(w + L.spsum), FINAL ? S_in : nullptr, spst, s));
+        S_st = spst;
+    }
     switch (d.Q) {
         case 64:
-            return launch_chunk_y<T, P, N, 64, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst, S_in,
-                                                      D, y_zero, yo, s);
+            return launch_chunk_y<T, P, N, 64, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst, sp,
+                                                      S_st, D, y_zero, yo, s);
         case 128:
-            return launch_chunk_y<T, P, N, 128, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst,
-                                                       S_in, D, y_zero, yo, s);
+            return launch_chunk_y<T, P, N, 128, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst, sp,
+                                                       S_st, D, y_zero, yo, s);
         case 256:
-            return launch_chunk_y<T, P, N, 256, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst,
-                                                       S_in, D, y_zero, yo, s);
+            return launch_chunk_y<T, P, N, 256, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst, sp,
+                                                       S_st, D, y_zero, yo, s);
         default:
             return hipErrorInvalidValue;
     }
@@ -584,7 +615,7 @@ template <typename T, int P, int N>
 static hipError_t apply_init_t(const Dims& d, const SegTab& t, const float* y_zero, const void* xc,
                                const float* D, const int32_t* seq, const float* S_in,
                                const void* ws, void* y, hipStream_t s) {
-    const FwdWs L = fwd_ws_layout(d, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
+    const FwdWs L = fwd_ws_layout(d, t, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
     const char* w = (const char*)ws;
     return launch(k_apply_init<T, P, N>, chunk_head_grid(d), dim3(256), s, d, t, y_zero,
                   (const T*)xc, D, seq, S_in, (const float*)(w + L.cs),
@@ -642,8 +673,7 @@ hipError_t launch_segment_states(const Dims& d, const SegTab& t, int act, const 
 }
 
 hipError_t launch_segment_output(const Dims& d, const SegTab& t, int act, const void* xBC_conv,
-                                 const int32_t* seq, const void* ws, float* y_zero,
-                                 hipStream_t s) {
+                                 const int32_t* seq, void* ws, float* y_zero, hipStream_t s) {
 #define X(p, n)                                                                                 \
     if (d.P == p && d.N == n) {                                                                 \
         return segment_output_t<T, p, n, false>(d, t, xBC_conv, seq, ws, nullptr, nullptr, y_zero, \
@@ -662,7 +692,7 @@ hipError_t launch_segment_output(const Dims& d, const SegTab& t, int act, const 
 
 hipError_t launch_segment_output_fused(const Dims& d, const SegTab& t, int act,
                                        const void* xBC_conv, const float* D, const int32_t* seq,
-                                       const float* S_in, const void* ws, void* y, hipStream_t s) {
+                                       const float* S_in, void* ws, void* y, hipStream_t s) {
 #define X(p, n)                                                                                 \
     if (d.P == p && d.N == n) {                                                                 \
         return segment_output_t<T, p, n, true>(d, t, xBC_conv, seq, ws, S_in, D, nullptr, y, s); \

@@ -27,8 +27,10 @@ struct Dims {
     int H, P, N, G, Q, W, C, hpg;
     int nchunk;        // L / Q
     int nseg;
+    int act;           // ssd_dtype of the activations
     float dt_min, dt_max;
 };
+inline int act_of_dims(const Dims& d) { return d.act; }
 
 // Kernel launch that returns the launch's own status (hipLaunchKernel), so a
 // call made of several launches stops at the first that fails.  The arguments
@@ -228,6 +230,56 @@ template <> struct Mma<float> {
 #define SSD_F32_SHAPES(X) X(16, 16) X(32, 32) X(64, 64) X(64, 128)
 #define SSD_BF16_SHAPES(X) X(32, 64) X(64, 64) X(64, 128)
 
+// Spans of the forward state walk.  One walk workgroup carries the running
+// state through a run of chunks in causal order; a segment much longer than
+// the others' total work would leave most CUs idle, so the forward walk splits
+// each segment into spans of `cps` chunks (the last span of a segment may be
+// shorter), walks every span from a zero state and composes the span
+// summaries into the segment summary afterwards (the same affine composition
+// as the boundary scan: S_out = a_span S_in + S_span).  cps is halved from the
+// longest segment's chunk count while the walk grid has fewer than
+// WALK_TARGET_BLOCKS workgroups (one per CU on the 256 CUs of an MI355X) and a
+// span would keep at least WALK_MIN_SPAN_TOKENS tokens.  A plan with one span
+// per segment ("trivial") needs no composition.
+constexpr int WALK_TARGET_BLOCKS = 256;
+constexpr int WALK_MIN_SPAN_TOKENS = 1024;
+struct SpanPlan {
+    int cps;                          // chunks per span
+    int n;                            // spans over all segments
+    int first[SSD_MAX_SEGMENTS + 1];  // first span of each segment; first[nseg] = n
+};
+// Heads per forward-walk workgroup (two heads of a group share B rows in bf16).
+inline int walk_heads_of(const Dims& d, int act) {
+    return (act == SSD_BF16 && d.hpg % 2 == 0) ? 2 : 1;
+}
+inline SpanPlan span_plan(const Dims& d, const SegTab& t, bool split) {
+    SpanPlan p = {};
+    int maxnc = 1;
+    for (int k = 0; k < t.n; ++k) maxnc = (int)(t.len[k] / d.Q) > maxnc ? (int)(t.len[k] / d.Q) : maxnc;
+    auto count = [&](int cps) {
+        int64_t n = 0;
+        for (int k = 0; k < t.n; ++k) n += (t.len[k] / d.Q + cps - 1) / cps;
+        return n;
+    };
+    int cps = maxnc;
+    if (split) {
+        const int hw = walk_heads_of(d, act_of_dims(d));
+        const int min_cps = WALK_MIN_SPAN_TOKENS / d.Q > 1 ? WALK_MIN_SPAN_TOKENS / d.Q : 1;
+        while (cps > min_cps && count(cps) * (d.H / hw) * d.batch < WALK_TARGET_BLOCKS)
+            cps = (cps + 1) / 2 > min_cps ? (cps + 1) / 2 : min_cps;
+    }
+    p.cps = cps;
+    int n = 0;
+    for (int k = 0; k < t.n; ++k) {
+        p.first[k] = n;
+        n += (int)((t.len[k] / d.Q + cps - 1) / cps);
+    }
+    p.first[t.n] = n;
+    p.n = n;
+    return p;
+}
+inline bool plan_trivial(const SpanPlan& p, const SegTab& t) { return p.n == t.n; }
+
 // Size of the fixed device scratch of ssd_segment_fwd_noalloc (noalloc.hip),
 // and its device address on the current device (taken once per device).
 constexpr size_t SCRATCH_BYTES = SSD_SCRATCH_BYTES;
@@ -241,16 +293,19 @@ hipError_t launch_segment_states(const Dims& d, const SegTab& t, int act, const 
                                  const void* dt_raw, const float* dt_bias, const float* A_log,
                                  const int32_t* seq, float* summary, void* ws, hipStream_t s);
 hipError_t launch_segment_output(const Dims& d, const SegTab& t, int act, const void* xBC_conv,
-                                 const int32_t* seq, const void* ws, float* y_zero,
-                                 hipStream_t s);
+                                 const int32_t* seq, void* ws, float* y_zero, hipStream_t s);
 hipError_t launch_segment_output_fused(const Dims& d, const SegTab& t, int act,
                                        const void* xBC_conv, const float* D, const int32_t* seq,
-                                       const float* S_in, const void* ws, void* y, hipStream_t s);
+                                       const float* S_in, void* ws, void* y, hipStream_t s);
 hipError_t launch_boundary_scan(const Dims& d, int nseg, const float* summary, const float* init,
                                 int reverse, float* out, float* final_state, hipStream_t s);
 hipError_t launch_apply_init_state(const Dims& d, const SegTab& t, int act, const float* y_zero,
                                    const void* xBC_conv, const float* D, const int32_t* seq,
                                    const float* S_in, const void* ws, void* y, hipStream_t s);
+hipError_t launch_span_combine(const Dims& d, const SpanPlan& sp, const float* spsum,
+                               float* summary, hipStream_t s);
+hipError_t launch_span_scan(const Dims& d, const SpanPlan& sp, const float* spsum,
+                            const float* S_in, float* spst, hipStream_t s);
 bool kernels_supported(int P, int N, int act);
 hipError_t launch_dt_prep(const Dims& d, int act, const void* dt_raw, const float* dt_bias,
                           const float* A_log, const int32_t* seq, float* dt_ws, float* cs_ws,
@@ -279,11 +334,14 @@ bool bwd_supported(int P, int N, int Q, int act);
 bool chunk_supported(int P, int N, int Q, int act);
 
 // Forward workspace layout (byte offsets), shared by the host code and launchers.
+// With a non-trivial span plan it also holds the span summaries (S_span then
+// a_span, the summary layout over spans) and the state entering every span
+// (filled by the output calls).
 struct FwdWs {
-    size_t dt, cs, ctot, hst, gram, total;
+    size_t dt, cs, ctot, hst, gram, spsum, spst, total;
 };
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline FwdWs fwd_ws_layout(const Dims& d, int act) {
+inline FwdWs fwd_ws_layout(const Dims& d, const SegTab& t, int act) {
     FwdWs w;
     const size_t esz = act == SSD_BF16 ? 2 : 4;
     const size_t bhl = (size_t)d.batch * d.H * d.L;
@@ -293,7 +351,16 @@ inline FwdWs fwd_ws_layout(const Dims& d, int act) {
     w.hst = align256(w.ctot + (size_t)d.batch * d.H * d.nchunk * 4);
     w.gram = align256(w.hst + (size_t)d.batch * d.nchunk * d.H * d.P * d.N * esz);
     const size_t qt = (size_t)d.Q / 16;
-    w.total = align256(w.gram + (size_t)d.batch * d.nchunk * d.G * (qt * (qt + 1) / 2) * 256 * esz);
+    w.spsum = align256(w.gram + (size_t)d.batch * d.nchunk * d.G * (qt * (qt + 1) / 2) * 256 * esz);
+    const SpanPlan sp = span_plan(d, t, true);
+    const size_t bh = (size_t)d.batch * d.H;
+    if (plan_trivial(sp, t)) {
+        w.spst = w.spsum;
+        w.total = w.spsum;
+    } else {
+        w.spst = align256(w.spsum + (size_t)sp.n * bh * ((size_t)d.P * d.N + 1) * 4);
+        w.total = align256(w.spst + (size_t)sp.n * bh * d.P * d.N * 4);
+    }
     return w;
 }
 

@@ -13,12 +13,14 @@
 //             entering the chunk]; the stored value is the gradient of the
 //             state leaving the chunk.
 //
-// The walk starts from `init` ([S][b][H][P][N] FP32: S_in forward, dS_out
-// backward) or from zero; from zero, the forward walk stores nothing for a
-// segment's first chunk (its entering state is zero).  The final value is
-// S_ext (forward) or dL/dS_in of the segment's own outputs (backward), and the
-// product of the alphas the block decay a_block, both written to `summary` if
-// given.
+// A walk covers one span of a segment (a run of its chunks; see SpanPlan:
+// the whole segment unless the forward walk splits long segments).  It starts
+// from `init` ([S][b][H][P][N] FP32: S_in forward, dS_out backward, for walks
+// with one span per segment) or from zero; from zero, the forward walk stores
+// nothing for a span's first chunk (its entering state from the span's own
+// chunks is zero).  The final value is the span's S_ext (forward) or dL/dS_in
+// of the segment's own outputs (backward), and the product of the alphas its
+// block decay, both written to `summary` (summary layout over spans) if given.
 //
 // This is the decay-weighted sum over earlier chunk states that
 // state-spaces/mamba #482 (second comment) identifies as the part of the scan
@@ -51,7 +53,9 @@ struct WalkArgs {
     const int32_t* seq;    // packed sequence ids or null
     const float* init;     // starting value [S][b][H][P][N] or null (zero)
     T* store;              // value at every chunk start, or null
-    float* summary;        // final value and block decay, or null
+    float* summary;        // final value and block decay per span, or null
+    SpanPlan sp;           // the runs of chunks walked (spans; one per segment
+                           // unless the forward walk splits segments)
 };
 
 constexpr int WALK_KT = 64;  // tokens per slice
@@ -94,13 +98,14 @@ __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, con
     auto sB = reinterpret_cast<T(*)[KT * BR]>(lds + 2 * HW * KT * XR);
     typedef T vt __attribute__((ext_vector_type(VEC)));
 
-    // block -> (row, segment, HW heads of one group): the walks of one (row,
-    // segment) are consecutive items and consecutive items go to one XCD, so
+    // block -> (row, span, HW heads of one group): the walks of one (row,
+    // span) are consecutive items and consecutive items go to one XCD, so
     // they share that XCD's L2 for the B (or C) rows they all read.  The HW
     // heads of a block share its B (or C) rows in LDS; threads hs*256 ..
-    // hs*256+255 (four waves) walk head h0 + hs.
+    // hs*256+255 (four waves) walk head h0 + hs.  Span sg is span j of
+    // segment k: its chunks j*cps .. of the segment.
     const int hs = threadIdx.x / HTH;
-    int h, k;
+    int h, k, sg;
     int64_t b;
     {
         constexpr int NXCD = 8;
@@ -108,19 +113,24 @@ __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, con
         int64_t item = (n % NXCD == 0) ? (i % NXCD) * (n / NXCD) + i / NXCD : i;
         h = (int)(item % (d.H / HW)) * HW + hs;
         item /= d.H / HW;
-        k = (int)(item % d.nseg);
-        b = item / d.nseg;
+        sg = (int)(item % wa.sp.n);
+        b = item / wa.sp.n;
+        k = 0;
+        for (int q = 1; q < tab.n; ++q)
+            if (sg >= wa.sp.first[q]) k = q;
     }
+    const int jsp = sg - wa.sp.first[k];  // span index within the segment
     const int wave = wave_id() % 4, lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
     const int ht = threadIdx.x % HTH;  // thread index within the head
     const int g = h / d.hpg;
     const int Q = d.Q;
     const int64_t rb = b * d.L;
-    const int64_t s0 = tab.start[k];
-    const int nc = (int)(tab.len[k] / Q);
+    const int nck = (int)(tab.len[k] / Q);
+    const int64_t s0 = tab.start[k] + (int64_t)jsp * wa.sp.cps * Q;
+    const int nc = min(wa.sp.cps, nck - jsp * wa.sp.cps);
     const int spc = Q / KT;  // slices per chunk
     const int ns = nc * spc;
-    const int64_t pred = seg_pred_token(tab, k);
+    const int64_t pred = jsp > 0 ? s0 - 1 : seg_pred_token(tab, k);
     const float* dtp = dt_ws + ((int64_t)b * d.H + h) * d.L;
     const float* csp = cs_ws + ((int64_t)b * d.H + h) * d.L;
     const int64_t astr = BWD ? (int64_t)d.H * P : (int64_t)d.C;
@@ -197,7 +207,7 @@ __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, con
     };
 
     const int64_t per = (int64_t)d.batch * d.H * P * N;
-    const int64_t sg = ((int64_t)k * d.batch + b) * d.H + h;
+    const int64_t ig = ((int64_t)k * d.batch + b) * d.H + h;  // init walks: one span per segment
     f32x4 acc[PT][NTW];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
@@ -207,7 +217,7 @@ __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, con
             if (init && (NFULL || nt < NTT)) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    acc[pt][j][r] = init[sg * (P * N) + (pt * 16 + 4 * lg + r) * N + nt * 16 + lr];
+                    acc[pt][j][r] = init[ig * (P * N) + (pt * 16 + 4 * lg + r) * N + nt * 16 + lr];
             } else {
                 acc[pt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
@@ -290,7 +300,7 @@ __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, con
     }
 
     if (!summary) return;
-    float* sx = summary + (int64_t)k * per + ((int64_t)b * d.H + h) * (P * N);
+    float* sx = summary + (int64_t)sg * per + ((int64_t)b * d.H + h) * (P * N);
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
@@ -303,7 +313,7 @@ __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, con
             }
         }
     if (ht == 0)
-        summary[(int64_t)d.nseg * per + ((int64_t)k * d.batch + b) * d.H + h] = ablk;
+        summary[(int64_t)wa.sp.n * per + ((int64_t)sg * d.batch + b) * d.H + h] = ablk;
 }
 
 // Two heads per block: four waves per SIMD, so that two blocks (of one walk or
@@ -341,7 +351,7 @@ template <typename T, int P, int N, bool BWD>
 inline hipError_t launch_state_walk(const Dims& d, const SegTab& t, const WalkArgs<T>& wa,
                                     hipStream_t s) {
     const int hw = walk_heads<T>(d);
-    const dim3 grid((unsigned)((int64_t)(d.H / hw) * d.nseg * d.batch));
+    const dim3 grid((unsigned)((int64_t)(d.H / hw) * wa.sp.n * d.batch));
     const dim3 block(256 * hw);
     if (hw == 2) {
         if (wa.seq) return launch(k_state_walk<T, P, N, BWD, true, 2>, grid, block, s, d, t, wa);
@@ -356,6 +366,8 @@ template <typename T, int P, int N>
 inline hipError_t launch_state_walk_pair(const Dims& d, const SegTab& t, const WalkArgs<T>& bwd,
                                          const WalkArgs<T>& fwd, hipStream_t s) {
     const int hw = walk_heads<T>(d);
+    // both walks start from a state per segment: one span per segment
+    if (bwd.sp.n != t.n || fwd.sp.n != t.n) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(2 * (int64_t)(d.H / hw) * d.nseg * d.batch));
     const dim3 block(256 * hw);
     if (hw == 2) {

@@ -214,3 +214,25 @@ def test_grid_overflow_is_refused():
     """batch x heads x P x N beyond 2^32 work-items of the boundary scan's grid."""
     p = _p(batch=4096, seqlen=256, nheads=4096, headdim=64, dstate=128, chunk=256)
     assert _conv(p, [(0, 256)]) == -2
+
+
+def test_forward_workspace_holds_span_regions_for_long_segments():
+    """The packed 32768-token batch (4 segments of 32 chunks, 32 heads walked two per
+    workgroup) has too few walk workgroups per segment-long walk: the walk splits each
+    segment into spans until 256 workgroups (one per CU) exist or a span would drop
+    below 1024 tokens: 16 spans of 8 chunks.  The forward workspace then holds the span summaries
+    and the states entering the spans (FP32, [32][1][32][64*128] each, the summaries
+    with their block decays)."""
+    p = _p(batch=1, seqlen=32768, nheads=32, headdim=64, dstate=128, chunk=256)
+    segs = [(i * 8192, 8192) for i in range(4)]
+    al = lambda x: (x + 255) // 256 * 256
+    b, H, L, nc, P, N = 1, 32, 32768, 128, 64, 128
+    base = al(al(al(b * H * L * 4) + b * H * L * 4) + b * H * nc * 4)
+    base = al(base + b * nc * H * P * N * 2)
+    qt = 256 // 16
+    base = al(base + b * nc * (qt * (qt + 1) // 2) * 256 * 2)
+    nsp = 16
+    want = al(al(base + nsp * b * H * (P * N + 1) * 4) + nsp * b * H * P * N * 4)
+    assert ssd.ssd_workspace_bytes(p, segs) == want
+    # the mixer shard's segments are walked whole: no span regions
+    assert ssd.ssd_workspace_bytes(_p(), SEGS8) < want

@@ -42,6 +42,16 @@ def _small(name):
     if name == "bf16_q64":
         return mk(name, batch=1, seqlen=1024, nheads=4, headdim=64, dstate=64, ngroups=2,
                   chunk=64, act="bf16", seed=106, seg_lens=[64, 320, 640], slow_decay=True)
+    if name == "bf16_spans":
+        # long segments on few heads: the state walk splits them into spans of
+        # four chunks (8 spans), composed afterwards
+        return mk(name, batch=1, seqlen=8192, nheads=2, headdim=64, dstate=128, ngroups=1,
+                  chunk=256, act="bf16", seed=108, seg_lens=[2048, 6144], packed=(700, 3000),
+                  slow_decay=True)
+    if name == "f32_spans":
+        # float32, chunk 64: spans of sixteen chunks, two per segment
+        return mk(name, batch=2, seqlen=2048, nheads=2, headdim=32, dstate=32, ngroups=1,
+                  chunk=64, act="f32", seed=109, nseg=1, packed=(300, 900), slow_decay=True)
     if name == "bf16_q128":
         return mk(name, batch=2, seqlen=1024, nheads=2, headdim=32, dstate=64, ngroups=1,
                   chunk=128, act="bf16", seed=107, nseg=2, packed=(60, 300))
@@ -49,7 +59,7 @@ def _small(name):
 
 
 SMALL = ["tiny_f32", "slow_tiny_f32", "f32_head_thd", "f32_virtual", "bf16_small", "bf16_virtual", "bf16_thd",
-         "bf16_q64", "bf16_q128"]
+         "bf16_q64", "bf16_q128", "bf16_spans", "f32_spans"]
 
 
 @pytest.fixture(scope="module", params=SMALL)
