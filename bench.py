@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--no-extra-configs", action="store_true",
                     help="time only the chosen workload (by default the headline run also times "
                          "the forward of every other configuration)")
+    ap.add_argument("--conv-fused", action="store_true",
+                    help="run the headline's forward conv-fused (ssd_conv_segment_states and "
+                         "ssd_conv_segment_output instead of ssd_conv1d_fwd and the two phases)")
     ap.add_argument("--cpu-runs", type=int, default=8)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one device-to-device copy of this many MB before timing, so that "
@@ -77,6 +80,7 @@ def parse():
 CALL_KERNEL = {
     "ssd_conv1d_fwd": r"k_conv1d_silu<",
     "ssd_segment_output_fused": r"k_chunk_y<",
+    "ssd_conv_segment_output": r"k_chunk_y<",
     "ssd_boundary_scan": r"k_boundary_scan<",
     "ssd_boundary_scan(reverse)": r"k_boundary_scan<",
     "ssd_segment_bwd_chunks": r"k_chunk_bwd(_hb)?<",
@@ -304,6 +308,14 @@ def algorithmic_bytes(wl):
         "ssd_boundary_scan": summary + states,
         # x, C, Gram tiles, entering states, S_in, decays in; y out
         "ssd_segment_output_fused": x + bc // 2 + gram + hst + states + dtcs + x + seq,
+        # conv-fused forward: the B/C conv (raw B, C in, convolved out), then the states
+        # phase reading the raw x (same bytes as the convolved x; the halo rows are
+        # L1/L2 hits); the output pass reading the raw x; each with its conv taps
+        "ssd_conv_segment_states": 2 * bc + 2 * G * N * wl.conv_width * 4
+                                   + BL * H * e + dtcs + x + bc // 2 + dtcs + hst + summary
+                                   + bc + gram + seq + H * P * wl.conv_width * 4,
+        "ssd_conv_segment_output": x + bc // 2 + gram + hst + states + dtcs + x + seq
+                                   + H * P * wl.conv_width * 4,
         "ssd_segment_output": x + bc // 2 + gram + hst + dtcs + BL * H * P * 4 + seq,
         "ssd_apply_init_state": BL * H * P * 4 + x + bc // 2 + BL * H * 4 + states + x + seq,
         # conv recompute (xBC in, conv output out), dt prep, the transposed Gram tiles
@@ -400,9 +412,10 @@ def cpu_baseline(wl, runs, backward, heads=None):
                       f"runs ({med:.2f} s each)"}
 
 
-def run_workload(wl, which, steps, warmup, dev, copy_probe_mb=0):
+def run_workload(wl, which, steps, warmup, dev, copy_probe_mb=0, conv_fused=False):
     """Times one workload: a breakdown pass with events around every call, then
     `steps` whole steps with events around the dominant single-kernel call only.
+    conv_fused: the forward runs the conv inside the two forward phases.
     Returns the measurements (no JSON formatting)."""
     import numpy as np
     import torch
@@ -435,6 +448,15 @@ def run_workload(wl, which, steps, warmup, dev, copy_probe_mb=0):
         ("ssd_segment_output_fused", lambda: ssd.ssd_segment_output_fused(
             p, segs, bufs.xBC_conv, D, seq, bufs.S_in, bufs.ws, bufs.y)),
     ]
+    if conv_fused:
+        calls = [
+            ("ssd_conv_segment_states", lambda: ssd.ssd_conv_segment_states(
+                p, segs, xBC, conv_w, dt_raw, dt_bias, A_log, seq, bufs.summary, bufs.ws)),
+            ("ssd_boundary_scan", lambda: ssd.ssd_boundary_scan(
+                p, segs.n, bufs.summary, None, False, bufs.S_in)),
+            ("ssd_conv_segment_output", lambda: ssd.ssd_conv_segment_output(
+                p, segs, xBC, conv_w, D, seq, bufs.S_in, bufs.ws, bufs.y)),
+        ]
     if do_bwd:
         calls += [
             ("ssd_segment_bwd_summary", lambda: ssd.ssd_segment_bwd_summary(
@@ -525,7 +547,9 @@ def run_workload(wl, which, steps, warmup, dev, copy_probe_mb=0):
 def flops_entries(wl, m, do_bwd, peaks=None):
     mfma_peak = BF16_PEAK_TFLOPS if wl.act == "bf16" else F32_PEAK_TFLOPS
     mfma = {}
-    for name, fl in [("ssd_segment_output_fused", output_flops(wl))] + \
+    out_call = ("ssd_conv_segment_output" if "ssd_conv_segment_output" in m["per_call"]
+                else "ssd_segment_output_fused")
+    for name, fl in [(out_call, output_flops(wl))] + \
             ([("ssd_segment_bwd_chunks", chunk_bwd_flops(wl))] if do_bwd else []):
         ms = m["dom_ms"] if name == m["dom"] else m["per_call"][name]["ms"]
         tf = fl / (ms * 1e-3) / 1e12
@@ -581,7 +605,8 @@ def main():
         raise SystemExit("this workload has no dy; use --pass fwd")
     do_bwd = which == "fwd+bwd"
     dev = torch.device("cuda:0")
-    m = run_workload(wl, which, args.steps, args.warmup, dev, args.copy_probe_mb)
+    m = run_workload(wl, which, args.steps, args.warmup, dev, args.copy_probe_mb,
+                     conv_fused=args.conv_fused)
     torch.cuda.empty_cache()
     peaks = None if args.no_peaks else measure_peaks(torch, dev, torch.cuda.current_stream())
     ms_step, dom, dom_ms, abytes = m["ms_step"], m["dom"], m["dom_ms"], m["abytes"]
@@ -604,7 +629,8 @@ def main():
                    "seq_len": wl.seqlen, "nheads": wl.nheads, "headdim": wl.headdim,
                    "dstate": wl.dstate, "ngroups": wl.ngroups, "chunk": wl.chunk,
                    "conv_width": wl.conv_width, "segments": len(wl.segments),
-                   "layout": wl.layout, "packed": wl.seq_idx is not None},
+                   "layout": wl.layout, "packed": wl.seq_idx is not None,
+                   "conv_fused": args.conv_fused},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(wl.name, CALL_KERNEL[dom]),
@@ -645,6 +671,14 @@ def main():
                  "path_roofline": path_entry(xw, xm["ms_step"], False),
                  "mfma": flops_entries(xw, xm, False),
                  "calls": {k: v["ms"] for k, v in xm["per_call"].items()}}
+            # the same forward with the conv inside the two forward phases
+            xf = run_workload(xw, "fwd", args.steps, args.warmup, dev, conv_fused=True)
+            torch.cuda.empty_cache()
+            fo = xf["per_call"]["ssd_conv_segment_output"]
+            e["conv_fused"] = {"value": round(xw.tokens / (xf["ms_step"] * 1e-3), 1),
+                               "ms_per_step": round(xf["ms_step"], 5),
+                               "output_pass_frac": round(fo["GB_per_s"] / HBM_PEAK_GBS, 4),
+                               "calls": {k: v["ms"] for k, v in xf["per_call"].items()}}
             if not args.no_cpu_baseline:
                 e["cpu_baseline"] = cpu_baseline(xw, 1, False, heads=heads)
             extra[name] = e

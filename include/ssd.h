@@ -99,7 +99,7 @@ typedef struct {
 } ssd_segment;
 
 /* Workspace kinds for ssd_workspace_bytes. */
-enum { SSD_WS_FORWARD = 0, SSD_WS_BACKWARD = 1 };
+enum { SSD_WS_FORWARD = 0, SSD_WS_BACKWARD = 1, SSD_WS_FORWARD_CONV = 2 };
 
 /* Human-readable text for an ssd_status value (static storage). */
 const char* ssd_status_string(int status);
@@ -116,8 +116,10 @@ int32_t ssd_abi_version(void);
 int32_t ssd_supported(int32_t headdim, int32_t dstate, int32_t act_dtype);
 
 /* Bytes of device workspace the forward (SSD_WS_FORWARD: ssd_segment_fwd, read
- * again by ssd_apply_init_state) or backward (SSD_WS_BACKWARD) calls need for
- * this problem.  Returns 0 for an invalid problem or kind. */
+ * again by ssd_apply_init_state), conv-fused forward (SSD_WS_FORWARD_CONV:
+ * ssd_conv_segment_states and ssd_conv_segment_output) or backward
+ * (SSD_WS_BACKWARD) calls need for this problem.  Returns 0 for an invalid
+ * problem or kind, and for SSD_WS_FORWARD_CONV when conv_width is not 4. */
 size_t ssd_workspace_bytes(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
                            int32_t kind);
 
@@ -243,6 +245,35 @@ int ssd_segment_output_fused(const ssd_problem* problem, const ssd_segment* segs
                              const void* xBC_conv, const float* D, const int32_t* seq_idx,
                              const float* S_in, void* ws, size_t ws_bytes, void* y,
                              void* stream);
+
+/* The conv-fused forward: ssd_conv1d_fwd folded into the two forward phases,
+ * so the convolved x channels never go to memory (#6808's first commit names
+ * the conv halo as part of the fused Conv1d + SSD function; state-spaces/mamba
+ * #482, second comment, puts the conv before the scan).  Both calls take the
+ * raw xBC and the conv taps instead of xBC_conv.  ssd_conv_segment_states
+ * convolves the B and C channels into `ws` and then does what
+ * ssd_segment_states does, its state walk convolving the x channels as it
+ * reads them (each segment's first W-1 taps read its causal predecessor's
+ * last tokens, as in ssd_conv1d_fwd); after the boundary scan,
+ * ssd_conv_segment_output does what ssd_segment_output_fused does, again
+ * convolving the x channels itself.  The results equal ssd_conv1d_fwd
+ * followed by ssd_segment_states, ssd_boundary_scan and
+ * ssd_segment_output_fused: the conv arithmetic is the same, operation for
+ * operation.  Compiled for conv_width 4 only (SSD_ERR_UNSUPPORTED otherwise).
+ *   xBC, conv_w   as for ssd_conv1d_fwd                                     (in)
+ *   dt_raw, dt_bias, A_log, seq_idx, summary   as for ssd_segment_states
+ *   D, S_in, y    as for ssd_segment_output_fused
+ *   ws    ssd_workspace_bytes(..., SSD_WS_FORWARD_CONV) bytes: filled by the
+ *         states call, read (and for long segments written) by the output
+ *         call for the same problem, segments and inputs                 (in/out) */
+int ssd_conv_segment_states(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                            const void* xBC, const float* conv_w, const void* dt_raw,
+                            const float* dt_bias, const float* A_log, const int32_t* seq_idx,
+                            float* summary, void* ws, size_t ws_bytes, void* stream);
+int ssd_conv_segment_output(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                            const void* xBC, const float* conv_w, const float* D,
+                            const int32_t* seq_idx, const float* S_in, void* ws,
+                            size_t ws_bytes, void* y, void* stream);
 
 /* Backward, summary phase (Megatron-LM #6808, first commit: the backward
  * mirrors the forward, each segment summarising the gradient its own outputs

@@ -17,6 +17,7 @@ SSD_F32 = 0
 SSD_BF16 = 1
 SSD_WS_FORWARD = 0
 SSD_WS_BACKWARD = 1
+SSD_WS_FORWARD_CONV = 2
 SSD_MAX_SEGMENTS = 64
 SSD_SCRATCH_BYTES = 64 << 20
 
@@ -70,6 +71,10 @@ SIGNATURES = {
                                                 ctypes.c_size_t, _vp, _vp]),
     "ssd_segment_fwd_noalloc": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                _vp]),
+    "ssd_conv_segment_states": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                               _vp, ctypes.c_size_t, _vp]),
+    "ssd_conv_segment_output": (ctypes.c_int, [_PP, _SP, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                               ctypes.c_size_t, _vp, _vp]),
 }
 
 _lib = None

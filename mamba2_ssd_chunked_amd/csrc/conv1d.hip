@@ -15,19 +15,23 @@
 
 namespace ssd {
 
+// Channels c0 .. c0 + nc - 1 of xBC go to columns 0 .. nc - 1 of `out`, whose
+// token rows are ostr elements apart (the whole conv output: c0 = 0, nc =
+// ostr = C).
 template <typename T, int W>
 __global__ void __launch_bounds__(256) k_conv1d_silu(Dims d, SegTab tab, const T* __restrict__ xBC,
                                                     const float* __restrict__ w,
                                                     const int32_t* __restrict__ seq,
+                                                    int c0, int nc, int64_t ostr,
                                                     T* __restrict__ out) {
     constexpr int R = CONV_TPT + W - 1;
     typedef typename Vec4<T>::type vt;
     const int lane = threadIdx.x % 64;
-    const int c = (blockIdx.x * 64 + lane) * CONV_VEC;
+    const int c = c0 + (blockIdx.x * 64 + lane) * CONV_VEC;
     const int64_t b = blockIdx.z;
     const int64_t t0 = (int64_t)blockIdx.y * CONV_TT + wave_id() * CONV_TPT;
     const int64_t rb = b * d.L;
-    if (c >= d.C) return;  // no barriers below
+    if (c >= c0 + nc) return;  // no barriers below
     const int k = conv_seg(tab, t0);
 
     float wr[CONV_VEC][W];
@@ -82,7 +86,7 @@ __global__ void __launch_bounds__(256) k_conv1d_silu(Dims d, SegTab tab, const T
 #pragma unroll
             for (int e = 0; e < CONV_VEC; ++e)
                 o[e] = (T)(acc[e] * __builtin_amdgcn_rcpf(1.f + __expf(-acc[e])));
-            *(vt*)(out + (rb + t0 + t) * d.C + c) = o;
+            *(vt*)(out + (rb + t0 + t) * ostr + (c - c0)) = o;
         }
     };
     if (clean) run(std::false_type{});
@@ -91,32 +95,44 @@ __global__ void __launch_bounds__(256) k_conv1d_silu(Dims d, SegTab tab, const T
 
 template <typename T, int W>
 static hipError_t launch_w(const Dims& d, const SegTab& t, const void* xBC, const float* w,
-                           const int32_t* seq, void* out, hipStream_t s) {
-    dim3 grid((d.C + 64 * CONV_VEC - 1) / (64 * CONV_VEC), (unsigned)(d.L / CONV_TT),
+                           const int32_t* seq, int c0, int nc, int64_t ostr, void* out,
+                           hipStream_t s) {
+    dim3 grid((nc + 64 * CONV_VEC - 1) / (64 * CONV_VEC), (unsigned)(d.L / CONV_TT),
               (unsigned)d.batch);
-    return launch(k_conv1d_silu<T, W>, grid, dim3(256), s, d, t, (const T*)xBC, w, seq, (T*)out);
+    return launch(k_conv1d_silu<T, W>, grid, dim3(256), s, d, t, (const T*)xBC, w, seq, c0, nc,
+                  ostr, (T*)out);
 }
 
 template <typename T>
 static hipError_t launch_t(const Dims& d, const SegTab& t, const void* xBC, const float* w,
-                           const int32_t* seq, void* out, hipStream_t s) {
+                           const int32_t* seq, int c0, int nc, int64_t ostr, void* out,
+                           hipStream_t s) {
     switch (d.W) {
-        case 1: return launch_w<T, 1>(d, t, xBC, w, seq, out, s);
-        case 2: return launch_w<T, 2>(d, t, xBC, w, seq, out, s);
-        case 3: return launch_w<T, 3>(d, t, xBC, w, seq, out, s);
-        case 4: return launch_w<T, 4>(d, t, xBC, w, seq, out, s);
-        case 5: return launch_w<T, 5>(d, t, xBC, w, seq, out, s);
-        case 6: return launch_w<T, 6>(d, t, xBC, w, seq, out, s);
-        case 7: return launch_w<T, 7>(d, t, xBC, w, seq, out, s);
-        case 8: return launch_w<T, 8>(d, t, xBC, w, seq, out, s);
+        case 1: return launch_w<T, 1>(d, t, xBC, w, seq, c0, nc, ostr, out, s);
+        case 2: return launch_w<T, 2>(d, t, xBC, w, seq, c0, nc, ostr, out, s);
+        case 3: return launch_w<T, 3>(d, t, xBC, w, seq, c0, nc, ostr, out, s);
+        case 4: return launch_w<T, 4>(d, t, xBC, w, seq, c0, nc, ostr, out, s);
+        case 5: return launch_w<T, 5>(d, t, xBC, w, seq, c0, nc, ostr, out, s);
+        case 6: return launch_w<T, 6>(d, t, xBC, w, seq, c0, nc, ostr, out, s);
+        case 7: return launch_w<T, 7>(d, t, xBC, w, seq, c0, nc, ostr, out, s);
+        case 8: return launch_w<T, 8>(d, t, xBC, w, seq, c0, nc, ostr, out, s);
         default: return hipErrorInvalidValue;
     }
 }
 
+hipError_t launch_conv1d_channels(const Dims& d, const SegTab& t, int act, const void* xBC,
+                                  const float* w, const int32_t* seq, int c0, int nc,
+                                  int64_t ostr, void* out, hipStream_t s) {
+    // whole 16-byte vectors of channels, inside the row
+    if (c0 < 0 || nc < 1 || c0 % CONV_VEC || nc % CONV_VEC || c0 + nc > d.C || ostr < nc)
+        return hipErrorInvalidValue;
+    if (act == SSD_BF16) return launch_t<bf16>(d, t, xBC, w, seq, c0, nc, ostr, out, s);
+    return launch_t<float>(d, t, xBC, w, seq, c0, nc, ostr, out, s);
+}
+
 hipError_t launch_conv1d_fwd(const Dims& d, const SegTab& t, int act, const void* xBC,
                              const float* w, const int32_t* seq, void* out, hipStream_t s) {
-    if (act == SSD_BF16) return launch_t<bf16>(d, t, xBC, w, seq, out, s);
-    return launch_t<float>(d, t, xBC, w, seq, out, s);
+    return launch_conv1d_channels(d, t, act, xBC, w, seq, 0, d.C, d.C, out, s);
 }
 
 }  // namespace ssd

@@ -27,9 +27,10 @@ __host__ __device__ constexpr int gram_index(int a, int b) { return a * (a + 1) 
 // independent tile products to keep loads in flight.
 constexpr int GSPLIT = 4;
 // One block of the Gram pass: bx = (tile pair, source-tile part), by =
-// (chunk, group), b = row.
+// (chunk, group), b = row.  The B and C channels of token row m are at bc +
+// m * bstr (B of group g at g N, C at (G + g) N).
 template <typename T, int N, bool TRANS>
-__device__ __forceinline__ void gram_block(const Dims& d, const T* __restrict__ xc,
+__device__ __forceinline__ void gram_block(const Dims& d, const T* __restrict__ bc, int64_t bstr,
                                            T* __restrict__ gram, int bx, int by, int64_t b) {
     typedef Mma<T> M;
     typedef typename M::Frag Frag;
@@ -40,7 +41,7 @@ __device__ __forceinline__ void gram_block(const Dims& d, const T* __restrict__ 
     const int g = by % d.G, cm = by / d.G;
     const int lane = threadIdx.x, lr = lane % 16, lg = lane / 16;
     const int64_t t0 = b * d.L + (int64_t)cm * d.Q;
-    const int64_t boff = (int64_t)d.H * d.P + (int64_t)g * N;
+    const int64_t boff = (int64_t)g * N;
     const int64_t coff = boff + (int64_t)d.G * N;
     T* out = gram + (((int64_t)b * d.nchunk + cm) * d.G + g) * (int64_t)gram_tiles(QT) * 256;
     for (int side = 0; side < 2; ++side) {
@@ -49,13 +50,13 @@ __device__ __forceinline__ void gram_block(const Dims& d, const T* __restrict__ 
         Frag cf[NKF];
 #pragma unroll
         for (int kn = 0; kn < NKF; ++kn)
-            cf[kn] = M::load(xc + (t0 + a * 16 + lr) * d.C + coff + kn * KS + SL * lg);
+            cf[kn] = M::load(bc + (t0 + a * 16 + lr) * bstr + coff + kn * KS + SL * lg);
 #pragma unroll 2
         for (int bt = part; bt <= a; bt += GSPLIT) {
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kn = 0; kn < NKF; ++kn) {
-                const Frag bf = M::load(xc + (t0 + bt * 16 + lr) * d.C + boff + kn * KS + SL * lg);
+                const Frag bf = M::load(bc + (t0 + bt * 16 + lr) * bstr + boff + kn * KS + SL * lg);
                 acc = TRANS ? M::mma(cf[kn], bf, acc) : M::mma(bf, cf[kn], acc);
             }
             *(t4*)(out + (int64_t)gram_index(a, bt) * 256 + lane * 4) =
@@ -69,7 +70,7 @@ __device__ __forceinline__ void gram_block(const Dims& d, const T* __restrict__ 
 // inputs (B, C and dt_raw) and have no order between them, so their blocks
 // share the chip instead of running one kernel after the other.
 template <typename T, int N, bool TRANS>
-__global__ void __launch_bounds__(64) k_gram_dt(Dims d, const T* __restrict__ xc,
+__global__ void __launch_bounds__(64) k_gram_dt(Dims d, const T* __restrict__ bc, int64_t bstr,
                                                T* __restrict__ gram, int64_t ngram,
                                                const T* __restrict__ dt_raw,
                                                const float* __restrict__ dt_bias,
@@ -81,7 +82,8 @@ __global__ void __launch_bounds__(64) k_gram_dt(Dims d, const T* __restrict__ xc
     const int64_t i = blockIdx.x;
     if (i < ngram) {
         const int gx = d.Q / 16 / 2 * GSPLIT, gy = d.nchunk * d.G;
-        gram_block<T, N, TRANS>(d, xc, gram, (int)(i % gx), (int)((i / gx) % gy), i / gx / gy);
+        gram_block<T, N, TRANS>(d, bc, bstr, gram, (int)(i % gx), (int)((i / gx) % gy),
+                                i / gx / gy);
     } else {
         const int64_t j = i - ngram;
         dt_prep_wave<T>(d, dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot,
@@ -91,13 +93,14 @@ __global__ void __launch_bounds__(64) k_gram_dt(Dims d, const T* __restrict__ xc
 }
 
 template <typename T, int N, bool TRANS = false>
-inline hipError_t launch_gram_dt(const Dims& d, const T* xc, T* gram, const void* dt_raw,
+inline hipError_t launch_gram_dt(const Dims& d, const T* bc, int64_t bstr, T* gram,
+                                 const void* dt_raw,
                                  const float* dt_bias, const float* A_log, const int32_t* seq,
                                  float* dt_ws, float* cs_ws, float* ctot, hipStream_t s) {
     const int64_t ngram = (int64_t)(d.Q / 16 / 2 * GSPLIT) * d.nchunk * d.G * d.batch;
     const int64_t ndt = (int64_t)d.nchunk * d.H * d.batch;
-    return launch(k_gram_dt<T, N, TRANS>, dim3((unsigned)(ngram + ndt)), dim3(64), s, d, xc, gram,
-                  ngram, (const T*)dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot);
+    return launch(k_gram_dt<T, N, TRANS>, dim3((unsigned)(ngram + ndt)), dim3(64), s, d, bc, bstr,
+                  gram, ngram, (const T*)dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot);
 }
 
 }  // namespace ssd

@@ -148,6 +148,10 @@ size_t ssd_workspace_bytes(const ssd_problem* problem, const ssd_segment* segs, 
     if (check_problem(problem, &d) != SSD_OK) return 0;
     if (check_segments(segs, nseg, &d, &t) != SSD_OK) return 0;
     if (kind == SSD_WS_FORWARD) return fwd_ws_layout(d, t, problem->act_dtype).total;
+    if (kind == SSD_WS_FORWARD_CONV) {
+        if (d.W != FUSED_CONV_W) return 0;
+        return fwd_ws_layout(d, t, problem->act_dtype, true).total;
+    }
     if (kind == SSD_WS_BACKWARD) {
         if (!bwd_supported(d.P, d.N, d.Q, problem->act_dtype)) return 0;
         return bwd_ws_layout(d, problem->act_dtype).total;
@@ -322,6 +326,47 @@ int ssd_segment_output_fused(const ssd_problem* problem, const ssd_segment* segs
         return SSD_ERR_ALIGN;
     return hip_status(launch_segment_output_fused(d, t, problem->act_dtype, xBC_conv, D, seq_idx,
                                                   S_in, ws, y, (hipStream_t)stream));
+}
+
+int ssd_conv_segment_states(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                            const void* xBC, const float* conv_w, const void* dt_raw,
+                            const float* dt_bias, const float* A_log, const int32_t* seq_idx,
+                            float* summary, void* ws, size_t ws_bytes, void* stream) {
+    Dims d;
+    SegTab t;
+    int rc = check_problem(problem, &d);
+    if (rc) return rc;
+    if ((rc = check_segments(segs, nseg, &d, &t))) return rc;
+    if (d.W != FUSED_CONV_W) return SSD_ERR_UNSUPPORTED;
+    if (!xBC || !conv_w || !dt_raw || !dt_bias || !A_log || !summary) return SSD_ERR_NULL;
+    if (!ws) return SSD_ERR_WORKSPACE;
+    if (ws_bytes < fwd_ws_layout(d, t, problem->act_dtype, true).total) return SSD_ERR_WORKSPACE;
+    if (!aligned16(xBC) || !aligned16(conv_w) || !aligned16(dt_raw) || !aligned16(dt_bias) ||
+        !aligned16(A_log) || !aligned16(seq_idx) || !aligned16(summary) || !aligned16(ws))
+        return SSD_ERR_ALIGN;
+    return hip_status(launch_conv_segment_states(d, t, problem->act_dtype, xBC, conv_w, dt_raw,
+                                                 dt_bias, A_log, seq_idx, summary, ws,
+                                                 (hipStream_t)stream));
+}
+
+int ssd_conv_segment_output(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,
+                            const void* xBC, const float* conv_w, const float* D,
+                            const int32_t* seq_idx, const float* S_in, void* ws,
+                            size_t ws_bytes, void* y, void* stream) {
+    Dims d;
+    SegTab t;
+    int rc = check_problem(problem, &d);
+    if (rc) return rc;
+    if ((rc = check_segments(segs, nseg, &d, &t))) return rc;
+    if (d.W != FUSED_CONV_W) return SSD_ERR_UNSUPPORTED;
+    if (!xBC || !conv_w || !D || !S_in || !y) return SSD_ERR_NULL;
+    if (!ws) return SSD_ERR_WORKSPACE;
+    if (ws_bytes < fwd_ws_layout(d, t, problem->act_dtype, true).total) return SSD_ERR_WORKSPACE;
+    if (!aligned16(xBC) || !aligned16(conv_w) || !aligned16(D) || !aligned16(seq_idx) ||
+        !aligned16(S_in) || !aligned16(ws) || !aligned16(y))
+        return SSD_ERR_ALIGN;
+    return hip_status(launch_conv_segment_output(d, t, problem->act_dtype, xBC, conv_w, D,
+                                                 seq_idx, S_in, ws, y, (hipStream_t)stream));
 }
 
 int ssd_segment_bwd_summary(const ssd_problem* problem, const ssd_segment* segs, int32_t nseg,

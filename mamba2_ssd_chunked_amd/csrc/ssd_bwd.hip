@@ -554,9 +554,9 @@ static hipError_t bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a
     T* xc = (T*)(ws + L.xc);
     SSD_TRY(launch_conv1d_fwd(d, t, act, a.xBC, a.conv_w, a.seq, xc, s));
     // the transposed Gram tiles and dt prep in one launch
-    SSD_TRY(launch_gram_dt<T, N, true>(d, xc, (T*)(ws + L.gramt), a.dt_raw, a.dt_bias, a.A_log,
-                                       a.seq, (float*)(ws + L.dt), (float*)(ws + L.cs),
-                                       (float*)(ws + L.ctot), s));
+    SSD_TRY(launch_gram_dt<T, N, true>(d, xc + (int64_t)d.H * P, (int64_t)d.C, (T*)(ws + L.gramt),
+                                       a.dt_raw, a.dt_bias, a.A_log, a.seq, (float*)(ws + L.dt),
+                                       (float*)(ws + L.cs), (float*)(ws + L.ctot), s));
     // the reverse walk from a zero final gradient: dL/dS_in of each segment's own
     // outputs and its block decay
     const WalkArgs<T> wa = {(const T*)xc, (const T*)a.dy, (const float*)(ws + L.dt),

@@ -27,6 +27,7 @@
 //                  callers that keep y_zero.
 #include <type_traits>
 
+#include "conv_fused.h"
 #include "dt_prep.h"
 #include "gram.h"
 #include "ssd_internal.h"
@@ -98,8 +99,10 @@ __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ d
 //                memory and x and C are read once.  D is folded into the
 //                diagonal of the weight matrix (j = i), so D x comes out of the
 //                same MFMA.
-template <typename T, int P, int N, int Q, bool FINAL>
+template <typename T, int P, int N, int Q, bool FINAL, bool XC>
 __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims d, SegTab tab, const T* __restrict__ xc,
+                                                        const T* __restrict__ bc, int64_t bstr,
+                                                        const float* __restrict__ conv_w,
                                                         const T* __restrict__ gram,
                                                         const float* __restrict__ dt_ws,
                                                         const float* __restrict__ cs_ws,
@@ -162,7 +165,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
     const int seq_span = (seq && jsp > 0) ? seq[rb + (int64_t)cspan0 * Q - 1] : seq_ref;
     const bool split = seq && seq[rb + t0] != seq[rb + t0 + Q - 1];
     const int64_t xoff = (int64_t)h * P;
-    const int64_t coff = (int64_t)d.H * P + (int64_t)d.G * N + (int64_t)g * N;
+    const int64_t coff = (int64_t)d.G * N + (int64_t)g * N;  // C of group g in a bc row
     const int64_t hl = ((int64_t)b * d.H + h) * d.L + t0;
     const bool inter = FINAL || !first;
     const int a0 = wave, a1 = QT - 1 - wave;
@@ -174,7 +177,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
     i0[0] = a0 * 16;
     i0[1] = a1 * 16;
     auto cload = [&](int it, int kn) {
-        return M::load(xc + (rb + t0 + i0[it] + lr) * d.C + coff + kn * KS + SL * lg);
+        return M::load(bc + (rb + t0 + i0[it] + lr) * bstr + coff + kn * KS + SL * lg);
     };
     Frag cfc[2];
     if (inter) {
@@ -182,13 +185,24 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
         cfc[1] = cload(1, 0);
     }
     constexpr int V_X = (Q * (P / VEC) + NTH - 1) / NTH;
-    vt rx[V_X];
+    // XC (conv-fused): xc is the raw input; the thread owns column vector xpv of
+    // rows xj0 .. xj0 + V_X - 1 and holds the conv window under them
+    constexpr int CW = FUSED_CONV_W, RV = P / VEC;
+    constexpr int NRW = XC ? V_X + CW - 1 : 1;
+    static_assert(!XC || (FINAL && Q * RV % NTH == 0), "conv-fused output pass");
+    const int xpv = threadIdx.x % RV, xj0 = (threadIdx.x / RV) * V_X;
+    ConvWindow<T, VEC, NRW> xw;
+    vt rx[XC ? 1 : V_X];
+    if constexpr (XC) {
+        load_window<T, VEC, CW, NRW>(xw, xc, seq, tab, k, rb, t0 + xj0, d.C, xoff + xpv * VEC);
+    } else {
 #pragma unroll
-    for (int q = 0; q < V_X; ++q) {
-        const int idx = threadIdx.x + q * NTH;
-        if (idx < Q * (P / VEC)) {
-            const int j = idx / (P / VEC), pv = idx % (P / VEC);
-            rx[q] = *(const vt*)(xc + (rb + t0 + j) * d.C + xoff + pv * VEC);
+        for (int q = 0; q < V_X; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (idx < Q * (P / VEC)) {
+                const int j = idx / (P / VEC), pv = idx % (P / VEC);
+                rx[q] = *(const vt*)(xc + (rb + t0 + j) * d.C + xoff + pv * VEC);
+            }
         }
     }
     constexpr int V_H = (P * (N / VEC) + NTH - 1) / NTH;
@@ -232,10 +246,23 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
         for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
         if (lane == 0) s_eps = (seq_prev == seq_span) ? expf(part) : 0.f;
     }
+    if constexpr (XC) {
+        float taps[VEC][CW];
+        load_taps<VEC, CW>(taps, conv_w, xoff + xpv * VEC);
+        auto rows = [&](auto masked_tag) {
+            constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-    for (int q = 0; q < V_X; ++q) {
-        const int idx = threadIdx.x + q * NTH;
-        if (idx < Q * (P / VEC)) *(vt*)&sX[(idx / (P / VEC)) * XR + (idx % (P / VEC)) * VEC] = rx[q];
+            for (int q = 0; q < V_X; ++q)
+                *(vt*)&sX[(xj0 + q) * XR + xpv * VEC] = conv_silu<T, VEC, CW, NRW, MASKED>(xw, q, taps);
+        };
+        if (window_clean(xw)) rows(std::false_type{});
+        else rows(std::true_type{});
+    } else {
+#pragma unroll
+        for (int q = 0; q < V_X; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (idx < Q * (P / VEC)) *(vt*)&sX[(idx / (P / VEC)) * XR + (idx % (P / VEC)) * VEC] = rx[q];
+        }
     }
     __syncthreads();
     // The factored decay needs every tile's span cs(first) - cs(last) small
@@ -419,7 +446,6 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
                 t4{(T)acc[it][pt][0], (T)acc[it][pt][1], (T)acc[it][pt][2], (T)acc[it][pt][3]};
     }
     __syncthreads();
-    constexpr int RV = P / VEC;  // 16-byte vectors per token row
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const T* st = sY + (wave * 2 + it) * 16 * YP;
@@ -533,54 +559,87 @@ static bool shape_ok(int Q) {
     return false;
 }
 
+// The B and C channels of the pass's inputs: bc + m * bstr for token row m.
+template <typename T>
+struct BCSrc {
+    const T* bc;
+    int64_t bstr;
+};
+
 template <typename T, int P, int N, int Q, bool FINAL>
-static hipError_t launch_chunk_y(const Dims& d, const SegTab& t, const T* xc, const T* gram,
-                                 const float* dtw, const float* csw, const float* ctot,
-                                 const int32_t* seq, const T* hst, const SpanPlan& sp,
-                                 const float* S_st, const float* D, float* y_zero, T* y,
-                                 hipStream_t s) {
+static hipError_t launch_chunk_y(const Dims& d, const SegTab& t, const T* xc, BCSrc<T> bc,
+                                 const float* conv_w, const T* gram, const float* dtw,
+                                 const float* csw, const float* ctot, const int32_t* seq,
+                                 const T* hst, const SpanPlan& sp, const float* S_st,
+                                 const float* D, float* y_zero, T* y, hipStream_t s) {
     if constexpr (chunk_y_lds<T, P, N, Q>() <= LDS_LIMIT) {
-        return launch(k_chunk_y<T, P, N, Q, FINAL>, chunk_head_grid(d), dim3(Q / 32 * 64), s, d, t,
-                      xc, gram, dtw, csw, ctot, seq, hst, sp, S_st, D, y_zero, y);
+        if constexpr (FINAL) {
+            if (conv_w)
+                return launch(k_chunk_y<T, P, N, Q, true, true>, chunk_head_grid(d),
+                              dim3(Q / 32 * 64), s, d, t, xc, bc.bc, bc.bstr, conv_w, gram, dtw,
+                              csw, ctot, seq, hst, sp, S_st, D, y_zero, y);
+        }
+        if (conv_w) return hipErrorInvalidValue;
+        return launch(k_chunk_y<T, P, N, Q, FINAL, false>, chunk_head_grid(d), dim3(Q / 32 * 64),
+                      s, d, t, xc, bc.bc, bc.bstr, conv_w, gram, dtw, csw, ctot, seq, hst, sp,
+                      S_st, D, y_zero, y);
     }
     return hipErrorInvalidValue;
 }
 
+// conv_w null: xc_ is the conv output.  Otherwise (conv-fused) xc_ is the raw
+// input: the B and C channels are convolved into the workspace first, and the
+// walk convolves the x channels as it reads them.
 template <typename T, int P, int N>
 static hipError_t segment_states_t(const Dims& d, const SegTab& t, const void* xc_,
-                                   const void* dt_raw, const float* dt_bias, const float* A_log,
-                                   const int32_t* seq, float* summary, void* ws, hipStream_t s) {
+                                   const float* conv_w, const void* dt_raw, const float* dt_bias,
+                                   const float* A_log, const int32_t* seq, float* summary,
+                                   void* ws, hipStream_t s) {
     const T* xc = (const T*)xc_;
-    const FwdWs L = fwd_ws_layout(d, t, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
+    constexpr int act = std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32;
+    const bool xconv = conv_w != nullptr;
+    const FwdWs L = fwd_ws_layout(d, t, act, xconv);
     char* w = (char*)ws;
     float* dtw = (float*)(w + L.dt);
     float* csw = (float*)(w + L.cs);
     float* ctot = (float*)(w + L.ctot);
     T* hst = (T*)(w + L.hst);
+    BCSrc<T> bc = {xc + (int64_t)d.H * P, (int64_t)d.C};
+    if (xconv) {
+        bc = {(const T*)(w + L.bc), 2LL * d.G * N};
+        SSD_TRY(launch_conv1d_channels(d, t, act, xc, conv_w, seq, d.H * P, 2 * d.G * N,
+                                       bc.bstr, w + L.bc, s));
+    }
     // the group Gram tiles the output pass reads and dt prep share one launch
     // (independent inputs); the walk then needs dt and the cumulative sums
-    SSD_TRY(launch_gram_dt<T, N>(d, xc, (T*)(w + L.gram), dt_raw, dt_bias, A_log, seq, dtw, csw,
-                                 ctot, s));
+    SSD_TRY(launch_gram_dt<T, N>(d, bc.bc, bc.bstr, (T*)(w + L.gram), dt_raw, dt_bias, A_log,
+                                 seq, dtw, csw, ctot, s));
     const SpanPlan sp = span_plan(d, t, true);
-    if (plan_trivial(sp, t)) {
-        const WalkArgs<T> wa = {xc, nullptr, dtw, csw, seq, nullptr, hst, summary, sp};
-        return launch_state_walk<T, P, N, false>(d, t, wa, s);
-    }
+    const bool trivial = plan_trivial(sp, t);
     // long segments: walk their spans, then compose the span summaries
-    float* spsum = (float*)(w + L.spsum);
-    const WalkArgs<T> wa = {xc, nullptr, dtw, csw, seq, nullptr, hst, spsum, sp};
-    SSD_TRY(launch_state_walk<T, P, N, false>(d, t, wa, s));
-    return launch_span_combine(d, sp, spsum, summary, s);
+    const WalkArgs<T> wa = {xc,  nullptr, dtw, csw, seq, nullptr, hst,
+                            trivial ? summary : (float*)(w + L.spsum),
+                            sp,  bc.bc,   bc.bstr, conv_w};
+    if (xconv) SSD_TRY(launch_state_walk<T, P, N, false, true>(d, t, wa, s));
+    else SSD_TRY(launch_state_walk<T, P, N, false>(d, t, wa, s));
+    if (trivial) return hipSuccess;
+    return launch_span_combine(d, sp, (const float*)(w + L.spsum), summary, s);
 }
 
 // y_zero (FINAL = false) or the corrected y (FINAL = true), from the workspace
 // that segment_states_t filled (decays, entering states, Gram tiles).
+// conv_w as for segment_states_t (conv-fused: FINAL only).
 template <typename T, int P, int N, bool FINAL>
 static hipError_t segment_output_t(const Dims& d, const SegTab& t, const void* xc_,
-                                   const int32_t* seq, void* ws, const float* S_in,
-                                   const float* D, float* y_zero, void* y, hipStream_t s) {
+                                   const float* conv_w, const int32_t* seq, void* ws,
+                                   const float* S_in, const float* D, float* y_zero, void* y,
+                                   hipStream_t s) {
     const T* xc = (const T*)xc_;
-    const FwdWs L = fwd_ws_layout(d, t, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32);
+    const bool xconv = conv_w != nullptr;
+    const FwdWs L =
+        fwd_ws_layout(d, t, std::is_same<T, bf16>::value ? SSD_BF16 : SSD_F32, xconv);
+    const BCSrc<T> bc = xconv ? BCSrc<T>{(const T*)((const char*)ws + L.bc), 2LL * d.G * N}
+                              : BCSrc<T>{xc + (int64_t)d.H * P, (int64_t)d.C};
     char* w = (char*)ws;
     const float* dtw = (const float*)(w + L.dt);
     const float* csw = (const float*)(w + L.cs);
@@ -598,14 +657,14 @@ static hipError_t segment_output_t(const Dims& d, const SegTab& t, const void* x
     }
     switch (d.Q) {
         case 64:
-            return launch_chunk_y<T, P, N, 64, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst, sp,
-                                                      S_st, D, y_zero, yo, s);
+            return launch_chunk_y<T, P, N, 64, FINAL>(d, t, xc, bc, conv_w, gram, dtw, csw, ctot,
+                                                      seq, hst, sp, S_st, D, y_zero, yo, s);
         case 128:
-            return launch_chunk_y<T, P, N, 128, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst, sp,
-                                                       S_st, D, y_zero, yo, s);
+            return launch_chunk_y<T, P, N, 128, FINAL>(d, t, xc, bc, conv_w, gram, dtw, csw, ctot,
+                                                       seq, hst, sp, S_st, D, y_zero, yo, s);
         case 256:
-            return launch_chunk_y<T, P, N, 256, FINAL>(d, t, xc, gram, dtw, csw, ctot, seq, hst, sp,
-                                                       S_st, D, y_zero, yo, s);
+            return launch_chunk_y<T, P, N, 256, FINAL>(d, t, xc, bc, conv_w, gram, dtw, csw, ctot,
+                                                       seq, hst, sp, S_st, D, y_zero, yo, s);
         default:
             return hipErrorInvalidValue;
     }
@@ -659,7 +718,8 @@ hipError_t launch_segment_states(const Dims& d, const SegTab& t, int act, const 
                                  const int32_t* seq, float* summary, void* ws, hipStream_t s) {
 #define X(p, n)                                                                               \
     if (d.P == p && d.N == n) {                                                               \
-        return segment_states_t<T, p, n>(d, t, xBC_conv, dt_raw, dt_bias, A_log, seq, summary, ws, s); \
+        return segment_states_t<T, p, n>(d, t, xBC_conv, nullptr, dt_raw, dt_bias, A_log, seq, \
+                                         summary, ws, s);                                      \
     }
     if (act == SSD_F32) {
         typedef float T;
@@ -676,8 +736,8 @@ hipError_t launch_segment_output(const Dims& d, const SegTab& t, int act, const 
                                  const int32_t* seq, void* ws, float* y_zero, hipStream_t s) {
 #define X(p, n)                                                                                 \
     if (d.P == p && d.N == n) {                                                                 \
-        return segment_output_t<T, p, n, false>(d, t, xBC_conv, seq, ws, nullptr, nullptr, y_zero, \
-                                                nullptr, s);                                  \
+        return segment_output_t<T, p, n, false>(d, t, xBC_conv, nullptr, seq, ws, nullptr,     \
+                                                nullptr, y_zero, nullptr, s);                  \
     }
     if (act == SSD_F32) {
         typedef float T;
@@ -695,7 +755,50 @@ hipError_t launch_segment_output_fused(const Dims& d, const SegTab& t, int act,
                                        const float* S_in, void* ws, void* y, hipStream_t s) {
 #define X(p, n)                                                                                 \
     if (d.P == p && d.N == n) {                                                                 \
-        return segment_output_t<T, p, n, true>(d, t, xBC_conv, seq, ws, S_in, D, nullptr, y, s); \
+        return segment_output_t<T, p, n, true>(d, t, xBC_conv, nullptr, seq, ws, S_in, D,     \
+                                               nullptr, y, s);                                 \
+    }
+    if (act == SSD_F32) {
+        typedef float T;
+        SSD_F32_SHAPES(X)
+    } else {
+        typedef bf16 T;
+        SSD_BF16_SHAPES(X)
+    }
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_conv_segment_states(const Dims& d, const SegTab& t, int act, const void* xBC,
+                                      const float* conv_w, const void* dt_raw,
+                                      const float* dt_bias, const float* A_log,
+                                      const int32_t* seq, float* summary, void* ws,
+                                      hipStream_t s) {
+    if (!conv_w || d.W != FUSED_CONV_W) return hipErrorInvalidValue;
+#define X(p, n)                                                                           \
+    if (d.P == p && d.N == n) {                                                           \
+        return segment_states_t<T, p, n>(d, t, xBC, conv_w, dt_raw, dt_bias, A_log, seq,   \
+                                         summary, ws, s);                                  \
+    }
+    if (act == SSD_F32) {
+        typedef float T;
+        SSD_F32_SHAPES(X)
+    } else {
+        typedef bf16 T;
+        SSD_BF16_SHAPES(X)
+    }
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_conv_segment_output(const Dims& d, const SegTab& t, int act, const void* xBC,
+                                      const float* conv_w, const float* D, const int32_t* seq,
+                                      const float* S_in, void* ws, void* y, hipStream_t s) {
+    if (!conv_w || d.W != FUSED_CONV_W) return hipErrorInvalidValue;
+#define X(p, n)                                                                               \
+    if (d.P == p && d.N == n) {                                                               \
+        return segment_output_t<T, p, n, true>(d, t, xBC, conv_w, seq, ws, S_in, D, nullptr,   \
+                                               y, s);                                          \
     }
     if (act == SSD_F32) {
         typedef float T;

@@ -84,6 +84,9 @@ __device__ __forceinline__ float to_f(T v) { return (float)v; }
 constexpr int CONV_VEC = 4;   // channels per thread
 constexpr int CONV_TPT = 16;  // tokens per thread
 constexpr int CONV_TT = 4 * CONV_TPT;  // tokens per workgroup (one group per wave)
+// The conv width the conv-fused forward kernels are compiled for (Mamba2's
+// d_conv).
+constexpr int FUSED_CONV_W = 4;
 
 template <typename T>
 struct Vec4 {
@@ -289,9 +292,25 @@ hipError_t scratch_address(void** out);
 // the launch error.
 hipError_t launch_conv1d_fwd(const Dims& d, const SegTab& t, int act, const void* xBC,
                              const float* w, const int32_t* seq, void* out, hipStream_t s);
+// conv + SiLU of channels c0 .. c0 + nc - 1 only, into columns 0 .. nc - 1 of
+// `out` (token rows ostr elements apart)
+hipError_t launch_conv1d_channels(const Dims& d, const SegTab& t, int act, const void* xBC,
+                                  const float* w, const int32_t* seq, int c0, int nc,
+                                  int64_t ostr, void* out, hipStream_t s);
 hipError_t launch_segment_states(const Dims& d, const SegTab& t, int act, const void* xBC_conv,
                                  const void* dt_raw, const float* dt_bias, const float* A_log,
                                  const int32_t* seq, float* summary, void* ws, hipStream_t s);
+// The conv-fused forward: xBC is the raw input, conv_w its [C][W] taps; the B
+// and C channels are convolved into the workspace, the x channels are
+// recomputed by the walk and the output pass.
+hipError_t launch_conv_segment_states(const Dims& d, const SegTab& t, int act, const void* xBC,
+                                      const float* conv_w, const void* dt_raw,
+                                      const float* dt_bias, const float* A_log,
+                                      const int32_t* seq, float* summary, void* ws,
+                                      hipStream_t s);
+hipError_t launch_conv_segment_output(const Dims& d, const SegTab& t, int act, const void* xBC,
+                                      const float* conv_w, const float* D, const int32_t* seq,
+                                      const float* S_in, void* ws, void* y, hipStream_t s);
 hipError_t launch_segment_output(const Dims& d, const SegTab& t, int act, const void* xBC_conv,
                                  const int32_t* seq, void* ws, float* y_zero, hipStream_t s);
 hipError_t launch_segment_output_fused(const Dims& d, const SegTab& t, int act,
@@ -338,10 +357,12 @@ bool chunk_supported(int P, int N, int Q, int act);
 // a_span, the summary layout over spans) and the state entering every span
 // (filled by the output calls).
 struct FwdWs {
-    size_t dt, cs, ctot, hst, gram, spsum, spst, total;
+    size_t dt, cs, ctot, hst, gram, spsum, spst, bc, total;
 };
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline FwdWs fwd_ws_layout(const Dims& d, const SegTab& t, int act) {
+// The conv-fused forward (xconv) adds the convolved B and C channels,
+// [b][L][2 G N] in the activation type, at `bc`.
+inline FwdWs fwd_ws_layout(const Dims& d, const SegTab& t, int act, bool xconv = false) {
     FwdWs w;
     const size_t esz = act == SSD_BF16 ? 2 : 4;
     const size_t bhl = (size_t)d.batch * d.H * d.L;
@@ -361,6 +382,8 @@ inline FwdWs fwd_ws_layout(const Dims& d, const SegTab& t, int act) {
         w.spst = align256(w.spsum + (size_t)sp.n * bh * ((size_t)d.P * d.N + 1) * 4);
         w.total = align256(w.spst + (size_t)sp.n * bh * d.P * d.N * 4);
     }
+    w.bc = w.total;
+    if (xconv) w.total = align256(w.bc + (size_t)d.batch * d.L * 2 * d.G * d.N * esz);
     return w;
 }
 

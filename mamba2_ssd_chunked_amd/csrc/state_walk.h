@@ -38,6 +38,7 @@
 
 #include <type_traits>
 
+#include "conv_fused.h"
 #include "ssd_internal.h"
 #include "xt.h"
 
@@ -56,6 +57,13 @@ struct WalkArgs {
     float* summary;        // final value and block decay per span, or null
     SpanPlan sp;           // the runs of chunks walked (spans; one per segment
                            // unless the forward walk splits segments)
+    // B and C channels of token row m at bc + m * bstr (B of group g at g N, C
+    // at (G + g) N); null: inside xc's rows
+    const T* bc = nullptr;
+    int64_t bstr = 0;
+    // conv-fused forward walk (XC): xc is the raw input and the x channels are
+    // convolved here with these [C][W] taps
+    const float* conv_w = nullptr;
 };
 
 constexpr int WALK_KT = 64;  // tokens per slice
@@ -67,8 +75,10 @@ constexpr int walk_lds() {
 }
 
 // One walk block: block `blk` of `nblk` (the XCD-aware item mapping is over
-// this range), its slice buffers at `lds`.
-template <typename T, int P, int N, bool BWD, bool SEQ, int HW>
+// this range), its slice buffers at `lds`.  XC: the conv-fused forward walk,
+// whose threads each own one column vector of VX consecutive x rows of a slice
+// and the conv window under them (conv_fused.h).
+template <typename T, int P, int N, bool BWD, bool SEQ, int HW, bool XC = false>
 __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, const WalkArgs<T>& wa,
                                            T* lds, int64_t blk, int64_t nblk) {
     const T* __restrict__ xc = wa.xc;
@@ -94,6 +104,9 @@ __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, con
     // and forces full waits for the outstanding loads at their joins)
     constexpr bool XFULL = KT * (P / VEC) % HTH == 0, BFULL = KT * (N / VEC) % NTH == 0;
     constexpr bool NFULL = NTT % 4 == 0;
+    constexpr int CW = FUSED_CONV_W, RV = P / VEC;
+    constexpr int NRW = XC ? VX + CW - 1 : 1;  // conv window rows (XC)
+    static_assert(!XC || (!BWD && XFULL), "the conv-fused walk is the forward walk");
     auto sX = reinterpret_cast<T(*)[HW][KT * XR]>(lds);
     auto sB = reinterpret_cast<T(*)[KT * BR]>(lds + 2 * HW * KT * XR);
     typedef T vt __attribute__((ext_vector_type(VEC)));
@@ -135,12 +148,19 @@ __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, con
     const float* csp = cs_ws + ((int64_t)b * d.H + h) * d.L;
     const int64_t astr = BWD ? (int64_t)d.H * P : (int64_t)d.C;
     const T* arow = (BWD ? dy + rb * astr : xc + rb * astr) + (int64_t)h * P;
-    const T* brow = xc + rb * d.C + (int64_t)d.H * P + (BWD ? (int64_t)d.G * N : 0) + (int64_t)g * N;
+    const T* bsrc = wa.bc ? wa.bc : xc + (int64_t)d.H * P;
+    const int64_t bstr = wa.bc ? wa.bstr : (int64_t)d.C;
+    const T* brow = bsrc + rb * bstr + (BWD ? (int64_t)d.G * N : 0) + (int64_t)g * N;
+    // XC: the thread's column vector and first row of a slice, and the taps
+    const int xpv = ht % RV, xj0 = (ht / RV) * VX;
+    float taps[XC ? VEC : 1][CW];
+    if constexpr (XC) load_taps<VEC, CW>(taps, wa.conv_w, (int64_t)h * P + xpv * VEC);
     auto chunk_of = [&](int si) { return BWD ? nc - 1 - si / spc : si / spc; };
 
     // ---- one slice in registers, with the values of its chunk
     struct Slice {
-        vt x[VX], b[VB];
+        vt x[XC ? 1 : VX], b[VB];
+        ConvWindow<T, VEC, NRW> win;  // XC: raw x rows xj0 - (W-1) .. xj0 + VX - 1
         float cs[VX], dt[VX];
         int sq[VX];
         float cse;       // cumulative log decay at the chunk's last token
@@ -157,15 +177,26 @@ __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, con
         const int64_t ptok = c > 0 ? t0 - 1 : (pred >= 0 ? pred : s0);
         r.seqe = SEQ ? seq[rb + t0 + Q - 1] : 0;
         r.seqr = SEQ ? seq[rb + ptok] : 0;
+        if constexpr (XC) {
+            load_window<T, VEC, CW, NRW>(r.win, xc, SEQ ? seq : nullptr, tab, k, rb, tb + xj0,
+                                         d.C, (int64_t)h * P + xpv * VEC);
 #pragma unroll
-        for (int q = 0; q < VX; ++q) {
-            const int idx = ht + q * HTH;
-            if (XFULL || idx < KT * (P / VEC)) {
-                const int jj = idx / (P / VEC), pv = idx % (P / VEC);
-                r.x[q] = *(const vt*)(arow + (tb + jj) * astr + pv * VEC);
-                r.cs[q] = csp[tb + jj];
-                r.dt[q] = BWD ? 0.f : dtp[tb + jj];
-                r.sq[q] = SEQ ? seq[rb + tb + jj] : 0;
+            for (int q = 0; q < VX; ++q) {
+                r.cs[q] = csp[tb + xj0 + q];
+                r.dt[q] = dtp[tb + xj0 + q];
+                r.sq[q] = r.win.sq[q + CW - 1];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < VX; ++q) {
+                const int idx = ht + q * HTH;
+                if (XFULL || idx < KT * (P / VEC)) {
+                    const int jj = idx / (P / VEC), pv = idx % (P / VEC);
+                    r.x[q] = *(const vt*)(arow + (tb + jj) * astr + pv * VEC);
+                    r.cs[q] = csp[tb + jj];
+                    r.dt[q] = BWD ? 0.f : dtp[tb + jj];
+                    r.sq[q] = SEQ ? seq[rb + tb + jj] : 0;
+                }
             }
         }
 #pragma unroll
@@ -173,7 +204,7 @@ __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, con
             const int idx = threadIdx.x + q * NTH;
             if (BFULL || idx < KT * (N / VEC)) {
                 const int jj = idx / (N / VEC), nv = idx % (N / VEC);
-                r.b[q] = *(const vt*)(brow + (tb + jj) * d.C + nv * VEC);
+                r.b[q] = *(const vt*)(brow + (tb + jj) * bstr + nv * VEC);
             }
         }
     };
@@ -182,8 +213,24 @@ __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, con
     // entering state's (backward)
     auto stash = [&](const Slice& r, int u) {
         const int sref = BWD ? r.seqr : r.seqe;
+        if constexpr (XC) {
+            auto rows = [&](auto masked_tag) {
+                constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-        for (int q = 0; q < VX; ++q) {
+                for (int q = 0; q < VX; ++q) {
+                    const float w = r.sq[q] != sref ? 0.f : __expf(r.cse - r.cs[q]) * r.dt[q];
+                    const vt xv = conv_silu<T, VEC, CW, NRW, MASKED>(r.win, q, taps);
+                    vt v;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) v[e] = (T)((float)xv[e] * w);
+                    *(vt*)&sX[u][hs][(xj0 + q) * XR + xpv * VEC] = v;
+                }
+            };
+            if (window_clean(r.win)) rows(std::false_type{});
+            else rows(std::true_type{});
+        }
+#pragma unroll
+        for (int q = 0; q < (XC ? 0 : VX); ++q) {
             const int idx = ht + q * HTH;
             if (XFULL || idx < KT * (P / VEC)) {
                 const int jj = idx / (P / VEC), pv = idx % (P / VEC);
@@ -317,12 +364,13 @@ __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, con
 }
 
 // Two heads per block: four waves per SIMD, so that two blocks (of one walk or
-// of the two walks of k_state_walk_pair) share a CU.
-template <typename T, int P, int N, bool BWD, bool SEQ, int HW>
-__global__ void __launch_bounds__(256 * HW, HW == 2 ? 4 : 1) k_state_walk(Dims d, SegTab tab,
+// of the two walks of k_state_walk_pair) share a CU.  The conv-fused walk (XC)
+// holds its conv windows and taps in registers and runs one block per CU.
+template <typename T, int P, int N, bool BWD, bool SEQ, int HW, bool XC = false>
+__global__ void __launch_bounds__(256 * HW, HW == 2 ? (XC ? 2 : 4) : 1) k_state_walk(Dims d, SegTab tab,
                                                                          WalkArgs<T> wa) {
     __shared__ __attribute__((aligned(16))) T lds[walk_lds<T, P, N, HW>()];
-    walk_block<T, P, N, BWD, SEQ, HW>(d, tab, wa, lds, blockIdx.x, gridDim.x);
+    walk_block<T, P, N, BWD, SEQ, HW, XC>(d, tab, wa, lds, blockIdx.x, gridDim.x);
 }
 
 // The reverse walk (blocks 0 .. n-1) and the forward walk (n .. 2n-1) in one
@@ -347,18 +395,19 @@ inline int walk_heads(const Dims& d) {
     return (std::is_same<T, bf16>::value && d.hpg % 2 == 0) ? 2 : 1;
 }
 
-template <typename T, int P, int N, bool BWD>
+template <typename T, int P, int N, bool BWD, bool XC = false>
 inline hipError_t launch_state_walk(const Dims& d, const SegTab& t, const WalkArgs<T>& wa,
                                     hipStream_t s) {
     const int hw = walk_heads<T>(d);
     const dim3 grid((unsigned)((int64_t)(d.H / hw) * wa.sp.n * d.batch));
     const dim3 block(256 * hw);
+    if (XC && (!wa.conv_w || d.W != FUSED_CONV_W)) return hipErrorInvalidValue;
     if (hw == 2) {
-        if (wa.seq) return launch(k_state_walk<T, P, N, BWD, true, 2>, grid, block, s, d, t, wa);
-        return launch(k_state_walk<T, P, N, BWD, false, 2>, grid, block, s, d, t, wa);
+        if (wa.seq) return launch(k_state_walk<T, P, N, BWD, true, 2, XC>, grid, block, s, d, t, wa);
+        return launch(k_state_walk<T, P, N, BWD, false, 2, XC>, grid, block, s, d, t, wa);
     }
-    if (wa.seq) return launch(k_state_walk<T, P, N, BWD, true, 1>, grid, block, s, d, t, wa);
-    return launch(k_state_walk<T, P, N, BWD, false, 1>, grid, block, s, d, t, wa);
+    if (wa.seq) return launch(k_state_walk<T, P, N, BWD, true, 1, XC>, grid, block, s, d, t, wa);
+    return launch(k_state_walk<T, P, N, BWD, false, 1, XC>, grid, block, s, d, t, wa);
 }
 
 // The reverse and the forward walk of the backward pass in one launch.

@@ -14,7 +14,8 @@ from typing import List, Optional, Sequence, Tuple
 import torch
 
 from . import _lib
-from ._lib import SSD_BF16, SSD_F32, SSD_WS_BACKWARD, SSD_WS_FORWARD, Problem, SSDError
+from ._lib import (SSD_BF16, SSD_F32, SSD_WS_BACKWARD, SSD_WS_FORWARD, SSD_WS_FORWARD_CONV,
+                   Problem, SSDError)
 
 _TORCH_ACT = {SSD_F32: torch.float32, SSD_BF16: torch.bfloat16}
 
@@ -215,6 +216,39 @@ def ssd_segment_output_fused(problem: Problem, segs, xBC_conv, D, seq_idx, S_in,
         ctypes.byref(problem), s.ptr(), s.n, *args, ws_p, nbytes, y_p, _stream(stream)))
 
 
+def ssd_conv_segment_states(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log, seq_idx,
+                            summary, ws, stream=None):
+    s = _segs(segs)
+    act = _TORCH_ACT[problem.act_dtype]
+    BL, C, H = problem.batch * problem.seqlen, _conv_dim(problem), problem.nheads
+    f32 = torch.float32
+    args = (_need(xBC, "xBC", BL * C, act),
+            _need(conv_w, "conv_w", C * problem.conv_width, f32),
+            _need(dt_raw, "dt_raw", BL * H, act),
+            _need(dt_bias, "dt_bias", H, f32), _need(A_log, "A_log", H, f32),
+            _need(seq_idx, "seq_idx", BL, torch.int32, optional=True),
+            _need(summary, "summary", summary_numel(problem, s.n), f32))
+    ws_p, nbytes = _ws(ws)
+    _check("ssd_conv_segment_states", _lib.load().ssd_conv_segment_states(
+        ctypes.byref(problem), s.ptr(), s.n, *args, ws_p, nbytes, _stream(stream)))
+
+
+def ssd_conv_segment_output(problem: Problem, segs, xBC, conv_w, D, seq_idx, S_in, ws, y,
+                            stream=None):
+    s = _segs(segs)
+    act = _TORCH_ACT[problem.act_dtype]
+    BL, C, H, P = problem.batch * problem.seqlen, _conv_dim(problem), problem.nheads, problem.headdim
+    f32 = torch.float32
+    args = (_need(xBC, "xBC", BL * C, act),
+            _need(conv_w, "conv_w", C * problem.conv_width, f32), _need(D, "D", H, f32),
+            _need(seq_idx, "seq_idx", BL, torch.int32, optional=True),
+            _need(S_in, "S_in", s.n * problem.batch * H * P * problem.dstate, f32))
+    ws_p, nbytes = _ws(ws)
+    y_p = _need(y, "y", BL * H * P, act)
+    _check("ssd_conv_segment_output", _lib.load().ssd_conv_segment_output(
+        ctypes.byref(problem), s.ptr(), s.n, *args, ws_p, nbytes, y_p, _stream(stream)))
+
+
 def ssd_segment_bwd_summary(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log, seq_idx,
                             dy, summary, ws, stream=None):
     s = _segs(segs)
@@ -325,6 +359,8 @@ class ForwardBuffers:
         wsb = ssd_workspace_bytes(problem, s, SSD_WS_FORWARD)
         if wsb == 0:
             raise SSDError("ssd_workspace_bytes", -2)
+        # room for the conv-fused forward too, where it is compiled (width 4)
+        wsb = max(wsb, ssd_workspace_bytes(problem, s, SSD_WS_FORWARD_CONV))
         return ForwardBuffers(
             xBC_conv=torch.empty((b, L, C), dtype=act, device=device),
             y_zero=torch.empty((b, L, H, P), dtype=torch.float32, device=device),
@@ -337,9 +373,13 @@ class ForwardBuffers:
 
 def forward(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log, D, seq_idx=None,
             init=None, bufs: Optional[ForwardBuffers] = None, stream=None,
-            fused: bool = True, want_final: bool = False) -> ForwardBuffers:
+            fused: bool = True, want_final: bool = False,
+            conv_fused: bool = False) -> ForwardBuffers:
     """The forward path; returns the buffers.
 
+    conv_fused=True: conv-fused segment states -> boundary scan -> conv-fused
+                 output pass (the conv runs inside the two phases; y only,
+                 bufs.xBC_conv and bufs.y_zero are left untouched).
     fused=True : conv1d -> segment states -> boundary scan -> fused output pass
                  (y only; bufs.y_zero is left untouched).
     fused=False: conv1d -> segment-local SSD (states and y_zero) -> boundary scan
@@ -350,6 +390,14 @@ def forward(problem: Problem, segs, xBC, conv_w, dt_raw, dt_bias, A_log, D, seq_
     s = _segs(segs)
     if bufs is None:
         bufs = ForwardBuffers.allocate(problem, s, xBC.device)
+    if conv_fused:
+        ssd_conv_segment_states(problem, s, xBC, conv_w, dt_raw, dt_bias, A_log, seq_idx,
+                                bufs.summary, bufs.ws, stream)
+        ssd_boundary_scan(problem, s.n, bufs.summary, init, False, bufs.S_in,
+                          bufs.final_state if want_final else None, stream)
+        ssd_conv_segment_output(problem, s, xBC, conv_w, D, seq_idx, bufs.S_in, bufs.ws, bufs.y,
+                                stream)
+        return bufs
     ssd_conv1d_fwd(problem, s, xBC, conv_w, seq_idx, bufs.xBC_conv, stream)
     if fused:
         ssd_segment_states(problem, s, bufs.xBC_conv, dt_raw, dt_bias, A_log, seq_idx,

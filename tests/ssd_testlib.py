@@ -73,15 +73,17 @@ def device_inputs(wl, device="cuda"):
     return d
 
 
-def run_forward(wl, inputs=None, init=None, fused=True):
+def run_forward(wl, inputs=None, init=None, fused=True, conv_fused=False):
     """The forward path through the C ABI.  fused=True runs the states-first order
     (segment states, boundary scan, fused output pass); fused=False runs the
-    zero-state output (y_zero) and the separate correction pass."""
+    zero-state output (y_zero) and the separate correction pass; conv_fused=True
+    runs the states-first order with the conv inside the two phases."""
     import mamba2_ssd_chunked_amd as ssd
     p = problem_of(wl)
     x = inputs or device_inputs(wl)
     bufs = ssd.forward(p, wl.segments, x["xBC"], x["conv_w"], x["dt_raw"], x["dt_bias"],
-                       x["A_log"], x["D"], x["seq_idx"], init=init, fused=fused)
+                       x["A_log"], x["D"], x["seq_idx"], init=init, fused=fused,
+                       conv_fused=conv_fused)
     torch.cuda.synchronize()
     return p, x, bufs
 

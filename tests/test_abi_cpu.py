@@ -236,3 +236,27 @@ def test_forward_workspace_holds_span_regions_for_long_segments():
     assert ssd.ssd_workspace_bytes(p, segs) == want
     # the mixer shard's segments are walked whole: no span regions
     assert ssd.ssd_workspace_bytes(_p(), SEGS8) < want
+
+
+def test_conv_fused_forward_workspace_and_refusals():
+    """The conv-fused forward's workspace is the forward one plus the convolved B
+    and C channels ([b][L][2 G N] bf16); it is compiled for conv width 4 only, and
+    both of its calls refuse other widths, missing pointers and a short workspace
+    before launching anything."""
+    p = _p()
+    b, L, G, N = 2, 8192, 1, 128
+    base = ssd.ssd_workspace_bytes(p, SEGS8)
+    want = base + (b * L * 2 * G * N * 2 + 255) // 256 * 256
+    assert ssd.ssd_workspace_bytes(p, SEGS8, ssd.SSD_WS_FORWARD_CONV) == want
+    assert ssd.ssd_workspace_bytes(_p(conv_width=3), SEGS8, ssd.SSD_WS_FORWARD_CONV) == 0
+    lib = _lib.load()
+    s = ssd.Segments(SEGS8)
+    st = lambda pp, xbc=FAKE, ws_bytes=want: lib.ssd_conv_segment_states(
+        ctypes.byref(pp), s.ptr(), s.n, xbc, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws_bytes,
+        None)
+    out = lambda pp, w=FAKE, ws_bytes=want: lib.ssd_conv_segment_output(
+        ctypes.byref(pp), s.ptr(), s.n, FAKE, w, FAKE, None, FAKE, FAKE, ws_bytes, FAKE, None)
+    assert st(_p(conv_width=3)) == -3 and out(_p(conv_width=5)) == -3
+    assert st(p, xbc=None) == -1 and out(p, w=None) == -1
+    assert st(p, ws_bytes=want - 1) == -5 and out(p, ws_bytes=base) == -5
+    assert st(p, xbc=MISALIGNED) == -4
