@@ -41,6 +41,7 @@ int main(void) {
                     total += ssd_workspace_bytes(&q, s, 4, SSD_WS_FORWARD);
                     total += ssd_workspace_bytes(&q, s, 4, SSD_WS_BACKWARD);
                     total += ssd_workspace_bytes(&q, s, 1, SSD_WS_FORWARD); /* does not tile */
+                    total += ssd_workspace_bytes(&q, s, 4, SSD_WS_FORWARD_CONV);
                 }
     printf("workspace sum %zu\n", total);
     EXPECT(ssd_workspace_bytes(&p, segs, 8, SSD_WS_FORWARD) > 0, 1);
@@ -64,6 +65,13 @@ int main(void) {
            SSD_ERR_WORKSPACE);
     EXPECT(ssd_segment_output_fused(&p, segs, 8, F, NULL, NULL, Ff, F, 1 << 30, F, NULL),
            SSD_ERR_NULL);
+    EXPECT(ssd_conv_segment_states(&p, segs, 8, F, NULL, F, Ff, Ff, NULL, (float*)F, F,
+                                   1 << 30, NULL),
+           SSD_ERR_NULL);
+    EXPECT(ssd_conv_segment_output(&p, segs, 8, F, Ff, Ff, mis, Ff, F, (size_t)1 << 40, F, NULL),
+           SSD_ERR_ALIGN);
+    EXPECT(ssd_conv_segment_output(&p, segs, 8, F, Ff, Ff, NULL, Ff, F, 1, F, NULL),
+           SSD_ERR_WORKSPACE);
     EXPECT(ssd_segment_bwd_summary(&p, segs, 8, F, Ff, F, Ff, Ff, mis, F, (float*)F, F,
                                    (size_t)1 << 40, NULL),
            SSD_ERR_ALIGN);
