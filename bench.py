@@ -573,6 +573,34 @@ def path_entry(wl, ms_step, do_bwd):
     return out
 
 
+# One rank's shard at cp8, at its real shape: the contiguous shard (b rows of L/8
+# tokens) and the virtual layout's two half-shards run as 2b rows of L/16 tokens
+# (Megatron-LM #6808, "Why virtual is the mode to prefer": 2 x batch program
+# instances); one causal segment per row, no predecessor on this GPU.
+SHARDS = [("mixer_shard_bf16", "fwd+bwd"), ("mixer_shard_bf16", "fwd"), ("long_context_bf16", "fwd")]
+
+
+def shard_latency(steps, warmup, dev):
+    import torch
+
+    import ssd_workloads as W
+    out = {}
+    for name, which in SHARDS:
+        base = dict(W.WORKLOADS[name])
+        L, b = base["seqlen"], base["batch"]
+        entry = {}
+        for layout, bb, ll in (("contiguous", b, L // 8), ("virtual", 2 * b, L // 16)):
+            kw = dict(base, batch=bb, seqlen=ll, nseg=1, layout="contiguous",
+                      with_dy=which == "fwd+bwd")
+            wl = W.make_workload(f"{name}_shard_{layout}", **kw)
+            m = run_workload(wl, which, steps, warmup, dev)
+            torch.cuda.empty_cache()
+            entry[layout] = {"batch": bb, "seq_len": ll, "us_per_call_sequence": round(m["ms_step"] * 1e3, 2),
+                             "tokens_per_s": round(wl.tokens / (m["ms_step"] * 1e-3), 1)}
+        out[f"{name}:{which}"] = entry
+    return out
+
+
 # Configurations measured beside the headline (forward of each; the headline is the
 # forward + backward of the mixer shard), and the head sample their oracle baseline uses.
 EXTRA_CONFIGS = [("tiny_f32", None), ("mixer_shard_bf16", None), ("packed_thd_bf16", None),
@@ -685,6 +713,7 @@ def main():
             del xw, xm
             gc.collect()
         result["configs"] = extra
+        result["per_shard"] = shard_latency(args.steps, args.warmup, dev)
     print(json.dumps(result), flush=True)
 
 

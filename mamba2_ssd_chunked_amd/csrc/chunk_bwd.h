@@ -26,10 +26,16 @@
 // column tile the rows i >= j are visited one MFMA k step (KS tokens, TPK
 // row tiles) at a time; the (k step, column) blocks of the wave are mapped to
 // NKS + 1 fixed register slots of Z (column QT-1-w: slots 0.., column w:
-// slot = k step + 1), so Z stays in registers across the heads.  x, dy, G and
-// H of a head sit in LDS in their natural rows: row reads for the W and state
-// products, transposed reads (XT) of dy for dx; the Gram tiles come from L2 one
-// k step ahead of their use.  After the heads, Z goes to LDS as rows for dC,
+// slot = k step + 1), so Z stays in registers across the heads.  The chunk's
+// Gram tiles are the same for every head: they are staged in LDS once per
+// workgroup, so the k steps issue no global loads.  dy, G and H of a head sit
+// in LDS in their natural rows: row reads for the W and state products,
+// transposed reads (XT) of dy for dx.  x is read only by the wave that owns
+// its rows: each wave loads its two column tiles' x rows from memory straight
+// into MFMA operands, in the k-slot order of KPermRow (the W product reads dy
+// in the same order), which is also the order of the dx accumulator's values,
+// so the same registers give the x . dx, x . (state term) and dy . x dot
+// products.  After the heads, Z goes to LDS as rows for dC,
 // the chunk's C and B rows are staged in turn for the Z products (read
 // transposed), and each
 // head's G and H for its state terms (read transposed); dB is finished before
@@ -84,9 +90,11 @@ struct ChunkBwdHB {
         return o;
     }
     static constexpr int cmax(int a, int b) { return a > b ? a : b; }
-    // head loop: x, dy, G, H of the head and the per-wave row sums
-    static constexpr int O_D = Q * XR, O_G = 2 * Q * XR, O_H = O_G + P * GR, O_RW = O_H + P * GR;
-    static constexpr int E_HEAD = O_RW + NW * Q * 4 / (int)sizeof(T);
+    // head loop: dy, G, H of the head, the per-wave row sums and the chunk's
+    // Gram tiles
+    static constexpr int O_D = 0, O_G = Q * XR, O_H = O_G + P * GR, O_RW = O_H + P * GR;
+    static constexpr int O_GM = O_RW + NW * Q * 4 / (int)sizeof(T);
+    static constexpr int E_HEAD = O_GM + gram_tiles(QT) * 256;
     // final phase: Z rows and C^T (then G of HG heads), later B^T and H
     // heads per round of state terms: 2 below Q = 256 keeps the LDS of a
     // workgroup within half a CU's, so two workgroups share a CU
@@ -117,11 +125,11 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     typedef T vt __attribute__((ext_vector_type(VEC)));
     typedef T t4 __attribute__((ext_vector_type(4)));
     __shared__ __attribute__((aligned(16))) T U[K::E_U];
-    T* const sX = U;                            // x of the current head [Q][XR]
     T* const sD = U + K::O_D;                   // dy of the current head [Q][XR]
     T* const sG = U + K::O_G;                   // exit gradient G [P][GR]
     T* const sH = U + K::O_H;                   // entering state H [P][GR]
     float* const s_rw = (float*)(U + K::O_RW);  // per-wave row sums of F [NW][Q]
+    T* const sGm = U + K::O_GM;                 // the chunk's Gram tiles (head loop)
     T* const sZ = U;                            // final phase: Z rows, strip per row tile
     T* const sBT = U + K::O_BT;                 // final phase: C rows, then B rows [Q][BR]
     constexpr int GR = K::GR, BR = K::BR;
@@ -163,17 +171,18 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     const int64_t boff = HPd + (int64_t)g * N;
     const int64_t coff = HPd + (int64_t)d.G * N + (int64_t)g * N;
     const int64_t cg = ((int64_t)b * d.nchunk + cm) * d.G + g;
-    const T* gT0 = gramT + cg * (int64_t)gram_tiles(QT) * 256 + lane * 4;
     const int j0 = wave, j1 = QT - 1 - wave;  // the wave's tiles
     const int ks0 = j0 / TPK, ks1 = j1 / TPK;  // first k step of each as a column
     const int n1 = NKS - ks1;                  // k steps of column j1
     auto st_of = [&](int h) { return (((int64_t)b * d.nchunk + cm) * d.H + h) * (int64_t)(P * N); };
     auto hl_of = [&](int h) { return ((int64_t)b * d.H + h) * d.L + t0; };
 
-    // ---- staging of x, dy, G and H of one head (registers, then LDS)
+    // ---- staging of dy, G and H of one head (registers, then LDS), and the x
+    // rows of the wave's columns j0, j1 (registers, in KPermRow order)
     constexpr int V_X = (Q * (P / VEC) + NTH - 1) / NTH;
     constexpr int V_S = (P * (N / VEC) + NTH - 1) / NTH;
-    vt rx[V_X], rd[V_X], rg[V_S], rh[V_S];
+    vt rd[V_X], rg[V_S], rh[V_S];
+    Frag xf[2][KP];
     float rcs = 0.f, rdt = 0.f;  // cumulative sum and dt of token threadIdx.x (< Q)
     auto fetch = [&](int h) {
         const int64_t so = st_of(h);
@@ -186,10 +195,15 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
             const int idx = threadIdx.x + q * NTH;
             if (idx < Q * (P / VEC)) {
                 const int j = idx / (P / VEC), pv = idx % (P / VEC);
-                rx[q] = *(const vt*)(xc + (rb + t0 + j) * d.C + (int64_t)h * P + pv * VEC);
                 rd[q] = *(const vt*)(dy + (rb + t0 + j) * HPd + (int64_t)h * P + pv * VEC);
             }
         }
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int kp = 0; kp < KP; ++kp)
+                xf[c][kp] = KPermRow<T>::load(
+                    xc + (rb + t0 + (c == 0 ? j0 : j1) * 16 + lr) * d.C + (int64_t)h * P + kp * KS, lg);
 #pragma unroll
         for (int q = 0; q < V_S; ++q) {
             const int idx = threadIdx.x + q * NTH;
@@ -205,7 +219,6 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
             const int idx = threadIdx.x + q * NTH;
             if (idx < Q * (P / VEC)) {
                 const int j = idx / (P / VEC), pv = idx % (P / VEC);
-                *(vt*)&sX[j * XR + pv * VEC] = rx[q];
                 *(vt*)&sD[j * XR + pv * VEC] = rd[q];
             }
         }
@@ -233,6 +246,14 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
         for (int it = 0; it < TPK; ++it) Z[s][it] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     for (int j = threadIdx.x; j < Q; j += NTH) ssq[j] = seq ? seq[rb + t0 + j] : 0;
+    {
+        // the chunk's Gram tiles, read by every head's k steps (the first head's
+        // barriers order these writes before the first read)
+        const T* gsrc = gramT + cg * (int64_t)gram_tiles(QT) * 256;
+        constexpr int NGV = gram_tiles(QT) * 256 / VEC;
+        for (int idx = threadIdx.x; idx < NGV; idx += NTH)
+            *(vt*)&sGm[idx * VEC] = *(const vt*)(gsrc + (int64_t)idx * VEC);
+    }
 
     for (int hh = 0; hh < hbs; ++hh) {
         const int h = h0 + hh;
@@ -245,7 +266,6 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
         int opq;
         asm volatile("s_mov_b32 %0, 0" : "=s"(opq));
         const int lane = threadIdx.x % 64 + opq, lr = lane % 16, lg = lane / 16;
-        const T* const gT = gT0 + opq;
         // C rows of the wave's two tiles and B rows of tile j1 (state products)
         Frag cfr[2][KN], bfr[KN];
 #pragma unroll
@@ -314,7 +334,10 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
         int sqj = 0;
         f32x4 acc[PT];
         Frag xB[KP];
-        auto col_begin = [&](int jc_, const Frag (&bf)[KN]) {
+        // element p = pt * 16 + 4 lg + r of the column's x row (this lane's row
+        // j): KPermRow order puts it in slot (pt % TPK) * 4 + r of block pt / TPK
+        auto xval = [&](int pt, int r) { return (float)xB[pt / TPK][(pt % TPK) * 4 + r]; };
+        auto col_begin = [&](int jc_, const Frag (&bf)[KN], const Frag (&xq)[KP]) {
             jc = jc_;
             const int j = 16 * jc + lr;
             csj = scs[j];
@@ -323,7 +346,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
             e2j = exact ? 0.f : seb[j];
             const float gj = (sqj == seq_e) ? __expf(cs_e - csj) : 0.f;
 #pragma unroll
-            for (int kp = 0; kp < KP; ++kp) xB[kp] = M::load(&sX[j * XR + kp * KS + SL * lg]);
+            for (int kp = 0; kp < KP; ++kp) xB[kp] = xq[kp];
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -335,24 +358,14 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
                 acc[pt] *= gj;
-                float xv[4];
-                load4(&sX[j * XR + pt * 16 + 4 * lg], xv);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) vp += xv[r] * acc[pt][r];
+                for (int r = 0; r < 4; ++r) vp += xval(pt, r) * acc[pt][r];
             }
             vj = dtj * sum_groups(vp);
             kacc = 0.f;
         };
-        // Gram tiles of a k step (loaded one k step ahead of their use)
-        auto gload = [&](t4 (&dst)[TPK], int jc_, int ks_) {
-#pragma unroll
-            for (int it = 0; it < TPK; ++it) {
-                const int a = ks_ * TPK + it;
-                if (a >= jc_) dst[it] = *(const t4*)(gT + (int64_t)gram_index(a, jc_) * 256);
-            }
-        };
         // k step ks of the current column, accumulating into Z slot z
-        auto kstep = [&](f32x4 (&z)[TPK], int ks, const t4 (&gv)[TPK]) {
+        auto kstep = [&](f32x4 (&z)[TPK], int ks) {
             Frag sl;
 #pragma unroll
             for (int it = 0; it < TPK; ++it) {
@@ -361,9 +374,10 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
                 f32x4 w = f32x4{0.f, 0.f, 0.f, 0.f};
                 const bool live = a >= jc;  // wave-uniform
                 if (live) {
+                    const t4 gv = *(const t4*)&sGm[gram_index(a, jc) * 256 + lane * 4];
 #pragma unroll
                     for (int kp = 0; kp < KP; ++kp)
-                        w = M::mma(M::load(&sD[(16 * a + lr) * XR + kp * KS + SL * lg]), xB[kp], w);
+                        w = M::mma(KPermRow<T>::load(&sD[(16 * a + lr) * XR + kp * KS], lg), xB[kp], w);
                     const int ib = 16 * a + 4 * lg;
                     if (!exact) {
                         const float bj = stab[a * QT + jc] * e2j;
@@ -383,7 +397,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
                             dd[r] = (ib + r >= 16 * jc + lr && si[r] == sqj) ? __expf(ci[r] - csj) : 0.f;
                     }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) ss[r] = (float)gv[it][r];
+                    for (int r = 0; r < 4; ++r) ss[r] = (float)gv[r];
                 }
                 float fr[4];
 #pragma unroll
@@ -411,15 +425,15 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
             float qp = 0.f;
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                float xv[4], dyv[4];
-                load4(&sX[j * XR + pt * 16 + 4 * lg], xv);
+                float dyv[4];
                 load4(&sD[j * XR + pt * 16 + 4 * lg], dyv);
                 t4 o;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    qp += xv[r] * acc[pt][r];
+                    const float xv = xval(pt, r);
+                    qp += xv * acc[pt][r];
                     o[r] = (T)(dtj * acc[pt][r] + Dh * dyv[r]);
-                    ddp += dyv[r] * xv[r];
+                    ddp += dyv[r] * xv;
                 }
                 *(t4*)(dv + (rb + t0 + j) * HPd + (int64_t)h * P + pt * 16 + 4 * lg) = o;
             }
@@ -435,38 +449,23 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
 
         // (scheduling barriers keep the unrolled k steps from being interleaved,
         // which would need more registers than Z leaves)
-        col_begin(j1, bfr);
+        col_begin(j1, bfr, xf[1]);
         Frag bf0[KN];  // B rows of tile j0, for its column start
 #pragma unroll
         for (int kn = 0; kn < KN; ++kn)
             bf0[kn] = M::load(xc + (rb + t0 + j0 * 16 + lr) * d.C + boff + kn * KS + SL * lg);
-        t4 gn[TPK];
-        gload(gn, j1, ks1);
 #pragma unroll
         for (int m = 0; m < MAXA; ++m) {
             __builtin_amdgcn_sched_barrier(0);
-            if (m < n1) {
-                t4 gc[TPK];
-#pragma unroll
-                for (int it = 0; it < TPK; ++it) gc[it] = gn[it];
-                if (m + 1 < n1) gload(gn, j1, ks1 + m + 1);
-                else gload(gn, j0, ks0);
-                kstep(Z[m], ks1 + m, gc);
-            }
+            if (m < n1) kstep(Z[m], ks1 + m);
         }
         __builtin_amdgcn_sched_barrier(0);
         col_end(u[1]);
-        col_begin(j0, bf0);
+        col_begin(j0, bf0, xf[0]);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             __builtin_amdgcn_sched_barrier(0);
-            if (ks >= ks0) {
-                t4 gc[TPK];
-#pragma unroll
-                for (int it = 0; it < TPK; ++it) gc[it] = gn[it];
-                if (ks + 1 < NKS) gload(gn, j0, ks + 1);
-                kstep(Z[ks + 1], ks, gc);
-            }
+            if (ks >= ks0) kstep(Z[ks + 1], ks);
         }
         __builtin_amdgcn_sched_barrier(0);
         col_end(u[0]);

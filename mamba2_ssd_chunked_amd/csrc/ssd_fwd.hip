@@ -139,7 +139,6 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
     __shared__ __attribute__((aligned(16))) float seb[Q];  // exp(L(t) - cs_t) dt_t
     __shared__ __attribute__((aligned(16))) int ssq[Q];
     __shared__ float stab[QT * QT];                         // exp(F_a - L_b), a >= b
-    __shared__ float s_eps;
 
     const ChunkHead ch = chunk_head_of_block(d);
     const int cm = ch.cm, h = ch.h;
@@ -179,11 +178,28 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
     auto cload = [&](int it, int kn) {
         return M::load(bc + (rb + t0 + i0[it] + lr) * bstr + coff + kn * KS + SL * lg);
     };
-    Frag cfc[2];
+    // every k step's C rows at once: each inter-chunk step would otherwise wait
+    // a memory round trip for a few products (the conv-fused variant, whose
+    // conv windows hold registers meanwhile, loads them one k step ahead)
+    constexpr int CPRE = XC ? 1 : NKF;
+    Frag cfc[2][NKF];
     if (inter) {
-        cfc[0] = cload(0, 0);
-        cfc[1] = cload(1, 0);
+#pragma unroll
+        for (int kn = 0; kn < CPRE; ++kn) {
+            cfc[0][kn] = cload(0, kn);
+            cfc[1][kn] = cload(1, kn);
+        }
     }
+    // the span's earlier chunk totals, for eps (reduced after the first barrier;
+    // loaded there by the conv-fused variant, whose windows hold registers now)
+    float ctp = 0.f;
+    auto ct_load = [&]() {
+        if (use_st) {
+            const float* ct = ctot + ((int64_t)b * d.H + h) * d.nchunk;
+            for (int c = cspan0 + lane; c < cm; c += 64) ctp += ct[c];
+        }
+    };
+    if constexpr (!XC) ct_load();
     constexpr int V_X = (Q * (P / VEC) + NTH - 1) / NTH;
     // XC (conv-fused): xc is the raw input; the thread owns column vector xpv of
     // rows xj0 .. xj0 + V_X - 1 and holds the conv window under them
@@ -236,16 +252,6 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
         sdt[j] = dt_ws[hl + j];
         ssq[j] = seq ? seq[rb + t0 + j] : 0;
     }
-    if (use_st && wave == 0) {
-        // eps = exp(sum of the span's earlier chunk totals), if no sequence
-        // started between the span start and this chunk
-        const float* ct = ctot + ((int64_t)b * d.H + h) * d.nchunk;
-        float part = 0.f;
-        for (int c = cspan0 + lane; c < cm; c += 64) part += ct[c];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-        if (lane == 0) s_eps = (seq_prev == seq_span) ? expf(part) : 0.f;
-    }
     if constexpr (XC) {
         float taps[VEC][CW];
         load_taps<VEC, CW>(taps, conv_w, xoff + xpv * VEC);
@@ -273,8 +279,17 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
     const bool exact = __syncthreads_or(wide) || split;
     if (inter) {
         // entering state [p][n]: zero-state part from the span's own chunks + eps
-        // times the state entering the span
-        const float eps = use_st ? s_eps : 0.f;
+        // times the state entering the span; eps = exp(sum of the span's earlier
+        // chunk totals), 0 if a sequence started between the span start and
+        // this chunk (every wave reduces the totals itself)
+        float eps = 0.f;
+        if constexpr (XC) ct_load();
+        if (use_st) {
+            float part = ctp;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+            eps = (seq_prev == seq_span) ? expf(part) : 0.f;
+        }
 #pragma unroll
         for (int q = 0; q < V_H; ++q) {
             const int idx = threadIdx.x + q * NTH;
@@ -341,20 +356,15 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
     if (inter) {
 #pragma unroll
         for (int kn = 0; kn < NKF; ++kn) {
-            Frag cfn[2];
-            if (kn + 1 < NKF) {
-                cfn[0] = cload(0, kn + 1);
-                cfn[1] = cload(1, kn + 1);
+            if (kn + 1 >= CPRE && kn + 1 < NKF) {
+                cfc[0][kn + 1] = cload(0, kn + 1);
+                cfc[1][kn + 1] = cload(1, kn + 1);
             }
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
                 const Frag hf = M::load(&sH[(pt * 16 + lr) * HP + kn * KS + SL * lg]);
-                acc[0][pt] = M::mma(hf, cfc[0], acc[0][pt]);
-                acc[1][pt] = M::mma(hf, cfc[1], acc[1][pt]);
-            }
-            if (kn + 1 < NKF) {
-                cfc[0] = cfn[0];
-                cfc[1] = cfn[1];
+                acc[0][pt] = M::mma(hf, cfc[0][kn], acc[0][pt]);
+                acc[1][pt] = M::mma(hf, cfc[1][kn], acc[1][pt]);
             }
         }
 #pragma unroll
