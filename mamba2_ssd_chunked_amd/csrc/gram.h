@@ -22,85 +22,122 @@ namespace ssd {
 __host__ __device__ constexpr int gram_tiles(int qt) { return qt * (qt + 1) / 2; }
 __host__ __device__ constexpr int gram_index(int a, int b) { return a * (a + 1) / 2 + b; }
 
-// One wave per (output tiles w and QT-1-w, every GSPLIT-th source tile, chunk,
-// group, row): 2048 waves at the mixer shard's shape, each with a few
-// independent tile products to keep loads in flight.
-constexpr int GSPLIT = 4;
-// One block of the Gram pass: bx = (tile pair, source-tile part), by =
-// (chunk, group), b = row.  The B and C channels of token row m are at bc +
-// m * bstr (B of group g at g N, C at (G + g) N).
-template <typename T, int N, bool TRANS>
-__device__ __forceinline__ void gram_block(const Dims& d, const T* __restrict__ bc, int64_t bstr,
-                                           T* __restrict__ gram, int bx, int by, int64_t b) {
+// One workgroup of QT / 2 waves per (row, chunk, group), split S ways over the
+// source tiles when there are fewer than 256 (row, chunk, group) items: split z
+// forms the tiles whose source tile b has b % S == z.  It stages those B rows
+// in LDS once; wave w holds the C rows of output tiles w and QT-1-w as MFMA
+// operands and forms their tiles of the split from the staged rows.  Every B
+// row is read from memory once per (chunk, group), every C row once per split.
+// The same workgroups run dt prep for the group's heads of their chunk (head j
+// of the group in split j % S, one head per wave and round): the two read
+// different inputs.
+inline int gram_split(const Dims& d) {
+    const int64_t items = (int64_t)d.nchunk * d.G * d.batch;
+    const int pairs = d.Q / 32;
+    int S = 1;
+    while (S < pairs && items * S < 256) S *= 2;
+    return S;
+}
+
+template <typename T, int N, int Q, bool TRANS>
+__global__ void __launch_bounds__(Q / 32 * 64) k_gram_dt(Dims d, int S, const T* __restrict__ bc,
+                                                        int64_t bstr, T* __restrict__ gram,
+                                                        const T* __restrict__ dt_raw,
+                                                        const float* __restrict__ dt_bias,
+                                                        const float* __restrict__ A_log,
+                                                        const int32_t* __restrict__ seq,
+                                                        float* __restrict__ dt_ws,
+                                                        float* __restrict__ cs_ws,
+                                                        float* __restrict__ ctot) {
     typedef Mma<T> M;
     typedef typename M::Frag Frag;
-    constexpr int SL = M::SL, KS = M::KS, NKF = N / KS;
+    constexpr int SL = M::SL, KS = M::KS, NKF = N / KS, QT = Q / 16;
+    constexpr int VEC = 16 / (int)sizeof(T), BR = N + VEC;
+    typedef T vt __attribute__((ext_vector_type(VEC)));
     typedef T t4 __attribute__((ext_vector_type(4)));
-    const int QT = d.Q / 16;
-    const int w = bx / GSPLIT, part = bx % GSPLIT;
-    const int g = by % d.G, cm = by / d.G;
-    const int lane = threadIdx.x, lr = lane % 16, lg = lane / 16;
-    const int64_t t0 = b * d.L + (int64_t)cm * d.Q;
+    __shared__ __attribute__((aligned(16))) T sB[Q * BR];
+
+    // block -> (split, group, chunk, row); the S splits of a (chunk, group) are
+    // consecutive items, and each XCD takes one contiguous range of items
+    constexpr int NXCD = 8;
+    const int64_t n = gridDim.x, j = blockIdx.x;
+    int64_t item = (n % NXCD == 0) ? (j % NXCD) * (n / NXCD) + j / NXCD : j;
+    const int z = (int)(item % S);
+    item /= S;
+    const int g = (int)(item % d.G);
+    item /= d.G;
+    const int cm = (int)(item % d.nchunk);
+    const int64_t b = item / d.nchunk;
+    constexpr int GW = QT / 2;  // waves of the workgroup
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, lr = lane % 16, lg = lane / 16;
+    const int a0 = wave, a1 = QT - 1 - wave;
+    const int64_t t0 = b * d.L + (int64_t)cm * Q;
     const int64_t boff = (int64_t)g * N;
     const int64_t coff = boff + (int64_t)d.G * N;
-    T* out = gram + (((int64_t)b * d.nchunk + cm) * d.G + g) * (int64_t)gram_tiles(QT) * 256;
-    for (int side = 0; side < 2; ++side) {
-        const int a = side == 0 ? w : QT - 1 - w;
-        if (side == 1 && a == w) break;
-        Frag cf[NKF];
+
+    Frag cf[2][NKF];
 #pragma unroll
-        for (int kn = 0; kn < NKF; ++kn)
-            cf[kn] = M::load(bc + (t0 + a * 16 + lr) * bstr + coff + kn * KS + SL * lg);
-#pragma unroll 2
-        for (int bt = part; bt <= a; bt += GSPLIT) {
+    for (int kn = 0; kn < NKF; ++kn) {
+        cf[0][kn] = M::load(bc + (t0 + a0 * 16 + lr) * bstr + coff + kn * KS + SL * lg);
+        cf[1][kn] = M::load(bc + (t0 + a1 * 16 + lr) * bstr + coff + kn * KS + SL * lg);
+    }
+    // B rows of the split's source tiles z, z + S, ...: LDS row (bt / S) * 16 + r
+    const int rows = (QT - z + S - 1) / S * 16;
+    for (int idx = threadIdx.x; idx < rows * (N / VEC); idx += GW * 64) {
+        const int r = idx / (N / VEC), v = idx % (N / VEC);
+        const int tok = ((r / 16) * S + z) * 16 + r % 16;
+        *(vt*)&sB[r * BR + v * VEC] = *(const vt*)(bc + (t0 + tok) * bstr + boff + v * VEC);
+    }
+    __syncthreads();
+    T* out = gram + (((int64_t)b * d.nchunk + cm) * d.G + g) * (int64_t)gram_tiles(QT) * 256 + lane * 4;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int a = it == 0 ? a0 : a1;
+        for (int bt = z; bt <= a; bt += S) {
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kn = 0; kn < NKF; ++kn) {
-                const Frag bf = M::load(bc + (t0 + bt * 16 + lr) * bstr + boff + kn * KS + SL * lg);
-                acc = TRANS ? M::mma(cf[kn], bf, acc) : M::mma(bf, cf[kn], acc);
+                const Frag bf = M::load(&sB[((bt / S) * 16 + lr) * BR + kn * KS + SL * lg]);
+                acc = TRANS ? M::mma(cf[it][kn], bf, acc) : M::mma(bf, cf[it][kn], acc);
             }
-            *(t4*)(out + (int64_t)gram_index(a, bt) * 256 + lane * 4) =
-                t4{(T)acc[0], (T)acc[1], (T)acc[2], (T)acc[3]};
+            *(t4*)(out + (int64_t)gram_index(a, bt) * 256) = t4{(T)acc[0], (T)acc[1], (T)acc[2], (T)acc[3]};
         }
     }
+    for (int hj = z + S * wave; hj < d.hpg; hj += S * GW)
+        dt_prep_wave<T>(d, dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot, cm, g * d.hpg + hj, b, lane);
 }
 
-// The Gram pass and dt prep in one launch: the first blocks are Gram blocks,
-// the rest one wave per (row, chunk, head) of dt prep.  The two read different
-// inputs (B, C and dt_raw) and have no order between them, so their blocks
-// share the chip instead of running one kernel after the other.
-template <typename T, int N, bool TRANS>
-__global__ void __launch_bounds__(64) k_gram_dt(Dims d, const T* __restrict__ bc, int64_t bstr,
-                                               T* __restrict__ gram, int64_t ngram,
-                                               const T* __restrict__ dt_raw,
-                                               const float* __restrict__ dt_bias,
-                                               const float* __restrict__ A_log,
-                                               const int32_t* __restrict__ seq,
-                                               float* __restrict__ dt_ws,
-                                               float* __restrict__ cs_ws,
-                                               float* __restrict__ ctot) {
-    const int64_t i = blockIdx.x;
-    if (i < ngram) {
-        const int gx = d.Q / 16 / 2 * GSPLIT, gy = d.nchunk * d.G;
-        gram_block<T, N, TRANS>(d, bc, bstr, gram, (int)(i % gx), (int)((i / gx) % gy),
-                                i / gx / gy);
-    } else {
-        const int64_t j = i - ngram;
-        dt_prep_wave<T>(d, dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot,
-                        (int)((j / d.H) % d.nchunk), (int)(j % d.H), j / d.H / d.nchunk,
-                        threadIdx.x);
-    }
+template <typename T, int N, int Q, bool TRANS>
+inline hipError_t launch_gram_dt_q(const Dims& d, const T* bc, int64_t bstr, T* gram,
+                                   const void* dt_raw, const float* dt_bias, const float* A_log,
+                                   const int32_t* seq, float* dt_ws, float* cs_ws, float* ctot,
+                                   hipStream_t s) {
+    const int S = gram_split(d);
+    const int64_t nblk = (int64_t)d.nchunk * d.G * d.batch * S;
+    return launch(k_gram_dt<T, N, Q, TRANS>, dim3((unsigned)nblk), dim3(Q / 32 * 64), s, d, S,
+                  bc, bstr, gram, (const T*)dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot);
 }
 
+// The Gram tiles and dt prep in one launch.  B and C channels of token row m at
+// bc + m * bstr (B of group g at g N, C at (G + g) N).
 template <typename T, int N, bool TRANS = false>
 inline hipError_t launch_gram_dt(const Dims& d, const T* bc, int64_t bstr, T* gram,
-                                 const void* dt_raw,
-                                 const float* dt_bias, const float* A_log, const int32_t* seq,
-                                 float* dt_ws, float* cs_ws, float* ctot, hipStream_t s) {
-    const int64_t ngram = (int64_t)(d.Q / 16 / 2 * GSPLIT) * d.nchunk * d.G * d.batch;
-    const int64_t ndt = (int64_t)d.nchunk * d.H * d.batch;
-    return launch(k_gram_dt<T, N, TRANS>, dim3((unsigned)(ngram + ndt)), dim3(64), s, d, bc, bstr,
-                  gram, ngram, (const T*)dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot);
+                                 const void* dt_raw, const float* dt_bias, const float* A_log,
+                                 const int32_t* seq, float* dt_ws, float* cs_ws, float* ctot,
+                                 hipStream_t s) {
+    switch (d.Q) {
+        case 64:
+            return launch_gram_dt_q<T, N, 64, TRANS>(d, bc, bstr, gram, dt_raw, dt_bias, A_log, seq,
+                                                     dt_ws, cs_ws, ctot, s);
+        case 128:
+            return launch_gram_dt_q<T, N, 128, TRANS>(d, bc, bstr, gram, dt_raw, dt_bias, A_log,
+                                                      seq, dt_ws, cs_ws, ctot, s);
+        case 256:
+            return launch_gram_dt_q<T, N, 256, TRANS>(d, bc, bstr, gram, dt_raw, dt_bias, A_log,
+                                                      seq, dt_ws, cs_ws, ctot, s);
+        default:
+            return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace ssd

@@ -36,7 +36,7 @@ bool grids_fit(const ssd_problem* p, int64_t C) {
     };
     const u128 cx = (CC + 255) / 256;  // conv workgroups along channels
     bool ok = x_ok(cx, 256) && L / 64 <= 65535 && b <= 65535;                   // conv forward
-    ok = ok && x_ok((Q / 32 * 4) * nc * G * b + nc * H * b, 64);                   // Gram + dt prep
+    ok = ok && x_ok(nc * G * b * (Q / 32), Q / 32 * 64);                           // Gram + dt prep
     ok = ok && x_ok(2 * H * nseg * b, 512);                                        // state walks
     ok = ok && x_ok(nc * H * b, 512);                                              // output passes
     ok = ok && x_ok((b * H * PN / 4 + 255) / 256, 256);                            // boundary scan
