@@ -39,28 +39,33 @@ inline int gram_split(const Dims& d) {
     return S;
 }
 
+// LDS of a Gram workgroup (elements of T): the staged B rows.
+template <typename T, int N, int Q>
+constexpr int gram_lds() {
+    return Q * (N + 16 / (int)sizeof(T));
+}
+
+// One Gram workgroup: workgroup j of n (the XCD-aware item mapping is over this
+// range), its B rows staged at sB; with_dt: also the dt prep of its heads.
 template <typename T, int N, int Q, bool TRANS>
-__global__ void __launch_bounds__(Q / 32 * 64) k_gram_dt(Dims d, int S, const T* __restrict__ bc,
-                                                        int64_t bstr, T* __restrict__ gram,
-                                                        const T* __restrict__ dt_raw,
-                                                        const float* __restrict__ dt_bias,
-                                                        const float* __restrict__ A_log,
-                                                        const int32_t* __restrict__ seq,
-                                                        float* __restrict__ dt_ws,
-                                                        float* __restrict__ cs_ws,
-                                                        float* __restrict__ ctot) {
+__device__ __forceinline__ void gram_block(const Dims& d, int S, const T* __restrict__ bc,
+                                           int64_t bstr, T* __restrict__ gram, T* sB, int64_t j,
+                                           int64_t n, bool with_dt, const T* __restrict__ dt_raw,
+                                           const float* __restrict__ dt_bias,
+                                           const float* __restrict__ A_log,
+                                           const int32_t* __restrict__ seq,
+                                           float* __restrict__ dt_ws, float* __restrict__ cs_ws,
+                                           float* __restrict__ ctot) {
     typedef Mma<T> M;
     typedef typename M::Frag Frag;
     constexpr int SL = M::SL, KS = M::KS, NKF = N / KS, QT = Q / 16;
     constexpr int VEC = 16 / (int)sizeof(T), BR = N + VEC;
     typedef T vt __attribute__((ext_vector_type(VEC)));
     typedef T t4 __attribute__((ext_vector_type(4)));
-    __shared__ __attribute__((aligned(16))) T sB[Q * BR];
 
     // block -> (split, group, chunk, row); the S splits of a (chunk, group) are
     // consecutive items, and each XCD takes one contiguous range of items
     constexpr int NXCD = 8;
-    const int64_t n = gridDim.x, j = blockIdx.x;
     int64_t item = (n % NXCD == 0) ? (j % NXCD) * (n / NXCD) + j / NXCD : j;
     const int z = (int)(item % S);
     item /= S;
@@ -103,8 +108,24 @@ __global__ void __launch_bounds__(Q / 32 * 64) k_gram_dt(Dims d, int S, const T*
             *(t4*)(out + (int64_t)gram_index(a, bt) * 256) = t4{(T)acc[0], (T)acc[1], (T)acc[2], (T)acc[3]};
         }
     }
+    if (!with_dt) return;
     for (int hj = z + S * wave; hj < d.hpg; hj += S * GW)
         dt_prep_wave<T>(d, dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot, cm, g * d.hpg + hj, b, lane);
+}
+
+template <typename T, int N, int Q, bool TRANS>
+__global__ void __launch_bounds__(Q / 32 * 64) k_gram_dt(Dims d, int S, const T* __restrict__ bc,
+                                                        int64_t bstr, T* __restrict__ gram,
+                                                        const T* __restrict__ dt_raw,
+                                                        const float* __restrict__ dt_bias,
+                                                        const float* __restrict__ A_log,
+                                                        const int32_t* __restrict__ seq,
+                                                        float* __restrict__ dt_ws,
+                                                        float* __restrict__ cs_ws,
+                                                        float* __restrict__ ctot) {
+    __shared__ __attribute__((aligned(16))) T sB[gram_lds<T, N, Q>()];
+    gram_block<T, N, Q, TRANS>(d, S, bc, bstr, gram, sB, blockIdx.x, gridDim.x, true, dt_raw,
+                               dt_bias, A_log, seq, dt_ws, cs_ws, ctot);
 }
 
 template <typename T, int N, int Q, bool TRANS>

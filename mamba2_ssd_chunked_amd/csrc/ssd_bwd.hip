@@ -42,6 +42,7 @@
 #include "gram.h"
 #include "ssd_internal.h"
 #include "state_walk.h"
+#include "walk_gram.h"
 #include "xt.h"
 
 namespace ssd {
@@ -553,15 +554,23 @@ static hipError_t bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a
     char* ws = (char*)ws_;
     T* xc = (T*)(ws + L.xc);
     SSD_TRY(launch_conv1d_fwd(d, t, act, a.xBC, a.conv_w, a.seq, xc, s));
-    // the transposed Gram tiles and dt prep in one launch
-    SSD_TRY(launch_gram_dt<T, N, true>(d, xc + (int64_t)d.H * P, (int64_t)d.C, (T*)(ws + L.gramt),
-                                       a.dt_raw, a.dt_bias, a.A_log, a.seq, (float*)(ws + L.dt),
-                                       (float*)(ws + L.cs), (float*)(ws + L.ctot), s));
+    float* dtw = (float*)(ws + L.dt);
+    float* csw = (float*)(ws + L.cs);
+    float* ctot = (float*)(ws + L.ctot);
+    const T* bc = xc + (int64_t)d.H * P;
+    T* gramt = (T*)(ws + L.gramt);
     // the reverse walk from a zero final gradient: dL/dS_in of each segment's own
     // outputs and its block decay
-    const WalkArgs<T> wa = {(const T*)xc, (const T*)a.dy, (const float*)(ws + L.dt),
-                            (const float*)(ws + L.cs), a.seq, nullptr, nullptr, summary,
-                            span_plan(d, t, false)};
+    const WalkArgs<T> wa = {(const T*)xc, (const T*)a.dy, dtw, csw, a.seq, nullptr, nullptr,
+                            summary, span_plan(d, t, false)};
+    if (walk_gram_fits<T>(d)) {
+        // dt prep, then the walk and the transposed Gram tiles in one launch
+        SSD_TRY(launch_dt_prep(d, act, a.dt_raw, a.dt_bias, a.A_log, a.seq, dtw, csw, ctot, s));
+        return launch_walk_gram<T, P, N, true, true>(d, t, wa, bc, (int64_t)d.C, gramt, s);
+    }
+    // the transposed Gram tiles and dt prep in one launch, then the walk
+    SSD_TRY(launch_gram_dt<T, N, true>(d, bc, (int64_t)d.C, gramt, a.dt_raw, a.dt_bias, a.A_log,
+                                       a.seq, dtw, csw, ctot, s));
     return launch_state_walk<T, P, N, true>(d, t, wa, s);
 }
 

@@ -32,6 +32,7 @@
 #include "gram.h"
 #include "ssd_internal.h"
 #include "state_walk.h"
+#include "walk_gram.h"
 #include "xt.h"
 
 namespace ssd {
@@ -620,18 +621,26 @@ static hipError_t segment_states_t(const Dims& d, const SegTab& t, const void* x
         SSD_TRY(launch_conv1d_channels(d, t, act, xc, conv_w, seq, d.H * P, 2 * d.G * N,
                                        bc.bstr, w + L.bc, s));
     }
-    // the group Gram tiles the output pass reads and dt prep share one launch
-    // (independent inputs); the walk then needs dt and the cumulative sums
-    SSD_TRY(launch_gram_dt<T, N>(d, bc.bc, bc.bstr, (T*)(w + L.gram), dt_raw, dt_bias, A_log,
-                                 seq, dtw, csw, ctot, s));
     const SpanPlan sp = span_plan(d, t, true);
     const bool trivial = plan_trivial(sp, t);
     // long segments: walk their spans, then compose the span summaries
     const WalkArgs<T> wa = {xc,  nullptr, dtw, csw, seq, nullptr, hst,
                             trivial ? summary : (float*)(w + L.spsum),
                             sp,  bc.bc,   bc.bstr, conv_w};
-    if (xconv) SSD_TRY(launch_state_walk<T, P, N, false, true>(d, t, wa, s));
-    else SSD_TRY(launch_state_walk<T, P, N, false>(d, t, wa, s));
+    T* gram = (T*)(w + L.gram);
+    if (!xconv && walk_gram_fits<T>(d)) {
+        // dt prep first (the walk reads dt and the cumulative sums), then the
+        // walk and the group Gram tiles the output pass reads in one launch
+        SSD_TRY(launch_dt_prep(d, act, dt_raw, dt_bias, A_log, seq, dtw, csw, ctot, s));
+        SSD_TRY(launch_walk_gram<T, P, N, false, false>(d, t, wa, bc.bc, bc.bstr, gram, s));
+    } else {
+        // the Gram tiles and dt prep share one launch (independent inputs); the
+        // walk then needs dt and the cumulative sums
+        SSD_TRY(launch_gram_dt<T, N>(d, bc.bc, bc.bstr, gram, dt_raw, dt_bias, A_log, seq, dtw,
+                                     csw, ctot, s));
+        if (xconv) SSD_TRY(launch_state_walk<T, P, N, false, true>(d, t, wa, s));
+        else SSD_TRY(launch_state_walk<T, P, N, false>(d, t, wa, s));
+    }
     if (trivial) return hipSuccess;
     return launch_span_combine(d, sp, (const float*)(w + L.spsum), summary, s);
 }
