@@ -11,6 +11,7 @@
 // sequence start are zero.  HBM-bound: 2*C*sizeof(act) bytes per token.
 #include <type_traits>
 
+#include "dt_prep.h"
 #include "ssd_internal.h"
 
 namespace ssd {
@@ -18,18 +19,19 @@ namespace ssd {
 // Channels c0 .. c0 + nc - 1 of xBC go to columns 0 .. nc - 1 of `out`, whose
 // token rows are ostr elements apart (the whole conv output: c0 = 0, nc =
 // ostr = C).
+// Workgroup (bx, by, bz) of the (channel block, token block, row) grid.
 template <typename T, int W>
-__global__ void __launch_bounds__(256) k_conv1d_silu(Dims d, SegTab tab, const T* __restrict__ xBC,
-                                                    const float* __restrict__ w,
-                                                    const int32_t* __restrict__ seq,
-                                                    int c0, int nc, int64_t ostr,
-                                                    T* __restrict__ out) {
+__device__ __forceinline__ void conv_block(const Dims& d, const SegTab& tab,
+                                           const T* __restrict__ xBC, const float* __restrict__ w,
+                                           const int32_t* __restrict__ seq, int c0, int nc,
+                                           int64_t ostr, T* __restrict__ out, int bx, int by,
+                                           int bz) {
     constexpr int R = CONV_TPT + W - 1;
     typedef typename Vec4<T>::type vt;
     const int lane = threadIdx.x % 64;
-    const int c = c0 + (blockIdx.x * 64 + lane) * CONV_VEC;
-    const int64_t b = blockIdx.z;
-    const int64_t t0 = (int64_t)blockIdx.y * CONV_TT + wave_id() * CONV_TPT;
+    const int c = c0 + (bx * 64 + lane) * CONV_VEC;
+    const int64_t b = bz;
+    const int64_t t0 = (int64_t)by * CONV_TT + wave_id() * CONV_TPT;
     const int64_t rb = b * d.L;
     if (c >= c0 + nc) return;  // no barriers below
     const int k = conv_seg(tab, t0);
@@ -94,6 +96,44 @@ __global__ void __launch_bounds__(256) k_conv1d_silu(Dims d, SegTab tab, const T
 }
 
 template <typename T, int W>
+__global__ void __launch_bounds__(256) k_conv1d_silu(Dims d, SegTab tab, const T* __restrict__ xBC,
+                                                    const float* __restrict__ w,
+                                                    const int32_t* __restrict__ seq,
+                                                    int c0, int nc, int64_t ostr,
+                                                    T* __restrict__ out) {
+    conv_block<T, W>(d, tab, xBC, w, seq, c0, nc, ostr, out, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// The whole conv pass and dt prep in one launch: the grid's first gx channel
+// blocks convolve; the extra ones (their (x - gx, y) numbered within the row)
+// run dt prep for four heads of one chunk each, one head per wave.  The conv is
+// bound by memory bandwidth and dt prep by latency, so the two overlap.
+template <typename T, int W>
+__global__ void __launch_bounds__(256) k_conv1d_silu_dt(Dims d, SegTab tab,
+                                                       const T* __restrict__ xBC,
+                                                       const float* __restrict__ w,
+                                                       const int32_t* __restrict__ seq, int gx,
+                                                       T* __restrict__ out,
+                                                       const T* __restrict__ dt_raw,
+                                                       const float* __restrict__ dt_bias,
+                                                       const float* __restrict__ A_log,
+                                                       float* __restrict__ dt_ws,
+                                                       float* __restrict__ cs_ws,
+                                                       float* __restrict__ ctot) {
+    if ((int)blockIdx.x < gx) {
+        conv_block<T, W>(d, tab, xBC, w, seq, 0, d.C, d.C, out, blockIdx.x, blockIdx.y,
+                         blockIdx.z);
+        return;
+    }
+    const int64_t item = (int64_t)(blockIdx.x - gx) * gridDim.y + blockIdx.y;
+    if (item >= (int64_t)d.nchunk * ((d.H + 3) / 4)) return;
+    const int cm = (int)(item % d.nchunk), h = (int)(item / d.nchunk) * 4 + wave_id();
+    if (h >= d.H) return;
+    dt_prep_wave<T>(d, dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot, cm, h, blockIdx.z,
+                    threadIdx.x % 64);
+}
+
+template <typename T, int W>
 static hipError_t launch_w(const Dims& d, const SegTab& t, const void* xBC, const float* w,
                            const int32_t* seq, int c0, int nc, int64_t ostr, void* out,
                            hipStream_t s) {
@@ -133,6 +173,47 @@ hipError_t launch_conv1d_channels(const Dims& d, const SegTab& t, int act, const
 hipError_t launch_conv1d_fwd(const Dims& d, const SegTab& t, int act, const void* xBC,
                              const float* w, const int32_t* seq, void* out, hipStream_t s) {
     return launch_conv1d_channels(d, t, act, xBC, w, seq, 0, d.C, d.C, out, s);
+}
+
+template <typename T, int W>
+static hipError_t launch_dt_w(const Dims& d, const SegTab& t, const void* xBC, const float* w,
+                              const int32_t* seq, void* out, const void* dt_raw,
+                              const float* dt_bias, const float* A_log, float* dt_ws,
+                              float* cs_ws, float* ctot, hipStream_t s) {
+    const int gx = (d.C + 64 * CONV_VEC - 1) / (64 * CONV_VEC);
+    const int gy = (int)(d.L / CONV_TT);
+    const int items = d.nchunk * ((d.H + 3) / 4);  // dt prep workgroups per row
+    const dim3 grid((unsigned)(gx + (items + gy - 1) / gy), (unsigned)gy, (unsigned)d.batch);
+    return launch(k_conv1d_silu_dt<T, W>, grid, dim3(256), s, d, t, (const T*)xBC, w, seq, gx,
+                  (T*)out, (const T*)dt_raw, dt_bias, A_log, dt_ws, cs_ws, ctot);
+}
+
+template <typename T>
+static hipError_t launch_dt_t(const Dims& d, const SegTab& t, const void* xBC, const float* w,
+                              const int32_t* seq, void* out, const void* dt_raw,
+                              const float* dt_bias, const float* A_log, float* dt_ws,
+                              float* cs_ws, float* ctot, hipStream_t s) {
+#define SSD_CONV_DT(WW)                                                                     \
+    case WW:                                                                                \
+        return launch_dt_w<T, WW>(d, t, xBC, w, seq, out, dt_raw, dt_bias, A_log, dt_ws, cs_ws, \
+                                  ctot, s);
+    switch (d.W) {
+        SSD_CONV_DT(1) SSD_CONV_DT(2) SSD_CONV_DT(3) SSD_CONV_DT(4)
+        SSD_CONV_DT(5) SSD_CONV_DT(6) SSD_CONV_DT(7) SSD_CONV_DT(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef SSD_CONV_DT
+}
+
+hipError_t launch_conv1d_dt(const Dims& d, const SegTab& t, int act, const void* xBC,
+                            const float* w, const int32_t* seq, void* out, const void* dt_raw,
+                            const float* dt_bias, const float* A_log, float* dt_ws, float* cs_ws,
+                            float* ctot, hipStream_t s) {
+    if (act == SSD_BF16)
+        return launch_dt_t<bf16>(d, t, xBC, w, seq, out, dt_raw, dt_bias, A_log, dt_ws, cs_ws,
+                                 ctot, s);
+    return launch_dt_t<float>(d, t, xBC, w, seq, out, dt_raw, dt_bias, A_log, dt_ws, cs_ws, ctot,
+                              s);
 }
 
 }  // namespace ssd

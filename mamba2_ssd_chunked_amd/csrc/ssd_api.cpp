@@ -36,6 +36,8 @@ bool grids_fit(const ssd_problem* p, int64_t C) {
     };
     const u128 cx = (CC + 255) / 256;  // conv workgroups along channels
     bool ok = x_ok(cx, 256) && L / 64 <= 65535 && b <= 65535;                   // conv forward
+    const u128 ty = L / 64 > 0 ? L / 64 : 1;
+    ok = ok && x_ok(cx + (nc * ((H + 3) / 4) + ty - 1) / ty, 256);                // conv + dt prep
     ok = ok && x_ok(nc * G * b * (Q / 32), Q / 32 * 64);                           // Gram + dt prep
     ok = ok && x_ok(2 * H * nseg * b, 512);                                        // state walks
     ok = ok && x_ok(nc * H * b, 512);                                              // output passes

@@ -553,7 +553,6 @@ static hipError_t bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a
     const BwdWs L = bwd_ws_layout(d, act);
     char* ws = (char*)ws_;
     T* xc = (T*)(ws + L.xc);
-    SSD_TRY(launch_conv1d_fwd(d, t, act, a.xBC, a.conv_w, a.seq, xc, s));
     float* dtw = (float*)(ws + L.dt);
     float* csw = (float*)(ws + L.cs);
     float* ctot = (float*)(ws + L.ctot);
@@ -564,10 +563,13 @@ static hipError_t bwd_summary_t(const Dims& d, const SegTab& t, const BwdArgs& a
     const WalkArgs<T> wa = {(const T*)xc, (const T*)a.dy, dtw, csw, a.seq, nullptr, nullptr,
                             summary, span_plan(d, t, false)};
     if (walk_gram_fits<T>(d)) {
-        // dt prep, then the walk and the transposed Gram tiles in one launch
-        SSD_TRY(launch_dt_prep(d, act, a.dt_raw, a.dt_bias, a.A_log, a.seq, dtw, csw, ctot, s));
+        // the conv recompute with dt prep, then the walk and the transposed Gram
+        // tiles in one launch
+        SSD_TRY(launch_conv1d_dt(d, t, act, a.xBC, a.conv_w, a.seq, xc, a.dt_raw, a.dt_bias,
+                                 a.A_log, dtw, csw, ctot, s));
         return launch_walk_gram<T, P, N, true, true>(d, t, wa, bc, (int64_t)d.C, gramt, s);
     }
+    SSD_TRY(launch_conv1d_fwd(d, t, act, a.xBC, a.conv_w, a.seq, xc, s));
     // the transposed Gram tiles and dt prep in one launch, then the walk
     SSD_TRY(launch_gram_dt<T, N, true>(d, bc, (int64_t)d.C, gramt, a.dt_raw, a.dt_bias, a.A_log,
                                        a.seq, dtw, csw, ctot, s));

@@ -191,16 +191,26 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
             cfc[1][kn] = cload(1, kn);
         }
     }
-    // the span's earlier chunk totals, for eps (reduced after the first barrier;
-    // loaded there by the conv-fused variant, whose windows hold registers now)
-    float ctp = 0.f;
-    auto ct_load = [&]() {
+    // the span's earlier chunk totals, for eps, reduced after the first barrier.
+    // Lane l's first one (chunk cspan0 + l, clamped into the row and masked
+    // later) is loaded with the workgroup's other rows, without a wait; spans
+    // of more than 64 chunks add the rest after the barrier.  The conv-fused
+    // variant, whose windows hold registers now, loads them all there.
+    const float* ctb = ctot + ((int64_t)b * d.H + h) * d.nchunk;
+    float ct_first = 0.f;
+    if (!XC && use_st) ct_first = ctb[min(cspan0 + lane, d.nchunk - 1)];
+    auto ct_sum = [&]() {
+        float ctp = 0.f;
         if (use_st) {
-            const float* ct = ctot + ((int64_t)b * d.H + h) * d.nchunk;
-            for (int c = cspan0 + lane; c < cm; c += 64) ctp += ct[c];
+            if constexpr (!XC) {
+                if (cspan0 + lane < cm) ctp = ct_first;
+                for (int c = cspan0 + 64 + lane; c < cm; c += 64) ctp += ctb[c];
+            } else {
+                for (int c = cspan0 + lane; c < cm; c += 64) ctp += ctb[c];
+            }
         }
+        return ctp;
     };
-    if constexpr (!XC) ct_load();
     constexpr int V_X = (Q * (P / VEC) + NTH - 1) / NTH;
     // XC (conv-fused): xc is the raw input; the thread owns column vector xpv of
     // rows xj0 .. xj0 + V_X - 1 and holds the conv window under them
@@ -248,10 +258,16 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
             }
         }
     }
-    for (int j = threadIdx.x; j < Q; j += NTH) {
-        scs[j] = cs_ws[hl + j];
-        sdt[j] = dt_ws[hl + j];
-        ssq[j] = seq ? seq[rb + t0 + j] : 0;
+    // the chunk's cumulative sums, dt and sequence ids, one token per thread
+    // (NTH = 2 Q), into registers first: a load followed by its LDS write here
+    // would wait for every load issued before it
+    static_assert(NTH >= Q, "one token per thread");
+    float rcs = 0.f, rdt = 0.f;
+    int rsq = 0;
+    if (threadIdx.x < Q) {
+        rcs = cs_ws[hl + threadIdx.x];
+        rdt = dt_ws[hl + threadIdx.x];
+        if (seq) rsq = seq[rb + t0 + threadIdx.x];
     }
     if constexpr (XC) {
         float taps[VEC][CW];
@@ -271,6 +287,11 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
             if (idx < Q * (P / VEC)) *(vt*)&sX[(idx / (P / VEC)) * XR + (idx % (P / VEC)) * VEC] = rx[q];
         }
     }
+    if (threadIdx.x < Q) {
+        scs[threadIdx.x] = rcs;
+        sdt[threadIdx.x] = rdt;
+        ssq[threadIdx.x] = rsq;
+    }
     __syncthreads();
     // The factored decay needs every tile's span cs(first) - cs(last) small
     // enough that its exponential stays a normal float; chunks with a sequence
@@ -284,9 +305,8 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
         // chunk totals), 0 if a sequence started between the span start and
         // this chunk (every wave reduces the totals itself)
         float eps = 0.f;
-        if constexpr (XC) ct_load();
         if (use_st) {
-            float part = ctp;
+            float part = ct_sum();
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
             eps = (seq_prev == seq_span) ? expf(part) : 0.f;

@@ -297,6 +297,11 @@ hipError_t launch_conv1d_fwd(const Dims& d, const SegTab& t, int act, const void
 hipError_t launch_conv1d_channels(const Dims& d, const SegTab& t, int act, const void* xBC,
                                   const float* w, const int32_t* seq, int c0, int nc,
                                   int64_t ostr, void* out, hipStream_t s);
+// the whole conv pass and dt prep (dt, cumulative sums, chunk totals) in one launch
+hipError_t launch_conv1d_dt(const Dims& d, const SegTab& t, int act, const void* xBC,
+                            const float* w, const int32_t* seq, void* out, const void* dt_raw,
+                            const float* dt_bias, const float* A_log, float* dt_ws, float* cs_ws,
+                            float* ctot, hipStream_t s);
 hipError_t launch_segment_states(const Dims& d, const SegTab& t, int act, const void* xBC_conv,
                                  const void* dt_raw, const float* dt_bias, const float* A_log,
                                  const int32_t* seq, float* summary, void* ws, hipStream_t s);
