@@ -184,18 +184,21 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     vt rd[V_X], rg[V_S], rh[V_S];
     Frag xf[2][KP];
     float rcs = 0.f, rdt = 0.f;  // cumulative sum and dt of token threadIdx.x (< Q)
-    auto fetch = [&](int h) {
+    // tid: threadIdx.x plus the head's opaque zero (below), so that the lane
+    // offsets are recomputed per head instead of held across the head loop
+    auto fetch = [&](int h, int tid) {
         const int64_t so = st_of(h);
-        if (threadIdx.x < Q) {
-            rcs = cs_ws[hl_of(h) + threadIdx.x];
-            rdt = dt_ws[hl_of(h) + threadIdx.x];
+        if (tid < Q) {
+            rcs = *at32(cs_ws + hl_of(h), tid);
+            rdt = *at32(dt_ws + hl_of(h), tid);
         }
+        const T* const dyh = dy + (rb + t0) * HPd + (int64_t)h * P;
 #pragma unroll
         for (int q = 0; q < V_X; ++q) {
-            const int idx = threadIdx.x + q * NTH;
-            if (idx < Q * (P / VEC)) {
+            const int idx = tid + q * NTH;
+            if (V_X * NTH == Q * (P / VEC) || idx < Q * (P / VEC)) {
                 const int j = idx / (P / VEC), pv = idx % (P / VEC);
-                rd[q] = *(const vt*)(dy + (rb + t0 + j) * HPd + (int64_t)h * P + pv * VEC);
+                rd[q] = *(const vt*)at32(dyh, (uint32_t)(j * HPd + pv * VEC));
             }
         }
 #pragma unroll
@@ -213,11 +216,11 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
             }
         }
     };
-    auto stash = [&]() {
+    auto stash = [&](int tid) {
 #pragma unroll
         for (int q = 0; q < V_X; ++q) {
-            const int idx = threadIdx.x + q * NTH;
-            if (idx < Q * (P / VEC)) {
+            const int idx = tid + q * NTH;
+            if (V_X * NTH == Q * (P / VEC) || idx < Q * (P / VEC)) {
                 const int j = idx / (P / VEC), pv = idx % (P / VEC);
                 *(vt*)&sD[j * XR + pv * VEC] = rd[q];
             }
@@ -225,8 +228,8 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
         float gh = 0.f;  // this thread's part of <G, H>
 #pragma unroll
         for (int q = 0; q < V_S; ++q) {
-            const int idx = threadIdx.x + q * NTH;
-            if (idx < P * (N / VEC)) {
+            const int idx = tid + q * NTH;
+            if (V_S * NTH == P * (N / VEC) || idx < P * (N / VEC)) {
                 const int p = idx / (N / VEC), nv = idx % (N / VEC);
                 *(vt*)&sG[p * GR + nv * VEC] = rg[q];
                 *(vt*)&sH[p * GR + nv * VEC] = rh[q];
@@ -236,7 +239,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) gh += __shfl_xor(gh, off, 64);
-        if (threadIdx.x % 64 == 0) s_gh[wave] = gh;
+        if (tid % 64 == 0) s_gh[wave] = gh;
     };
 
     f32x4 Z[NB][TPK];
@@ -258,14 +261,15 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     for (int hh = 0; hh < hbs; ++hh) {
         const int h = h0 + hh;
         const int64_t hl = hl_of(h);
-        fetch(h);
-        // An opaque zero, new every head: lane-derived indices, masks and the
-        // Gram tile addresses depend on it, so they are recomputed where they
-        // are used instead of being hoisted out of the head loop (where they
-        // would hold registers for its whole length).
+        // An opaque zero, new every head: lane-derived indices, masks, load
+        // offsets and the Gram tile addresses depend on it, so they are
+        // recomputed where they are used instead of being hoisted out of the
+        // head loop (where they would hold registers for its whole length).
         int opq;
         asm volatile("s_mov_b32 %0, 0" : "=s"(opq));
-        const int lane = threadIdx.x % 64 + opq, lr = lane % 16, lg = lane / 16;
+        const int tid = (int)threadIdx.x + opq;
+        fetch(h, tid);
+        const int lane = tid % 64, lr = lane % 16, lg = lane / 16;
         // C rows of the wave's two tiles and B rows of tile j1 (state products)
         Frag cfr[2][KN], bfr[KN];
 #pragma unroll
@@ -275,25 +279,23 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
             bfr[kn] = M::load(xc + (rb + t0 + j1 * 16 + lr) * d.C + boff + kn * KS + SL * lg);
         }
         __syncthreads();  // the previous head is done with the LDS
-        stash();
-        if (threadIdx.x < Q) {  // loaded with the head's rows
-            scs[threadIdx.x] = rcs;
-            sdt[threadIdx.x] = rdt;
+        stash(tid);
+        if (tid < Q) {  // loaded with the head's rows
+            scs[tid] = rcs;
+            sdt[tid] = rdt;
         }
-        for (int j = threadIdx.x; j < NW * Q; j += NTH) s_rw[j] = 0.f;
+        for (int j = tid; j < NW * Q; j += NTH) s_rw[j] = 0.f;
         __syncthreads();
         // factored decay unless a sequence starts in the chunk or a tile's span
         // would leave the normal float range
-        int wide = 0;
-        for (int a = threadIdx.x; a < QT; a += NTH) wide |= (scs[16 * a] - scs[16 * a + 15] > 80.f);
-        const bool exact = __syncthreads_or(wide) || split;
+        const bool exact = split || tile_span_wide<QT>(scs, lane);
         if (!exact) {
-            for (int t = threadIdx.x; t < Q; t += NTH) {
+            for (int t = tid; t < Q; t += NTH) {
                 const int t16 = t & ~15;
                 sea[t] = __expf(scs[t] - scs[t16]);
                 seb[t] = __expf(scs[t16 + 15] - scs[t]);
             }
-            for (int q = threadIdx.x; q < QT * QT; q += NTH) {
+            for (int q = tid; q < QT * QT; q += NTH) {
                 const int a = q / QT, c = q % QT;
                 stab[q] = a >= c ? __expf(scs[16 * a] - scs[16 * c + 15]) : 0.f;
             }
@@ -474,13 +476,13 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
         for (int off = 32; off > 0; off >>= 1) ddp += __shfl_xor(ddp, off, 64);
         if (lane % 64 == 0) s_dd[wave] = ddp;
         __syncthreads();
-        for (int t = threadIdx.x; t < Q; t += NTH) {
+        for (int t = tid; t < Q; t += NTH) {
             float rsum = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) rsum += s_rw[w * Q + t];
             rpart[hl + t] = rsum;
         }
-        if (threadIdx.x == 0) {
+        if (tid == 0) {
             float dd = 0.f, gh = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) {

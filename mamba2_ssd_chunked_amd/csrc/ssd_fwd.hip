@@ -260,7 +260,8 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
     }
     // the chunk's cumulative sums, dt and sequence ids, one token per thread
     // (NTH = 2 Q), into registers first: a load followed by its LDS write here
-    // would wait for every load issued before it
+    // would wait for every load issued before it.  (The conv-fused variant,
+    // whose windows hold registers now, writes them to LDS straight away.)
     static_assert(NTH >= Q, "one token per thread");
     float rcs = 0.f, rdt = 0.f;
     int rsq = 0;
@@ -268,6 +269,11 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
         rcs = cs_ws[hl + threadIdx.x];
         rdt = dt_ws[hl + threadIdx.x];
         if (seq) rsq = seq[rb + t0 + threadIdx.x];
+        if constexpr (XC) {
+            scs[threadIdx.x] = rcs;
+            sdt[threadIdx.x] = rdt;
+            ssq[threadIdx.x] = rsq;
+        }
     }
     if constexpr (XC) {
         float taps[VEC][CW];
@@ -287,7 +293,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
             if (idx < Q * (P / VEC)) *(vt*)&sX[(idx / (P / VEC)) * XR + (idx % (P / VEC)) * VEC] = rx[q];
         }
     }
-    if (threadIdx.x < Q) {
+    if (!XC && threadIdx.x < Q) {
         scs[threadIdx.x] = rcs;
         sdt[threadIdx.x] = rdt;
         ssq[threadIdx.x] = rsq;
@@ -296,9 +302,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
     // The factored decay needs every tile's span cs(first) - cs(last) small
     // enough that its exponential stays a normal float; chunks with a sequence
     // start or a wider span take the exact per-element path.
-    int wide = 0;
-    for (int a = threadIdx.x; a < QT; a += NTH) wide |= (scs[16 * a] - scs[16 * a + 15] > 80.f);
-    const bool exact = __syncthreads_or(wide) || split;
+    const bool exact = split || tile_span_wide<QT>(scs, lane);
     if (inter) {
         // entering state [p][n]: zero-state part from the span's own chunks + eps
         // times the state entering the span; eps = exp(sum of the span's earlier

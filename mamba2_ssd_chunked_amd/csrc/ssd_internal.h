@@ -10,6 +10,7 @@
 
 #include <array>
 #include <tuple>
+#include <type_traits>
 #include <utility>
 
 #include "../../include/ssd.h"
@@ -139,6 +140,27 @@ inline dim3 chunk_head_grid(const Dims& d) {
 // so that branches on it compile to scalar branches rather than exec masks.
 __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / 64));
+}
+
+// True if some 16-token tile's decay span (cumulative sum at its first token
+// minus that at its last) exceeds 80, read from the chunk's cumulative sums in
+// LDS.  Every wave evaluates all QT tiles itself (lane a takes tile a), so the
+// workgroup agrees without a barrier.
+template <int QT>
+__device__ __forceinline__ bool tile_span_wide(const float* scs, int lane) {
+    static_assert(QT <= 64, "one tile per lane");
+    const bool w = lane < QT && (scs[16 * lane] - scs[16 * lane + 15] > 80.f);
+    return __ballot(w) != 0ull;
+}
+
+// base + e elements with e a 32-bit lane offset.  With a base that is the same
+// for the whole wave the compiler keeps the base in scalar registers and
+// addresses the access with one vector register holding the byte offset (which
+// must stay below 2^32), instead of a 64-bit address per lane.
+template <typename T>
+__device__ __forceinline__ T* at32(T* base, uint32_t e) {
+    typedef typename std::conditional<std::is_const<T>::value, const char, char>::type B;
+    return (T*)((B*)base + e * (uint32_t)sizeof(T));
 }
 
 // Raw buffer access (gfx9 resource word 3): a resource spans `bytes` bytes from
