@@ -92,6 +92,10 @@ typedef struct {
     float dt_min;       /* clamp bounds of dt, 0 <= dt_min <= dt_max             */
     float dt_max;
 } ssd_problem;
+/* Size limits (SSD_ERR_SHAPE beyond them): with C = nheads * headdim + 2 *
+ * ngroups * dstate channels, chunk * C * sizeof(activation) < 2^31 bytes;
+ * batch and nheads <= 65535; seqlen <= 2^31 - 1; and every launch grid within
+ * the hardware's limits. */
 
 typedef struct {
     int64_t start; /* memory offset of the segment's first token            */

@@ -66,9 +66,10 @@ int check_problem(const ssd_problem* p, Dims* d) {
     if (p->batch > 65535 || p->nheads > 65535 || p->seqlen > INT32_MAX) return SSD_ERR_SHAPE;
     const int64_t C = (int64_t)p->nheads * p->headdim + 2LL * p->ngroups * p->dstate;
     const int64_t esz = p->act_dtype == SSD_BF16 ? 2 : 4;
-    // a token row of xBC must be addressable with 32-bit byte offsets (the conv
-    // backward's buffer accesses), and every launch grid must fit
-    if (C * esz > INT32_MAX) return SSD_ERR_SHAPE;
+    // the token rows of one chunk of xBC must be addressable with 32-bit byte
+    // offsets (the conv backward's buffer accesses, the chunk backward's lane
+    // offsets), and every launch grid must fit
+    if (C * esz * p->chunk > INT32_MAX) return SSD_ERR_SHAPE;
     if (!grids_fit(p, C)) return SSD_ERR_SHAPE;
     d->batch = p->batch;
     d->L = p->seqlen;

@@ -210,6 +210,15 @@ def test_over_long_row_is_refused_before_launching():
     assert ssd.ssd_workspace_bytes(ok, [(0, ok.seqlen)], ssd.SSD_WS_FORWARD) > 0
 
 
+def test_chunk_rows_beyond_31_bit_offsets_are_refused():
+    """chunk x C x sizeof(activation) must stay below 2^31 bytes: 65535 heads of
+    headdim 64 (C = 4194496 channels) at bf16 pass with 128-token chunks and are
+    refused with 256-token chunks."""
+    kw = dict(batch=1, seqlen=256, nheads=65535, headdim=64, dstate=128, ngroups=1)
+    assert ssd.ssd_workspace_bytes(_p(chunk=128, **kw), [(0, 256)], ssd.SSD_WS_FORWARD) > 0
+    assert _conv(_p(chunk=256, **kw), [(0, 256)]) == -2
+
+
 def test_grid_overflow_is_refused():
     """batch x heads x P x N beyond 2^32 work-items of the boundary scan's grid."""
     p = _p(batch=4096, seqlen=256, nheads=4096, headdim=64, dstate=128, chunk=256)
