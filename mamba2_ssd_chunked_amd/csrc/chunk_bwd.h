@@ -176,6 +176,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     const int n1 = NKS - ks1;                  // k steps of column j1
     auto st_of = [&](int h) { return (((int64_t)b * d.nchunk + cm) * d.H + h) * (int64_t)(P * N); };
     auto hl_of = [&](int h) { return ((int64_t)b * d.H + h) * d.L + t0; };
+    const uint32_t Cu = (uint32_t)d.C;  // token row pitch of xBC (32-bit lane offsets)
 
     // ---- staging of dy, G and H of one head (registers, then LDS), and the x
     // rows of the wave's columns j0, j1 (registers, in KPermRow order)
@@ -502,10 +503,23 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     asm volatile("s_mov_b32 %0, 0" : "=s"(opq));
     const int lane2 = threadIdx.x % 64 + opq, lr2 = lane2 % 16, lg2 = lane2 / 16;
     constexpr int V_T = (N * (Q / VEC) + NTH - 1) / NTH;
-    auto stage_rows = [&](int64_t choff) {  // B or C rows of the chunk -> sBT [Q][BR]
-        for (int idx = threadIdx.x; idx < Q * (N / VEC); idx += NTH) {
-            const int j = idx / (N / VEC), nv = idx % (N / VEC);
-            *(vt*)&sBT[j * BR + nv * VEC] = *(const vt*)(xc + (rb + t0 + j) * d.C + choff + nv * VEC);
+    // B or C rows of the chunk -> sBT [Q][BR]: every load of the thread before
+    // the first LDS write (a load followed by its write would wait for it
+    // before the next load is issued)
+    auto stage_rows = [&](int64_t choff) {
+        vt rv[V_T];
+        const T* const src = xc + (rb + t0) * d.C + choff;
+#pragma unroll
+        for (int q = 0; q < V_T; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (V_T * NTH == Q * (N / VEC) || idx < Q * (N / VEC))
+                rv[q] = *(const vt*)at32(src, (uint32_t)(idx / (N / VEC)) * Cu + (idx % (N / VEC)) * VEC);
+        }
+#pragma unroll
+        for (int q = 0; q < V_T; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (V_T * NTH == Q * (N / VEC) || idx < Q * (N / VEC))
+                *(vt*)&sBT[(idx / (N / VEC)) * BR + (idx % (N / VEC)) * VEC] = rv[q];
         }
     };
     T* const dbp = dbcp + (int64_t)hbi * 2 * N;
