@@ -139,8 +139,11 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     __shared__ __attribute__((aligned(16))) float seb[Q];  // exp(L(t) - cs_t)
     __shared__ __attribute__((aligned(16))) int ssq[Q];
     __shared__ float stab[QT * QT];  // exp(F_a - L_b), a >= b
-    __shared__ float s_dd[NW];
-    __shared__ float s_gh[NW];  // per-wave parts of <G, H> of the current head
+    // per-wave parts of dy . x and <G, H> of a head, by head parity (a head's are
+    // summed after the next head's first barrier, while the next head writes
+    // its own)
+    __shared__ float s_dd[2][NW];
+    __shared__ float s_gh[2][NW];
 
     // block -> (head block, chunk, row); the head blocks of a chunk are adjacent
     // items, and consecutive items go to one XCD
@@ -217,7 +220,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
             }
         }
     };
-    auto stash = [&](int tid) {
+    auto stash = [&](int tid, int par) {
 #pragma unroll
         for (int q = 0; q < V_X; ++q) {
             const int idx = tid + q * NTH;
@@ -240,7 +243,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) gh += __shfl_xor(gh, off, 64);
-        if (tid % 64 == 0) s_gh[wave] = gh;
+        if (tid % 64 == 0) s_gh[par][wave] = gh;
     };
 
     f32x4 Z[NB][TPK];
@@ -259,6 +262,32 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
             *(vt*)&sGm[idx * VEC] = *(const vt*)(gsrc + (int64_t)idx * VEC);
     }
 
+    // The end of head h (parity par), once every wave is past its k steps: the
+    // token row sums of F (rpart; each thread then clears the s_rw entries it
+    // read, for the next head), dy . x and <G, H>.
+    auto finish_head = [&](int h, int par, int tid) {
+        const int64_t hl = hl_of(h);
+        for (int t = tid; t < Q; t += NTH) {
+            float rsum = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                rsum += s_rw[w * Q + t];
+                s_rw[w * Q + t] = 0.f;
+            }
+            *at32(rpart + hl, t) = rsum;
+        }
+        if (tid == 0) {
+            float dd = 0.f, gh = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                dd += s_dd[par][w];
+                gh += s_gh[par][w];
+            }
+            red4[((int64_t)b * d.nchunk + cm) * d.H + h] = dd;
+            dotgh[((int64_t)b * d.nchunk + cm) * d.H + h] = gh;
+        }
+    };
+    for (int j = threadIdx.x; j < NW * Q; j += NTH) s_rw[j] = 0.f;  // ordered by the first barrier
     for (int hh = 0; hh < hbs; ++hh) {
         const int h = h0 + hh;
         const int64_t hl = hl_of(h);
@@ -280,12 +309,12 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
             bfr[kn] = M::load(xc + (rb + t0 + j1 * 16 + lr) * d.C + boff + kn * KS + SL * lg);
         }
         __syncthreads();  // the previous head is done with the LDS
-        stash(tid);
+        if (hh > 0) finish_head(h - 1, (hh - 1) & 1, tid);
+        stash(tid, hh & 1);
         if (tid < Q) {  // loaded with the head's rows
             scs[tid] = rcs;
             sdt[tid] = rdt;
         }
-        for (int j = tid; j < NW * Q; j += NTH) s_rw[j] = 0.f;
         __syncthreads();
         // factored decay unless a sequence starts in the chunk or a tile's span
         // would leave the normal float range
@@ -475,25 +504,10 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
 
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) ddp += __shfl_xor(ddp, off, 64);
-        if (lane % 64 == 0) s_dd[wave] = ddp;
-        __syncthreads();
-        for (int t = tid; t < Q; t += NTH) {
-            float rsum = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) rsum += s_rw[w * Q + t];
-            rpart[hl + t] = rsum;
-        }
-        if (tid == 0) {
-            float dd = 0.f, gh = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                dd += s_dd[w];
-                gh += s_gh[w];
-            }
-            red4[((int64_t)b * d.nchunk + cm) * d.H + h] = dd;
-            dotgh[((int64_t)b * d.nchunk + cm) * d.H + h] = gh;
-        }
+        if (lane % 64 == 0) s_dd[hh & 1][wave] = ddp;
     }
+    __syncthreads();  // every wave is past the last head's k steps
+    finish_head(h0 + hbs - 1, (hbs - 1) & 1, threadIdx.x);
 
     // ================= dB and dC of the head block =================
     // dB first (Z from registers, then the exit-gradient terms), then dC (Z

@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(256) k_conv1d_silu(Dims d, SegTab tab, const T
 
 // The whole conv pass and dt prep in one launch: the grid's first gx channel
 // blocks convolve; the extra ones (their (x - gx, y) numbered within the row)
-// run dt prep for four heads of one chunk each, one head per wave.  The conv is
+// run dt prep for DTB heads of one chunk each (dt_prep_block).  The conv is
 // bound by memory bandwidth and dt prep by latency, so the two overlap.
 template <typename T, int W>
 __global__ void __launch_bounds__(256) k_conv1d_silu_dt(Dims d, SegTab tab,
@@ -125,12 +125,11 @@ __global__ void __launch_bounds__(256) k_conv1d_silu_dt(Dims d, SegTab tab,
                          blockIdx.z);
         return;
     }
+    __shared__ DtLds sm;
     const int64_t item = (int64_t)(blockIdx.x - gx) * gridDim.y + blockIdx.y;
-    if (item >= (int64_t)d.nchunk * ((d.H + 3) / 4)) return;
-    const int cm = (int)(item % d.nchunk), h = (int)(item / d.nchunk) * 4 + wave_id();
-    if (h >= d.H) return;
-    dt_prep_wave<T>(d, dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot, cm, h, blockIdx.z,
-                    threadIdx.x % 64);
+    if (item >= (int64_t)d.nchunk * ((d.H + DTB - 1) / DTB)) return;  // whole workgroup
+    const int cm = (int)(item % d.nchunk), h0 = (int)(item / d.nchunk) * DTB;
+    dt_prep_block<T>(d, dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot, cm, h0, blockIdx.z, sm);
 }
 
 template <typename T, int W>
@@ -182,7 +181,7 @@ static hipError_t launch_dt_w(const Dims& d, const SegTab& t, const void* xBC, c
                               float* cs_ws, float* ctot, hipStream_t s) {
     const int gx = (d.C + 64 * CONV_VEC - 1) / (64 * CONV_VEC);
     const int gy = (int)(d.L / CONV_TT);
-    const int items = d.nchunk * ((d.H + 3) / 4);  // dt prep workgroups per row
+    const int items = d.nchunk * ((d.H + DTB - 1) / DTB);  // dt prep workgroups per row
     const dim3 grid((unsigned)(gx + (items + gy - 1) / gy), (unsigned)gy, (unsigned)d.batch);
     return launch(k_conv1d_silu_dt<T, W>, grid, dim3(256), s, d, t, (const T*)xBC, w, seq, gx,
                   (T*)out, (const T*)dt_raw, dt_bias, A_log, dt_ws, cs_ws, ctot);

@@ -37,12 +37,12 @@ bool grids_fit(const ssd_problem* p, int64_t C) {
     const u128 cx = (CC + 255) / 256;  // conv workgroups along channels
     bool ok = x_ok(cx, 256) && L / 64 <= 65535 && b <= 65535;                   // conv forward
     const u128 ty = L / 64 > 0 ? L / 64 : 1;
-    ok = ok && x_ok(cx + (nc * ((H + 3) / 4) + ty - 1) / ty, 256);                // conv + dt prep
+    ok = ok && x_ok(cx + (nc * ((H + 7) / 8) + ty - 1) / ty, 256);                // conv + dt prep
     ok = ok && x_ok(nc * G * b * (Q / 32), Q / 32 * 64);                           // Gram + dt prep
     ok = ok && x_ok(2 * H * nseg * b, 512);                                        // state walks
     ok = ok && x_ok(nc * H * b, 512);                                              // output passes
     ok = ok && x_ok((b * H * PN / 4 + 255) / 256, 256);                            // boundary scan
-    ok = ok && nc <= 0x7fffffffu && (H + 3) / 4 <= 65535;                         // dt prep alone
+    ok = ok && nc <= 0x7fffffffu && (H + 7) / 8 <= 65535;                         // dt prep alone
     ok = ok && x_ok((b * L * G * 2 * (u128)p->dstate / 4 + 255) / 256, 256);       // dB, dC sums
     ok = ok && x_ok(cx * (L / 64) * b + (nc * H * b + 3) / 4, 256);                // conv backward
     ok = ok && x_ok((CC * (u128)p->conv_width + 3 * H + 31) / 32, 256);            // reductions

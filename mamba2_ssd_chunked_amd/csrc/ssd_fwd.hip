@@ -53,7 +53,7 @@ template <> struct KPerm<float> {
 };
 
 // ---------------------------------------------------------------------------
-// dt prep on its own (the paths without Gram tiles), four heads per workgroup.
+// dt prep on its own, DTB heads of one chunk per workgroup.
 template <typename T>
 __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ dt_raw,
                                                 const float* __restrict__ dt_bias,
@@ -61,10 +61,9 @@ __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ d
                                                 const int32_t* __restrict__ seq,
                                                 float* __restrict__ dt_ws, float* __restrict__ cs_ws,
                                                 float* __restrict__ ctot) {
-    const int h = blockIdx.y * 4 + wave_id();
-    if (h >= d.H) return;
-    dt_prep_wave<T>(d, dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot, blockIdx.x, h, blockIdx.z,
-                    threadIdx.x % 64);
+    __shared__ DtLds sm;
+    dt_prep_block<T>(d, dt_raw, dt_bias, A_log, seq, dt_ws, cs_ws, ctot, blockIdx.x,
+                     blockIdx.y * DTB, blockIdx.z, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -727,7 +726,7 @@ static hipError_t apply_init_t(const Dims& d, const SegTab& t, const float* y_ze
 hipError_t launch_dt_prep(const Dims& d, int act, const void* dt_raw, const float* dt_bias,
                           const float* A_log, const int32_t* seq, float* dt_ws, float* cs_ws,
                           float* ctot, hipStream_t s) {
-    const dim3 grid((unsigned)d.nchunk, (unsigned)((d.H + 3) / 4), (unsigned)d.batch);
+    const dim3 grid((unsigned)d.nchunk, (unsigned)((d.H + DTB - 1) / DTB), (unsigned)d.batch);
     if (act == SSD_BF16)
         return launch(k_dt_prep<bf16>, grid, dim3(256), s, d, (const bf16*)dt_raw, dt_bias, A_log,
                       seq, dt_ws, cs_ws, ctot);
