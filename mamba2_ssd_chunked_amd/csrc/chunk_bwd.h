@@ -102,7 +102,7 @@ struct ChunkBwdHB {
     static constexpr int O_BT = zoff(QT), E_FIN = O_BT + Q * BR, E_FS = O_BT + HG * P * GR;
     static constexpr int E_U = cmax(E_HEAD, cmax(E_FIN, E_FS));
     static constexpr size_t LDS =
-        (size_t)E_U * sizeof(T) + (size_t)Q * 20 + (size_t)QT * QT * 4 + (size_t)NW * 4 + 64;
+        (size_t)E_U * sizeof(T) + (size_t)Q * 20 + (size_t)QT * QT * 4 + (size_t)NW * 16 + 64;
     static_assert(QT % 2 == 0 && P % KS == 0 && N % KS == 0, "shape");
 };
 

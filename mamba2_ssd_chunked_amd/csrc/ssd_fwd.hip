@@ -138,7 +138,6 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
     __shared__ __attribute__((aligned(16))) float sea[Q];  // exp(cs_t - F(t))
     __shared__ __attribute__((aligned(16))) float seb[Q];  // exp(L(t) - cs_t) dt_t
     __shared__ __attribute__((aligned(16))) int ssq[Q];
-    __shared__ float stab[QT * QT];                         // exp(F_a - L_b), a >= b
 
     const ChunkHead ch = chunk_head_of_block(d);
     const int cm = ch.cm, h = ch.h;
@@ -292,17 +291,26 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
             if (idx < Q * (P / VEC)) *(vt*)&sX[(idx / (P / VEC)) * XR + (idx % (P / VEC)) * VEC] = rx[q];
         }
     }
+    // the factored decay's token factors (unused on the exact path), from the
+    // cumulative sums at the first and last token of the token's 16-token tile
+    auto tables_lds = [&]() {  // from the cumulative sums in LDS
+        for (int t = threadIdx.x; t < Q; t += NTH) {
+            const int t16 = t & ~15;
+            sea[t] = __expf(scs[t] - scs[t16]);
+            seb[t] = __expf(scs[t16 + 15] - scs[t]) * sdt[t];
+        }
+    };
     if (!XC && threadIdx.x < Q) {
         scs[threadIdx.x] = rcs;
         sdt[threadIdx.x] = rdt;
         ssq[threadIdx.x] = rsq;
+        // from registers: lanes of this wave hold the tile's first and last
+        // token (Q = NTH / 2: whole waves take this branch)
+        const float cf = __shfl(rcs, lane & ~15, 64), cl = __shfl(rcs, lane | 15, 64);
+        sea[threadIdx.x] = __expf(rcs - cf);
+        seb[threadIdx.x] = __expf(cl - rcs) * rdt;
     }
-    __syncthreads();
-    // The factored decay needs every tile's span cs(first) - cs(last) small
-    // enough that its exponential stays a normal float; chunks with a sequence
-    // start or a wider span take the exact per-element path.
-    const bool exact = split || tile_span_wide<QT>(scs, lane);
-    if (inter) {
+    auto stage_state = [&]() {
         // entering state [p][n]: zero-state part from the span's own chunks + eps
         // times the state entering the span; eps = exp(sum of the span's earlier
         // chunk totals), 0 if a sequence started between the span start and
@@ -327,19 +335,23 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
                 *(vt*)&sH[(idx / (N / VEC)) * HP + (idx % (N / VEC)) * VEC] = v;
             }
         }
-    }
-    if (!exact) {
-        for (int t = threadIdx.x; t < Q; t += NTH) {
-            const int t16 = t & ~15;
-            sea[t] = __expf(scs[t] - scs[t16]);
-            seb[t] = __expf(scs[t16 + 15] - scs[t]) * sdt[t];
-        }
-        for (int q = threadIdx.x; q < QT * QT; q += NTH) {
-            const int a = q / QT, c = q % QT;
-            stab[q] = a >= c ? __expf(scs[16 * a] - scs[16 * c + 15]) : 0.f;
-        }
+    };
+    // The entering state goes to LDS before the barrier; the conv-fused variant
+    // loads the chunk totals for eps only after it, and stages the state behind
+    // a second barrier.
+    if constexpr (!XC) {
+        if (inter) stage_state();
     }
     __syncthreads();
+    // The factored decay needs every tile's span cs(first) - cs(last) small
+    // enough that its exponential stays a normal float; chunks with a sequence
+    // start or a wider span take the exact per-element path.
+    const bool exact = split || tile_span_wide<QT>(scs, lane);
+    if constexpr (XC) {
+        if (inter) stage_state();
+        tables_lds();
+        __syncthreads();
+    }
 
     // Gram tiles of the wave's output tiles, DEPTH k steps ahead of their use
     // (the first ones overlap the inter-chunk term).  A source tile past the
@@ -405,7 +417,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
         const int js = bt * 16;
         const int i = i0[it] + lr;
         if (!exact) {
-            const float rsc = rsc_i[it] * stab[at * QT + bt];
+            const float rsc = rsc_i[it] * __expf(scs[16 * at] - scs[16 * bt + 15]);
             const f32x4 ej = *(const f32x4*)&seb[js + 4 * lg];
 #pragma unroll
             for (int r = 0; r < 4; ++r) vv[r] = (float)cgv[r] * (rsc * ej[r]);
