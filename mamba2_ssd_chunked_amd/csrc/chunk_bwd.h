@@ -60,10 +60,19 @@ template <> struct KPermRow<bf16> {
         const bf16x4 hi = *(const bf16x4*)(row + 16 + 4 * lg);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
+    // the row at base + off (elements, a 32-bit lane offset: see at32)
+    __device__ static __forceinline__ bf16x8 load(const bf16* base, uint32_t off, int lg) {
+        const bf16x4 lo = *(const bf16x4*)at32(base, off + 4 * lg);
+        const bf16x4 hi = *(const bf16x4*)at32(base, off + 16 + 4 * lg);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
 };
 template <> struct KPermRow<float> {
     __device__ static __forceinline__ f32x4 load(const float* row, int lg) {
         return *(const f32x4*)(row + 4 * lg);
+    }
+    __device__ static __forceinline__ f32x4 load(const float* base, uint32_t off, int lg) {
+        return *(const f32x4*)at32(base, off + 4 * lg);
     }
 };
 
@@ -98,7 +107,7 @@ struct ChunkBwdHB {
     // final phase: Z rows and C^T (then G of HG heads), later B^T and H
     // heads per round of state terms: 2 below Q = 256 keeps the LDS of a
     // workgroup within half a CU's, so two workgroups share a CU
-    static constexpr int HG = Q >= 256 ? 4 : 2;
+    static constexpr int HG = 2;
     static constexpr int O_BT = zoff(QT), E_FIN = O_BT + Q * BR, E_FS = O_BT + HG * P * GR;
     static constexpr int E_U = cmax(E_HEAD, cmax(E_FIN, E_FS));
     static constexpr size_t LDS =
@@ -545,7 +554,10 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) ab[c][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
-    auto ab_store = [&](int part) {
+    // lane ids are passed in: each part takes them from its own opaque zero, so
+    // that the addresses derived from them are recomputed per part instead of
+    // being held (and spilled) across the other part
+    auto ab_store = [&](int part, int lr2, int lg2) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             T* o = dbp + (rb + t0 + (c == 0 ? j0 : j1) * 16 + lr2) * dbs + part * N;
@@ -561,7 +573,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     // transposed (XT), the rows in the matching k order
     constexpr int HG = K::HG;
     constexpr int V_GT = (P * (N / VEC) + NTH - 1) / NTH;
-    auto state_terms = [&](bool dB, T* sS) {
+    auto state_terms = [&](bool dB, T* sS, int lane2, int lr2, int lg2) {
         for (int hf = 0; hf < hbs; hf += HG) {
             vt rs[HG][V_GT];
             Frag rr[HG][2][KP];
@@ -587,8 +599,10 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
                     const int t = (c == 0 ? j0 : j1) * 16 + lr2;
 #pragma unroll
                     for (int kp = 0; kp < KP; ++kp)
-                        rr[q][c][kp] = dB ? KPermRow<T>::load(xc + (rb + t0 + t) * d.C + (int64_t)h * P + kp * KS, lg2)
-                                          : KPermRow<T>::load(dy + (rb + t0 + t) * HPd + (int64_t)h * P + kp * KS, lg2);
+                        rr[q][c][kp] = dB ? KPermRow<T>::load(xc + (rb + t0) * d.C + (int64_t)h * P,
+                                                              (uint32_t)t * Cu + kp * KS, lg2)
+                                          : KPermRow<T>::load(dy + (rb + t0) * HPd + (int64_t)h * P,
+                                                              (uint32_t)(t * HPd + kp * KS), lg2);
                     cst_r[q][c] = cs_ws[hl + t];
                     dt_r[q][c] = dB ? dt_ws[hl + t] : 0.f;
                 }
@@ -687,11 +701,15 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
                 ab[0][nt] = M::mma(XT<T>::load(sBT, BR, ks * KS, nt * 16, lane2), zf, ab[0][nt]);
         }
     }
-    state_terms(true, sBT);  // G goes where the C rows were (the Z rows stay)
-    ab_store(0);
+    state_terms(true, sBT, lane2, lr2, lg2);  // G goes where the C rows were (the Z rows stay)
+    ab_store(0, lr2, lg2);
 
     // ---- dC^T [n][i] = sum_j B^T[n][j] Z[i][j] + state terms (B^T read transposed)
     __syncthreads();  // every wave is done with sBT
+    int opq3;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(opq3));
+    {
+    const int lane2 = threadIdx.x % 64 + opq3, lr2 = lane2 % 16, lg2 = lane2 / 16;
     stage_rows(boff);
     __syncthreads();
     ab_zero();
@@ -713,8 +731,9 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
                 ab[it][nt] = M::mma(XT<T>::load(sBT, BR, ks * KS, nt * 16, lane2), zf, ab[it][nt]);
         }
     }
-    state_terms(false, sZ);  // H^T goes where the Z rows were (after the first sync)
-    ab_store(1);
+    state_terms(false, sZ, lane2, lr2, lg2);  // H^T goes where the Z rows were (after the first sync)
+    ab_store(1, lr2, lg2);
+    }
 }
 
 }  // namespace ssd
