@@ -413,11 +413,21 @@ __global__ void __launch_bounds__(Q / 32 * 64, (P <= 64 ? 4 : 1)) k_chunk_y(Dims
     const float Dh = FINAL ? Dp[h] : 0.f;
 
     // ---- intra-chunk term, one 32-token (KS = 32) or 16-token (KS = 16) k step at a time
+    // the tile factor exp(F_a - L_b) of the wave's output tile a (it = 0, 1) and
+    // source tile b <= a, held by lane b and read with readlane in the k steps
+    // (a wave-uniform value: no LDS access per step)
+    float stw[2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int at = it == 0 ? a0 : a1, l = lane < QT ? lane : 0;
+        stw[it] = (!exact && l <= at) ? __expf(scs[16 * at] - scs[16 * l + 15]) : 0.f;
+    }
     auto weight = [&](int it, int at, int bt, const t4& cgv, float (&vv)[4]) {
         const int js = bt * 16;
         const int i = i0[it] + lr;
         if (!exact) {
-            const float rsc = rsc_i[it] * __expf(scs[16 * at] - scs[16 * bt + 15]);
+            const float rsc = rsc_i[it] * __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, stw[it]), bt));
             const f32x4 ej = *(const f32x4*)&seb[js + 4 * lg];
 #pragma unroll
             for (int r = 0; r < 4; ++r) vv[r] = (float)cgv[r] * (rsc * ej[r]);
