@@ -105,8 +105,9 @@ struct ChunkBwdHB {
     static constexpr int O_GM = O_RW + NW * Q * 4 / (int)sizeof(T);
     static constexpr int E_HEAD = O_GM + gram_tiles(QT) * 256;
     // final phase: Z rows and C^T (then G of HG heads), later B^T and H
-    // heads per round of state terms: 2 below Q = 256 keeps the LDS of a
-    // workgroup within half a CU's, so two workgroups share a CU
+    // heads per round of state terms: two keep a round's loaded rows beside the
+    // dB / dC accumulators within the register file (four spilled), and below
+    // Q = 256 keep the LDS of a workgroup within half a CU's
     static constexpr int HG = 2;
     static constexpr int O_BT = zoff(QT), E_FIN = O_BT + Q * BR, E_FS = O_BT + HG * P * GR;
     static constexpr int E_U = cmax(E_HEAD, cmax(E_FIN, E_FS));

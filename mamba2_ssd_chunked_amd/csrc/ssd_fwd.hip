@@ -3,6 +3,9 @@
 // Kernels, in launch order:
 //   k_dt_prep      dt = clamp(softplus(dt_raw + dt_bias)), l = dt*A, and the
 //                  chunk-local inclusive cumsum cs of l, per (row, head, chunk).
+//   k_walk_gram    (walk_gram.h) the state walk below and the group Gram tiles
+//                  (gram.h) in one launch; shapes it does not fit launch the
+//                  Gram tiles with dt prep (k_gram_dt), then k_state_walk.
 //   k_state_walk   (state_walk.h) one workgroup per (row, segment, head) walks
 //                  the segment's chunks in causal order.  The running state H (P x N, FP32)
 //                  lives in MFMA accumulators: for chunk c it first writes H
@@ -73,7 +76,7 @@ __global__ void __launch_bounds__(256) k_dt_prep(Dims d, const T* __restrict__ d
 //
 // For output token i and source token j <= i of the same packed sequence the
 // intra-chunk weight is (C_i . B_j) exp(cs_i - cs_j) dt_j.  C_i . B_j comes
-// from the group's Gram tiles (k_gram_dt); every load the workgroup needs (X of the
+// from the group's Gram tiles (gram.h); every load the workgroup needs (X of the
 // head in its natural layout, the entering state, the Gram tiles of the wave's
 // two output tiles, the decays) is issued up front, so one memory latency is
 // paid per workgroup and about 58 KB of LDS lets two workgroups share a CU.
