@@ -112,7 +112,7 @@ struct ChunkBwdHB {
     static constexpr int O_BT = zoff(QT), E_FIN = O_BT + Q * BR, E_FS = O_BT + HG * P * GR;
     static constexpr int E_U = cmax(E_HEAD, cmax(E_FIN, E_FS));
     static constexpr size_t LDS =
-        (size_t)E_U * sizeof(T) + (size_t)Q * 20 + (size_t)QT * QT * 4 + (size_t)NW * 16 + 64;
+        (size_t)E_U * sizeof(T) + (size_t)Q * 20 + (size_t)NW * 16 + 64;
     static_assert(QT % 2 == 0 && P % KS == 0 && N % KS == 0, "shape");
 };
 
@@ -148,7 +148,6 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     __shared__ __attribute__((aligned(16))) float sea[Q];  // exp(cs_t - F(t))
     __shared__ __attribute__((aligned(16))) float seb[Q];  // exp(L(t) - cs_t)
     __shared__ __attribute__((aligned(16))) int ssq[Q];
-    __shared__ float stab[QT * QT];  // exp(F_a - L_b), a >= b
     // per-wave parts of dy . x and <G, H> of a head, by head parity (a head's are
     // summed after the next head's first barrier, while the next head writes
     // its own)
@@ -324,23 +323,18 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
         if (tid < Q) {  // loaded with the head's rows
             scs[tid] = rcs;
             sdt[tid] = rdt;
+            // the factored decay's token factors (unused on the exact path), from
+            // the cumulative sums at the first and last token of the token's
+            // 16-token tile, which lanes of this wave hold (Q = NTH / 2: whole
+            // waves take this branch)
+            const float cf = __shfl(rcs, lane & ~15, 64), cl = __shfl(rcs, lane | 15, 64);
+            sea[tid] = __expf(rcs - cf);
+            seb[tid] = __expf(cl - rcs);
         }
         __syncthreads();
         // factored decay unless a sequence starts in the chunk or a tile's span
         // would leave the normal float range
         const bool exact = split || tile_span_wide<QT>(scs, lane);
-        if (!exact) {
-            for (int t = tid; t < Q; t += NTH) {
-                const int t16 = t & ~15;
-                sea[t] = __expf(scs[t] - scs[t16]);
-                seb[t] = __expf(scs[t16 + 15] - scs[t]);
-            }
-            for (int q = tid; q < QT * QT; q += NTH) {
-                const int a = q / QT, c = q % QT;
-                stab[q] = a >= c ? __expf(scs[16 * a] - scs[16 * c + 15]) : 0.f;
-            }
-        }
-        __syncthreads();
         const float cs_e = scs[Q - 1];
         const float Dh = Dp[h];
         float ddp = 0.f;  // dy . x over the wave's tokens
@@ -373,6 +367,9 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
         // ---- one column tile: its state part, its k steps, its outputs
         int jc = 0;
         float csj = 0.f, dtj = 0.f, e2j = 0.f, vj = 0.f, kacc = 0.f;
+        // the column's tile factors exp(F_a - L_jc), a >= jc: lane a holds row
+        // tile a's, read with readlane in the k steps
+        float stc = 0.f;
         int sqj = 0;
         f32x4 acc[PT];
         Frag xB[KP];
@@ -386,6 +383,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
             dtj = sdt[j];
             sqj = ssq[j];
             e2j = exact ? 0.f : seb[j];
+            stc = (!exact && lane < QT && lane >= jc) ? __expf(scs[16 * lane] - scs[16 * jc + 15]) : 0.f;
             const float gj = (sqj == seq_e) ? __expf(cs_e - csj) : 0.f;
 #pragma unroll
             for (int kp = 0; kp < KP; ++kp) xB[kp] = xq[kp];
@@ -422,7 +420,8 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
                         w = M::mma(KPermRow<T>::load(&sD[(16 * a + lr) * XR + kp * KS], lg), xB[kp], w);
                     const int ib = 16 * a + 4 * lg;
                     if (!exact) {
-                        const float bj = stab[a * QT + jc] * e2j;
+                        const float bj = __builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, stc), a)) * e2j;
                         const f32x4 ea = *(const f32x4*)&sea[ib];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) dd[r] = ea[r] * bj;
