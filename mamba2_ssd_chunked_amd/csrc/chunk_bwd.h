@@ -340,28 +340,36 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
         float ddp = 0.f;  // dy . x over the wave's tokens
 
         // u_i = f_i dy_i . (H C_i) for the wave's two tiles as rows
+        // (both tiles from each H fragment read)
         float u[2];
+        {
+            f32x4 ys[2][PT];
 #pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int i = (it == 0 ? j0 : j1) * 16 + lr;
-            f32x4 ys[PT];
+            for (int it = 0; it < 2; ++it)
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) ys[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int pt = 0; pt < PT; ++pt) ys[it][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kn = 0; kn < KN; ++kn)
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-                    ys[pt] = M::mma(M::load(&sH[(pt * 16 + lr) * GR + kn * KS + SL * lg]), cfr[it][kn], ys[pt]);
-            float up = 0.f;
+                for (int pt = 0; pt < PT; ++pt) {
+                    const Frag hf = M::load(&sH[(pt * 16 + lr) * GR + kn * KS + SL * lg]);
+                    ys[0][pt] = M::mma(hf, cfr[0][kn], ys[0][pt]);
+                    ys[1][pt] = M::mma(hf, cfr[1][kn], ys[1][pt]);
+                }
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                float dyv[4];
-                load4(&sD[i * XR + pt * 16 + 4 * lg], dyv);
+            for (int it = 0; it < 2; ++it) {
+                const int i = (it == 0 ? j0 : j1) * 16 + lr;
+                float up = 0.f;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) up += dyv[r] * ys[pt][r];
+                for (int pt = 0; pt < PT; ++pt) {
+                    float dyv[4];
+                    load4(&sD[i * XR + pt * 16 + 4 * lg], dyv);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) up += dyv[r] * ys[it][pt][r];
+                }
+                const float f_i = (ssq[i] == seq_refc) ? __expf(scs[i]) : 0.f;
+                u[it] = f_i * sum_groups(up);
             }
-            const float f_i = (ssq[i] == seq_refc) ? __expf(scs[i]) : 0.f;
-            u[it] = f_i * sum_groups(up);
         }
 
         // ---- one column tile: its state part, its k steps, its outputs
