@@ -643,15 +643,18 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
                 if (hf + q < hbs) {
                     const T* sq_ = sS + q * P * GR;
 #pragma unroll
-                    for (int c = 0; c < 2; ++c) {
+                    for (int kp = 0; kp < KP; ++kp) {
+                        // both tiles from each S fragment read
+                        Frag sf[2];
 #pragma unroll
-                        for (int kp = 0; kp < KP; ++kp) {
-                            Frag sf;
+                        for (int c = 0; c < 2; ++c)
 #pragma unroll
-                            for (int e = 0; e < SL; ++e) sf[e] = (E)((float)rr[q][c][kp][e] * sc[q][c]);
+                            for (int e = 0; e < SL; ++e) sf[c][e] = (E)((float)rr[q][c][kp][e] * sc[q][c]);
 #pragma unroll
-                            for (int nt = 0; nt < NT; ++nt)
-                                ab[c][nt] = M::mma(XT<T>::load(sq_, GR, kp * KS, nt * 16, lane2), sf, ab[c][nt]);
+                        for (int nt = 0; nt < NT; ++nt) {
+                            const Frag xs = XT<T>::load(sq_, GR, kp * KS, nt * 16, lane2);
+                            ab[0][nt] = M::mma(xs, sf[0], ab[0][nt]);
+                            ab[1][nt] = M::mma(xs, sf[1], ab[1][nt]);
                         }
                     }
                 }
@@ -721,11 +724,11 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     stage_rows(boff);
     __syncthreads();
     ab_zero();
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int a = it == 0 ? j0 : j1;
-        const T* zr = sZ + K::zoff(a) + lr2 * K::zpitch(a);
-        for (int ks = 0; ks <= a / TPK; ++ks) {
+    {
+        // the row tiles j0 < j1 over their k steps, both from each B^T fragment
+        // read while both have the step
+        auto zrow = [&](int a, int ks) {
+            const T* zr = sZ + K::zoff(a) + lr2 * K::zpitch(a);
             Frag zf;
             if constexpr (TPK == 2) {
                 const t4 lo = *(const t4*)&zr[ks * KS + 4 * lg2];
@@ -734,9 +737,18 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
             } else {
                 zf = *(const Frag*)&zr[ks * KS + 4 * lg2];
             }
+            return zf;
+        };
+        for (int ks = 0; ks <= j1 / TPK; ++ks) {
+            const bool both = ks <= j0 / TPK;  // wave-uniform
+            const Frag zf1 = zrow(j1, ks);
+            const Frag zf0 = both ? zrow(j0, ks) : zf1;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                ab[it][nt] = M::mma(XT<T>::load(sBT, BR, ks * KS, nt * 16, lane2), zf, ab[it][nt]);
+            for (int nt = 0; nt < NT; ++nt) {
+                const Frag xs = XT<T>::load(sBT, BR, ks * KS, nt * 16, lane2);
+                if (both) ab[0][nt] = M::mma(xs, zf0, ab[0][nt]);
+                ab[1][nt] = M::mma(xs, zf1, ab[1][nt]);
+            }
         }
     }
     state_terms(false, sZ, lane2, lr2, lg2);  // H^T goes where the Z rows were (after the first sync)
