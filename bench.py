@@ -102,7 +102,7 @@ def source_digest():
 
 
 def kernel_short(sym):
-    """Kernel name with its mangled template arguments, e.g. k_state_pass<DF16bLi64ELi128ELi1>."""
+    """Kernel name with its mangled template arguments, e.g. k_state_walk_pair<DF16bLi64ELi128ELb0ELi2E>."""
     import re
     m = re.match(r"_ZN3ssd\d+(k_\w+?)I(.*?)EEv", sym)
     if m:

@@ -5,21 +5,21 @@
 // intermediate instead of saving it.  Here:
 //
 //   summary phase (ssd_segment_bwd_summary)
-//     conv recompute -> xBC_conv (+ a chunk-transposed copy of the B and C
-//     channels, k_bc_transpose), dt/cumsum recompute (k_dt_prep), every
-//     chunk's own contribution to the state and to the state gradient, in
-//     parallel over chunks (k_bwd_chunk_states), and the reverse passing of
-//     those contributions inside each segment (k_state_pass) that leaves, per
-//     segment, dL/dS_in of the segment's own outputs and its block decay, in
-//     the same packed layout as the forward summary.
+//     conv recompute -> xBC_conv and dt/cumsum recompute in one launch
+//     (k_conv1d_silu_dt), then the reverse walk of every segment from a zero
+//     state gradient and the chunk's causal Gram tiles in transposed
+//     orientation, in one launch (k_walk_gram<bwd, TRANS>; other shapes run
+//     k_gram_dt<TRANS> and k_state_walk<bwd>), which leaves, per segment,
+//     dL/dS_in of the segment's own outputs and its block decay, in the same
+//     packed layout as the forward summary.
 //   reverse boundary scan (ssd_boundary_scan, reverse = 1) -> the gradient of
 //     every segment's final state.
-//   pass phase (ssd_segment_bwd_pass): the true exit gradient and entering
-//     state of every chunk (the reverse walk from dS_out and the forward walk
-//     from S_in; k_state_pass on the headdim-128 path).
-//   chunk phase (ssd_segment_bwd_chunks): k_chunk_bwd per chunk and head: dx,
-//     dB, dC and the ddt partial sums, written into the buffers the conv
-//     backward consumes.
+//   pass phase (ssd_segment_bwd_pass): the exit gradient and the entering
+//     state of every chunk, the reverse walk from dS_out and the forward walk
+//     from S_in as the two halves of one launch (k_state_walk_pair).
+//   chunk phase (ssd_segment_bwd_chunks): k_chunk_bwd_hb per chunk and block
+//     of heads of one group: dx, dB, dC and the ddt partial sums, written into
+//     the buffers the conv backward consumes.
 //   conv phase (ssd_conv1d_bwd): k_bc_blocksum (dB, dC summed over head
 //     blocks), k_conv_bwd_ddt (SiLU' and the transposed conv, with a right halo
 //     from the causal successor segment, and in the same launch the ddt
