@@ -28,9 +28,12 @@
 // NKS + 1 fixed register slots of Z (column QT-1-w: slots 0.., column w:
 // slot = k step + 1), so Z stays in registers across the heads.  The chunk's
 // Gram tiles are the same for every head: they are staged in LDS once per
-// workgroup, so the k steps issue no global loads.  dy, G and H of a head sit
+// workgroup, so the k steps issue no global loads.  dy and G of a head sit
 // in LDS in their natural rows: row reads for the W and state products,
-// transposed reads (XT) of dy for dx.  x is read only by the wave that owns
+// transposed reads (XT) of dy for dx.  (H is loaded for <G, H> only: u is
+// formed in the final phase from the H and dy rows its dC rounds load anyway,
+// which spares the head loop the group's C rows and the u products; at shapes
+// where that would not fit the registers, H is staged and u formed here.)  x is read only by the wave that owns
 // its rows: each wave loads its two column tiles' x rows from memory straight
 // into MFMA operands, in the k-slot order of KPermRow (the W product reads dy
 // in the same order), which is also the order of the dx accumulator's values,
@@ -39,7 +42,8 @@
 // the chunk's C and B rows are staged in turn for the Z products (read
 // transposed), and each
 // head's G and H for its state terms (read transposed); dB is finished before
-// dC starts.
+// dC starts.  The per-token partials of the ddt assembly are -K_j, q_j, v_j
+// and u_j.
 #pragma once
 
 #include "bwd_util.h"
@@ -99,9 +103,15 @@ struct ChunkBwdHB {
         return o;
     }
     static constexpr int cmax(int a, int b) { return a > b ? a : b; }
-    // head loop: dy, G, H of the head, the per-wave row sums and the chunk's
-    // Gram tiles
-    static constexpr int O_D = 0, O_G = Q * XR, O_H = O_G + P * GR, O_RW = O_H + P * GR;
+    // u_t = f_t dy_t . (H C_t) in the final phase's dC rounds, from the H and
+    // dy rows loaded there, where a round's loaded rows take at most two
+    // vectors per thread (every Q = 256 shape); otherwise in the head loop
+    // (the C rows and H beside the u products spill at those shapes)
+    static constexpr bool U_FIN = (P * (N / VEC) + NTH - 1) / NTH <= 2;
+    // head loop: dy, G (and H, for u) of the head, the per-wave row sums and
+    // the chunk's Gram tiles
+    static constexpr int O_D = 0, O_G = Q * XR, O_H = O_G + P * GR;
+    static constexpr int O_RW = O_H + (U_FIN ? 0 : P * GR);
     static constexpr int O_GM = O_RW + NW * Q * 4 / (int)sizeof(T);
     static constexpr int E_HEAD = O_GM + gram_tiles(QT) * 256;
     // final phase: Z rows and C^T (then G of HG heads), later B^T and H
@@ -137,7 +147,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     __shared__ __attribute__((aligned(16))) T U[K::E_U];
     T* const sD = U + K::O_D;                   // dy of the current head [Q][XR]
     T* const sG = U + K::O_G;                   // exit gradient G [P][GR]
-    T* const sH = U + K::O_H;                   // entering state H [P][GR]
+    T* const sH = U + K::O_H;                   // entering state H [P][GR] (u in the head loop)
     float* const s_rw = (float*)(U + K::O_RW);  // per-wave row sums of F [NW][Q]
     T* const sGm = U + K::O_GM;                 // the chunk's Gram tiles (head loop)
     T* const sZ = U;                            // final phase: Z rows, strip per row tile
@@ -190,7 +200,8 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     auto hl_of = [&](int h) { return ((int64_t)b * d.H + h) * d.L + t0; };
     const uint32_t Cu = (uint32_t)d.C;  // token row pitch of xBC (32-bit lane offsets)
 
-    // ---- staging of dy, G and H of one head (registers, then LDS), and the x
+    // ---- staging of dy, G and H of one head (registers, then LDS; H only for
+    // <G, H> unless u is formed in the head loop), and the x
     // rows of the wave's columns j0, j1 (registers, in KPermRow order)
     constexpr int V_X = (Q * (P / VEC) + NTH - 1) / NTH;
     constexpr int V_S = (P * (N / VEC) + NTH - 1) / NTH;
@@ -245,7 +256,7 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
             if (V_S * NTH == P * (N / VEC) || idx < P * (N / VEC)) {
                 const int p = idx / (N / VEC), nv = idx % (N / VEC);
                 *(vt*)&sG[p * GR + nv * VEC] = rg[q];
-                *(vt*)&sH[p * GR + nv * VEC] = rh[q];
+                if constexpr (!K::U_FIN) *(vt*)&sH[p * GR + nv * VEC] = rh[q];
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) gh += (float)rg[q][e] * (float)rh[q][e];
             }
@@ -309,12 +320,15 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
         const int tid = (int)threadIdx.x + opq;
         fetch(h, tid);
         const int lane = tid % 64, lr = lane % 16, lg = lane / 16;
-        // C rows of the wave's two tiles and B rows of tile j1 (state products)
-        Frag cfr[2][KN], bfr[KN];
+        // B rows of tile j1 (its column's state part); C rows of the wave's two
+        // tiles where u is formed here
+        Frag bfr[KN], cfr[2][KN];
 #pragma unroll
         for (int kn = 0; kn < KN; ++kn) {
-            cfr[0][kn] = M::load(xc + (rb + t0 + j0 * 16 + lr) * d.C + coff + kn * KS + SL * lg);
-            cfr[1][kn] = M::load(xc + (rb + t0 + j1 * 16 + lr) * d.C + coff + kn * KS + SL * lg);
+            if constexpr (!K::U_FIN) {
+                cfr[0][kn] = M::load(xc + (rb + t0 + j0 * 16 + lr) * d.C + coff + kn * KS + SL * lg);
+                cfr[1][kn] = M::load(xc + (rb + t0 + j1 * 16 + lr) * d.C + coff + kn * KS + SL * lg);
+            }
             bfr[kn] = M::load(xc + (rb + t0 + j1 * 16 + lr) * d.C + boff + kn * KS + SL * lg);
         }
         __syncthreads();  // the previous head is done with the LDS
@@ -339,10 +353,10 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
         const float Dh = Dp[h];
         float ddp = 0.f;  // dy . x over the wave's tokens
 
-        // u_i = f_i dy_i . (H C_i) for the wave's two tiles as rows
-        // (both tiles from each H fragment read)
-        float u[2];
-        {
+        // u_i = f_i dy_i . (H C_i) for the wave's two tiles as rows, where it is
+        // formed in the head loop (both tiles from each H fragment read)
+        float u[2] = {0.f, 0.f};
+        if constexpr (!K::U_FIN) {
             f32x4 ys[2][PT];
 #pragma unroll
             for (int it = 0; it < 2; ++it)
@@ -490,7 +504,10 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
             const float Kj = sum_groups(kacc);
             if (lg == 0) {
                 float* tp = tokp + (hl + j) * 4;
-                tp[0] = ui - Kj;  // R_j is added by the ddt assembly from the row sums
+                // R_j (row sums) and u_j (the fourth float, from here or the
+                // final phase) are added by the ddt assembly
+                tp[0] = -Kj;
+                if constexpr (!K::U_FIN) tp[3] = ui;
                 tp[1] = qj;
                 tp[2] = vj;
             }
@@ -578,10 +595,23 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     // the state terms of one part over the heads: ab[c] += S^T (scaled rows of
     // tile c), S = G (dB, rows of x scaled by dt g) or H (dC, rows of dy scaled
     // by f); HG heads per round, their S staged at sS as [p][n] rows and read
-    // transposed (XT), the rows in the matching k order
+    // transposed (XT), the rows in the matching k order.  The dC part also
+    // forms u_t = f_t dy_t . (H C_t) of every head for the wave's two tiles as
+    // rows, from the same staged H and loaded dy rows, into the fourth float of
+    // the token's partials (H C_t with H read as rows, the C rows held as
+    // operands: the same for every head).
     constexpr int HG = K::HG;
     constexpr int V_GT = (P * (N / VEC) + NTH - 1) / NTH;
     auto state_terms = [&](bool dB, T* sS, int lane2, int lr2, int lg2) {
+        Frag cfr[2][KN];
+        if (!dB && K::U_FIN) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int kn = 0; kn < KN; ++kn)
+                    cfr[c][kn] = M::load(xc + (rb + t0 + (c == 0 ? j0 : j1) * 16 + lr2) * d.C + coff +
+                                         kn * KS + SL * lg2);
+        }
         for (int hf = 0; hf < hbs; hf += HG) {
             vt rs[HG][V_GT];
             Frag rr[HG][2][KP];
@@ -655,6 +685,36 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
                             const Frag xs = XT<T>::load(sq_, GR, kp * KS, nt * 16, lane2);
                             ab[0][nt] = M::mma(xs, sf[0], ab[0][nt]);
                             ab[1][nt] = M::mma(xs, sf[1], ab[1][nt]);
+                        }
+                    }
+                    if (!dB && K::U_FIN) {
+                        // (both tiles from each H fragment read)
+                        f32x4 ys[2][PT];
+#pragma unroll
+                        for (int c = 0; c < 2; ++c)
+#pragma unroll
+                            for (int pt = 0; pt < PT; ++pt) ys[c][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kn = 0; kn < KN; ++kn)
+#pragma unroll
+                            for (int pt = 0; pt < PT; ++pt) {
+                                const Frag hr = M::load(&sq_[(pt * 16 + lr2) * GR + kn * KS + SL * lg2]);
+                                ys[0][pt] = M::mma(hr, cfr[0][kn], ys[0][pt]);
+                                ys[1][pt] = M::mma(hr, cfr[1][kn], ys[1][pt]);
+                            }
+                        const int64_t hl = hl_of(h0 + hf + q);
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) {
+                            // dy element p = pt 16 + 4 lg2 + r of the row sits in
+                            // slot (pt % TPK) 4 + r of block pt / TPK (KPermRow)
+                            float up = 0.f;
+#pragma unroll
+                            for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    up += (float)rr[q][c][pt / TPK][(pt % TPK) * 4 + r] * ys[c][pt][r];
+                            const float u = sc[q][c] * sum_groups(up);
+                            if (lg2 == 0) tokp[(hl + (c == 0 ? j0 : j1) * 16 + lr2) * 4 + 3] = u;
                         }
                     }
                 }

@@ -98,17 +98,15 @@ __device__ __forceinline__ void ddt_wave(const Dims& d, const SegTab& tab, const
                          dotgh[((int64_t)b * d.nchunk + cm) * d.H + h];
     // every per-token input of the lane's tokens lane*E .. lane*E+E-1 up front
     // (one memory round trip), with the sequence ids of the tokens on either side
-    // (three of tokp's four floats per token: a loaded register that is never
-    // read gets reused at once, and the reuse waits for that load)
-    typedef float f32x3 __attribute__((ext_vector_type(3)));
-    f32x3 tp[4];
+    // (tokp per token: -K, q, v, u)
+    f32x4 tp[4];
     float rp[4], dtr[4], dtw[4];
     int sqv[6];  // sequence ids of tokens lane*E-1 .. lane*E+E
     // (slots e >= E load token lane*E+E-1 again, unused: no branch around the loads)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int t = lane * E + min(e, E - 1);
-        tp[e] = *(const f32x3*)&tokp[(hl + t) * 4];
+        tp[e] = *(const f32x4*)&tokp[(hl + t) * 4];
         rp[e] = rpart[hl + t];
         dtr[e] = (float)dt_raw[(rb + t0 + t) * d.H + h];
         dtw[e] = dt_ws[hl + t];
@@ -133,7 +131,7 @@ __device__ __forceinline__ void ddt_wave(const Dims& d, const SegTab& tab, const
             const bool cut = t < Q - 1 && sq(e + 1) != sq(e);
             if (cut) run = 0.f;
             cut_any = cut_any || cut;
-            const float s = tp[e][0] + rp[e];
+            const float s = tp[e][0] + tp[e][3] + rp[e];
             run += s;
             sl[e] = run;
             rs[e] = cut_any;
