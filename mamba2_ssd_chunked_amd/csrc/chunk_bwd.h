@@ -33,7 +33,8 @@
 // transposed reads (XT) of dy for dx.  (H is loaded for <G, H> only: u is
 // formed in the final phase from the H and dy rows its dC rounds load anyway,
 // which spares the head loop the group's C rows and the u products; at shapes
-// where that would not fit the registers, H is staged and u formed here.)  x is read only by the wave that owns
+// where that would not fit the registers, H is staged and u formed here.)
+// x is read only by the wave that owns
 // its rows: each wave loads its two column tiles' x rows from memory straight
 // into MFMA operands, in the k-slot order of KPermRow (the W product reads dy
 // in the same order), which is also the order of the dx accumulator's values,
