@@ -140,6 +140,9 @@ __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, con
     const int64_t rb = b * d.L;
     const int nck = (int)(tab.len[k] / Q);
     const int64_t s0 = tab.start[k] + (int64_t)jsp * wa.sp.cps * Q;
+    // the walk's first chunk (segment starts are whole chunks): chunk c of the
+    // walk is cm0 + c, without a 64-bit division per chunk in the slice loop
+    const int cm0 = (int)(s0 / Q);
     const int nc = min(wa.sp.cps, nck - jsp * wa.sp.cps);
     const int spc = Q / KT;  // slices per chunk
     const int ns = nc * spc;
@@ -275,21 +278,27 @@ __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, con
     // apply the chunk's decay.
     auto chunk_start = [&](const Slice& r, int si) {
         const int c = chunk_of(si);
-        const int cm = (int)((s0 + (int64_t)c * Q) / Q);
+        const int cm = cm0 + c;
         const float alpha = (r.seqr == r.seqe) ? expf(r.cse) : 0.f;
         ablk *= alpha;
         if (store && (init || BWD || c > 0)) {
             T* hp = store + (((int64_t)b * d.nchunk + cm) * d.H + h) * (P * N);
+            // lane ids from an opaque zero: the stores take the uniform base plus
+            // a 32-bit lane offset recomputed here, instead of a 64-bit per-lane
+            // address held (and spilled) across the slice loop
+            int opq;
+            asm volatile("s_mov_b32 %0, 0" : "=s"(opq));
+            const int l2 = lane + opq, lr2 = l2 % 16, lg2 = l2 / 16;
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
                 for (int j = 0; j < NTW; ++j) {
                     const int nt = wave + 4 * j;
                     if (NFULL || nt < NTT) {
-                        const int n = nt * 16 + lr;
+                        const int n = nt * 16 + lr2;
 #pragma unroll
                         for (int rr = 0; rr < 4; ++rr)
-                            hp[(pt * 16 + 4 * lg + rr) * N + n] = (T)acc[pt][j][rr];
+                            *at32(hp, (uint32_t)((pt * 16 + 4 * lg2 + rr) * N + n)) = (T)acc[pt][j][rr];
                     }
                 }
         }
