@@ -277,10 +277,21 @@ __global__ void __launch_bounds__(Q / 32 * 64, 2) k_chunk_bwd_hb(
     {
         // the chunk's Gram tiles, read by every head's k steps (the first head's
         // barriers order these writes before the first read)
+        // Every load of the thread before the first LDS write: a load followed
+        // by its write in the loop would wait for it before the next is issued.
         const T* gsrc = gramT + cg * (int64_t)gram_tiles(QT) * 256;
-        constexpr int NGV = gram_tiles(QT) * 256 / VEC;
-        for (int idx = threadIdx.x; idx < NGV; idx += NTH)
-            *(vt*)&sGm[idx * VEC] = *(const vt*)(gsrc + (int64_t)idx * VEC);
+        constexpr int NGV = gram_tiles(QT) * 256 / VEC, NGI = (NGV + NTH - 1) / NTH;
+        vt gv[NGI];
+#pragma unroll
+        for (int q = 0; q < NGI; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (NGV % NTH == 0 || idx < NGV) gv[q] = *(const vt*)(gsrc + (int64_t)idx * VEC);
+        }
+#pragma unroll
+        for (int q = 0; q < NGI; ++q) {
+            const int idx = threadIdx.x + q * NTH;
+            if (NGV % NTH == 0 || idx < NGV) *(vt*)&sGm[idx * VEC] = gv[q];
+        }
     }
 
     // The end of head h (parity par), once every wave is past its k steps: the
