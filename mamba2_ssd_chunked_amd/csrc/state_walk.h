@@ -117,7 +117,10 @@ __device__ __forceinline__ void walk_block(const Dims& d, const SegTab& tab, con
     // heads of a block share its B (or C) rows in LDS; threads hs*256 ..
     // hs*256+255 (four waves) walk head h0 + hs.  Span sg is span j of
     // segment k: its chunks j*cps .. of the segment.
-    const int hs = threadIdx.x / HTH;
+    // head of the block this thread works on: whole waves per head (HTH = 256),
+    // so it is the same for the wave; readfirstlane tells the compiler, which
+    // keeps the per-head bases (rows, sums, state stores) in scalar registers
+    const int hs = __builtin_amdgcn_readfirstlane(threadIdx.x / HTH);
     int h, k, sg;
     int64_t b;
     {
